@@ -1,0 +1,130 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching) and
+require that at least one pin catches each of them."""
+import numpy as np
+import pytest
+
+import oracle.mtla as om
+import pins
+
+
+def _mut_group_final_zero(mp):
+    mp.setattr(om, "is_group_final", lambda n, s: n % s == 0)
+
+    def mask(T, s):
+        m = np.arange(T)[:, None]
+        n = np.arange(T)[None, :]
+        return (n == m) | ((n < m) & (n % s == 0))
+    mp.setattr(om, "mask_matrix", mask)
+
+    def cache(Cp, KR, s):
+        T = Cp.shape[0]
+        e = np.array([min(s * j, T - 1) for j in range(om.n_slots(T, s))], dtype=np.int64)
+        return Cp[e].copy(), KR[e].copy(), e
+    mp.setattr(om, "compressed_cache", cache)
+
+
+def _mut_drop_rope(mp):
+    orig = om.prefill
+
+    def prefill(X, QR, KR, W, s, scale):
+        return orig(X, QR * 0.0, KR, W, s, scale)
+    mp.setattr(om, "prefill", prefill)
+
+
+def _mut_transpose_whc(mp):
+    mp.setattr(om, "merge_weight",
+               lambda c, j, W_hc, b_hc, P: om.sigmoid((W_hc.T @ c + b_hc) * P[j]))
+
+
+def _mut_position_by_frame(mp):
+    def fu(x_i, i, W, s):
+        c = om.latent(x_i, W["W_dkv"])
+        w = om.merge_weight(c, min(i, W["P"].shape[0] - 1), W["W_hc"], W["b_hc"], W["P"])
+        return c, w, w * c
+    mp.setattr(om, "frame_update", fu)
+
+
+def _mut_additive_gate(mp):
+    mp.setattr(om, "merge_weight",
+               lambda c, j, W_hc, b_hc, P: om.sigmoid((W_hc @ c + b_hc) + P[j]))
+
+
+def _mut_no_reset(mp):
+    def ma(lat, rk, t, x_t, kr_t, W, s):
+        _, _, u = om.frame_update(x_t, t, W, s)
+        j = om.slot_of(t, s)
+        lat[j] = lat[j] + u          # accumulates even when t opens a new group
+        rk[j] = kr_t
+        return j
+    mp.setattr(om, "merge_append", ma)
+
+
+def _mut_rope_key_first_frame(mp):
+    orig = om.merge_append
+
+    def ma(lat, rk, t, x_t, kr_t, W, s):
+        keep = rk[om.slot_of(t, s)].copy()
+        j = orig(lat, rk, t, x_t, kr_t, W, s)
+        if t % s != 0:
+            rk[j] = keep
+        return j
+    mp.setattr(om, "merge_append", ma)
+
+
+def _mut_plain_prefix_sum(mp):
+    mp.setattr(om, "intermediate_states", lambda U, s: np.cumsum(U, axis=0))
+
+
+def _mut_bvo_transposed(mp):
+    mp.setattr(om, "output_projection", lambda O, Bvo: np.einsum("...hr,rhd->...d", O, Bvo))
+
+
+def _mut_a_transposed(mp):
+    # reads A[h] as if it were stored [d, r] (shape-compatible since d == r)
+    mp.setattr(om, "absorbed_queries", lambda X, A: np.einsum("td,hdr->thr", X, A))
+
+
+def _mut_latent_transposed(mp):
+    mp.setattr(om, "latent", lambda x, W: W.T @ x)
+
+
+def _mut_scale_with_rope_width(mp):
+    orig = om.prefill
+
+    def prefill(X, QR, KR, W, s, scale):
+        return orig(X, QR, KR, W, s, 1.0 / np.sqrt(1.0 / scale ** 2 + KR.shape[1]))
+    mp.setattr(om, "prefill", prefill)
+
+
+def _mut_sigmoid_sign(mp):
+    mp.setattr(om, "sigmoid", lambda x: 1.0 / (1.0 + np.exp(x)))
+
+
+def _mut_decode_excludes_newest(mp):
+    def ds(lat, rk, t, x_t, qr_t, kr_t, W, s, scale):
+        j = om.merge_append(lat, rk, t, x_t, kr_t, W, s)
+        qt = W["A"] @ x_t
+        n = j + 1 if (t % s == s - 1 or j == 0) else j
+        o = om.attend_cache(qt, qr_t, lat[:n], rk[:n], scale)
+        return om.output_projection(o, W["Bvo"]), o
+    mp.setattr(om, "decode_step", ds)
+
+
+MUTANTS = [
+    _mut_group_final_zero, _mut_drop_rope, _mut_transpose_whc, _mut_position_by_frame,
+    _mut_additive_gate, _mut_no_reset, _mut_rope_key_first_frame, _mut_plain_prefix_sum,
+    _mut_bvo_transposed, _mut_a_transposed, _mut_latent_transposed,
+    _mut_scale_with_rope_width, _mut_sigmoid_sign, _mut_decode_excludes_newest,
+]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
+def test_some_pin_catches(mutant, monkeypatch):
+    mutant(monkeypatch)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 - a crash also counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"{mutant.__name__} passed every pin"
