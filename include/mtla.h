@@ -1,0 +1,168 @@
+/*
+ * mtla.h -- C ABI of the Multi-head Temporal Latent Attention (MTLA) hot path
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [Notes] "Multi-head Temporal Latent Attention" paper notes (zhaoyang97
+ *           Paper-Notes, NeurIPS 2025), method section: overall framework,
+ *           key designs (hyper-network temporal merging, stride-aware causal
+ *           mask, decoupled RoPE with temporal compression), hyper-parameters.
+ *   [Fig1]  "Multi-head Temporal Latent Attention" (sciencestack.ai), Figure 1.
+ *   [Fig2]  same page, Figure 2 (a) incremental inference, (c) training.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor argument is a DEVICE pointer to row-major data in the
+ *    storage type named by mtla_dims.dtype (fp32 or bf16), except where a
+ *    parameter says otherwise.  Accumulation is always fp32.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - Linear maps are stored [out, in] (y = x W^T), the nn.Linear layout.
+ *  - The caller owns all memory.  The library never allocates, frees or
+ *    synchronises: every call only enqueues kernels on `stream` (a
+ *    hipStream_t; NULL is the null stream) and returns.  It writes only the
+ *    outputs, the cache rows and the workspace its documentation names.
+ *  - Errors: argument checks run on the host before anything is enqueued.  On
+ *    MTLA_ERR_ARG, MTLA_ERR_CAPACITY or MTLA_ERR_UNSUPPORTED nothing is
+ *    written.  MTLA_ERR_HIP reports a failed launch.  No C++ exception crosses
+ *    this boundary.  mtla_last_error_detail() describes the last failure of
+ *    the calling thread.
+ *  - Frame positions are 0-based.  Frame i belongs to slot floor(i/s); slot j
+ *    is complete once frame s*j + s - 1 has been merged (the pages count from
+ *    1 and call that frame's index a multiple of s).
+ *  - Supported shapes: (r, d_hR) in {(256, 32), (512, 64)} (r = 4 d_h and
+ *    d_hR = d_h/2 for d_h = 64 or 128), H <= 64, d a multiple of 32, s >= 1.
+ *    Other shapes return MTLA_ERR_UNSUPPORTED.
+ *  - Calls on one stream are ordered; calls on different streams that touch
+ *    the same cache or workspace race.
+ */
+#ifndef MTLA_H
+#define MTLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTLA_OK = 0,
+  MTLA_ERR_ARG = 1,          /* bad dimension, null or misaligned pointer */
+  MTLA_ERR_CAPACITY = 2,     /* a position does not fit the cache or gate table */
+  MTLA_ERR_UNSUPPORTED = 3,  /* valid but not implemented shape or dtype */
+  MTLA_ERR_HIP = 4           /* a HIP launch failed */
+} mtla_status;
+
+typedef enum { MTLA_F32 = 0, MTLA_BF16 = 1 } mtla_dtype;
+
+/* Layer dimensions ([Notes] hyper-parameters: r = 4 d_h, d_hR = d_h / 2,
+ * default s = 2). */
+typedef struct {
+  int32_t d;      /* width of an input frame x_i */
+  int32_t H;      /* attention heads */
+  int32_t d_h;    /* head width; only sets the default softmax scale */
+  int32_t r;      /* latent width of c_i and of a cache slot */
+  int32_t d_hR;   /* decoupled-RoPE key width, one key shared by all heads */
+  int32_t s;      /* temporal compression ratio: s frames per cache slot */
+  float scale;    /* softmax scale; 0 selects 1/sqrt(d_h) ([Notes] Y formula) */
+  int32_t dtype;  /* mtla_dtype of all tensor arguments */
+} mtla_dims;
+
+/* Weights of one layer (device pointers, storage dtype unless noted). */
+typedef struct {
+  const void *W_dkv;      /* [r, d]    latent map, c_i = W_dkv x_i ([Notes] overall framework) */
+  const void *W_hc;       /* [r, r]    hyper-network content branch Linear(c_i) ... */
+  const void *b_hc;       /* [r]       ... and its bias ([Notes] temporal merging) */
+  const float *gate_pos;  /* [gate_pos_rows, r] FP32: Linear(pe_j) for slot j, from
+                             mtla_gate_pos_table ([Notes] temporal merging) */
+  int32_t gate_pos_rows;  /* rows of gate_pos; every slot index used must be below it */
+  const void *A;          /* [H, r, d] absorbed query map: A[h] = (W_Q^(h) W_K^(h)T)^T,
+                             q~_h = A[h] x ([Notes] Y formula, [Fig1]) */
+  const void *Bvo;        /* [d, H, r] absorbed output map: Bvo[:, h, :] = (W_V^(h) W_O^(h))^T,
+                             y = sum_h Bvo[:, h, :] o_h ([Notes] Y formula, [Fig1]) */
+} mtla_weights;
+
+/* Compressed cache ([Notes] overall framework: ceil(T/s) slots of r latent
+ * values; decoupled RoPE: one compressed RoPE key per slot).  Slot j of
+ * sequence b starts at element b*batch_stride + j*(r + d_hR): the merged
+ * latent c^_j (r values) followed by the RoPE key k^R_j (d_hR values) of the
+ * newest frame merged into it.  16-byte aligned; batch_stride >=
+ * max_slots*(r + d_hR) and a multiple of 8 elements. */
+typedef struct {
+  void *slots;
+  int64_t batch_stride;   /* elements between consecutive sequences */
+  int32_t max_slots;      /* slots allocated per sequence */
+} mtla_cache;
+
+/* Position branch of the hyper-network, evaluated once into a table
+ * ([Notes] temporal merging: w_i = Sigmoid(Linear(c_i) * Linear(pe_j))):
+ *   table[j, :] = W_hp pe_j + b_hp, fp32, for j < rows.
+ * pe [rows, d_pe] and W_hp [r, d_pe], b_hp [r] in storage dtype; d_pe a
+ * multiple of 32.  table [rows, r] fp32 (device).  Only dims->r and
+ * dims->dtype are read. */
+mtla_status mtla_gate_pos_table(const mtla_dims *dims, const void *pe, int32_t rows, int32_t d_pe,
+                                const void *W_hp, const void *b_hp, float *table, void *stream);
+
+/* Merge-append ([Notes] temporal merging; [Fig2] (a)): for every sequence b
+ * with frame position t = pos[b] and j = floor(t/s):
+ *   c = W_dkv x_t;  w = Sigmoid((W_hc c + b_hc) * gate_pos[j]);  u = w * c
+ *   slot j latent <- u            if t mod s == 0 (t opens slot j)
+ *   slot j latent <- slot j + u   otherwise (accumulated in place)
+ *   slot j RoPE key <- KR_t[b]
+ * X_t [B, d], KR_t [B, d_hR] (already rotated), pos [B] int32 device array.
+ * max_pos: host-side upper bound of every pos[b] (the caller's contract);
+ * floor(max_pos/s) must be < cache->max_slots and < gate_pos_rows
+ * (else MTLA_ERR_CAPACITY).  Workspace: mtla_workspace_bytes(op=0). */
+mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                              const void *X_t, const void *KR_t, const int32_t *pos, int32_t B,
+                              int32_t max_pos, void *workspace, size_t ws_bytes, void *stream);
+
+/* One incremental decoding step ([Notes] stride-aware mask motivation and Y
+ * formula; [Fig2] (a)): mtla_merge_append at pos[b], then for every head h
+ *   q~_h = A[h] x_t
+ *   z_j  = (q~_h . c^_j + QR_t[b, h] . k^R_j) * scale,  j = 0 .. floor(pos[b]/s)
+ *   o_h  = sum_j softmax(z)_j c^_j        (the newest slot may be temporary)
+ *   Y[b] = sum_h Bvo[:, h, :] o_h
+ * QR_t [B, H, d_hR] already rotated; Y [B, d].  Workspace:
+ * mtla_workspace_bytes(op=1). */
+mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                             const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
+                             int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,
+                             void *stream);
+
+/* Parallel (prefill / training-forward) form under the stride-aware causal
+ * mask ([Notes] stride-aware causal mask and decoupled RoPE; [Fig2] (c)), for
+ * frames 0..T-1 of B sequences:
+ *   C'_i = sum over the frames i' of i's group with i' <= i of w_i' * c_i'
+ *   query m sees column n iff n = m, or n < m and n mod s = s - 1
+ *   z = (q~_{m,h} . C'_n + QR[m, h] . KR[n]) * scale over the visible n
+ *   Y[m] = sum_h Bvo[:, h, :] sum_n softmax(z)_n C'_n
+ * X [B, T, d], QR [B, T, H, d_hR], KR [B, T, d_hR] (rotated at positions
+ * 0..T-1), Y [B, T, d].
+ * cache_out (nullable): receives slots 0..ceil(T/s)-1 of every sequence; the
+ *   last one is partial when T mod s != 0, so decoding can continue at t = T.
+ * Cprime_out (nullable): [B, T, r] intermediate states C'.
+ * floor((T-1)/s) must be < gate_pos_rows (and < cache_out->max_slots).
+ * Workspace: mtla_workspace_bytes(op=2, T). */
+mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                                 const void *QR, const void *KR, int32_t B, int32_t T, void *Y,
+                                 const mtla_cache *cache_out, void *Cprime_out, void *workspace,
+                                 size_t ws_bytes, void *stream);
+
+/* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
+ * T_or_max_pos = max_pos) or 2 (prefill, with T_or_max_pos = T).  Returns 0
+ * for invalid arguments.  Pure host function. */
+size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos);
+
+/* Static description of a status code.  Pure host function. */
+const char *mtla_status_string(mtla_status status);
+
+/* Description of the last failure on the calling thread ("" if none).
+ * Pure host function. */
+const char *mtla_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTLA_H */

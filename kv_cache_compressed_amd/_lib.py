@@ -1,0 +1,188 @@
+"""ctypes binding of libmtla.so -- argument marshalling only.
+
+Every function here converts torch tensors to device pointers, passes the
+current HIP stream, calls the C entry point of the same name and raises
+``MtlaError`` on a non-OK status.  No arithmetic of the method happens here;
+when the built library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtla.so")
+
+MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = range(5)
+MTLA_F32, MTLA_BF16 = 0, 1
+OP_MERGE, OP_DECODE, OP_PREFILL = 0, 1, 2
+
+EXPORTED = ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided",
+            "mtla_workspace_bytes", "mtla_status_string", "mtla_last_error_detail")
+
+
+class MtlaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"MTLA status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("d", c_int32), ("H", c_int32), ("d_h", c_int32), ("r", c_int32),
+                ("d_hR", c_int32), ("s", c_int32), ("scale", c_float), ("dtype", c_int32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("W_dkv", c_void_p), ("W_hc", c_void_p), ("b_hc", c_void_p),
+                ("gate_pos", c_void_p), ("gate_pos_rows", c_int32), ("A", c_void_p),
+                ("Bvo", c_void_p)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("slots", c_void_p), ("batch_stride", c_int64), ("max_slots", c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmtla.so (built in-tree by ``kv_cache_compressed_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P = POINTER
+    lib.mtla_gate_pos_table.argtypes = [P(Dims), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p]
+    lib.mtla_merge_append.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
+                                      c_int32, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.mtla_decode_step.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t,
+                                     c_void_p]
+    lib.mtla_prefill_strided.argtypes = [P(Dims), P(Weights), c_void_p, c_void_p, c_void_p,
+                                         c_int32, c_int32, c_void_p, P(Cache), c_void_p, c_void_p,
+                                         c_size_t, c_void_p]
+    for f in ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step",
+              "mtla_prefill_strided"):
+        getattr(lib, f).restype = c_int32
+    lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
+    lib.mtla_workspace_bytes.restype = c_size_t
+    lib.mtla_status_string.argtypes = [c_int32]
+    lib.mtla_status_string.restype = c_char_p
+    lib.mtla_last_error_detail.argtypes = []
+    lib.mtla_last_error_detail.restype = c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != MTLA_OK:
+        lib = load_library()
+        raise MtlaError(status, lib.mtla_status_string(status).decode() + ": "
+                        + lib.mtla_last_error_detail().decode())
+
+
+def _stream() -> c_void_p:
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> c_void_p:
+    if t is None:
+        return c_void_p(None)
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return c_void_p(t.data_ptr())
+
+
+def torch_dtype(code: int):
+    return torch.bfloat16 if code == MTLA_BF16 else torch.float32
+
+
+def make_dims(d, H, d_h, r, d_hR, s, dtype=MTLA_BF16, scale=0.0) -> Dims:
+    return Dims(int(d), int(H), int(d_h), int(r), int(d_hR), int(s), float(scale), int(dtype))
+
+
+def make_weights(W_dkv, W_hc, b_hc, gate_pos, A=None, Bvo=None) -> Weights:
+    """Gather device weight tensors ([out, in] layouts) into the C struct.
+    The tensors must stay alive while the struct is used."""
+    return Weights(_ptr(W_dkv), _ptr(W_hc), _ptr(b_hc), _ptr(gate_pos), int(gate_pos.shape[0]),
+                   _ptr(A), _ptr(Bvo))
+
+
+def make_cache(slots: torch.Tensor) -> Cache:
+    """Cache struct over a [B, max_slots, r + d_hR] tensor."""
+    B, max_slots, row = slots.shape
+    return Cache(_ptr(slots), int(max_slots * row), int(max_slots))
+
+
+def mtla_workspace_bytes(dims: Dims, op: int, B: int, T_or_max_pos: int) -> int:
+    return int(load_library().mtla_workspace_bytes(ctypes.byref(dims), op, B, T_or_max_pos))
+
+
+def mtla_status_string(status: int) -> str:
+    return load_library().mtla_status_string(status).decode()
+
+
+def workspace(dims: Dims, op: int, B: int, T_or_max_pos: int, device="cuda") -> torch.Tensor:
+    n = mtla_workspace_bytes(dims, op, B, T_or_max_pos)
+    if n == 0:
+        raise MtlaError(MTLA_ERR_ARG, "workspace size query rejected the arguments")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mtla_gate_pos_table(dims: Dims, pe, W_hp, b_hp, table=None):
+    rows, d_pe = pe.shape
+    if table is None:
+        table = torch.empty(rows, dims.r, dtype=torch.float32, device=pe.device)
+    _check(load_library().mtla_gate_pos_table(ctypes.byref(dims), _ptr(pe), rows, d_pe, _ptr(W_hp),
+                                              _ptr(b_hp), _ptr(table), _stream()))
+    return table
+
+
+def mtla_merge_append(dims: Dims, w: Weights, cache: Cache, X_t, KR_t, pos, max_pos: int,
+                      ws=None):
+    B = X_t.shape[0]
+    if ws is None:
+        ws = workspace(dims, OP_MERGE, B, max_pos, X_t.device)
+    _check(load_library().mtla_merge_append(ctypes.byref(dims), ctypes.byref(w),
+                                            ctypes.byref(cache), _ptr(X_t), _ptr(KR_t), _ptr(pos),
+                                            B, int(max_pos), _ptr(ws), ws.numel(), _stream()))
+
+
+def mtla_decode_step(dims: Dims, w: Weights, cache: Cache, X_t, QR_t, KR_t, pos, max_pos: int,
+                     Y=None, ws=None):
+    B = X_t.shape[0]
+    if Y is None:
+        Y = torch.empty(B, dims.d, dtype=X_t.dtype, device=X_t.device)
+    if ws is None:
+        ws = workspace(dims, OP_DECODE, B, max_pos, X_t.device)
+    _check(load_library().mtla_decode_step(ctypes.byref(dims), ctypes.byref(w),
+                                           ctypes.byref(cache), _ptr(X_t), _ptr(QR_t), _ptr(KR_t),
+                                           _ptr(pos), B, int(max_pos), _ptr(Y), _ptr(ws),
+                                           ws.numel(), _stream()))
+    return Y
+
+
+def mtla_prefill_strided(dims: Dims, w: Weights, X, QR, KR, Y=None, cache: Cache | None = None,
+                         Cprime=None, ws=None):
+    B, T = X.shape[0], X.shape[1]
+    if Y is None:
+        Y = torch.empty(B, T, dims.d, dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(dims, OP_PREFILL, B, T, X.device)
+    cptr = ctypes.byref(cache) if cache is not None else None
+    _check(load_library().mtla_prefill_strided(ctypes.byref(dims), ctypes.byref(w), _ptr(X),
+                                               _ptr(QR), _ptr(KR), B, T, _ptr(Y), cptr,
+                                               _ptr(Cprime), _ptr(ws), ws.numel(), _stream()))
+    return Y
+
+
+def n_slots(T: int, s: int) -> int:
+    return math.ceil(T / s)

@@ -1,0 +1,331 @@
+// C ABI of the MTLA hot path: host-side argument checks, workspace layout and
+// the launch sequence of each entry point.  Declarations and their contracts
+// are in include/mtla.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/mtla.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+mtla_status fail(mtla_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mtla_status ok() {
+  g_detail[0] = '\0';
+  return MTLA_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int esize(const mtla_dims *d) { return d->dtype == MTLA_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+float eff_scale(const mtla_dims *d) {
+  return d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)d->d_h);
+}
+
+mtla_status check_dims(const mtla_dims *d) {
+  if (!d) return fail(MTLA_ERR_ARG, "dims is null");
+  if (d->dtype != MTLA_F32 && d->dtype != MTLA_BF16) return fail(MTLA_ERR_ARG, "dtype %d", d->dtype);
+  if (d->d <= 0 || d->H <= 0 || d->d_h <= 0 || d->r <= 0 || d->d_hR <= 0)
+    return fail(MTLA_ERR_ARG, "non-positive dimension (d=%d H=%d d_h=%d r=%d d_hR=%d)", d->d, d->H,
+                d->d_h, d->r, d->d_hR);
+  if (d->s < 1) return fail(MTLA_ERR_ARG, "stride s=%d < 1", d->s);
+  if (!(d->scale >= 0.0f) || isinf(d->scale)) return fail(MTLA_ERR_ARG, "scale must be finite and >= 0");
+  if (d->d % 32 != 0) return fail(MTLA_ERR_UNSUPPORTED, "d=%d is not a multiple of 32", d->d);
+  if (!((d->r == 256 && d->d_hR == 32) || (d->r == 512 && d->d_hR == 64)))
+    return fail(MTLA_ERR_UNSUPPORTED, "(r, d_hR) = (%d, %d) not in {(256,32), (512,64)}", d->r,
+                d->d_hR);
+  if (d->H > 64) return fail(MTLA_ERR_UNSUPPORTED, "H=%d > 64", d->H);
+  return MTLA_OK;
+}
+
+#define CHECK_PTR(p)                                                     \
+  do {                                                                   \
+    if (!(p)) return fail(MTLA_ERR_ARG, "%s is null", #p);               \
+    if (!aligned16(p)) return fail(MTLA_ERR_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+mtla_status check_weights(const mtla_weights *w, bool need_attn) {
+  if (!w) return fail(MTLA_ERR_ARG, "weights is null");
+  CHECK_PTR(w->W_dkv);
+  CHECK_PTR(w->W_hc);
+  CHECK_PTR(w->b_hc);
+  CHECK_PTR(w->gate_pos);
+  if (w->gate_pos_rows <= 0) return fail(MTLA_ERR_ARG, "gate_pos_rows=%d", w->gate_pos_rows);
+  if (need_attn) {
+    CHECK_PTR(w->A);
+    CHECK_PTR(w->Bvo);
+  }
+  return MTLA_OK;
+}
+
+mtla_status check_cache(const mtla_dims *d, const mtla_cache *c) {
+  if (!c) return fail(MTLA_ERR_ARG, "cache is null");
+  CHECK_PTR(c->slots);
+  if (c->max_slots <= 0) return fail(MTLA_ERR_ARG, "max_slots=%d", c->max_slots);
+  const int64_t row = d->r + d->d_hR;
+  if (c->batch_stride < (int64_t)c->max_slots * row)
+    return fail(MTLA_ERR_ARG, "batch_stride %lld < max_slots*(r+d_hR)", (long long)c->batch_stride);
+  if ((c->batch_stride * esize(d)) % 16 != 0)
+    return fail(MTLA_ERR_ARG, "batch_stride is not a multiple of 16 bytes");
+  return MTLA_OK;
+}
+
+mtla_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MTLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MTLA_OK;
+}
+
+#define LAUNCH(expr, what)                              \
+  do {                                                  \
+    mtla_status st_ = launched((expr), what);           \
+    if (st_ != MTLA_OK) return st_;                     \
+  } while (0)
+
+struct DecodeWs {
+  size_t c_f32, c_T, qt, part_o, part_ml, o, total;
+};
+
+DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
+  DecodeWs w;
+  const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r;
+  size_t off = 0;
+  w.c_f32 = off; off += align_up(B * r * 4);
+  w.c_T = off;   off += align_up(B * r * e);
+  if (plan) {
+    w.qt = off;      off += align_up(B * HR * e);
+    w.part_o = off;  off += align_up((size_t)B * plan->splits * HR * 4);
+    w.part_ml = off; off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
+    w.o = off;       off += align_up(B * HR * e);
+  } else {
+    w.qt = w.part_o = w.part_ml = w.o = 0;
+  }
+  w.total = off;
+  return w;
+}
+
+struct PrefillWs {
+  size_t c_f32, c_T, U, Cp, keys, qt, O, total;
+  int64_t keys_stride;
+};
+
+PrefillWs prefill_ws(const mtla_dims *d, int B, int T) {
+  PrefillWs w;
+  const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r, M = (size_t)B * T;
+  const int64_t nS = (T + d->s - 1) / d->s;
+  w.keys_stride = nS * (d->r + d->d_hR);
+  size_t off = 0;
+  w.c_f32 = off; off += align_up(M * r * 4);
+  w.c_T = off;   off += align_up(M * r * e);
+  w.U = off;     off += align_up(M * r * 4);
+  w.Cp = off;    off += align_up(M * r * e);
+  w.keys = off;  off += align_up((size_t)B * w.keys_stride * e);
+  w.qt = off;    off += align_up(M * HR * e);
+  w.O = off;     off += align_up(M * HR * e);
+  w.total = off;
+  return w;
+}
+
+mtla_status check_positions(const mtla_dims *d, const mtla_weights *w, const mtla_cache *c, int B,
+                            int max_pos) {
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (max_pos < 0) return fail(MTLA_ERR_ARG, "max_pos=%d < 0", max_pos);
+  const int jmax = max_pos / d->s;
+  if (jmax >= c->max_slots)
+    return fail(MTLA_ERR_CAPACITY, "slot %d (max_pos %d) >= max_slots %d", jmax, max_pos,
+                c->max_slots);
+  if (jmax >= w->gate_pos_rows)
+    return fail(MTLA_ERR_CAPACITY, "slot %d (max_pos %d) >= gate_pos_rows %d", jmax, max_pos,
+                w->gate_pos_rows);
+  return MTLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mtla_status_string(mtla_status s) {
+  switch (s) {
+    case MTLA_OK: return "ok";
+    case MTLA_ERR_ARG: return "invalid argument";
+    case MTLA_ERR_CAPACITY: return "position exceeds cache or gate-table capacity";
+    case MTLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MTLA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char *mtla_last_error_detail(void) { return g_detail; }
+
+size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos) {
+  if (check_dims(dims) != MTLA_OK || B < 1 || T_or_max_pos < 0) return 0;
+  if (op == 0) return decode_ws(dims, B, nullptr).total;
+  if (op == 1) {
+    mtla::DecodePlan plan;
+    if (!mtla::decode_plan(dims->dtype, dims->H, dims->r, dims->d_hR, dims->s, B, T_or_max_pos, &plan))
+      return 0;
+    return decode_ws(dims, B, &plan).total;
+  }
+  if (op == 2) {
+    if (T_or_max_pos < 1) return 0;
+    return prefill_ws(dims, B, T_or_max_pos).total;
+  }
+  return 0;
+}
+
+mtla_status mtla_gate_pos_table(const mtla_dims *dims, const void *pe, int32_t rows, int32_t d_pe,
+                                const void *W_hp, const void *b_hp, float *table, void *stream) {
+  if (!dims) return fail(MTLA_ERR_ARG, "dims is null");
+  if (dims->dtype != MTLA_F32 && dims->dtype != MTLA_BF16) return fail(MTLA_ERR_ARG, "dtype");
+  if (dims->r <= 0 || rows <= 0 || d_pe <= 0) return fail(MTLA_ERR_ARG, "r, rows and d_pe must be > 0");
+  if (d_pe % 32 != 0) return fail(MTLA_ERR_UNSUPPORTED, "d_pe=%d is not a multiple of 32", d_pe);
+  CHECK_PTR(pe);
+  CHECK_PTR(W_hp);
+  CHECK_PTR(b_hp);
+  CHECK_PTR(table);
+  LAUNCH(mtla::launch_pos_table(dims->dtype, pe, rows, d_pe, W_hp, b_hp, dims->r, table,
+                                (hipStream_t)stream),
+         "gate position table");
+  return ok();
+}
+
+mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                              const void *X_t, const void *KR_t, const int32_t *pos, int32_t B,
+                              int32_t max_pos, void *workspace, size_t ws_bytes, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if ((st = check_weights(w, false)) != MTLA_OK) return st;
+  if ((st = check_cache(dims, cache)) != MTLA_OK) return st;
+  CHECK_PTR(X_t);
+  CHECK_PTR(KR_t);
+  CHECK_PTR(pos);
+  CHECK_PTR(workspace);
+  if ((st = check_positions(dims, w, cache, B, max_pos)) != MTLA_OK) return st;
+  const DecodeWs ws = decode_ws(dims, B, nullptr);
+  if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  float *c_f32 = (float *)(base + ws.c_f32);
+  void *c_T = base + ws.c_T;
+  LAUNCH(mtla::launch_latent_query(dims->dtype, X_t, B, dims->d, w->W_dkv, dims->r, nullptr, 0,
+                                   c_f32, c_T, nullptr, s),
+         "latent projection");
+  LAUNCH(mtla::launch_gate_merge(dims->dtype, c_T, c_f32, B, dims->r, dims->d_hR, w->W_hc, w->b_hc,
+                                 w->gate_pos, pos, dims->s, cache->slots, cache->batch_stride, KR_t,
+                                 s),
+         "gate and merge");
+  return ok();
+}
+
+mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                             const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
+                             int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,
+                             void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if ((st = check_weights(w, true)) != MTLA_OK) return st;
+  if ((st = check_cache(dims, cache)) != MTLA_OK) return st;
+  CHECK_PTR(X_t);
+  CHECK_PTR(QR_t);
+  CHECK_PTR(KR_t);
+  CHECK_PTR(pos);
+  CHECK_PTR(Y);
+  CHECK_PTR(workspace);
+  if ((st = check_positions(dims, w, cache, B, max_pos)) != MTLA_OK) return st;
+  mtla::DecodePlan plan;
+  if (!mtla::decode_plan(dims->dtype, dims->H, dims->r, dims->d_hR, dims->s, B, max_pos, &plan))
+    return fail(MTLA_ERR_UNSUPPORTED, "no decode plan for this shape");
+  const DecodeWs ws = decode_ws(dims, B, &plan);
+  if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  float *c_f32 = (float *)(base + ws.c_f32);
+  void *c_T = base + ws.c_T, *qt = base + ws.qt, *o = base + ws.o;
+  float *part_o = (float *)(base + ws.part_o), *part_ml = (float *)(base + ws.part_ml);
+  const int HR = dims->H * dims->r;
+  LAUNCH(mtla::launch_latent_query(dims->dtype, X_t, B, dims->d, w->W_dkv, dims->r, w->A, HR, c_f32,
+                                   c_T, qt, s),
+         "latent and query projection");
+  LAUNCH(mtla::launch_gate_merge(dims->dtype, c_T, c_f32, B, dims->r, dims->d_hR, w->W_hc, w->b_hc,
+                                 w->gate_pos, pos, dims->s, cache->slots, cache->batch_stride, KR_t,
+                                 s),
+         "gate and merge");
+  LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
+                                       eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
+                                       QR_t, part_o, part_ml, s),
+         "decode attention");
+  LAUNCH(mtla::launch_decode_combine(dims->dtype, plan, B, dims->H, dims->r, dims->s, pos, part_o,
+                                     part_ml, o, s),
+         "split combine");
+  LAUNCH(mtla::launch_gemm_store(dims->dtype, o, HR, w->Bvo, HR, B, dims->d, HR, Y, dims->d, s),
+         "output projection");
+  return ok();
+}
+
+mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                                 const void *QR, const void *KR, int32_t B, int32_t T, void *Y,
+                                 const mtla_cache *cache_out, void *Cprime_out, void *workspace,
+                                 size_t ws_bytes, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if ((st = check_weights(w, true)) != MTLA_OK) return st;
+  CHECK_PTR(X);
+  CHECK_PTR(QR);
+  CHECK_PTR(KR);
+  CHECK_PTR(Y);
+  CHECK_PTR(workspace);
+  if (Cprime_out && !aligned16(Cprime_out)) return fail(MTLA_ERR_ARG, "Cprime_out is not 16-byte aligned");
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (T < 1) return fail(MTLA_ERR_ARG, "T=%d < 1", T);
+  if ((int64_t)B * T * dims->H > 0x7fffffffLL / 4)
+    return fail(MTLA_ERR_UNSUPPORTED, "B*T*H too large");
+  const int nS = (T + dims->s - 1) / dims->s;
+  if ((T - 1) / dims->s >= w->gate_pos_rows)
+    return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
+  if (cache_out) {
+    if ((st = check_cache(dims, cache_out)) != MTLA_OK) return st;
+    if (nS > cache_out->max_slots)
+      return fail(MTLA_ERR_CAPACITY, "ceil(T/s)=%d > max_slots %d", nS, cache_out->max_slots);
+  }
+  if (!mtla::prefill_attention_supported(dims->dtype, dims->H, dims->r, dims->d_hR))
+    return fail(MTLA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
+  const PrefillWs ws = prefill_ws(dims, B, T);
+  if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  float *c_f32 = (float *)(base + ws.c_f32), *U = (float *)(base + ws.U);
+  void *c_T = base + ws.c_T, *keys = base + ws.keys, *qt = base + ws.qt, *O = base + ws.O;
+  void *Cp = Cprime_out ? Cprime_out : (void *)(base + ws.Cp);
+  const int M = B * T, HR = dims->H * dims->r;
+  LAUNCH(mtla::launch_latent_query(dims->dtype, X, M, dims->d, w->W_dkv, dims->r, w->A, HR, c_f32,
+                                   c_T, qt, s),
+         "latent and query projection");
+  LAUNCH(mtla::launch_gate_prefill(dims->dtype, c_T, c_f32, M, dims->r, w->W_hc, w->b_hc,
+                                   w->gate_pos, T, dims->s, U, s),
+         "gate");
+  LAUNCH(mtla::launch_group_scan(dims->dtype, U, KR, B, T, dims->r, dims->d_hR, dims->s, Cp, keys,
+                                 ws.keys_stride, cache_out ? cache_out->slots : nullptr,
+                                 cache_out ? cache_out->batch_stride : 0, s),
+         "group scan");
+  LAUNCH(mtla::launch_prefill_attention(dims->dtype, B, T, dims->H, dims->r, dims->d_hR, dims->s,
+                                        eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s),
+         "strided attention");
+  LAUNCH(mtla::launch_gemm_store(dims->dtype, O, HR, w->Bvo, HR, M, dims->d, HR, Y, dims->d, s),
+         "output projection");
+  return ok();
+}
+
+}  // extern "C"

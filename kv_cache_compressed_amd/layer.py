@@ -1,0 +1,64 @@
+"""Convenience container for one MTLA layer on the GPU.
+
+Holds the device weights in the layouts the C ABI takes, the fp32
+position-branch table (built once on the GPU by mtla_gate_pos_table) and
+reusable workspaces, and forwards to the three hot-path entry points.  It
+only marshals arguments; all arithmetic runs in libmtla.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MTLALayer:
+    WEIGHTS = ("W_dkv", "W_hc", "b_hc", "W_hp", "b_hp", "pe", "A", "Bvo")
+
+    def __init__(self, d, H, d_h, r, d_hR, s, dtype=L.MTLA_BF16, scale=0.0, *, W_dkv, W_hc, b_hc,
+                 W_hp, b_hp, pe, A, Bvo):
+        self.dims = L.make_dims(d, H, d_h, r, d_hR, s, dtype, scale)
+        self.dtype = L.torch_dtype(dtype)
+        self.t = dict(W_dkv=W_dkv, W_hc=W_hc, b_hc=b_hc, W_hp=W_hp, b_hp=b_hp, pe=pe, A=A, Bvo=Bvo)
+        for k, v in self.t.items():
+            if v.dtype != self.dtype or not v.is_cuda or not v.is_contiguous():
+                raise ValueError(f"{k} must be a contiguous device tensor of {self.dtype}")
+        self.gate_pos = L.mtla_gate_pos_table(self.dims, pe, W_hp, b_hp)
+        self.w = L.make_weights(W_dkv, W_hc, b_hc, self.gate_pos, A, Bvo)
+        self._ws = {}
+
+    @classmethod
+    def from_arrays(cls, dims, arrays: dict, dtype=L.MTLA_BF16, device="cuda", scale=0.0):
+        """Upload a dict of host arrays (numpy or torch) holding the weights in
+        the ABI layouts.  ``dims`` has attributes d, H, d_h, r, d_hR, s."""
+        td = L.torch_dtype(dtype)
+        t = {k: torch.as_tensor(arrays[k]).to(td).to(device).contiguous() for k in cls.WEIGHTS}
+        return cls(dims.d, dims.H, dims.d_h, dims.r, dims.d_hR, dims.s, dtype, scale, **t)
+
+    @property
+    def row(self) -> int:
+        return self.dims.r + self.dims.d_hR
+
+    def new_cache(self, B: int, max_slots: int, fill: float = 0.0) -> torch.Tensor:
+        return torch.full((B, max_slots, self.row), fill, dtype=self.dtype, device="cuda")
+
+    def workspace(self, op: int, B: int, n: int) -> torch.Tensor:
+        need = L.mtla_workspace_bytes(self.dims, op, B, n)
+        ws = self._ws.get(op)
+        if ws is None or ws.numel() < need:
+            ws = L.workspace(self.dims, op, B, n)
+            self._ws[op] = ws
+        return ws
+
+    def merge_append(self, cache: torch.Tensor, X_t, KR_t, pos, max_pos: int):
+        L.mtla_merge_append(self.dims, self.w, L.make_cache(cache), X_t, KR_t, pos, max_pos,
+                            self.workspace(L.OP_MERGE, X_t.shape[0], max_pos))
+
+    def decode_step(self, cache: torch.Tensor, X_t, QR_t, KR_t, pos, max_pos: int, Y=None):
+        return L.mtla_decode_step(self.dims, self.w, L.make_cache(cache), X_t, QR_t, KR_t, pos,
+                                  max_pos, Y, self.workspace(L.OP_DECODE, X_t.shape[0], max_pos))
+
+    def prefill(self, X, QR, KR, Y=None, cache: torch.Tensor | None = None, Cprime=None):
+        c = L.make_cache(cache) if cache is not None else None
+        return L.mtla_prefill_strided(self.dims, self.w, X, QR, KR, Y, c, Cprime,
+                                      self.workspace(L.OP_PREFILL, X.shape[0], X.shape[1]))

@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before touching
+the GPU.  No kernel is launched here (no GPU needed): every call below fails
+validation, which runs before any HIP call, and the pointers passed are never
+dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_compressed_amd as K
+from kv_cache_compressed_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtla.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_hot_path_calls():
+    syms = declared_symbols()
+    for s in ("mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load_library()
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    assert sorted(L.EXPORTED) == declared_symbols()
+
+
+def test_status_strings():
+    for code in range(5):
+        assert K.mtla_status_string(code)
+    assert "capacity" in K.mtla_status_string(L.MTLA_ERR_CAPACITY)
+
+
+def _dims(**kw):
+    base = dict(d=512, H=8, d_h=64, r=256, d_hR=32, s=2, dtype=L.MTLA_BF16)
+    base.update(kw)
+    return K.make_dims(**base)
+
+
+def test_workspace_sizes():
+    d = _dims()
+    merge = K.mtla_workspace_bytes(d, L.OP_MERGE, 32, 2047)
+    dec = K.mtla_workspace_bytes(d, L.OP_DECODE, 32, 2047)
+    pre = K.mtla_workspace_bytes(d, L.OP_PREFILL, 16, 4096)
+    assert 0 < merge < dec
+    # prefill holds at least the absorbed queries and the attention output
+    assert pre >= 2 * 16 * 4096 * 8 * 256 * 2
+    assert K.mtla_workspace_bytes(_dims(s=0), L.OP_DECODE, 32, 2047) == 0
+    assert K.mtla_workspace_bytes(_dims(r=128, d_hR=16), L.OP_DECODE, 32, 2047) == 0
+    assert K.mtla_workspace_bytes(d, 7, 32, 2047) == 0
+    # fp32 storage doubles the element size of the cache-typed buffers
+    assert K.mtla_workspace_bytes(_dims(dtype=L.MTLA_F32), L.OP_PREFILL, 1, 64) > \
+        K.mtla_workspace_bytes(_dims(), L.OP_PREFILL, 1, 64)
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _weights(rows=1024, A=FAKE, misalign=0):
+    return L.Weights(FAKE + misalign, FAKE, FAKE, FAKE, rows, A, FAKE)
+
+
+def _decode(dims, w, cache, B=32, max_pos=2047, ws_bytes=1 << 30, pos=FAKE):
+    lib = K.load_library()
+    return lib.mtla_decode_step(ctypes.byref(dims) if dims is not None else None, ctypes.byref(w),
+                                ctypes.byref(cache), FAKE, FAKE, FAKE, pos, B, max_pos, FAKE, FAKE,
+                                ws_bytes, None)
+
+
+def _cache(max_slots=1024, stride=None):
+    return L.Cache(FAKE, stride if stride is not None else max_slots * 288, max_slots)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_dims", L.MTLA_ERR_ARG),
+    ("s_zero", L.MTLA_ERR_ARG),
+    ("negative_r", L.MTLA_ERR_ARG),
+    ("bad_dtype", L.MTLA_ERR_ARG),
+    ("unsupported_r", L.MTLA_ERR_UNSUPPORTED),
+    ("d_not_multiple_of_32", L.MTLA_ERR_UNSUPPORTED),
+    ("too_many_heads", L.MTLA_ERR_UNSUPPORTED),
+    ("misaligned_weight", L.MTLA_ERR_ARG),
+    ("null_pos", L.MTLA_ERR_ARG),
+    ("null_A", L.MTLA_ERR_ARG),
+    ("short_batch_stride", L.MTLA_ERR_ARG),
+    ("capacity_slots", L.MTLA_ERR_CAPACITY),
+    ("capacity_gate_table", L.MTLA_ERR_CAPACITY),
+    ("small_workspace", L.MTLA_ERR_ARG),
+    ("zero_batch", L.MTLA_ERR_ARG),
+])
+def test_decode_rejects(case, expect):
+    dims, w, cache = _dims(), _weights(), _cache()
+    kw = {}
+    if case == "null_dims":
+        dims = None
+    elif case == "s_zero":
+        dims = _dims(s=0)
+    elif case == "negative_r":
+        dims = _dims(r=-1)
+    elif case == "bad_dtype":
+        dims = _dims(dtype=9)
+    elif case == "unsupported_r":
+        dims = _dims(r=128, d_hR=16)
+    elif case == "d_not_multiple_of_32":
+        dims = _dims(d=500)
+    elif case == "too_many_heads":
+        dims = _dims(H=65)
+    elif case == "misaligned_weight":
+        w = _weights(misalign=2)
+    elif case == "null_pos":
+        kw["pos"] = None
+    elif case == "null_A":
+        w = _weights(A=None)
+    elif case == "short_batch_stride":
+        cache = _cache(stride=1024 * 288 - 8)
+    elif case == "capacity_slots":
+        kw["max_pos"] = 2 * 1024        # slot 1024 == max_slots
+    elif case == "capacity_gate_table":
+        w = _weights(rows=100)
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 1024
+    elif case == "zero_batch":
+        kw["B"] = 0
+    st = _decode(dims, w, cache, **kw)
+    assert st == expect, (case, st, K.load_library().mtla_last_error_detail())
+    assert K.load_library().mtla_last_error_detail()
+
+
+def test_prefill_and_merge_reject_before_launch():
+    lib = K.load_library()
+    d, w = _dims(), _weights(rows=8)
+    # T = 64 frames need slot 31 < gate_pos_rows = 8: capacity error
+    st = lib.mtla_prefill_strided(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, 1, 64, FAKE,
+                                  None, None, FAKE, 1 << 30, None)
+    assert st == L.MTLA_ERR_CAPACITY
+    st = lib.mtla_prefill_strided(ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 1,
+                                  0, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == L.MTLA_ERR_ARG
+    small = _cache(max_slots=16)
+    st = lib.mtla_prefill_strided(ctypes.byref(d), ctypes.byref(_weights()), FAKE, FAKE, FAKE, 1,
+                                  64, FAKE, ctypes.byref(small), None, FAKE, 1 << 30, None)
+    assert st == L.MTLA_ERR_CAPACITY
+    st = lib.mtla_merge_append(ctypes.byref(_dims(s=0)), ctypes.byref(_weights()),
+                               ctypes.byref(_cache()), FAKE, FAKE, FAKE, 4, 10, FAKE, 1 << 20, None)
+    assert st == L.MTLA_ERR_ARG
+    st = lib.mtla_gate_pos_table(ctypes.byref(d), FAKE, 16, 500, FAKE, FAKE, FAKE, None)
+    assert st == L.MTLA_ERR_UNSUPPORTED

@@ -1,0 +1,137 @@
+"""GPU parity of mtla_prefill_strided against the oracle's masked parallel
+form, and prefill -> decode hand-off."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.mtla as om
+import synth
+from synth import Dims
+from gpu_util import TOL, dev, host, layer, needs_gpu, relerr, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill_case(dims, B, T, storage, seed, with_cache=True):
+    ms = om.n_slots(T, dims.s) + 3
+    w, W, L = layer(dims, seed, storage, pe_rows=ms)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, storage)
+    cache = L.new_cache(B, ms, fill=float("nan")) if with_cache else None
+    Cp = torch.empty(B, T, dims.r, dtype=L.dtype, device="cuda")
+    Y = L.prefill(dev(seq["X"], storage), dev(seq["QR"], storage), dev(seq["KR"], storage),
+                  cache=cache, Cprime=Cp)
+    torch.cuda.synchronize()
+    Yg, Cpg = host(Y), host(Cp)
+    cg = host(cache) if with_cache else None
+    n = om.n_slots(T, dims.s)
+    for b in range(B):
+        ref = om.prefill(seq["X"][b], seq["QR"][b], seq["KR"][b], W, dims.s, dims.scale)
+        ey, ec = relerr(Yg[b], ref["Y"]), relerr(Cpg[b], ref["Cp"])
+        say(f"  b={b} Y relerr {ey:.3g}  C' relerr {ec:.3g}")
+        assert ey < TOL[storage], (b, ey)
+        assert ec < TOL[storage], (b, ec)
+        if with_cache:
+            assert relerr(cg[b, :n, :dims.r], ref["cache_lat"]) < TOL[storage]
+            assert np.array_equal(cg[b, :n, dims.r:], ref["cache_rope"])
+            assert np.all(np.isnan(cg[b, n:]))
+            # the cache rows are the group-final states, bit for bit
+            e = np.minimum(np.arange(n) * dims.s + dims.s - 1, T - 1)
+            assert np.array_equal(cg[b, :n, :dims.r], Cpg[b, e])
+    return Yg
+
+
+def test_tiny_fp32():
+    needs_gpu()
+    name, dims, ex = synth.config(1)
+    say("prefill", name)
+    _prefill_case(dims, ex["B"], ex["T"], "f32", synth.seed_for(1))
+
+
+@pytest.mark.parametrize("s,T", [(1, 40), (2, 1), (2, 129), (3, 67), (4, 5), (5, 200), (80, 64)])
+def test_fp32_strides_and_ragged_lengths(s, T):
+    needs_gpu()
+    dims = Dims(d=256, H=4, d_h=64, r=256, d_hR=32, s=s)
+    say("prefill fp32", s, T)
+    _prefill_case(dims, 2, T, "f32", 8000 + s * 7 + T)
+
+
+@pytest.mark.parametrize("s,T,H", [(2, 300, 8), (3, 250, 8), (2, 97, 16), (4, 160, 32), (2, 64, 3)])
+def test_bf16_multi_sequence(s, T, H):
+    needs_gpu()
+    dims = Dims(d=512, H=H, d_h=64, r=256, d_hR=32, s=s)
+    say("prefill bf16", s, T, H)
+    _prefill_case(dims, 3, T, "bf16", 8100 + s + T + H)
+
+
+def test_bf16_wide_latent():
+    needs_gpu()
+    dims = Dims(d=256, H=8, d_h=128, r=512, d_hR=64, s=2)
+    say("prefill r=512")
+    _prefill_case(dims, 2, 150, "bf16", 8200)
+
+
+def test_full_size_prefill_sampled():
+    """The benchmark's prefill launch (B=16, T=4096, s=2), checked on sampled
+    sequences and rows: intermediate states and cache in full, outputs on
+    sampled rows computed one by one from the oracle's visible sets."""
+    needs_gpu()
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    say("prefill", name, "inputs")
+    ms = om.n_slots(T, dims.s)
+    w, W, L = layer(dims, synth.seed_for(4), "bf16", pe_rows=ms)
+    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    cache = L.new_cache(B, ms)
+    Cp = torch.empty(B, T, dims.r, dtype=torch.bfloat16, device="cuda")
+    say("prefill", name, "running")
+    Y = L.prefill(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16"),
+                  cache=cache, Cprime=Cp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    for b in (0, 9, 15):
+        X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
+        _, U = om.gated_latents(X, W, dims.s)
+        Cpr = om.intermediate_states(U, dims.s)
+        lat, rk, _ = om.compressed_cache(Cpr, KR, dims.s)
+        Cpg = host(Cp[b])
+        assert relerr(Cpg, Cpr) < TOL["bf16"]
+        cg = host(cache[b])
+        assert relerr(cg[:, :dims.r], lat) < TOL["bf16"]
+        assert np.array_equal(cg[:, dims.r:], rk)
+        rows = sorted(set([0, 1, 2, 3, T - 2, T - 1] + list(rng.integers(0, T, size=40))))
+        Yg = host(Y[b, rows])
+        Yr = []
+        for m in rows:
+            vis = [n for n in range(m + 1) if om.visible(m, n, dims.s)]
+            qt = W["A"] @ X[m]
+            o = om.attend_cache(qt, QR[m], Cpr[vis], KR[vis], dims.scale)
+            Yr.append(om.output_projection(o, W["Bvo"]))
+        e = relerr(Yg, np.stack(Yr))
+        say(f"  b={b} sampled-row relerr {e:.3g}")
+        assert e < TOL["bf16"]
+
+
+def test_prefill_then_decode_resumes():
+    """Prefill ends inside a group (T mod s != 0); decoding continues from the
+    partial slot and matches decoding every frame from the start."""
+    needs_gpu()
+    dims = Dims(d=512, H=8, d_h=64, r=256, d_hR=32, s=4)
+    T0, T = 37, 46
+    ms = om.n_slots(T, dims.s) + 2
+    w, W, L = layer(dims, 8300, "bf16", pe_rows=ms)
+    seq = synth.make_sequence(dims, w, 2, T, 8301, "bf16")
+    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
+    cache = L.new_cache(2, ms, fill=float("nan"))
+    L.prefill(X[:, :T0].contiguous(), QR[:, :T0].contiguous(), KR[:, :T0].contiguous(), cache=cache)
+    ys = []
+    for t in range(T0, T):
+        pos = torch.full((2,), t, dtype=torch.int32, device="cuda")
+        ys.append(L.decode_step(cache, X[:, t].contiguous(), QR[:, t].contiguous(),
+                                KR[:, t].contiguous(), pos, t).clone())
+    torch.cuda.synchronize()
+    for b in range(2):
+        ref = om.decode_sequence(seq["X"][b], seq["QR"][b], seq["KR"][b], W, dims.s, dims.scale)
+        got = np.stack([host(y)[b] for y in ys])
+        e = relerr(got, ref["Y"][T0:])
+        say(f"  b={b} resumed relerr {e:.3g}")
+        assert e < TOL["bf16"]
