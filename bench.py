@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the MTLA hot path on one MI355X.
+
+Headline (the JSON line's `value`): decode tokens/s of one MTLA layer on the
+speech-decoder-shaped step (B=32, d=512, H=8, d_h=64, r=256, d_hR=32, s=2,
+2048 frames of context = 1024 compressed slots, bf16 cache, fp32
+accumulation).  One step is one full mtla_decode_step: latent and absorbed
+query projection, hyper-network gate with the in-place merge into slot
+floor(t/s), split-K attention over the compressed cache, combine and the
+absorbed output projection.  tokens/s = B / step time.
+
+The timed region is `--steps` consecutive decode steps enqueued while the GPU
+is held by a spin kernel, so that they then execute back to back: host launch
+latency stays out of the GPU timeline, as it would under graph replay, and
+the events recorded around a kernel bracket exactly that kernel.  Every step
+reads a different replica of the cache, the replicas together exceeding
+1 GiB, so the cache is streamed from HBM and not from the 256 MB Infinity
+Cache.
+
+`roofline` is that of the split-K attention kernel: algorithmic bytes (the
+compressed cache rows the step must read, sum_b (floor(t_b/s)+1) *
+(r + d_hR) * 2 B) over its average duration, taken from HIP events recorded
+around that kernel inside the timed region.
+
+Also reported (same line): the ragged and LLM-scale decode workloads, the
+strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
+of the whole forward), and the CPU oracle timed on the host cores on a bounded
+sample of the headline workload.
+
+All inputs are seeded synthetic tensors (no datasets or trained weights).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "decode tokens/s + achieved HBM GB/s (compressed cache); prefill TFLOP/s, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _decode_setup(cfg: int, seed_pos=None):
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    name, dims, ex = synth.config(cfg)
+    B = ex["B"]
+    if "ctx" in ex:
+        pos = np.full(B, ex["ctx"] - 1, dtype=np.int32)
+    else:
+        rng = np.random.default_rng(synth.seed_for(cfg))
+        pos = (rng.integers(ex["ctx_lo"], ex["ctx_hi"] + 1, size=B) - 1).astype(np.int32)
+    max_pos = int(pos.max())
+    ms = max_pos // dims.s + 1
+    w = synth.make_weights(dims, synth.seed_for(cfg), "bf16", pe_rows=ms)
+    layer = MTLALayer.from_arrays(dims, w, MTLA_BF16)
+    row = dims.r + dims.d_hR
+    one = B * ms * row * 2
+    n_rep = max(1, math.ceil((1 << 30) / one)) if one < (1 << 30) else 1
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.seed_for(cfg))
+    caches = []
+    for _ in range(n_rep):
+        c = torch.empty(B, ms, row, dtype=torch.bfloat16, device="cuda")
+        c[..., :dims.r].normal_(0.0, 0.7, generator=gen)
+        c[..., dims.r:].normal_(0.0, 1.0, generator=gen)
+        caches.append(c)
+    step = synth.make_step(dims, w, pos, seed=synth.seed_for(cfg) + 2)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    inputs = (dev(step["x"]), dev(step["QR"]), dev(step["KR"]), torch.from_numpy(pos).cuda())
+    Y = torch.empty(B, dims.d, dtype=torch.bfloat16, device="cuda")
+    cache_bytes = int(np.sum(pos // dims.s + 1)) * row * 2
+    return dict(name=name, dims=dims, B=B, pos=pos, max_pos=max_pos, layer=layer, caches=caches,
+                inputs=inputs, Y=Y, cache_bytes=cache_bytes, weights=w, ms=ms)
+
+
+def _host_ahead(fn, n, sleep_cycles):
+    """Enqueue n calls of fn(i) while the GPU is held busy by a spin kernel,
+    so the GPU then runs them back to back: host launch latency stays out of
+    the GPU timeline and events recorded between kernels bracket exactly the
+    kernel between them.  Returns (total_ms, ok) where ok says the spin
+    outlasted the host's enqueueing."""
+    import torch
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spin_done = torch.cuda.Event()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(sleep_cycles)
+    spin_done.record()
+    t0.record()
+    for i in range(n):
+        fn(i)
+    t1.record()
+    ok = not spin_done.query()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), ok
+
+
+def _timed_loop(fn, n):
+    """_host_ahead with a spin long enough to cover the enqueueing."""
+    cycles = 20_000_000
+    for _ in range(6):
+        total, ok = _host_ahead(fn, n, cycles)
+        if ok:
+            return total
+        cycles *= 4
+    raise RuntimeError("could not keep the GPU busy while enqueueing the timed steps")
+
+
+def run_decode(cfg: int, steps: int, warmup: int) -> dict:
+    """Time `steps` decode steps; returns step and attention-kernel times."""
+    import torch
+    S = _decode_setup(cfg)
+    layer, caches, (x, qr, kr, pos), Y = S["layer"], S["caches"], S["inputs"], S["Y"]
+    n_rep, max_pos = len(caches), S["max_pos"]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:              # create the underlying events up front
+        a.record()
+        b.record()
+
+    def one(i, events=None):
+        layer.decode_step(caches[i % n_rep], x, qr, kr, pos, max_pos, Y, events=events)
+
+    for i in range(max(warmup, 1)):
+        one(i)
+    torch.cuda.synchronize()
+    total_ms = _timed_loop(lambda i: one(i, ev[i]), steps)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    step_ms = total_ms / steps
+    attn_avg = float(np.mean(attn_ms))
+    return dict(name=S["name"], B=S["B"], dims=S["dims"].asdict(), steps=steps,
+                replicas=n_rep, step_ms=step_ms, attn_ms=attn_avg,
+                attn_ms_median=float(np.median(attn_ms)), cache_bytes=S["cache_bytes"],
+                tokens_per_s=S["B"] / (step_ms * 1e-3),
+                attn_gbs=S["cache_bytes"] / (attn_avg * 1e-3) / 1e9,
+                ctx_min=int(S["pos"].min()) + 1, ctx_max=int(S["pos"].max()) + 1)
+
+
+def prefill_flops(B, T, H, r, dR, s):
+    """Algorithmic flops of the strided attention (visible pairs only) and of
+    the projections of the parallel form."""
+    pairs_per_bh = sum(m // s + 1 for m in range(T))
+    attn = B * H * pairs_per_bh * (2 * (r + dR) + 2 * r)
+    return attn, pairs_per_bh
+
+
+def run_prefill(steps: int = 10, warmup: int = 3) -> dict:
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    ms = -(-T // dims.s)
+    w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
+    layer = MTLALayer.from_arrays(dims, w, MTLA_BF16)
+    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    X, QR, KR = dev(seq["X"]), dev(seq["QR"]), dev(seq["KR"])
+    del seq
+    Y = torch.empty(B, T, dims.d, dtype=torch.bfloat16, device="cuda")
+    cache = layer.new_cache(B, ms)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    for i in range(warmup):
+        layer.prefill(X, QR, KR, Y, cache=cache)
+    torch.cuda.synchronize()
+    fwd_ms = _timed_loop(lambda i: layer.prefill(X, QR, KR, Y, cache=cache, events=ev[i]),
+                         steps) / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_flops, pairs = prefill_flops(B, T, dims.H, dims.r, dims.d_hR, dims.s)
+    M = B * T
+    proj_flops = (2 * M * dims.d * dims.r            # latent
+                  + 2 * M * dims.r * dims.r          # gate content branch
+                  + 2 * M * dims.d * dims.H * dims.r  # absorbed queries
+                  + 2 * M * dims.H * dims.r * dims.d)  # absorbed output
+    return dict(name=name, B=B, T=T, dims=dims.asdict(), steps=steps, forward_ms=fwd_ms,
+                attn_ms=attn_ms, visible_pairs=B * dims.H * pairs, attn_flops=attn_flops,
+                proj_flops=proj_flops, attn_tflops=attn_flops / (attn_ms * 1e-3) / 1e12,
+                forward_tflops=(attn_flops + proj_flops) / (fwd_ms * 1e-3) / 1e12,
+                tokens_per_s=M / (fwd_ms * 1e-3))
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """The oracle (numpy, fp32) on the headline decode workload: full-batch
+    decode steps repeated until `seconds` of wall time have passed."""
+    import synth
+    import oracle.mtla as om
+    from threadpoolctl import threadpool_info
+    name, dims, ex = synth.config(2)
+    B, t = ex["B"], ex["ctx"] - 1
+    ms = t // dims.s + 1
+    w = synth.make_weights(dims, synth.seed_for(2), "bf16", pe_rows=ms)
+    W = om.with_position_table(w, ms)
+    W = {k: np.asarray(v, dtype=np.float32) for k, v in W.items()}
+    rng = np.random.default_rng(synth.seed_for(2))
+    lat = rng.normal(0, 0.7, size=(B, ms, dims.r)).astype(np.float32)
+    rk = rng.normal(0, 1.0, size=(B, ms, dims.d_hR)).astype(np.float32)
+    step = synth.make_step(dims, w, np.full(B, t), seed=synth.seed_for(2) + 2)
+    x, qr, kr = (np.asarray(step[k], dtype=np.float32) for k in ("x", "QR", "KR"))
+    n_tok, t0 = 0, time.perf_counter()
+    batches = 0
+    while True:
+        for b in range(B):
+            om.decode_step(lat[b], rk[b], t, x[b], qr[b], kr[b], W, dims.s, np.float32(dims.scale))
+            n_tok += 1
+        batches += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    return dict(value=n_tok / el, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{batches} full-batch decode steps of {name} (B={B}, {ms} slots), "
+                       f"numpy fp32, {el:.1f} s; host cores visible: {len(os.sched_getaffinity(0))}; "
+                       f"BLAS: {blas[0].get('internal_api') if blas else 'none'}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
+                                       "llm_decode_b128_ctx32768", "prefill_b16_t4096"],
+                    help="time one workload alone and print its record (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the MTLA hot path here has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+    if args.only:
+        cfg = {"decode_b32_ctx2048": 2, "ragged_decode_b64_s4": 3,
+               "llm_decode_b128_ctx32768": 5, "prefill_b16_t4096": 4}[args.only]
+        rec = run_prefill(args.steps, args.warmup) if cfg == 4 else \
+            run_decode(cfg, args.steps, args.warmup)
+        print(json.dumps(rec), flush=True)
+        return
+    log("decode_b32_ctx2048 ...")
+    head = run_decode(2, args.steps, args.warmup)
+    log(f"  step {head['step_ms']*1e3:.2f} us, attention {head['attn_ms']*1e3:.2f} us, "
+        f"{head['attn_gbs']:.0f} GB/s, {head['tokens_per_s']:.0f} tok/s")
+    extra = {}
+    cpu = None
+    if True:
+        log("ragged_decode_b64_s4 ...")
+        extra["ragged_decode_b64_s4"] = run_decode(3, 20, 5)
+        log("llm_decode_b128_ctx32768 ...")
+        extra["llm_decode_b128_ctx32768"] = run_decode(5, 10, 3)
+        torch.cuda.empty_cache()
+        log("prefill_b16_t4096 ...")
+        extra["prefill_b16_t4096"] = run_prefill()
+        for k in ("ragged_decode_b64_s4", "llm_decode_b128_ctx32768"):
+            e = extra[k]
+            e["attn_hbm_frac"] = e["attn_gbs"] / HBM_PEAK_GBS
+            log(f"  {k}: attention {e['attn_ms']*1e3:.1f} us {e['attn_gbs']:.0f} GB/s "
+                f"({e['attn_hbm_frac']:.1%}), {e['tokens_per_s']:.0f} tok/s")
+        p = extra["prefill_b16_t4096"]
+        p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
+        log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
+            f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
+        log("cpu baseline ...")
+        cpu = cpu_baseline(args.cpu_seconds)
+        cpu["value"] = round(cpu["value"], 2)
+    out = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["step_ms"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random inputs and random-init weights of the workload's shapes)",
+        "config": {"workload": "decode_b32_ctx2048", "B": 32, "d": 512, "H": 8, "d_h": 64,
+                   "r": 256, "d_hR": 32, "s": 2, "context_frames": 2048, "slots": 1024,
+                   "cache_replicas": head["replicas"]},
+        "roofline": {"bound": "hbm", "kernel": "decode_attn_kernel",
+                     "achieved": round(head["attn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": head["cache_bytes"],
+                     "avg_kernel_us": round(head["attn_ms"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

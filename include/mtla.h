@@ -149,6 +149,23 @@ mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, c
                                  const mtla_cache *cache_out, void *Cprime_out, void *workspace,
                                  size_t ws_bytes, void *stream);
 
+/* Profiling variants of mtla_decode_step and mtla_prefill_strided: the same
+ * computation, and in addition events[0] is recorded on `stream` just before
+ * the attention kernel (the split-K decode attention, resp. the strided
+ * prefill attention) and events[1] just after it, so the caller can time that
+ * kernel alone with hipEventElapsedTime.  `events` points to two hipEvent_t
+ * handles owned by the caller; a missing handle is MTLA_ERR_ARG. */
+mtla_status mtla_decode_step_timed(const mtla_dims *dims, const mtla_weights *w,
+                                   const mtla_cache *cache, const void *X_t, const void *QR_t,
+                                   const void *KR_t, const int32_t *pos, int32_t B, int32_t max_pos,
+                                   void *Y, void *workspace, size_t ws_bytes, void *stream,
+                                   void *const *events);
+mtla_status mtla_prefill_strided_timed(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                                       const void *QR, const void *KR, int32_t B, int32_t T,
+                                       void *Y, const mtla_cache *cache_out, void *Cprime_out,
+                                       void *workspace, size_t ws_bytes, void *stream,
+                                       void *const *events);
+
 /* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
  * T_or_max_pos = max_pos) or 2 (prefill, with T_or_max_pos = T).  Returns 0
  * for invalid arguments.  Pure host function. */

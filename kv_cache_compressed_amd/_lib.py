@@ -21,7 +21,8 @@ MTLA_F32, MTLA_BF16 = 0, 1
 OP_MERGE, OP_DECODE, OP_PREFILL = 0, 1, 2
 
 EXPORTED = ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided",
-            "mtla_workspace_bytes", "mtla_status_string", "mtla_last_error_detail")
+            "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_workspace_bytes",
+            "mtla_status_string", "mtla_last_error_detail")
 
 
 class MtlaError(RuntimeError):
@@ -69,8 +70,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtla_prefill_strided.argtypes = [P(Dims), P(Weights), c_void_p, c_void_p, c_void_p,
                                          c_int32, c_int32, c_void_p, P(Cache), c_void_p, c_void_p,
                                          c_size_t, c_void_p]
+    lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
+    lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
     for f in ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step",
-              "mtla_prefill_strided"):
+              "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
     lib.mtla_workspace_bytes.restype = c_size_t
@@ -156,31 +159,50 @@ def mtla_merge_append(dims: Dims, w: Weights, cache: Cache, X_t, KR_t, pos, max_
                                             B, int(max_pos), _ptr(ws), ws.numel(), _stream()))
 
 
+def _events(events):
+    """Two torch.cuda.Event objects -> the C array of their raw handles."""
+    for e in events:
+        if e.cuda_event == 0:      # torch creates the underlying event on first record
+            e.record()
+    return (c_void_p * 2)(events[0].cuda_event, events[1].cuda_event)
+
+
 def mtla_decode_step(dims: Dims, w: Weights, cache: Cache, X_t, QR_t, KR_t, pos, max_pos: int,
-                     Y=None, ws=None):
+                     Y=None, ws=None, events=None):
+    """``events``: optional pair of torch.cuda.Event recorded around the
+    split-K attention kernel (the profiling entry point is used then)."""
     B = X_t.shape[0]
     if Y is None:
         Y = torch.empty(B, dims.d, dtype=X_t.dtype, device=X_t.device)
     if ws is None:
         ws = workspace(dims, OP_DECODE, B, max_pos, X_t.device)
-    _check(load_library().mtla_decode_step(ctypes.byref(dims), ctypes.byref(w),
-                                           ctypes.byref(cache), _ptr(X_t), _ptr(QR_t), _ptr(KR_t),
-                                           _ptr(pos), B, int(max_pos), _ptr(Y), _ptr(ws),
-                                           ws.numel(), _stream()))
+    lib = load_library()
+    args = [ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache), _ptr(X_t), _ptr(QR_t),
+            _ptr(KR_t), _ptr(pos), B, int(max_pos), _ptr(Y), _ptr(ws), ws.numel(), _stream()]
+    if events is None:
+        _check(lib.mtla_decode_step(*args))
+    else:
+        _check(lib.mtla_decode_step_timed(*args, _events(events)))
     return Y
 
 
 def mtla_prefill_strided(dims: Dims, w: Weights, X, QR, KR, Y=None, cache: Cache | None = None,
-                         Cprime=None, ws=None):
+                         Cprime=None, ws=None, events=None):
+    """``events``: optional pair of torch.cuda.Event recorded around the
+    strided attention kernel (the profiling entry point is used then)."""
     B, T = X.shape[0], X.shape[1]
     if Y is None:
         Y = torch.empty(B, T, dims.d, dtype=X.dtype, device=X.device)
     if ws is None:
         ws = workspace(dims, OP_PREFILL, B, T, X.device)
     cptr = ctypes.byref(cache) if cache is not None else None
-    _check(load_library().mtla_prefill_strided(ctypes.byref(dims), ctypes.byref(w), _ptr(X),
-                                               _ptr(QR), _ptr(KR), B, T, _ptr(Y), cptr,
-                                               _ptr(Cprime), _ptr(ws), ws.numel(), _stream()))
+    lib = load_library()
+    args = [ctypes.byref(dims), ctypes.byref(w), _ptr(X), _ptr(QR), _ptr(KR), B, T, _ptr(Y), cptr,
+            _ptr(Cprime), _ptr(ws), ws.numel(), _stream()]
+    if events is None:
+        _check(lib.mtla_prefill_strided(*args))
+    else:
+        _check(lib.mtla_prefill_strided_timed(*args, _events(events)))
     return Y
 
 

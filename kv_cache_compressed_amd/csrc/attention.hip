@@ -462,9 +462,16 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   }
 }
 
-template <class K> void allow_lds(K kernel, size_t bytes) {
-  (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)bytes);
+// Raise the dynamic-LDS limit of a kernel to the full 160 KB once per
+// instantiation (thread-safe static initialisation), so that launches made
+// later -- possibly under graph capture -- issue nothing but the launch.
+template <auto Kernel> void allow_lds() {
+  static const bool once = [] {
+    (void)hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    return true;
+  }();
+  (void)once;
 }
 
 template <typename T, int R, int DR, int NHB>
@@ -473,7 +480,7 @@ hipError_t decode_attn_t(const DecodePlan &p, int B, int H, int s, float sl2, co
                          float *part_o, float *part_ml, hipStream_t stream) {
   constexpr bool PF = sizeof(T) == 2;
   auto kern = decode_attn_kernel<T, R, DR, NHB, PF>;
-  allow_lds(kern, p.lds);
+  allow_lds<decode_attn_kernel<T, R, DR, NHB, PF>>();
   DecodeArgs args{pos, cache, bstride, qt, QR, part_o, part_ml, H, s, p.chunk, p.splits, sl2};
   hipLaunchKernelGGL(kern, dim3(p.splits, B), dim3(256), p.lds, stream, args);
   return hipGetLastError();
@@ -500,7 +507,7 @@ hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void 
   const int tiles = (T_len * H + ROWS - 1) / ROWS;
   const size_t lds = (size_t)64 * row_stride<T>(R + DR);
   auto kern = prefill_attn_kernel<T, R, DR, NQ, PF>;
-  allow_lds(kern, lds);
+  allow_lds<prefill_attn_kernel<T, R, DR, NQ, PF>>();
   PrefillArgs args{qt, QR, keys, kstride, Cp, KR, O, B, T_len, H, s, tiles, sl2};
   hipLaunchKernelGGL(kern, dim3(tiles * B), dim3(256), lds, stream, args);
   return hipGetLastError();

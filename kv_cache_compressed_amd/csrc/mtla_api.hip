@@ -230,10 +230,19 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
   return ok();
 }
 
-mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+}  // extern "C"
+
+namespace {
+
+mtla_status record(void *const *events, int i, hipStream_t s) {
+  if (!events) return MTLA_OK;
+  return launched(hipEventRecord((hipEvent_t)events[i], s), "event record");
+}
+
+mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                              const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
                              int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,
-                             void *stream) {
+                             void *stream, void *const *events) {
   mtla_status st;
   if ((st = check_dims(dims)) != MTLA_OK) return st;
   if ((st = check_weights(w, true)) != MTLA_OK) return st;
@@ -263,10 +272,12 @@ mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const
                                  w->gate_pos, pos, dims->s, cache->slots, cache->batch_stride, KR_t,
                                  s),
          "gate and merge");
+  if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
                                        eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
                                        QR_t, part_o, part_ml, s),
          "decode attention");
+  if ((st = record(events, 1, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_decode_combine(dims->dtype, plan, B, dims->H, dims->r, dims->s, pos, part_o,
                                      part_ml, o, s),
          "split combine");
@@ -275,10 +286,10 @@ mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const
   return ok();
 }
 
-mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, const void *X,
-                                 const void *QR, const void *KR, int32_t B, int32_t T, void *Y,
-                                 const mtla_cache *cache_out, void *Cprime_out, void *workspace,
-                                 size_t ws_bytes, void *stream) {
+mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                         const void *QR, const void *KR, int32_t B, int32_t T, void *Y,
+                         const mtla_cache *cache_out, void *Cprime_out, void *workspace,
+                         size_t ws_bytes, void *stream, void *const *events) {
   mtla_status st;
   if ((st = check_dims(dims)) != MTLA_OK) return st;
   if ((st = check_weights(w, true)) != MTLA_OK) return st;
@@ -320,12 +331,54 @@ mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, c
                                  ws.keys_stride, cache_out ? cache_out->slots : nullptr,
                                  cache_out ? cache_out->batch_stride : 0, s),
          "group scan");
+  if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_prefill_attention(dims->dtype, B, T, dims->H, dims->r, dims->d_hR, dims->s,
                                         eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s),
          "strided attention");
+  if ((st = record(events, 1, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_gemm_store(dims->dtype, O, HR, w->Bvo, HR, M, dims->d, HR, Y, dims->d, s),
          "output projection");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                             const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
+                             int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,
+                             void *stream) {
+  return decode_step_impl(dims, w, cache, X_t, QR_t, KR_t, pos, B, max_pos, Y, workspace, ws_bytes,
+                          stream, nullptr);
+}
+
+mtla_status mtla_decode_step_timed(const mtla_dims *dims, const mtla_weights *w,
+                                   const mtla_cache *cache, const void *X_t, const void *QR_t,
+                                   const void *KR_t, const int32_t *pos, int32_t B, int32_t max_pos,
+                                   void *Y, void *workspace, size_t ws_bytes, void *stream,
+                                   void *const *events) {
+  if (!events || !events[0] || !events[1]) return fail(MTLA_ERR_ARG, "events must hold two handles");
+  return decode_step_impl(dims, w, cache, X_t, QR_t, KR_t, pos, B, max_pos, Y, workspace, ws_bytes,
+                          stream, events);
+}
+
+mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                                 const void *QR, const void *KR, int32_t B, int32_t T, void *Y,
+                                 const mtla_cache *cache_out, void *Cprime_out, void *workspace,
+                                 size_t ws_bytes, void *stream) {
+  return prefill_impl(dims, w, X, QR, KR, B, T, Y, cache_out, Cprime_out, workspace, ws_bytes,
+                      stream, nullptr);
+}
+
+mtla_status mtla_prefill_strided_timed(const mtla_dims *dims, const mtla_weights *w, const void *X,
+                                       const void *QR, const void *KR, int32_t B, int32_t T,
+                                       void *Y, const mtla_cache *cache_out, void *Cprime_out,
+                                       void *workspace, size_t ws_bytes, void *stream,
+                                       void *const *events) {
+  if (!events || !events[0] || !events[1]) return fail(MTLA_ERR_ARG, "events must hold two handles");
+  return prefill_impl(dims, w, X, QR, KR, B, T, Y, cache_out, Cprime_out, workspace, ws_bytes,
+                      stream, events);
 }
 
 }  // extern "C"

@@ -54,11 +54,15 @@ class MTLALayer:
         L.mtla_merge_append(self.dims, self.w, L.make_cache(cache), X_t, KR_t, pos, max_pos,
                             self.workspace(L.OP_MERGE, X_t.shape[0], max_pos))
 
-    def decode_step(self, cache: torch.Tensor, X_t, QR_t, KR_t, pos, max_pos: int, Y=None):
+    def decode_step(self, cache: torch.Tensor, X_t, QR_t, KR_t, pos, max_pos: int, Y=None,
+                    events=None):
         return L.mtla_decode_step(self.dims, self.w, L.make_cache(cache), X_t, QR_t, KR_t, pos,
-                                  max_pos, Y, self.workspace(L.OP_DECODE, X_t.shape[0], max_pos))
+                                  max_pos, Y, self.workspace(L.OP_DECODE, X_t.shape[0], max_pos),
+                                  events)
 
-    def prefill(self, X, QR, KR, Y=None, cache: torch.Tensor | None = None, Cprime=None):
+    def prefill(self, X, QR, KR, Y=None, cache: torch.Tensor | None = None, Cprime=None,
+                events=None):
         c = L.make_cache(cache) if cache is not None else None
         return L.mtla_prefill_strided(self.dims, self.w, X, QR, KR, Y, c, Cprime,
-                                      self.workspace(L.OP_PREFILL, X.shape[0], X.shape[1]))
+                                      self.workspace(L.OP_PREFILL, X.shape[0], X.shape[1]),
+                                      events)
