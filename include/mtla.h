@@ -30,7 +30,8 @@
  *    is complete once frame s*j + s - 1 has been merged (the pages count from
  *    1 and call that frame's index a multiple of s).
  *  - Supported shapes: (r, d_hR) in {(256, 32), (512, 64)} (r = 4 d_h and
- *    d_hR = d_h/2 for d_h = 64 or 128), H <= 64, d a multiple of 32, s >= 1.
+ *    d_hR = d_h/2 for d_h = 64 or 128), H <= 64 (H <= 32 when r = 512), d a
+ *    multiple of 32, s >= 1.
  *    Other shapes return MTLA_ERR_UNSUPPORTED.
  *  - Calls on one stream are ordered; calls on different streams that touch
  *    the same cache or workspace race.
@@ -71,8 +72,10 @@ typedef struct {
 /* Weights of one layer (device pointers, storage dtype unless noted). */
 typedef struct {
   const void *W_dkv;      /* [r, d]    latent map, c_i = W_dkv x_i ([Notes] overall framework) */
-  const void *W_hc;       /* [r, r]    hyper-network content branch Linear(c_i) ... */
-  const void *b_hc;       /* [r]       ... and its bias ([Notes] temporal merging) */
+  const void *W_gate;     /* [r, d]    W_hc W_dkv from mtla_gate_content_map: the weight of
+                             the hyper-network content branch Linear(c_i) = W_hc c_i + b_hc
+                             folded into the latent map, so W_gate x_i = W_hc c_i ... */
+  const void *b_hc;       /* [r]       ... and the bias b_hc ([Notes] temporal merging) */
   const float *gate_pos;  /* [gate_pos_rows, r] FP32: Linear(pe_j) for slot j, from
                              mtla_gate_pos_table ([Notes] temporal merging) */
   int32_t gate_pos_rows;  /* rows of gate_pos; every slot index used must be below it */
@@ -103,9 +106,19 @@ typedef struct {
 mtla_status mtla_gate_pos_table(const mtla_dims *dims, const void *pe, int32_t rows, int32_t d_pe,
                                 const void *W_hp, const void *b_hp, float *table, void *stream);
 
+/* Content branch of the hyper-network folded into the latent map, evaluated
+ * once ([Notes] temporal merging: Linear(c_i) with c_i = W_dkv x_i; matrix
+ * products are associative, the device the pages use to absorb W_K and W_V):
+ *   W_gate[r, d] = W_hc[r, r] W_dkv[r, d], accumulated in fp32 and stored in
+ * the storage dtype.  All three device pointers in that dtype; only dims->r,
+ * dims->d and dims->dtype are read. */
+mtla_status mtla_gate_content_map(const mtla_dims *dims, const void *W_hc, const void *W_dkv,
+                                  void *W_gate, void *stream);
+
 /* Merge-append ([Notes] temporal merging; [Fig2] (a)): for every sequence b
  * with frame position t = pos[b] and j = floor(t/s):
- *   c = W_dkv x_t;  w = Sigmoid((W_hc c + b_hc) * gate_pos[j]);  u = w * c
+ *   c = W_dkv x_t;  w = Sigmoid((W_gate x_t + b_hc) * gate_pos[j]);  u = w * c
+ *   (W_gate x_t = W_hc c, so w = Sigmoid(Linear(c) * Linear(pe_j)))
  *   slot j latent <- u            if t mod s == 0 (t opens slot j)
  *   slot j latent <- slot j + u   otherwise (accumulated in place)
  *   slot j RoPE key <- KR_t[b]

@@ -20,7 +20,7 @@ MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = r
 MTLA_F32, MTLA_BF16 = 0, 1
 OP_MERGE, OP_DECODE, OP_PREFILL = 0, 1, 2
 
-EXPORTED = ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided",
+EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided",
             "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_workspace_bytes",
             "mtla_status_string", "mtla_last_error_detail")
 
@@ -38,7 +38,7 @@ class Dims(ctypes.Structure):
 
 
 class Weights(ctypes.Structure):
-    _fields_ = [("W_dkv", c_void_p), ("W_hc", c_void_p), ("b_hc", c_void_p),
+    _fields_ = [("W_dkv", c_void_p), ("W_gate", c_void_p), ("b_hc", c_void_p),
                 ("gate_pos", c_void_p), ("gate_pos_rows", c_int32), ("A", c_void_p),
                 ("Bvo", c_void_p)]
 
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = POINTER
     lib.mtla_gate_pos_table.argtypes = [P(Dims), c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                         c_void_p, c_void_p]
+    lib.mtla_gate_content_map.argtypes = [P(Dims), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtla_merge_append.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
                                       c_int32, c_int32, c_void_p, c_size_t, c_void_p]
     lib.mtla_decode_step.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
@@ -72,7 +73,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_size_t, c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
-    for f in ("mtla_gate_pos_table", "mtla_merge_append", "mtla_decode_step",
+    for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append", "mtla_decode_step",
               "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
@@ -112,10 +113,11 @@ def make_dims(d, H, d_h, r, d_hR, s, dtype=MTLA_BF16, scale=0.0) -> Dims:
     return Dims(int(d), int(H), int(d_h), int(r), int(d_hR), int(s), float(scale), int(dtype))
 
 
-def make_weights(W_dkv, W_hc, b_hc, gate_pos, A=None, Bvo=None) -> Weights:
+def make_weights(W_dkv, W_gate, b_hc, gate_pos, A=None, Bvo=None) -> Weights:
     """Gather device weight tensors ([out, in] layouts) into the C struct.
-    The tensors must stay alive while the struct is used."""
-    return Weights(_ptr(W_dkv), _ptr(W_hc), _ptr(b_hc), _ptr(gate_pos), int(gate_pos.shape[0]),
+    ``W_gate`` comes from mtla_gate_content_map.  The tensors must stay alive
+    while the struct is used."""
+    return Weights(_ptr(W_dkv), _ptr(W_gate), _ptr(b_hc), _ptr(gate_pos), int(gate_pos.shape[0]),
                    _ptr(A), _ptr(Bvo))
 
 
@@ -147,6 +149,14 @@ def mtla_gate_pos_table(dims: Dims, pe, W_hp, b_hp, table=None):
     _check(load_library().mtla_gate_pos_table(ctypes.byref(dims), _ptr(pe), rows, d_pe, _ptr(W_hp),
                                               _ptr(b_hp), _ptr(table), _stream()))
     return table
+
+
+def mtla_gate_content_map(dims: Dims, W_hc, W_dkv, W_gate=None):
+    if W_gate is None:
+        W_gate = torch.empty(dims.r, dims.d, dtype=W_dkv.dtype, device=W_dkv.device)
+    _check(load_library().mtla_gate_content_map(ctypes.byref(dims), _ptr(W_hc), _ptr(W_dkv),
+                                                _ptr(W_gate), _stream()))
+    return W_gate
 
 
 def mtla_merge_append(dims: Dims, w: Weights, cache: Cache, X_t, KR_t, pos, max_pos: int,

@@ -1,8 +1,8 @@
-// Absorbed MTLA attention on gfx950: the split-K incremental-decoding kernel,
-// its log-sum-exp combine, the group scan that builds the intermediate states
-// of the parallel form, and the stride-aware masked prefill kernel.
+// Parallel (prefill / training-forward) form of MTLA on gfx950: the gate and
+// group scan that build the intermediate states C', and the stride-aware
+// masked attention kernel.
 //
-// Both attention kernels run the same wave-level step (attend32): a tile of 32
+// The attention kernel's wave-level step (attend32): a tile of 32
 // compressed rows (latent r values followed by the RoPE key) sits in LDS, and
 // a wave scores it against 16*NQ query columns held in registers:
 //
@@ -130,169 +130,17 @@ __device__ __forceinline__ void attend32(AttnState<T, R, DR, NQ> &st, const char
 template <typename T> constexpr int row_stride(int rk) { return rk * (int)sizeof(T) + 16; }
 
 // ---------------------------------------------------------------------------
-// incremental decoding ([Notes] Y formula over the compressed cache; [Fig2] (a))
-// ---------------------------------------------------------------------------
-
-struct DecodeArgs {
-  const int32_t *pos;
-  const void *cache;
-  int64_t bstride;
-  const void *qt;
-  const void *QR;
-  float *part_o;
-  float *part_ml;
-  int H, s, chunk, splits;
-  float sl2;
-};
-
-// grid (splits, B), 4 waves.  Wave w serves heads 16*(w % NHB) .. +15 and the
-// slot tiles sl = w / NHB of every staged block of NSL*32 slots.
-template <typename T, int R, int DR, int NHB, bool PREFETCH>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
-  constexpr int RK = R + DR, NSL = 4 / NHB, BLOCK = NSL * 32;
-  constexpr int STRIDE = row_stride<T>(RK);
-  constexpr int CH = RK * (int)sizeof(T) / 16, EPC = 16 / (int)sizeof(T);
-  constexpr int NCH = BLOCK * CH, NLD = (NCH + 255) / 256;
-  constexpr int KS = RK / 32;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-
-  const int b = blockIdx.y, split = blockIdx.x;
-  const int n = a.pos[b] / a.s + 1;                  // slots 0..floor(pos/s)
-  const int start = split * a.chunk;
-  if (start >= n) return;
-  const int end = min(n, start + a.chunk);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int hb = wave % NHB, sl = wave / NHB;
-  const int H = a.H;
-  const int head = hb * 16 + c;
-
-  AttnState<T, R, DR, 1> st;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int k = 32 * ks + 8 * g;
-    if (head < H) {
-      if (k < R)
-        load8(st.q[0][ks], (const T *)a.qt + ((size_t)b * H + head) * R + k);
-      else
-        load8(st.q[0][ks], (const T *)a.QR + ((size_t)b * H + head) * DR + (k - R));
-    } else {
-      st.q[0][ks] = zero_frag<T>();
-    }
-  }
-  st.m[0] = kNegInf;
-  st.l[0] = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < R / 16; ++mt) st.o[0][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const T *src = (const T *)a.cache + (size_t)b * a.bstride;
-  u32x4 pre[NLD];
-  auto fetch = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      pre[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (idx < NCH && blk + row < end) pre[i] = ldg16(src + (size_t)(blk + row) * RK + ch * EPC);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < NCH) sts16(smem + (idx / CH) * STRIDE + (idx % CH) * 16, pre[i]);
-    }
-  };
-
-  const int lim[1] = {end};
-  if (PREFETCH) fetch(start);
-  for (int blk = start; blk < end; blk += BLOCK) {
-    if (!PREFETCH) fetch(blk);
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (PREFETCH && blk + BLOCK < end) fetch(blk + BLOCK);
-    const int kb = blk + sl * 32;
-    if (kb < end) attend32<T, R, DR, 1>(st, smem + sl * 32 * STRIDE, STRIDE, kb, lim, a.sl2);
-  }
-
-  // Merge the NSL slot-parallel waves of each head block through LDS.
-  __syncthreads();
-  float *red = (float *)smem;                 // [NSL][H][R]
-  float *redm = red + (size_t)NSL * H * R;    // [NSL][H]
-  float *redl = redm + NSL * H;               // [NSL][H]
-  float lt = st.l[0] + wave_xor(st.l[0], 16);
-  lt += wave_xor(lt, 32);
-  if (head < H) {
-#pragma unroll
-    for (int mt = 0; mt < R / 16; ++mt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[((size_t)sl * H + head) * R + 16 * mt + 4 * g + e] = st.o[0][mt][e];
-    if (g == 0) {
-      redm[sl * H + head] = st.m[0];
-      redl[sl * H + head] = lt;
-    }
-  }
-  __syncthreads();
-  const size_t pbase = ((size_t)b * a.splits + split) * H;
-  for (int idx = tid; idx < H * R; idx += 256) {
-    const int h = idx / R, ch = idx % R;
-    float M = kNegInf;
-#pragma unroll
-    for (int k = 0; k < NSL; ++k) M = fmaxf(M, redm[k * H + h]);
-    float acc = 0.0f, L = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NSL; ++k) {
-      const float mk = redm[k * H + h];
-      const float w = (mk == kNegInf) ? 0.0f : exp2f(mk - M);
-      acc += w * red[((size_t)k * H + h) * R + ch];
-      L += w * redl[k * H + h];
-    }
-    a.part_o[(pbase + h) * R + ch] = acc;
-    if (ch == 0) {
-      a.part_ml[(pbase + h) * 2] = M;
-      a.part_ml[(pbase + h) * 2 + 1] = L;
-    }
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t *pos, int s, int chunk,
-                                                             int splits, int H, int R,
-                                                             const float *part_o,
-                                                             const float *part_ml, T *o) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int n = pos[b] / s + 1;
-  const int ns = (n + chunk - 1) / chunk;
-  const size_t base = (size_t)b * splits * H;
-  float M = kNegInf;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, part_ml[((base + (size_t)k * H) + h) * 2]);
-  float L = 0.0f;
-  for (int k = 0; k < ns; ++k) {
-    const size_t i = (base + (size_t)k * H) + h;
-    L += exp2f(part_ml[i * 2] - M) * part_ml[i * 2 + 1];
-  }
-  const float inv = 1.0f / L;
-  for (int ch = threadIdx.x; ch < R; ch += blockDim.x) {
-    float acc = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const size_t i = (base + (size_t)k * H) + h;
-      acc += exp2f(part_ml[i * 2] - M) * part_o[i * R + ch];
-    }
-    o[((size_t)b * H + h) * R + ch] = from_f32<T>(acc * inv);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // parallel form ([Notes] stride-aware causal mask; [Fig2] (c))
 // ---------------------------------------------------------------------------
 
-// One thread per (sequence b, slot j, channel): walks the s frames of group j.
+// One thread per (sequence b, slot j, channel): computes the gated latents
+// of the s frames of group j ([Notes] hyper-network temporal merging) and
+// their running sum ([Notes] stride-aware causal mask; [Fig2] (c)).
 template <typename T>
-__global__ __launch_bounds__(256) void group_scan_kernel(const float *U, const T *KR, int T_len,
-                                                         int R, int DR, int s, int nS, T *Cp,
-                                                         T *keys, int64_t kstride, T *cache,
+__global__ __launch_bounds__(256) void group_scan_kernel(const float *cg, const T *b_hc,
+                                                         const float *table, const T *KR,
+                                                         int T_len, int R, int DR, int s, int nS,
+                                                         T *Cp, T *keys, int64_t kstride, T *cache,
                                                          int64_t cstride) {
   const int b = blockIdx.y;
   const int RK = R + DR;
@@ -302,10 +150,12 @@ __global__ __launch_bounds__(256) void group_scan_kernel(const float *U, const T
   const int i0 = j * s, i1 = min(i0 + s, T_len) - 1;
   T v;
   if (ch < R) {
+    const float bb = to_f32(b_hc[ch]), pj = table[(size_t)j * R + ch];
     float acc = 0.0f;
     for (int i = i0; i <= i1; ++i) {
       const size_t row = (size_t)b * T_len + i;
-      acc += U[row * R + ch];
+      const float *r = cg + row * 2 * R;
+      acc += sigmoidf((r[R + ch] + bb) * pj) * r[ch];
       Cp[row * R + ch] = from_f32<T>(acc);
     }
     v = from_f32<T>(acc);
@@ -465,37 +315,6 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
 // Raise the dynamic-LDS limit of a kernel to the full 160 KB once per
 // instantiation (thread-safe static initialisation), so that launches made
 // later -- possibly under graph capture -- issue nothing but the launch.
-template <auto Kernel> void allow_lds() {
-  static const bool once = [] {
-    (void)hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    return true;
-  }();
-  (void)once;
-}
-
-template <typename T, int R, int DR, int NHB>
-hipError_t decode_attn_t(const DecodePlan &p, int B, int H, int s, float sl2, const int32_t *pos,
-                         const void *cache, int64_t bstride, const void *qt, const void *QR,
-                         float *part_o, float *part_ml, hipStream_t stream) {
-  constexpr bool PF = sizeof(T) == 2;
-  auto kern = decode_attn_kernel<T, R, DR, NHB, PF>;
-  allow_lds<decode_attn_kernel<T, R, DR, NHB, PF>>();
-  DecodeArgs args{pos, cache, bstride, qt, QR, part_o, part_ml, H, s, p.chunk, p.splits, sl2};
-  hipLaunchKernelGGL(kern, dim3(p.splits, B), dim3(256), p.lds, stream, args);
-  return hipGetLastError();
-}
-
-template <typename T, int R, int DR>
-hipError_t decode_attn_h(const DecodePlan &p, int B, int H, int s, float sl2, const int32_t *pos,
-                         const void *cache, int64_t bstride, const void *qt, const void *QR,
-                         float *part_o, float *part_ml, hipStream_t stream) {
-  switch (p.nhb) {
-    case 1: return decode_attn_t<T, R, DR, 1>(p, B, H, s, sl2, pos, cache, bstride, qt, QR, part_o, part_ml, stream);
-    case 2: return decode_attn_t<T, R, DR, 2>(p, B, H, s, sl2, pos, cache, bstride, qt, QR, part_o, part_ml, stream);
-    default: return decode_attn_t<T, R, DR, 4>(p, B, H, s, sl2, pos, cache, bstride, qt, QR, part_o, part_ml, stream);
-  }
-}
 
 template <typename T, int R, int DR>
 hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void *qt,
@@ -515,73 +334,21 @@ hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void 
 
 }  // namespace
 
-bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, DecodePlan *plan) {
-  if (!((r == 256 && dR == 32) || (r == 512 && dR == 64))) return false;
-  if (H < 1 || H > 64 || s < 1 || B < 1 || max_pos < 0) return false;
-  const int esz = dtype == 1 ? 2 : 4;
-  DecodePlan p;
-  p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
-  // Fewer slot-parallel waves (smaller staged blocks) when wide fp32 rows
-  // would not fit the 160 KB of LDS.
-  while (p.nhb < 4 && (size_t)(4 / p.nhb) * 32 * ((r + dR) * esz + 16) > 160 * 1024) p.nhb *= 2;
-  const int nsl = 4 / p.nhb;
-  p.block = nsl * 32;
-  const int nmax = max_pos / s + 1;
-  const int64_t total = (int64_t)B * nmax;
-  int64_t chunk = (total + 1023) / 1024;
-  chunk = ((chunk + p.block - 1) / p.block) * p.block;
-  if (chunk < p.block) chunk = p.block;
-  const int64_t cap = ((nmax + p.block - 1) / p.block) * (int64_t)p.block;
-  if (chunk > cap) chunk = cap;
-  p.chunk = (int)chunk;
-  p.splits = (int)((nmax + chunk - 1) / chunk);
-  const size_t stage = (size_t)p.block * ((r + dR) * esz + 16);
-  const size_t reduce = (size_t)nsl * H * r * 4 + (size_t)2 * nsl * H * 4;
-  p.lds = stage > reduce ? stage : reduce;
-  if (p.lds > 160 * 1024) return false;
-  *plan = p;
-  return true;
-}
-
-hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
-                                   int s, float scale, const int32_t *pos, const void *cache,
-                                   int64_t batch_stride, const void *qt, const void *QR,
-                                   float *part_o, float *part_ml, hipStream_t stream) {
-  const float sl2 = scale * kLog2e;
-  if (dtype == 1) {
-    if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, H, s, sl2, pos, cache, batch_stride, qt, QR, part_o, part_ml, stream);
-    return decode_attn_h<bf16, 512, 64>(plan, B, H, s, sl2, pos, cache, batch_stride, qt, QR, part_o, part_ml, stream);
-  }
-  if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, H, s, sl2, pos, cache, batch_stride, qt, QR, part_o, part_ml, stream);
-  return decode_attn_h<float, 512, 64>(plan, B, H, s, sl2, pos, cache, batch_stride, qt, QR, part_o, part_ml, stream);
-}
-
-hipError_t launch_decode_combine(int dtype, const DecodePlan &plan, int B, int H, int r, int s,
-                                 const int32_t *pos, const float *part_o, const float *part_ml,
-                                 void *o, hipStream_t stream) {
-  if (dtype == 1)
-    hipLaunchKernelGGL(decode_combine_kernel<bf16>, dim3(H, B), dim3(256), 0, stream, pos, s,
-                       plan.chunk, plan.splits, H, r, part_o, part_ml, (bf16 *)o);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(H, B), dim3(256), 0, stream, pos, s,
-                       plan.chunk, plan.splits, H, r, part_o, part_ml, (float *)o);
-  return hipGetLastError();
-}
-
-hipError_t launch_group_scan(int dtype, const float *U, const void *KR, int B, int T, int r, int dR,
-                             int s, void *Cp, void *keys, int64_t keys_stride, void *cache,
-                             int64_t cache_stride, hipStream_t stream) {
+hipError_t launch_group_scan(int dtype, const float *cg, const void *b_hc, const float *table,
+                             const void *KR, int B, int T, int r, int dR, int s, void *Cp,
+                             void *keys, int64_t keys_stride, void *cache, int64_t cache_stride,
+                             hipStream_t stream) {
   const int nS = (T + s - 1) / s;
   const int64_t work = (int64_t)nS * (r + dR);
   dim3 grid((unsigned)((work + 255) / 256), B);
   if (dtype == 1)
-    hipLaunchKernelGGL(group_scan_kernel<bf16>, grid, dim3(256), 0, stream, U, (const bf16 *)KR, T,
-                       r, dR, s, nS, (bf16 *)Cp, (bf16 *)keys, keys_stride, (bf16 *)cache,
-                       cache_stride);
+    hipLaunchKernelGGL(group_scan_kernel<bf16>, grid, dim3(256), 0, stream, cg, (const bf16 *)b_hc,
+                       table, (const bf16 *)KR, T, r, dR, s, nS, (bf16 *)Cp, (bf16 *)keys,
+                       keys_stride, (bf16 *)cache, cache_stride);
   else
-    hipLaunchKernelGGL(group_scan_kernel<float>, grid, dim3(256), 0, stream, U, (const float *)KR,
-                       T, r, dR, s, nS, (float *)Cp, (float *)keys, keys_stride, (float *)cache,
-                       cache_stride);
+    hipLaunchKernelGGL(group_scan_kernel<float>, grid, dim3(256), 0, stream, cg,
+                       (const float *)b_hc, table, (const float *)KR, T, r, dR, s, nS, (float *)Cp,
+                       (float *)keys, keys_stride, (float *)cache, cache_stride);
   return hipGetLastError();
 }
 

@@ -39,6 +39,23 @@ __device__ __forceinline__ f32x4 mma_k32(const f32x8 &a, const f32x8 &b, f32x4 c
   return c;
 }
 
+// K=16 step: O (16x16) += A (16 x 16) B (16 x 16); lane l holds row/col l%16
+// and k = 4*(l/16)+e, e < 4 (the layout of a ds_read_tr16_b64 result).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma_k16(const bf16x4 &a, const bf16x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_k16(const f32x4 &a, const f32x4 &b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+template <typename T> struct Frag4;
+template <> struct Frag4<bf16> { typedef bf16x4 type; };
+template <> struct Frag4<float> { typedef f32x4 type; };
+
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
@@ -69,5 +86,80 @@ __device__ __forceinline__ void sts16(void *p, u32x4 v) { *(u32x4 *)p = v; }
 __device__ __forceinline__ float sigmoidf(float g) { return 1.0f / (1.0f + expf(-g)); }
 
 __device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// ---- 16-row LDS tiles filled by direct global->LDS loads ------------------
+//
+// A tile holds 16 rows of RB bytes (RB a multiple of 64) as RB/64 blocks of
+// 1 KB: block q holds bytes [64q, 64q + 64) of the 16 rows, row i at offset
+// 64 i, with the row's four 16-byte chunks permuted by XOR with swz(i).  One
+// global_load_lds_dwordx4 (64 lanes x 16 B, lane l landing at 16 l) fills one
+// block when lane l fetches chunk (l%4) ^ swz(l/4) of row l/4.  The
+// permutation makes both read patterns conflict free whether the LDS serves
+// 128 or 256 bytes per clock: the 16-byte reads that feed an MFMA operand (16
+// rows, same columns) and the 8-byte transposing reads (4 rows x 32
+// contiguous bytes per 16 lanes).
+__device__ __forceinline__ int swz(int row) {
+  return ((((row >> 1) ^ (row >> 2) ^ (row >> 3)) & 1) << 1) | ((row >> 2) & 1);
+}
+
+__device__ __forceinline__ int tile_off(int row, int byte) {
+  return ((byte >> 6) << 10) + (row << 6) + ((((byte >> 4) & 3) ^ swz(row)) << 4) + (byte & 15);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issue one block load.  `row_ptr` is the global address of the row this
+// lane copies (row lane/4 of the block), `q` the block's 64-byte column
+// segment, `dst` the block's LDS address (wave-uniform).
+__device__ __forceinline__ void dma_block(const char *row_ptr, int q, char *dst) {
+  const int lane = threadIdx.x & 63;
+  const int u = (lane & 3) ^ swz(lane >> 2);
+  __builtin_amdgcn_global_load_lds((const void *)(row_ptr + q * 64 + u * 16), (lds_void *)dst, 16,
+                                   0, 0);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding direct-to-LDS load); the empty asm statements
+// keep the compiler from moving memory accesses across it.  Callers order
+// their own loads with wait_vm / wait_lgkm0 first.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still
+// outstanding (they complete in issue order).  Other counters untouched.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses have completed.
+__device__ __forceinline__ void wait_lgkm0() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+}
+
+// Raise a kernel's dynamic-LDS limit to everything its static LDS leaves of
+// the CU's 160 KB, once per instantiation (thread-safe static
+// initialisation), so that launches made later -- possibly under graph
+// capture -- issue nothing but the launch.  A failure here is cleared so it
+// cannot be mistaken for a launch error; the launch itself then reports it.
+template <auto Kernel> void allow_lds() {
+  static const bool once = [] {
+    hipFuncAttributes attr;
+    size_t stat = 0;
+    if (hipFuncGetAttributes(&attr, (const void *)Kernel) == hipSuccess) stat = attr.sharedSizeBytes;
+    if (hipFuncSetAttribute((const void *)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(160 * 1024 - stat)) != hipSuccess)
+      (void)hipGetLastError();
+    return true;
+  }();
+  (void)once;
+}
 
 }  // namespace mtla

@@ -1,0 +1,469 @@
+// Incremental decoding over the compressed cache on gfx950: the hyper-network
+// merge of the new frame into its slot, and the split-K absorbed attention
+// over slots 0..floor(t/s) with the temporary (partially merged) newest slot.
+//
+// [Notes] = "Multi-head Temporal Latent Attention" paper notes (zhaoyang97
+// Paper-Notes), method section, key designs: hyper-network temporal merging,
+// stride-aware causal mask (why inference attends a temporary slot), and
+// decoupled RoPE with temporal compression (the Y formula).
+// [Fig2] = "Multi-head Temporal Latent Attention" (sciencestack.ai), Fig. 2 (a).
+//
+// Attention kernel, one workgroup per (sequence b, split of `chunk` slots):
+//  * The cache rows of the split stream from HBM into a ring of LDS stages by
+//    direct global->LDS loads (global_load_lds_dwordx4, no register staging),
+//    up to `nst` stages in flight; a stage is 16*TP rows (TP 16-row tiles).
+//  * Every head of the sequence reads the same rows (one latent cache shared
+//    by all heads), so each byte is fetched once.  The 4 waves split the work
+//    as head block (16 heads) x tile of the stage x half of the latent
+//    channels of O (halves only for r = 512, where all of O would not fit the
+//    registers of one wave; both halves then compute the same scores).
+//  * Per 16-row tile a wave computes S^T (16 keys x 16 heads) = K . Q^T with
+//    K from LDS as the MFMA A operand (K = latent ++ RoPE key, r + d_hR
+//    wide), applies the online softmax in log2 units, and accumulates
+//    O^T (r x 16 heads) += C^T . P^T, reading C^T from the row-major tile with
+//    ds_read_tr16_b64 (the K=16 bf16 MFMA's A layout) and P^T straight from
+//    the score registers (the score layout is the B layout).
+//  * The split that owns the newest slot j = floor(t/s) first merges the new
+//    frame: u = Sigmoid((g + b_hc) * Linear(pe_j)) * c, slot j = u (t mod s
+//    == 0) or slot j + u, RoPE key j = K^R_t, written to the cache and into
+//    its LDS copy before that row is attended.
+//  * Splits write (max, sum, O) partials; the last split of a sequence to
+//    finish (device-scope atomic counter) merges them by log-sum-exp in
+//    split order, so results are deterministic.
+
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mtla {
+
+namespace {
+
+constexpr float kNegInf = -INFINITY;
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+template <typename T, int R, int DR, int NHB> struct DecCfg {
+  static constexpr int RK = R + DR, ES = (int)sizeof(T), RB = RK * ES, NSEG = RB / 64;
+  static constexpr int CS = R >= 512 ? 2 : 1;           // channel halves of O
+  static constexpr int TP = 4 / (NHB * CS), SROWS = 16 * TP;
+  static constexpr int TILE_B = 16 * RB, STAGE_B = TP * TILE_B;
+  static constexpr int NBLK = TP * NSEG, LPW = (NBLK + 3) / 4;
+  static constexpr int KS = RK / 32, MT = R / 16, MTW = MT / CS, NU = (R + 255) / 256;
+  static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
+  static_assert(TP >= 1, "too many head blocks for this width");
+};
+
+// S operand: the 8 values of row `row`, k-step ks (32 values) that lane
+// group g feeds to the K=32 MFMA.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type s_frag(const char *tile, int row, int ks, int g) {
+  if constexpr (sizeof(T) == 2) {
+    return *(const bf16x8 *)(tile + tile_off(row, ks * 64 + g * 16));
+  } else {
+    const f32x4 x = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32));
+    const f32x4 y = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32 + 16));
+    return (f32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
+// Transposed operand C^T for channels ch0..ch0+15 of the tile's keys
+// 4g..4g+3: lane (g, j) receives channel ch0 + j of those four keys.
+template <typename T>
+__device__ __forceinline__ typename Frag4<T>::type v_frag(const char *tile, int ch0, int g, int j) {
+  if constexpr (sizeof(T) == 2) {
+    // ds_read_tr16_b64: in each 16-lane group, lane i returns element
+    // [4e + i/4][i%4] of the 16 x 4 block whose row k lane k addressed; lane
+    // k addresses key 4g + k/4, channels ch0 + 4(k%4) .. +3.
+    const char *p = tile + tile_off(4 * g + (j >> 2), (ch0 + 4 * (j & 3)) * 2);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+  } else {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + tile_off(4 * g + e, (ch0 + j) * 4));
+    return v;
+  }
+}
+
+template <typename T, int R, int DR, int NHB> struct WaveState {
+  typename Frag<T>::type q[DecCfg<T, R, DR, NHB>::KS];
+  f32x4 o[DecCfg<T, R, DR, NHB>::MTW];   // channels 16 (half*MTW + mt) + 4g + e
+  float m, l;
+};
+
+// One 16-key tile: key kbase + k is visible iff kbase + k < end.
+template <typename T, int R, int DR, int NHB>
+__device__ __forceinline__ void attend16(WaveState<T, R, DR, NHB> &st, const char *tile, int kbase,
+                                         int end, int half, float sl2) {
+  using C = DecCfg<T, R, DR, NHB>;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) sc = mma_k32(s_frag<T>(tile, c, ks, g), st.q[ks], sc);
+  float v[4], mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = (kbase + 4 * g + e < end) ? sc[e] * sl2 : kNegInf;
+    mx = fmaxf(mx, v[e]);
+  }
+  mx = fmaxf(mx, wave_xor(mx, 16));
+  mx = fmaxf(mx, wave_xor(mx, 32));
+  const float mn = fmaxf(st.m, mx);   // finite: key kbase is visible
+  const float alpha = exp2f(st.m - mn);
+  typename Frag4<T>::type pf;
+  float ps = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p = exp2f(v[e] - mn);
+    ps += p;
+    pf[e] = from_f32<T>(p);
+  }
+  st.l = st.l * alpha + ps;
+  st.m = mn;
+  // Channel blocks in groups of 8, so the compiler does not hoist every
+  // transposing read of the tile ahead of the products (register pressure).
+  const int cb = half * C::MTW;
+#pragma unroll
+  for (int m0 = 0; m0 < C::MTW; m0 += 8) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = m0; mt < m0 + 8 && mt < C::MTW; ++mt) {
+      st.o[mt] *= alpha;
+      st.o[mt] = mma_k16(v_frag<T>(tile, 16 * (cb + mt), g, c), pf, st.o[mt]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait until at most `after` stages issued after the current one are still
+// in flight (each wave issues LPW loads per stage; loads complete in order).
+template <int N> constexpr int capped() { return N < 63 ? N : 63; }
+template <int LPW> __device__ __forceinline__ void wait_stages(int after) {
+  switch (after) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<capped<LPW>()>(); break;
+    case 2: wait_vm<capped<2 * LPW>()>(); break;
+    case 3: wait_vm<capped<3 * LPW>()>(); break;
+    case 4: wait_vm<capped<4 * LPW>()>(); break;
+    case 5: wait_vm<capped<5 * LPW>()>(); break;
+    case 6: wait_vm<capped<6 * LPW>()>(); break;
+    default: wait_vm<capped<7 * LPW>()>(); break;
+  }
+}
+
+struct DecodeArgs {
+  const int32_t *pos;
+  char *cache;
+  int64_t bstride_bytes;
+  const void *qt;      // [B, H, R]
+  const void *QR;      // [B, H, DR]
+  const void *KR;      // [B, DR]
+  const float *cg;     // [B, 2R]: latent c then gate pre-activation g
+  const void *b_hc;    // [R]
+  const float *gate_pos;
+  float *part_o;       // [B, splits, H, R]
+  float *part_ml;      // [B, splits, H, 2]
+  int *counters;       // [B], zero on entry
+  void *o;             // [B, H, R]
+  int H, s, chunk, splits, nst;
+  float sl2;
+};
+
+template <typename T, int R, int DR, int NHB>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
+  using C = DecCfg<T, R, DR, NHB>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int s_last;
+
+  const int b = blockIdx.y, split = blockIdx.x;
+  const int t = a.pos[b], s = a.s, jn = t / s, n = jn + 1;
+  const int start = split * a.chunk;
+  if (start >= n) return;
+  const int end = min(n, start + a.chunk);
+  const int ns = (n + a.chunk - 1) / a.chunk;
+  const bool owner = end == n;
+  const int nstage = (end - start + C::SROWS - 1) / C::SROWS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int hb = wave / (C::TP * C::CS), tt = (wave / C::CS) % C::TP, half = wave % C::CS;
+  const int H = a.H, head = hb * 16 + c;
+  char *seq = a.cache + (size_t)b * a.bstride_bytes;
+  char *dummy = smem + a.nst * C::STAGE_B;
+
+  // Everything read from global memory besides the stream is fetched first,
+  // so that later waits for it never wait for the cache loads behind it.
+  WaveState<T, R, DR, NHB> st;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int k = 32 * ks + 8 * g;
+    if (head < H) {
+      if (k < R) load8(st.q[ks], (const T *)a.qt + ((size_t)b * H + head) * R + k);
+      else load8(st.q[ks], (const T *)a.QR + ((size_t)b * H + head) * DR + (k - R));
+    } else {
+      st.q[ks] = zero_frag<T>();
+    }
+  }
+  float mc[C::NU], mg[C::NU], mb[C::NU], mp[C::NU], mkr = 0.0f;
+  if (owner) {
+#pragma unroll
+    for (int i = 0; i < C::NU; ++i) {
+      const int ch = tid + 256 * i;
+      mc[i] = mg[i] = mb[i] = mp[i] = 0.0f;
+      if (ch < R) {
+        mc[i] = a.cg[(size_t)b * 2 * R + ch];
+        mg[i] = a.cg[(size_t)b * 2 * R + R + ch];
+        mb[i] = to_f32(((const T *)a.b_hc)[ch]);
+        mp[i] = a.gate_pos[(size_t)jn * R + ch];
+      }
+    }
+    if (tid < DR) mkr = to_f32(((const T *)a.KR)[(size_t)b * DR + tid]);
+  }
+  asm volatile("" ::: "memory");
+
+  auto issue = [&](int sidx) {
+    char *sb = smem + (sidx % a.nst) * C::STAGE_B;
+    const int row0 = start + sidx * C::SROWS;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int blk = wave + 4 * i;
+      const bool real = (C::NBLK % 4 == 0) || blk < C::NBLK;
+      const int tl = real ? blk / C::NSEG : 0, q = real ? blk % C::NSEG : 0;
+      const int slot = min(row0 + tl * 16 + (lane >> 2), end - 1);
+      dma_block(seq + (size_t)slot * C::RB, q, real ? sb + tl * C::TILE_B + q * 1024 : dummy);
+    }
+  };
+  const int pro = min(a.nst, nstage);
+  for (int k = 0; k < pro; ++k) issue(k);
+
+  st.m = kNegInf;
+  st.l = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < C::MTW; ++mt) st.o[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  for (int k = 0; k < nstage; ++k) {
+    wait_stages<C::LPW>(min(a.nst - 1, nstage - 1 - k));
+    bar();
+    char *sb = smem + (k % a.nst) * C::STAGE_B;
+    const int row0 = start + k * C::SROWS;
+    if (k == nstage - 1) {
+      // Rows past the split read as zeros (their weight is exactly 0, but
+      // the P.V product must not meet stale non-finite LDS contents).
+      const int nz = row0 + C::SROWS - end;
+      for (int idx = tid; idx < nz * (C::RB / 16); idx += 256) {
+        const int r = end - row0 + idx / (C::RB / 16), ch = idx % (C::RB / 16);
+        *(u32x4 *)(sb + (r >> 4) * C::TILE_B + tile_off(r & 15, ch * 16)) = (u32x4){0u, 0u, 0u, 0u};
+      }
+      if (owner) {
+        // Merge the new frame into the newest slot ([Notes] hyper-network
+        // temporal merging; [Fig2] (a)), in the cache and in its LDS copy.
+        const int rr = jn - row0;
+        char *trow = sb + (rr >> 4) * C::TILE_B;
+        T *grow = (T *)(seq + (size_t)jn * C::RB);
+        const bool open = (t % s) == 0;
+#pragma unroll
+        for (int i = 0; i < C::NU; ++i) {
+          const int ch = tid + 256 * i;
+          if (ch < R) {
+            T *lp = (T *)(trow + tile_off(rr & 15, ch * C::ES));
+            const float u = sigmoidf((mg[i] + mb[i]) * mp[i]) * mc[i];
+            const T v = from_f32<T>(open ? u : to_f32(*lp) + u);
+            *lp = v;
+            grow[ch] = v;
+          }
+        }
+        if (tid < DR) {
+          const T v = from_f32<T>(mkr);
+          *(T *)(trow + tile_off(rr & 15, (R + tid) * C::ES)) = v;
+          grow[R + tid] = v;
+        }
+      }
+      wait_lgkm0();
+      bar();
+    }
+    const int kb = row0 + tt * 16;
+    if (kb < end) attend16<T, R, DR, NHB>(st, sb + tt * C::TILE_B, kb, end, half, a.sl2);
+    if (k + a.nst < nstage) {
+      wait_lgkm0();
+      bar();
+      issue(k + a.nst);
+    }
+  }
+
+  // Merge the TP tile streams of each head block through LDS.
+  float lt = st.l + wave_xor(st.l, 16);
+  lt += wave_xor(lt, 32);
+  wait_lgkm0();
+  bar();
+  float *red = (float *)smem;                        // [TP][H][R]
+  float *redm = red + (size_t)C::TP * H * R;         // [TP][H]
+  float *redl = redm + C::TP * H;                    // [TP][H]
+  if (head < H) {
+#pragma unroll
+    for (int mt = 0; mt < C::MTW; ++mt)
+      *(f32x4 *)(red + ((size_t)tt * H + head) * R + 16 * (half * C::MTW + mt) + 4 * g) = st.o[mt];
+    if (g == 0 && half == 0) {
+      redm[tt * H + head] = st.m;
+      redl[tt * H + head] = lt;
+    }
+  }
+  __syncthreads();
+  const size_t pbase = ((size_t)b * a.splits + split) * H;
+  for (int idx = tid; idx < H * R; idx += 256) {
+    const int h = idx / R, ch = idx % R;
+    float M = kNegInf;
+#pragma unroll
+    for (int k = 0; k < C::TP; ++k) M = fmaxf(M, redm[k * H + h]);
+    float acc = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < C::TP; ++k) {
+      const float w = exp2f(redm[k * H + h] - M);
+      acc += w * red[((size_t)k * H + h) * R + ch];
+      L += w * redl[k * H + h];
+    }
+    if (ns == 1) {
+      ((T *)a.o)[((size_t)b * H + h) * R + ch] = from_f32<T>(acc / L);
+    } else {
+      a.part_o[(pbase + h) * R + ch] = acc;
+      if (ch == 0) {
+        a.part_ml[(pbase + h) * 2] = M;
+        a.part_ml[(pbase + h) * 2 + 1] = L;
+      }
+    }
+  }
+  if (ns == 1) return;
+
+  // The last split of this sequence to finish combines all of them.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == ns - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const size_t base = (size_t)b * a.splits * H;
+  for (int idx = tid; idx < H * R; idx += 256) {
+    const int h = idx / R, ch = idx % R;
+    float M = kNegInf;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.part_ml[(base + (size_t)k * H + h) * 2]);
+    float acc = 0.0f, L = 0.0f;
+    for (int k = 0; k < ns; ++k) {
+      const size_t i = base + (size_t)k * H + h;
+      const float w = exp2f(a.part_ml[i * 2] - M);
+      L += w * a.part_ml[i * 2 + 1];
+      acc += w * a.part_o[i * R + ch];
+    }
+    ((T *)a.o)[((size_t)b * H + h) * R + ch] = from_f32<T>(acc / L);
+  }
+  if (tid == 0) a.counters[b] = 0;
+}
+
+// Stand-alone merge-append: one workgroup per sequence.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t *pos, int s, int R, int DR,
+                                                    const float *cg, const T *b_hc,
+                                                    const float *gate_pos, const T *KR,
+                                                    char *cache, int64_t bstride_bytes) {
+  const int b = blockIdx.x, t = pos[b], j = t / s;
+  const bool open = (t % s) == 0;
+  T *row = (T *)(cache + (size_t)b * bstride_bytes) + (size_t)j * (R + DR);
+  for (int ch = threadIdx.x; ch < R; ch += blockDim.x) {
+    const float u = sigmoidf((cg[(size_t)b * 2 * R + R + ch] + to_f32(b_hc[ch])) *
+                             gate_pos[(size_t)j * R + ch]) *
+                    cg[(size_t)b * 2 * R + ch];
+    row[ch] = from_f32<T>(open ? u : to_f32(row[ch]) + u);
+  }
+  for (int ch = threadIdx.x; ch < DR; ch += blockDim.x) row[R + ch] = KR[(size_t)b * DR + ch];
+}
+
+
+template <typename T, int R, int DR, int NHB>
+hipError_t decode_attn_t(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream) {
+  allow_lds<decode_attn_kernel<T, R, DR, NHB>>();
+  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR, NHB>), dim3(p.splits, B), dim3(256), p.lds,
+                     stream, args);
+  return hipGetLastError();
+}
+
+template <typename T, int R, int DR>
+hipError_t decode_attn_h(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream) {
+  if (p.nhb == 1) return decode_attn_t<T, R, DR, 1>(p, B, args, stream);
+  if (p.nhb == 2) return decode_attn_t<T, R, DR, 2>(p, B, args, stream);
+  if constexpr (R < 512) return decode_attn_t<T, R, DR, 4>(p, B, args, stream);
+  return hipErrorInvalidValue;   // decode_plan rejects this case
+}
+
+}  // namespace
+
+#ifndef MTLA_DECODE_TARGET_WGS
+#define MTLA_DECODE_TARGET_WGS 256
+#endif
+
+bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, DecodePlan *plan) {
+  if (!((r == 256 && dR == 32) || (r == 512 && dR == 64))) return false;
+  if (H < 1 || H > 64 || s < 1 || B < 1 || max_pos < 0) return false;
+  const int esz = dtype == 1 ? 2 : 4;
+  DecodePlan p;
+  p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
+  const int cs = r >= 512 ? 2 : 1;
+  if (p.nhb * cs > 4) return false;
+  const int tp = 4 / (p.nhb * cs), srows = 16 * tp;
+  const size_t stage = (size_t)srows * (r + dR) * esz;
+  if (stage + 1024 > 160 * 1024) return false;
+  const int64_t nmax = max_pos / s + 1;
+  const int64_t total = (int64_t)B * nmax;
+  int64_t chunk = (total + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS;
+  chunk = ((chunk + srows - 1) / srows) * srows;
+  const int64_t cap = ((nmax + srows - 1) / srows) * srows;
+  if (chunk > cap) chunk = cap;
+  p.block = srows;
+  p.chunk = (int)chunk;
+  p.splits = (int)((nmax + chunk - 1) / chunk);
+  // Ring: about 4 stages of 36 KB, or more of smaller stages (at most 8).
+  int nst = (int)(144 * 1024 / stage);
+  if (nst > 8) nst = 8;
+  if (nst > chunk / srows) nst = (int)(chunk / srows);
+  if (nst < 1) nst = 1;
+  p.nst = nst;
+  const size_t ring = nst * stage + 1024;
+  const size_t reduce = (size_t)tp * H * r * 4 + (size_t)2 * tp * H * 4;
+  p.lds = ring > reduce ? ring : reduce;
+  if (p.lds > 159 * 1024) return false;
+  *plan = p;
+  return true;
+}
+
+hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
+                                   int s, float scale, const int32_t *pos, void *cache,
+                                   int64_t batch_stride, const void *qt, const void *QR,
+                                   const void *KR_t, const float *cg, const void *b_hc,
+                                   const float *gate_pos, float *part_o, float *part_ml,
+                                   int *counters, void *o, hipStream_t stream) {
+  const int esz = dtype == 1 ? 2 : 4;
+  DecodeArgs args{pos,     (char *)cache, batch_stride * esz, qt,   QR,         KR_t,
+                  cg,      b_hc,          gate_pos,           part_o, part_ml, counters,
+                  o,       H,             s,                  plan.chunk, plan.splits, plan.nst,
+                  scale * kLog2e};
+  if (dtype == 1) {
+    if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream);
+    return decode_attn_h<bf16, 512, 64>(plan, B, args, stream);
+  }
+  if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, args, stream);
+  return decode_attn_h<float, 512, 64>(plan, B, args, stream);
+}
+
+hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,
+                        const void *b_hc, const float *gate_pos, const void *KR_t, void *cache,
+                        int64_t batch_stride, hipStream_t stream) {
+  const int esz = dtype == 1 ? 2 : 4;
+  if (dtype == 1)
+    hipLaunchKernelGGL(merge_kernel<bf16>, dim3(B), dim3(256), 0, stream, pos, s, r, dR, cg,
+                       (const bf16 *)b_hc, gate_pos, (const bf16 *)KR_t, (char *)cache,
+                       batch_stride * esz);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(B), dim3(256), 0, stream, pos, s, r, dR, cg,
+                       (const float *)b_hc, gate_pos, (const float *)KR_t, (char *)cache,
+                       batch_stride * esz);
+  return hipGetLastError();
+}
+
+}  // namespace mtla

@@ -1,17 +1,24 @@
 // Dense NT products C = A B^T on gfx950 MFMA, with fused epilogues for the
-// MTLA projections and the hyper-network gate.
+// MTLA projections ([Notes] = "Multi-head Temporal Latent Attention" paper
+// notes, method section: overall framework, hyper-network temporal merging,
+// the Y formula of decoupled RoPE).
 //
-// Tiling: a workgroup of 4 waves owns a BM x BN output tile; the waves are
-// arranged WGM x WGN and each computes (BM/WGM) x (BN/WGN) with 16x16 MFMA
-// tiles.  K advances 32 elements at a time through two LDS buffers: while a
-// step is multiplied out of one buffer, the next step's A and B chunks are
-// already in flight from global memory into registers, then stored to the
-// other buffer (one barrier per step).  LDS rows are padded by 16 bytes so
-// that the 16 rows a fragment read touches fall in distinct banks.
+// Two kernels:
+//  * gemm_nt_kernel, for many rows (the parallel form): a workgroup of 4
+//    waves owns a BM x BN output tile; K advances 32 at a time through two
+//    LDS buffers with register prefetch (one barrier per step); LDS rows are
+//    padded by 16 bytes so the 16 rows of a fragment read hit distinct banks.
+//  * skinny_gemm_kernel, for at most 128 rows (one decoding step): the
+//    product is bound by reading B once, so each workgroup owns a narrow
+//    column strip (16 or 32 columns) over all rows, and streams its A and B
+//    tiles through a ring of LDS stages by direct global->LDS loads, several
+//    stages in flight.  K may be split over workgroups; the partial tiles are
+//    then summed, in split order, by the last workgroup of the strip to
+//    finish (device-scope atomic counter).
 //
-// B may be split in two row segments (rows < N1 from B1, the rest from B2) so
-// one launch can produce the latent c = X W_dkv^T and the absorbed queries
-// q~ = X A^T from a single pass over X.
+// B may consist of three row segments (rows < N1 from B1, < N2 from B2, the
+// rest from B3), so that one pass over X yields the latent c = X W_dkv^T, the
+// gate pre-activation X W_gate^T and the absorbed queries q~ = X A^T.
 
 #include "common.h"
 #include "kernels.h"
@@ -22,10 +29,19 @@ namespace {
 
 constexpr int BK = 32;
 
+struct BSeg {
+  const void *B1, *B2, *B3;
+  int N1, N2;
+  int ldb;
+  template <typename T> __device__ __forceinline__ const T *row(int n) const {
+    if (n < N1) return (const T *)B1 + (size_t)n * ldb;
+    if (n < N2) return (const T *)B2 + (size_t)(n - N1) * ldb;
+    return (const T *)B3 + (size_t)(n - N2) * ldb;
+  }
+};
+
 template <typename T, int BM, int BN, int WGM, int WGN, class Epi>
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, int lda,
-                                                      const T *__restrict__ B1,
-                                                      const T *__restrict__ B2, int N1, int ldb,
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, int lda, BSeg bs,
                                                       int M, int N, int K, Epi epi) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
@@ -43,7 +59,13 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
   const int g = lane >> 4, c = lane & 15;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const T *Bseg = n0 < N1 ? B1 + (size_t)n0 * ldb : B2 + (size_t)(n0 - N1) * ldb;
+
+  const T *brow[BLD];
+#pragma unroll
+  for (int i = 0; i < BLD; ++i) {
+    const int idx = tid + 256 * i, row = idx / CPR;
+    brow[i] = (idx < BCH && n0 + row < N) ? bs.row<T>(n0 + row) : nullptr;
+  }
 
   u32x4 ra[ALD], rb[BLD];
   auto fetch = [&](int k0) {
@@ -60,10 +82,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
     for (int i = 0; i < BLD; ++i) {
       int idx = tid + 256 * i;
       rb[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (idx < BCH) {
-        int row = idx / CPR, ch = idx % CPR;
-        if (n0 + row < N) rb[i] = ldg16(Bseg + (size_t)row * ldb + k0 + ch * EPC);
-      }
+      if (brow[i]) rb[i] = ldg16(brow[i] + k0 + (idx % CPR) * EPC);
     }
   };
   auto stash = [&](int buf) {
@@ -123,6 +142,174 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
     }
 }
 
+// ---- skinny products (rows <= 128) -------------------------------------------
+
+template <typename T> struct SkinnyCfg {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int SK = 128 / ES / 32 * 2;   // 32-wide k-steps per stage (256-byte rows)
+  static constexpr int RB = SK * 32 * ES, NSEG = RB / 64, TILE_B = 16 * RB;
+};
+
+struct SkinnyArgs {
+  const void *X;
+  int ldx;
+  BSeg bs;
+  int M, N, KS;         // KS = K / 32
+  int kps, ksplit, nst; // k-steps per split, splits, ring stages
+  float *part;          // [ksplit, M, N] fp32 when ksplit > 1
+  int *counters;        // [n strips], zero on entry when ksplit > 1
+  int *zero;            // counters to clear before anything else (first workgroup)
+  int nzero;
+};
+
+template <typename T, int BM, int NT, class Epi>
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi) {
+  using C = SkinnyCfg<T>;
+  constexpr int XG = BM / 16, NG = NT / 16, OT = XG * NG;
+  constexpr int WPT = OT >= 4 ? 1 : 4 / OT, OTW = OT >= 4 ? OT / 4 : 1;
+  constexpr int STAGE_B = (XG + NG) * C::TILE_B;
+  constexpr int NBLK = (XG + NG) * C::NSEG, LPW = (NBLK + 3) / 4;
+  static_assert(OT >= 4 ? OT % 4 == 0 : 4 % OT == 0, "tile split");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int strip = blockIdx.x, split = blockIdx.y;
+  const int n0 = strip * NT;
+  if (a.nzero && strip == 0 && split == 0)
+    for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
+  const int ks0 = split * a.kps, ks1 = min(a.KS, ks0 + a.kps);
+  const int nstage = (ks1 - ks0 + C::SK - 1) / C::SK;
+  char *dummy = smem + a.nst * STAGE_B;
+
+  // Row pointers of the rows this lane copies, one per 16-row group.
+  const char *xrow[XG], *wrow[NG];
+#pragma unroll
+  for (int i = 0; i < XG; ++i)
+    xrow[i] = (const char *)((const T *)a.X + (size_t)min(16 * i + (lane >> 2), a.M - 1) * a.ldx);
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    wrow[i] = (const char *)a.bs.row<T>(min(n0 + 16 * i + (lane >> 2), a.N - 1));
+
+  auto issue = [&](int sidx) {
+    char *sb = smem + (sidx % a.nst) * STAGE_B;
+    const int kst = ks0 + sidx * C::SK;      // first k-step of the stage
+    const size_t koff = (size_t)kst * 32 * C::ES;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave + 4 * i;
+      const int grp = blk / C::NSEG, q = blk % C::NSEG;
+      // a block is real if it exists and its k-step lies inside the split
+      const bool real = blk < NBLK && kst + (q * 64) / (32 * C::ES) < ks1;
+      const char *rp = grp < XG ? xrow[grp < XG ? grp : 0] : wrow[grp - XG < NG ? grp - XG : 0];
+      dma_block(rp + (real ? koff : 0), real ? q : 0, real ? sb + grp * C::TILE_B + q * 1024 : dummy);
+    }
+  };
+
+  f32x4 acc[OTW];
+#pragma unroll
+  for (int i = 0; i < OTW; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int pro = min(a.nst, nstage);
+  for (int k = 0; k < pro; ++k) issue(k);
+  const int ot0 = OT >= 4 ? wave : wave % OT;   // first output tile of this wave
+  const int kpar = OT >= 4 ? 0 : wave / OT;     // k-step parity class when sharing a tile
+  for (int k = 0; k < nstage; ++k) {
+    const int after = min(a.nst - 1, nstage - 1 - k);
+    constexpr int A1 = LPW, A2 = 2 * LPW < 63 ? 2 * LPW : 63, A3 = 3 * LPW < 63 ? 3 * LPW : 63;
+    if (after >= 3) wait_vm<A3>();
+    else if (after == 2) wait_vm<A2>();
+    else if (after == 1) wait_vm<A1>();
+    else wait_vm<0>();
+    bar();
+    const char *sb = smem + (k % a.nst) * STAGE_B;
+    const int kst = ks0 + k * C::SK;
+#pragma unroll
+    for (int kk = 0; kk < C::SK; ++kk) {
+      if (kk % WPT != kpar || kst + kk >= ks1) continue;
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) {
+        const int ot = ot0 + 4 * i, xi = ot / NG, ni = ot % NG;
+        typename Frag<T>::type fa, fb;
+        if constexpr (sizeof(T) == 2) {
+          fa = *(const bf16x8 *)(sb + xi * C::TILE_B + tile_off(c, kk * 64 + g * 16));
+          fb = *(const bf16x8 *)(sb + (XG + ni) * C::TILE_B + tile_off(c, kk * 64 + g * 16));
+        } else {
+          const char *pa = sb + xi * C::TILE_B, *pb = sb + (XG + ni) * C::TILE_B;
+          const f32x4 a0 = *(const f32x4 *)(pa + tile_off(c, kk * 128 + g * 32));
+          const f32x4 a1 = *(const f32x4 *)(pa + tile_off(c, kk * 128 + g * 32 + 16));
+          const f32x4 b0 = *(const f32x4 *)(pb + tile_off(c, kk * 128 + g * 32));
+          const f32x4 b1 = *(const f32x4 *)(pb + tile_off(c, kk * 128 + g * 32 + 16));
+          fa = (f32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          fb = (f32x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        }
+        acc[i] = mma_k32(fa, fb, acc[i]);
+      }
+    }
+    if (k + a.nst < nstage) {
+      wait_lgkm0();
+      bar();
+      issue(k + a.nst);
+    }
+  }
+
+  // Waves that shared an output tile add their k-step classes, in order.
+  if constexpr (WPT > 1) {
+    wait_lgkm0();
+    bar();
+    f32x4 *red = (f32x4 *)smem;   // [4 waves][64 lanes]
+    red[wave * 64 + lane] = acc[0];
+    __syncthreads();
+    if (wave < OT) {
+#pragma unroll
+      for (int k = 1; k < WPT; ++k) acc[0] += red[(wave + k * OT) * 64 + lane];
+    }
+  }
+  const bool writer = OT >= 4 || wave < OT;
+  if (a.ksplit == 1) {
+    if (writer) {
+#pragma unroll
+      for (int i = 0; i < OTW; ++i) {
+        const int ot = ot0 + 4 * i, xi = ot / NG, ni = ot % NG;
+        const int n = n0 + 16 * ni + c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * xi + 4 * g + e;
+          if (m < a.M && n < a.N) epi(m, n, acc[i][e]);
+        }
+      }
+    }
+    return;
+  }
+  if (writer) {
+#pragma unroll
+    for (int i = 0; i < OTW; ++i) {
+      const int ot = ot0 + 4 * i, xi = ot / NG, ni = ot % NG;
+      const int n = n0 + 16 * ni + c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * xi + 4 * g + e;
+        if (m < a.M && n < a.N) a.part[((size_t)split * a.M + m) * a.N + n] = acc[i][e];
+      }
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[strip], 1) == a.ksplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int idx = tid; idx < BM * NT; idx += 256) {
+    const int m = idx / NT, n = n0 + idx % NT;
+    if (m >= a.M || n >= a.N) continue;
+    float v = 0.0f;
+    for (int k = 0; k < a.ksplit; ++k) v += a.part[((size_t)k * a.M + m) * a.N + n];
+    epi(m, n, v);
+  }
+  if (tid == 0) a.counters[strip] = 0;
+}
+
 // ---- epilogues ---------------------------------------------------------------
 
 template <typename T> struct EpiStore {
@@ -142,144 +329,178 @@ struct EpiBiasF32 {
   }
 };
 
-template <typename T> struct EpiLatentQuery {
-  float *c_f32;
-  T *c_T;
+// Columns [0, 2r): latent c and gate pre-activation, fp32 into cg [M, 2r];
+// columns [2r, 2r + HR): absorbed queries into qt [M, HR] (storage type).
+template <typename T> struct EpiProj {
+  float *cg;
   T *qt;
-  int r, HR;
+  int r2, HR;
   __device__ void operator()(int m, int n, float v) const {
-    if (n < r) {
-      c_f32[(size_t)m * r + n] = v;
-      c_T[(size_t)m * r + n] = from_f32<T>(v);
-    } else {
-      qt[(size_t)m * HR + (n - r)] = from_f32<T>(v);
-    }
+    if (n < r2) cg[(size_t)m * r2 + n] = v;
+    else qt[(size_t)m * HR + (n - r2)] = from_f32<T>(v);
   }
 };
 
-template <typename T> struct EpiGatePrefill {
-  const float *c_f32;
-  const T *b_hc;
-  const float *table;
-  float *U;
-  int r, T_len, s;
-  __device__ void operator()(int m, int n, float v) const {
-    const int i = m % T_len, j = i / s;
-    const float g = (v + to_f32(b_hc[n])) * table[(size_t)j * r + n];
-    U[(size_t)m * r + n] = sigmoidf(g) * c_f32[(size_t)m * r + n];
-  }
-};
+__global__ __launch_bounds__(256) void zero_kernel(int *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
-template <typename T> struct EpiGateMerge {
-  const float *c_f32;
-  const T *b_hc;
-  const float *table;
-  const int32_t *pos;
-  T *cache;
-  const T *KR;
-  int64_t bstride;
-  int r, dR, s;
-  __device__ void operator()(int b, int n, float v) const {
-    const int t = pos[b], j = t / s;
-    const float g = (v + to_f32(b_hc[n])) * table[(size_t)j * r + n];
-    const float u = sigmoidf(g) * c_f32[(size_t)b * r + n];
-    T *slot = cache + (size_t)b * bstride + (size_t)j * (r + dR);
-    const float prev = (t % s == 0) ? 0.0f : to_f32(slot[n]);
-    slot[n] = from_f32<T>(prev + u);
-    if (n < dR) slot[r + n] = KR[(size_t)b * dR + n];
-  }
-};
+// W_gate[i, k] = sum_j W_hc[i, j] W_dkv[j, k], accumulated in fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void gate_map_kernel(const T *W_hc, const T *W_dkv, int r, int d,
+                                                       T *W_gate) {
+  const int k = blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
+  if (k >= d) return;
+  float acc = 0.0f;
+  for (int j = 0; j < r; ++j) acc += to_f32(W_hc[(size_t)i * r + j]) * to_f32(W_dkv[(size_t)j * d + k]);
+  W_gate[(size_t)i * d + k] = from_f32<T>(acc);
+}
 
 // ---- dispatch ------------------------------------------------------------------
 
 template <typename T, class Epi>
-hipError_t run_gemm(const T *A, int lda, const T *B1, const T *B2, int N1, int ldb, int M, int N,
-                    int K, Epi epi, hipStream_t stream) {
+hipError_t run_gemm(const T *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
+                    hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (M <= 32) {
-    dim3 grid((N + 63) / 64, (M + 31) / 32);
-    hipLaunchKernelGGL((gemm_nt_kernel<T, 32, 64, 1, 4, Epi>), grid, dim3(256), 0, stream, A, lda,
-                       B1, B2, N1, ldb, M, N, K, epi);
-  } else if (M <= 128) {
-    dim3 grid((N + 63) / 64, (M + 127) / 128);
-    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 64, 4, 1, Epi>), grid, dim3(256), 0, stream, A, lda,
-                       B1, B2, N1, ldb, M, N, K, epi);
-  } else if (sizeof(T) == 4) {
+  if (M <= 128 || sizeof(T) == 4) {
     // fp32 tiles of 128 x 128 would need more than 64 KB of static LDS.
     dim3 grid((N + 63) / 64, (M + 127) / 128);
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 64, 4, 1, Epi>), grid, dim3(256), 0, stream, A, lda,
-                       B1, B2, N1, ldb, M, N, K, epi);
+                       bs, M, N, K, epi);
   } else {
     dim3 grid((N + 127) / 128, (M + 127) / 128);
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 128, 2, 2, Epi>), grid, dim3(256), 0, stream, A,
-                       lda, B1, B2, N1, ldb, M, N, K, epi);
+                       lda, bs, M, N, K, epi);
   }
   return hipGetLastError();
 }
 
+
+template <typename T, int BM, int NT, class Epi>
+hipError_t skinny_t(SkinnyArgs a, int strips, Epi epi, hipStream_t stream) {
+  using C = SkinnyCfg<T>;
+  constexpr size_t stage = (size_t)(BM / 16 + NT / 16) * C::TILE_B;
+  const int nstage_max = (a.kps + C::SK - 1) / C::SK;
+  int nst = nstage_max < 8 ? nstage_max : 8;
+  while (nst > 1 && nst * stage + 1024 > 150 * 1024) --nst;
+  a.nst = nst;
+  size_t lds = nst * stage + 1024;
+  if (lds < 4096) lds = 4096;   // room for the cross-wave reduction
+  allow_lds<skinny_gemm_kernel<T, BM, NT, Epi>>();
+  hipLaunchKernelGGL((skinny_gemm_kernel<T, BM, NT, Epi>), dim3(strips, a.ksplit), dim3(256), lds,
+                     stream, a, epi);
+  return hipGetLastError();
+}
+
+// Skinny product of M <= 128 rows: picks the row tile and column strip and,
+// when `ksplit` > 1, splits K (partials in `part`, counters per strip).
+template <typename T, class Epi>
+hipError_t run_skinny(const T *X, int ldx, const BSeg &bs, int M, int N, int K, int ksplit,
+                      float *part, int *counters, int *zero, int nzero, Epi epi,
+                      hipStream_t stream) {
+  SkinnyArgs a;
+  a.X = X;
+  a.ldx = ldx;
+  a.bs = bs;
+  a.M = M;
+  a.N = N;
+  a.KS = K / 32;
+  if (ksplit < 1 || !part || !counters) ksplit = 1;
+  if (ksplit > a.KS) ksplit = a.KS;
+  a.kps = (a.KS + ksplit - 1) / ksplit;
+  a.ksplit = (a.KS + a.kps - 1) / a.kps;
+  a.nst = 1;
+  a.part = part;
+  a.counters = counters;
+  a.zero = zero;
+  a.nzero = zero ? nzero : 0;
+  if (M <= 16) return skinny_t<T, 16, 16>(a, (N + 15) / 16, epi, stream);
+  if (M <= 32) return skinny_t<T, 32, 16>(a, (N + 15) / 16, epi, stream);
+  if (M <= 64) return skinny_t<T, 64, 16>(a, (N + 15) / 16, epi, stream);
+  return skinny_t<T, 128, 32>(a, (N + 31) / 32, epi, stream);
+}
+
 template <typename T>
-hipError_t latent_query_t(const void *X, int M, int d, const void *W_dkv, int r, const void *A,
-                          int HR, float *c_f32, void *c_T, void *qt, hipStream_t stream) {
-  EpiLatentQuery<T> epi{c_f32, (T *)c_T, (T *)qt, r, HR};
-  return run_gemm<T>((const T *)X, d, (const T *)W_dkv, (const T *)A, r, d, M, r + HR, d, epi,
-                     stream);
+hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_gate, int r,
+                  const void *A, int HR, float *cg, void *qt, int *zero, int nzero,
+                  hipStream_t stream) {
+  EpiProj<T> epi{cg, (T *)qt, 2 * r, HR};
+  BSeg bs{W_dkv, W_gate, A, r, 2 * r, d};
+  const int N = 2 * r + (A ? HR : 0);
+  if (M <= 128)
+    return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, nullptr, zero, nzero, epi,
+                         stream);
+  if (zero && nzero > 0) {
+    hipLaunchKernelGGL(zero_kernel, dim3((nzero + 255) / 256), dim3(256), 0, stream, zero, nzero);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return run_gemm<T>((const T *)X, d, bs, M, N, d, epi, stream);
 }
 
 }  // namespace
 
+int out_proj_splits(int M, int N, int K) {
+  if (M > 128) return 1;
+  const int strips = M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
+  int ks = (256 + strips - 1) / strips;   // aim at about 256 workgroups
+  const int KS = K / 32;
+  if (ks > KS / 4) ks = KS / 4 > 0 ? KS / 4 : 1;   // at least 4 k-steps per split
+  if (ks < 1) ks = 1;
+  return ks;
+}
+
+int out_proj_strips(int M, int N) { return M <= 64 ? (N + 15) / 16 : (N + 31) / 32; }
+
 hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, int ldb, int M,
                              int N, int K, void *out, int ldc, hipStream_t stream) {
+  BSeg bs{Bm, Bm, Bm, N, N, ldb};
   if (dtype == 1)
-    return run_gemm<bf16>((const bf16 *)A, lda, (const bf16 *)Bm, (const bf16 *)Bm, N, ldb, M, N,
-                          K, EpiStore<bf16>{(bf16 *)out, ldc}, stream);
-  return run_gemm<float>((const float *)A, lda, (const float *)Bm, (const float *)Bm, N, ldb, M, N,
-                         K, EpiStore<float>{(float *)out, ldc}, stream);
+    return run_gemm<bf16>((const bf16 *)A, lda, bs, M, N, K, EpiStore<bf16>{(bf16 *)out, ldc},
+                          stream);
+  return run_gemm<float>((const float *)A, lda, bs, M, N, K, EpiStore<float>{(float *)out, ldc},
+                         stream);
+}
+
+hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
+                           float *part, int *counters, hipStream_t stream) {
+  if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);
+  const int ks = out_proj_splits(M, N, K);
+  BSeg bs{Bvo, Bvo, Bvo, N, N, K};
+  if (dtype == 1)
+    return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
+                            EpiStore<bf16>{(bf16 *)Y, N}, stream);
+  return run_skinny<float>((const float *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
+                           EpiStore<float>{(float *)Y, N}, stream);
 }
 
 hipError_t launch_pos_table(int dtype, const void *pe, int rows, int d_pe, const void *W_hp,
                             const void *b_hp, int r, float *table, hipStream_t stream) {
   EpiBiasF32 epi{table, b_hp, dtype == 1, r};
+  BSeg bs{W_hp, W_hp, W_hp, r, r, d_pe};
+  if (dtype == 1) return run_gemm<bf16>((const bf16 *)pe, d_pe, bs, rows, r, d_pe, epi, stream);
+  return run_gemm<float>((const float *)pe, d_pe, bs, rows, r, d_pe, epi, stream);
+}
+
+hipError_t launch_gate_map(int dtype, const void *W_hc, const void *W_dkv, int r, int d,
+                           void *W_gate, hipStream_t stream) {
+  dim3 grid((d + 255) / 256, r);
   if (dtype == 1)
-    return run_gemm<bf16>((const bf16 *)pe, d_pe, (const bf16 *)W_hp, (const bf16 *)W_hp, r, d_pe,
-                          rows, r, d_pe, epi, stream);
-  return run_gemm<float>((const float *)pe, d_pe, (const float *)W_hp, (const float *)W_hp, r, d_pe,
-                         rows, r, d_pe, epi, stream);
+    hipLaunchKernelGGL(gate_map_kernel<bf16>, grid, dim3(256), 0, stream, (const bf16 *)W_hc,
+                       (const bf16 *)W_dkv, r, d, (bf16 *)W_gate);
+  else
+    hipLaunchKernelGGL(gate_map_kernel<float>, grid, dim3(256), 0, stream, (const float *)W_hc,
+                       (const float *)W_dkv, r, d, (float *)W_gate);
+  return hipGetLastError();
 }
 
-hipError_t launch_latent_query(int dtype, const void *X, int M, int d, const void *W_dkv, int r,
-                               const void *A, int HR, float *c_f32, void *c_T, void *qt,
-                               hipStream_t stream) {
-  if (dtype == 1) return latent_query_t<bf16>(X, M, d, W_dkv, r, A, HR, c_f32, c_T, qt, stream);
-  return latent_query_t<float>(X, M, d, W_dkv, r, A, HR, c_f32, c_T, qt, stream);
-}
-
-hipError_t launch_gate_prefill(int dtype, const void *c_T, const float *c_f32, int M, int r,
-                               const void *W_hc, const void *b_hc, const float *table, int T,
-                               int s, float *U, hipStream_t stream) {
-  if (dtype == 1) {
-    EpiGatePrefill<bf16> epi{c_f32, (const bf16 *)b_hc, table, U, r, T, s};
-    return run_gemm<bf16>((const bf16 *)c_T, r, (const bf16 *)W_hc, (const bf16 *)W_hc, r, r, M, r,
-                          r, epi, stream);
-  }
-  EpiGatePrefill<float> epi{c_f32, (const float *)b_hc, table, U, r, T, s};
-  return run_gemm<float>((const float *)c_T, r, (const float *)W_hc, (const float *)W_hc, r, r, M,
-                         r, r, epi, stream);
-}
-
-hipError_t launch_gate_merge(int dtype, const void *c_T, const float *c_f32, int B, int r, int dR,
-                             const void *W_hc, const void *b_hc, const float *table,
-                             const int32_t *pos, int s, void *cache, int64_t batch_stride,
-                             const void *KR_t, hipStream_t stream) {
-  if (dtype == 1) {
-    EpiGateMerge<bf16> epi{c_f32, (const bf16 *)b_hc, table, pos, (bf16 *)cache,
-                           (const bf16 *)KR_t, batch_stride, r, dR, s};
-    return run_gemm<bf16>((const bf16 *)c_T, r, (const bf16 *)W_hc, (const bf16 *)W_hc, r, r, B, r,
-                          r, epi, stream);
-  }
-  EpiGateMerge<float> epi{c_f32, (const float *)b_hc, table, pos, (float *)cache,
-                          (const float *)KR_t, batch_stride, r, dR, s};
-  return run_gemm<float>((const float *)c_T, r, (const float *)W_hc, (const float *)W_hc, r, r, B,
-                         r, r, epi, stream);
+hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv,
+                       const void *W_gate, int r, const void *A, int HR, float *cg, void *qt,
+                       int *zero, int nzero, hipStream_t stream) {
+  if (dtype == 1)
+    return proj_t<bf16>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
+  return proj_t<float>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
 }
 
 }  // namespace mtla

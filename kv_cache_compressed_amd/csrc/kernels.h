@@ -18,36 +18,35 @@ hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, 
 hipError_t launch_pos_table(int dtype, const void *pe, int rows, int d_pe, const void *W_hp,
                             const void *b_hp, int r, float *table, hipStream_t stream);
 
-// Latent projection c = X W_dkv^T for M frames, written both as fp32
-// (c_f32 [M, r]) and in the storage type (c_T [M, r]).  When HR > 0 the same
-// launch also produces the absorbed queries q~ = X A^T into qt [M, HR]
-// (storage type), A being [HR, d].
-hipError_t launch_latent_query(int dtype, const void *X, int M, int d, const void *W_dkv, int r,
-                               const void *A, int HR, float *c_f32, void *c_T, void *qt,
-                               hipStream_t stream);
+// W_gate[r, d] = W_hc[r, r] W_dkv[r, d] (fp32 accumulation, storage type).
+hipError_t launch_gate_map(int dtype, const void *W_hc, const void *W_dkv, int r, int d,
+                           void *W_gate, hipStream_t stream);
 
-// Hyper-network gate of the parallel form: for row m = b*T + i,
-//   U[m, :] = Sigmoid((c_T[m] W_hc^T + b_hc) * table[floor(i/s)]) * c_f32[m].
-hipError_t launch_gate_prefill(int dtype, const void *c_T, const float *c_f32, int M, int r,
-                               const void *W_hc, const void *b_hc, const float *table, int T,
-                               int s, float *U, hipStream_t stream);
+// One pass over X [M, d]: cg [M, 2r] (fp32) = (X W_dkv^T, X W_gate^T), and,
+// when A != nullptr, qt [M, HR] (storage type) = X A^T with A [HR, d].  When
+// `zero` is given, its first `nzero` ints are cleared before anything else
+// (the counters of the kernels that follow in a decoding step).
+hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv,
+                       const void *W_gate, int r, const void *A, int HR, float *cg, void *qt,
+                       int *zero, int nzero, hipStream_t stream);
 
-// Hyper-network gate of the incremental form, merged into the cache in
-// place: for sequence b with t = pos[b], j = floor(t/s),
-//   u = Sigmoid((c_T[b] W_hc^T + b_hc) * table[j]) * c_f32[b]
-//   slot j latent = (t mod s == 0 ? 0 : slot j latent) + u;  slot j key = KR_t[b].
-hipError_t launch_gate_merge(int dtype, const void *c_T, const float *c_f32, int B, int r, int dR,
-                             const void *W_hc, const void *b_hc, const float *table,
-                             const int32_t *pos, int s, void *cache, int64_t batch_stride,
-                             const void *KR_t, hipStream_t stream);
+// Y [M, N] = O [M, K] Bvo [N, K]^T.  For M <= 128 the product is split over
+// K (out_proj_splits) with fp32 partials in `part` [splits, M, N] and one
+// counter per column strip in `counters` [out_proj_strips] (zero on entry,
+// zero again on exit); both may be null to disable the split.
+hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
+                           float *part, int *counters, hipStream_t stream);
+int out_proj_splits(int M, int N, int K);
+int out_proj_strips(int M, int N);
 
-// ---- incremental-decoding attention ---------------------------------------
+// ---- incremental decoding ---------------------------------------------------
 
 struct DecodePlan {
-  int nhb;      // head blocks of 16 per wave
-  int block;    // slots staged per workgroup iteration
+  int nhb;      // head blocks of 16
+  int block;    // slots per LDS stage
   int chunk;    // slots per split (workgroup)
   int splits;   // splits per sequence (grid x)
+  int nst;      // LDS ring stages
   size_t lds;   // dynamic LDS bytes
 };
 
@@ -55,29 +54,34 @@ struct DecodePlan {
 // positions are all <= max_pos.  Returns false for unsupported shapes.
 bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, DecodePlan *plan);
 
-// Split-K attention over slots 0..floor(pos[b]/s) of every sequence.
-// qt [B, H, r] and QR [B, H, dR] in the storage type; partials fp32:
-// part_o [B, splits, H, r] (un-normalised, relative to part_ml's max) and
-// part_ml [B, splits, H, 2] = (running max in log2 units, sum of exponentials).
+// Merge of frame pos[b] into slot floor(pos[b]/s) of every sequence (from
+// cg = (c, gate pre-activation) and the tables), then attention over slots
+// 0..floor(pos[b]/s) into o [B, H, r] (storage type).  qt [B, H, r], QR
+// [B, H, dR], KR_t [B, dR]; partials part_o [B, splits, H, r] and part_ml
+// [B, splits, H, 2] fp32; counters [B] zero on entry (zero again on exit).
 hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
-                                   int s, float scale, const int32_t *pos, const void *cache,
+                                   int s, float scale, const int32_t *pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
-                                   float *part_o, float *part_ml, hipStream_t stream);
+                                   const void *KR_t, const float *cg, const void *b_hc,
+                                   const float *gate_pos, float *part_o, float *part_ml,
+                                   int *counters, void *o, hipStream_t stream);
 
-// Log-sum-exp combine of the splits into o [B, H, r] (storage type).
-hipError_t launch_decode_combine(int dtype, const DecodePlan &plan, int B, int H, int r, int s,
-                                 const int32_t *pos, const float *part_o, const float *part_ml,
-                                 void *o, hipStream_t stream);
+// Merge alone (no attention), one workgroup per sequence.
+hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,
+                        const void *b_hc, const float *gate_pos, const void *KR_t, void *cache,
+                        int64_t batch_stride, hipStream_t stream);
 
 // ---- parallel form ----------------------------------------------------------
 
-// Segmented (per group of s frames) inclusive sum of U into the intermediate
-// states C' [B, T, r], plus the compressed rows keys[b, j] = (C'_e(j), KR_e(j))
-// with e(j) = min(s*j + s - 1, T - 1), into `keys` [B, keys_stride] and, when
-// cache != nullptr, into the caller's cache.
-hipError_t launch_group_scan(int dtype, const float *U, const void *KR, int B, int T, int r, int dR,
-                             int s, void *Cp, void *keys, int64_t keys_stride, void *cache,
-                             int64_t cache_stride, hipStream_t stream);
+// Hyper-network gate and segmented (per group of s frames) inclusive sum:
+// U[b, i] = Sigmoid((g + b_hc) * table[floor(i/s)]) * c from cg [B*T, 2r],
+// then the intermediate states C' [B, T, r], plus the compressed rows
+// keys[b, j] = (C'_e(j), KR_e(j)) with e(j) = min(s*j + s - 1, T - 1), into
+// `keys` [B, keys_stride] and, when cache != nullptr, into the caller's cache.
+hipError_t launch_group_scan(int dtype, const float *cg, const void *b_hc, const float *table,
+                             const void *KR, int B, int T, int r, int dR, int s, void *Cp,
+                             void *keys, int64_t keys_stride, void *cache, int64_t cache_stride,
+                             hipStream_t stream);
 
 // Stride-aware masked attention: O [B, T, H, r] from queries qt [B, T, H, r],
 // QR [B, T, H, dR], the compressed keys [B, keys_stride] (ceil(T/s) rows of

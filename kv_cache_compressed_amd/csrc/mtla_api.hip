@@ -49,6 +49,7 @@ mtla_status check_dims(const mtla_dims *d) {
     return fail(MTLA_ERR_UNSUPPORTED, "(r, d_hR) = (%d, %d) not in {(256,32), (512,64)}", d->r,
                 d->d_hR);
   if (d->H > 64) return fail(MTLA_ERR_UNSUPPORTED, "H=%d > 64", d->H);
+  if (d->r == 512 && d->H > 32) return fail(MTLA_ERR_UNSUPPORTED, "H=%d > 32 with r=512", d->H);
   return MTLA_OK;
 }
 
@@ -61,7 +62,7 @@ mtla_status check_dims(const mtla_dims *d) {
 mtla_status check_weights(const mtla_weights *w, bool need_attn) {
   if (!w) return fail(MTLA_ERR_ARG, "weights is null");
   CHECK_PTR(w->W_dkv);
-  CHECK_PTR(w->W_hc);
+  CHECK_PTR(w->W_gate);
   CHECK_PTR(w->b_hc);
   CHECK_PTR(w->gate_pos);
   if (w->gate_pos_rows <= 0) return fail(MTLA_ERR_ARG, "gate_pos_rows=%d", w->gate_pos_rows);
@@ -96,29 +97,34 @@ mtla_status launched(hipError_t e, const char *what) {
   } while (0)
 
 struct DecodeWs {
-  size_t c_f32, c_T, qt, part_o, part_ml, o, total;
+  size_t cg, qt, part_o, part_ml, o, ypart, counters, total;
+  int ncount;
 };
 
+// Workspace of one decoding step (plan != nullptr) or of a merge-append.
 DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
   DecodeWs w;
   const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r;
   size_t off = 0;
-  w.c_f32 = off; off += align_up(B * r * 4);
-  w.c_T = off;   off += align_up(B * r * e);
+  w.cg = off; off += align_up(B * 2 * r * 4);
+  w.qt = w.part_o = w.part_ml = w.o = w.ypart = w.counters = 0;
+  w.ncount = 0;
   if (plan) {
-    w.qt = off;      off += align_up(B * HR * e);
-    w.part_o = off;  off += align_up((size_t)B * plan->splits * HR * 4);
-    w.part_ml = off; off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
-    w.o = off;       off += align_up(B * HR * e);
-  } else {
-    w.qt = w.part_o = w.part_ml = w.o = 0;
+    const int ks = mtla::out_proj_splits(B, d->d, (int)HR);
+    w.ncount = B + mtla::out_proj_strips(B, d->d);
+    w.qt = off;       off += align_up(B * HR * e);
+    w.part_o = off;   off += align_up((size_t)B * plan->splits * HR * 4);
+    w.part_ml = off;  off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
+    w.o = off;        off += align_up(B * HR * e);
+    w.ypart = off;    off += align_up((size_t)ks * B * d->d * 4);
+    w.counters = off; off += align_up((size_t)w.ncount * 4);
   }
   w.total = off;
   return w;
 }
 
 struct PrefillWs {
-  size_t c_f32, c_T, U, Cp, keys, qt, O, total;
+  size_t cg, Cp, keys, qt, O, total;
   int64_t keys_stride;
 };
 
@@ -128,9 +134,7 @@ PrefillWs prefill_ws(const mtla_dims *d, int B, int T) {
   const int64_t nS = (T + d->s - 1) / d->s;
   w.keys_stride = nS * (d->r + d->d_hR);
   size_t off = 0;
-  w.c_f32 = off; off += align_up(M * r * 4);
-  w.c_T = off;   off += align_up(M * r * e);
-  w.U = off;     off += align_up(M * r * 4);
+  w.cg = off;    off += align_up(M * 2 * r * 4);
   w.Cp = off;    off += align_up(M * r * e);
   w.keys = off;  off += align_up((size_t)B * w.keys_stride * e);
   w.qt = off;    off += align_up(M * HR * e);
@@ -202,6 +206,20 @@ mtla_status mtla_gate_pos_table(const mtla_dims *dims, const void *pe, int32_t r
   return ok();
 }
 
+mtla_status mtla_gate_content_map(const mtla_dims *dims, const void *W_hc, const void *W_dkv,
+                                  void *W_gate, void *stream) {
+  if (!dims) return fail(MTLA_ERR_ARG, "dims is null");
+  if (dims->dtype != MTLA_F32 && dims->dtype != MTLA_BF16) return fail(MTLA_ERR_ARG, "dtype");
+  if (dims->r <= 0 || dims->d <= 0) return fail(MTLA_ERR_ARG, "r and d must be > 0");
+  CHECK_PTR(W_hc);
+  CHECK_PTR(W_dkv);
+  CHECK_PTR(W_gate);
+  LAUNCH(mtla::launch_gate_map(dims->dtype, W_hc, W_dkv, dims->r, dims->d, W_gate,
+                               (hipStream_t)stream),
+         "gate content map");
+  return ok();
+}
+
 mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                               const void *X_t, const void *KR_t, const int32_t *pos, int32_t B,
                               int32_t max_pos, void *workspace, size_t ws_bytes, void *stream) {
@@ -217,16 +235,13 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
   const DecodeWs ws = decode_ws(dims, B, nullptr);
   if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
   hipStream_t s = (hipStream_t)stream;
-  char *base = (char *)workspace;
-  float *c_f32 = (float *)(base + ws.c_f32);
-  void *c_T = base + ws.c_T;
-  LAUNCH(mtla::launch_latent_query(dims->dtype, X_t, B, dims->d, w->W_dkv, dims->r, nullptr, 0,
-                                   c_f32, c_T, nullptr, s),
-         "latent projection");
-  LAUNCH(mtla::launch_gate_merge(dims->dtype, c_T, c_f32, B, dims->r, dims->d_hR, w->W_hc, w->b_hc,
-                                 w->gate_pos, pos, dims->s, cache->slots, cache->batch_stride, KR_t,
-                                 s),
-         "gate and merge");
+  float *cg = (float *)((char *)workspace + ws.cg);
+  LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, nullptr, 0,
+                           cg, nullptr, nullptr, 0, s),
+         "latent and gate projection");
+  LAUNCH(mtla::launch_merge(dims->dtype, B, dims->r, dims->d_hR, dims->s, pos, cg, w->b_hc,
+                            w->gate_pos, KR_t, cache->slots, cache->batch_stride, s),
+         "merge");
   return ok();
 }
 
@@ -261,27 +276,23 @@ mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const
   if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
   hipStream_t s = (hipStream_t)stream;
   char *base = (char *)workspace;
-  float *c_f32 = (float *)(base + ws.c_f32);
-  void *c_T = base + ws.c_T, *qt = base + ws.qt, *o = base + ws.o;
+  float *cg = (float *)(base + ws.cg);
+  void *qt = base + ws.qt, *o = base + ws.o;
   float *part_o = (float *)(base + ws.part_o), *part_ml = (float *)(base + ws.part_ml);
+  float *ypart = (float *)(base + ws.ypart);
+  int *counters = (int *)(base + ws.counters);
   const int HR = dims->H * dims->r;
-  LAUNCH(mtla::launch_latent_query(dims->dtype, X_t, B, dims->d, w->W_dkv, dims->r, w->A, HR, c_f32,
-                                   c_T, qt, s),
-         "latent and query projection");
-  LAUNCH(mtla::launch_gate_merge(dims->dtype, c_T, c_f32, B, dims->r, dims->d_hR, w->W_hc, w->b_hc,
-                                 w->gate_pos, pos, dims->s, cache->slots, cache->batch_stride, KR_t,
-                                 s),
-         "gate and merge");
+  LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
+                           qt, counters, ws.ncount, s),
+         "latent, gate and query projection");
   if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
                                        eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
-                                       QR_t, part_o, part_ml, s),
-         "decode attention");
+                                       QR_t, KR_t, cg, w->b_hc, w->gate_pos, part_o, part_ml,
+                                       counters, o, s),
+         "merge and decode attention");
   if ((st = record(events, 1, s)) != MTLA_OK) return st;
-  LAUNCH(mtla::launch_decode_combine(dims->dtype, plan, B, dims->H, dims->r, dims->s, pos, part_o,
-                                     part_ml, o, s),
-         "split combine");
-  LAUNCH(mtla::launch_gemm_store(dims->dtype, o, HR, w->Bvo, HR, B, dims->d, HR, Y, dims->d, s),
+  LAUNCH(mtla::launch_out_proj(dims->dtype, o, B, HR, w->Bvo, dims->d, Y, ypart, counters + B, s),
          "output projection");
   return ok();
 }
@@ -317,26 +328,24 @@ mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const voi
   if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
   hipStream_t s = (hipStream_t)stream;
   char *base = (char *)workspace;
-  float *c_f32 = (float *)(base + ws.c_f32), *U = (float *)(base + ws.U);
-  void *c_T = base + ws.c_T, *keys = base + ws.keys, *qt = base + ws.qt, *O = base + ws.O;
+  float *cg = (float *)(base + ws.cg);
+  void *keys = base + ws.keys, *qt = base + ws.qt, *O = base + ws.O;
   void *Cp = Cprime_out ? Cprime_out : (void *)(base + ws.Cp);
   const int M = B * T, HR = dims->H * dims->r;
-  LAUNCH(mtla::launch_latent_query(dims->dtype, X, M, dims->d, w->W_dkv, dims->r, w->A, HR, c_f32,
-                                   c_T, qt, s),
-         "latent and query projection");
-  LAUNCH(mtla::launch_gate_prefill(dims->dtype, c_T, c_f32, M, dims->r, w->W_hc, w->b_hc,
-                                   w->gate_pos, T, dims->s, U, s),
-         "gate");
-  LAUNCH(mtla::launch_group_scan(dims->dtype, U, KR, B, T, dims->r, dims->d_hR, dims->s, Cp, keys,
-                                 ws.keys_stride, cache_out ? cache_out->slots : nullptr,
+  LAUNCH(mtla::launch_proj(dims->dtype, X, M, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
+                           qt, nullptr, 0, s),
+         "latent, gate and query projection");
+  LAUNCH(mtla::launch_group_scan(dims->dtype, cg, w->b_hc, w->gate_pos, KR, B, T, dims->r,
+                                 dims->d_hR, dims->s, Cp, keys, ws.keys_stride,
+                                 cache_out ? cache_out->slots : nullptr,
                                  cache_out ? cache_out->batch_stride : 0, s),
-         "group scan");
+         "gate and group scan");
   if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_prefill_attention(dims->dtype, B, T, dims->H, dims->r, dims->d_hR, dims->s,
                                         eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s),
          "strided attention");
   if ((st = record(events, 1, s)) != MTLA_OK) return st;
-  LAUNCH(mtla::launch_gemm_store(dims->dtype, O, HR, w->Bvo, HR, M, dims->d, HR, Y, dims->d, s),
+  LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HR, w->Bvo, dims->d, Y, nullptr, nullptr, s),
          "output projection");
   return ok();
 }

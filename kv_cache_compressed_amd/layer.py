@@ -1,8 +1,8 @@
 """Convenience container for one MTLA layer on the GPU.
 
 Holds the device weights in the layouts the C ABI takes, the fp32
-position-branch table (built once on the GPU by mtla_gate_pos_table) and
-reusable workspaces, and forwards to the three hot-path entry points.  It
+position-branch table and the folded content-branch map (built once on the
+GPU by mtla_gate_pos_table and mtla_gate_content_map) and reusable workspaces, and forwards to the three hot-path entry points.  It
 only marshals arguments; all arithmetic runs in libmtla.so.
 """
 from __future__ import annotations
@@ -24,7 +24,8 @@ class MTLALayer:
             if v.dtype != self.dtype or not v.is_cuda or not v.is_contiguous():
                 raise ValueError(f"{k} must be a contiguous device tensor of {self.dtype}")
         self.gate_pos = L.mtla_gate_pos_table(self.dims, pe, W_hp, b_hp)
-        self.w = L.make_weights(W_dkv, W_hc, b_hc, self.gate_pos, A, Bvo)
+        self.W_gate = L.mtla_gate_content_map(self.dims, W_hc, W_dkv)
+        self.w = L.make_weights(W_dkv, self.W_gate, b_hc, self.gate_pos, A, Bvo)
         self._ws = {}
 
     @classmethod

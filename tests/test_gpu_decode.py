@@ -110,6 +110,17 @@ def test_decode_head_counts(H):
     _decode_case(dims, [5, 700, 1999], "bf16", 7100 + H)
 
 
+def test_decode_batch_above_128():
+    """More than 128 sequences: the projections take the tiled path and the
+    split counters are cleared by their own kernel."""
+    needs_gpu()
+    dims = Dims(d=256, H=8, d_h=64, r=256, d_hR=32, s=2)
+    rng = np.random.default_rng(7300)
+    pos = rng.integers(0, 600, size=136)
+    say("decode B=136")
+    _decode_case(dims, pos, "bf16", 7300, check=[0, 1, 67, 135])
+
+
 def test_decode_wide_latent_fp32():
     needs_gpu()
     dims = Dims(d=256, H=4, d_h=128, r=512, d_hR=64, s=2)

@@ -51,3 +51,16 @@ def test_merge_append_matches_oracle(storage, s, B):
         assert np.array_equal(after[b][other], before[b][other], equal_nan=True), b
         assert relerr(after[b, j, :dims.r], lat[j]) < TOL[storage], (b, relerr(after[b, j, :dims.r], lat[j]))
         assert np.array_equal(after[b, j, dims.r:], rk[j])
+
+
+def test_gate_content_map_matches_product():
+    """W_gate = W_hc W_dkv, the content branch folded into the latent map:
+    W_gate x = W_hc (W_dkv x) by associativity."""
+    needs_gpu()
+    dims = Dims(d=512, H=8, d_h=64, r=256, d_hR=32, s=2)
+    w, W, L = layer(dims, 12, "bf16", pe_rows=8)
+    got = host(L.W_gate)
+    ref = w["W_hc"] @ w["W_dkv"]
+    e = relerr(got, ref)
+    say("gate content map relerr", e)
+    assert e < 1e-2      # one bf16 rounding of each entry
