@@ -49,6 +49,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class HipEvents:
+    """Timing events of the HIP runtime torch has loaded, created with
+    hipEventDisableSystemFence: recording them adds no system-scope release
+    (no L2 write-back), so a pair recorded around one kernel brackets that
+    kernel alone."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7")   # already loaded by torch: same runtime
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
 def _decode_setup(cfg: int, seed_pos=None):
     import torch
     import synth
@@ -122,11 +156,8 @@ def run_decode(cfg: int, steps: int, warmup: int) -> dict:
     S = _decode_setup(cfg)
     layer, caches, (x, qr, kr, pos), Y = S["layer"], S["caches"], S["inputs"], S["Y"]
     n_rep, max_pos = len(caches), S["max_pos"]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:              # create the underlying events up front
-        a.record()
-        b.record()
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(steps)]
 
     def one(i, events=None):
         layer.decode_step(caches[i % n_rep], x, qr, kr, pos, max_pos, Y, events=events)
@@ -135,7 +166,10 @@ def run_decode(cfg: int, steps: int, warmup: int) -> dict:
         one(i)
     torch.cuda.synchronize()
     total_ms = _timed_loop(lambda i: one(i, ev[i]), steps)
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
     step_ms = total_ms / steps
     attn_avg = float(np.mean(attn_ms))
     return dict(name=S["name"], B=S["B"], dims=S["dims"].asdict(), steps=steps,
@@ -169,17 +203,17 @@ def run_prefill(steps: int = 10, warmup: int = 3) -> dict:
     del seq
     Y = torch.empty(B, T, dims.d, dtype=torch.bfloat16, device="cuda")
     cache = layer.new_cache(B, ms)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        b.record()
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(steps)]
     for i in range(warmup):
         layer.prefill(X, QR, KR, Y, cache=cache)
     torch.cuda.synchronize()
     fwd_ms = _timed_loop(lambda i: layer.prefill(X, QR, KR, Y, cache=cache, events=ev[i]),
                          steps) / steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
     attn_flops, pairs = prefill_flops(B, T, dims.H, dims.r, dims.d_hR, dims.s)
     M = B * T
     proj_flops = (2 * M * dims.d * dims.r            # latent

@@ -170,11 +170,17 @@ def mtla_merge_append(dims: Dims, w: Weights, cache: Cache, X_t, KR_t, pos, max_
 
 
 def _events(events):
-    """Two torch.cuda.Event objects -> the C array of their raw handles."""
+    """Two events -> the C array of their raw hipEvent_t handles.  Accepts
+    torch.cuda.Event objects or raw handles (ints / c_void_p)."""
+    handles = []
     for e in events:
-        if e.cuda_event == 0:      # torch creates the underlying event on first record
-            e.record()
-    return (c_void_p * 2)(events[0].cuda_event, events[1].cuda_event)
+        if isinstance(e, torch.cuda.Event):
+            if e.cuda_event == 0:      # torch creates the underlying event on first record
+                e.record()
+            handles.append(e.cuda_event)
+        else:
+            handles.append(e.value if isinstance(e, c_void_p) else int(e))
+    return (c_void_p * 2)(*handles)
 
 
 def mtla_decode_step(dims: Dims, w: Weights, cache: Cache, X_t, QR_t, KR_t, pos, max_pos: int,

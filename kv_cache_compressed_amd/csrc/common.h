@@ -118,6 +118,33 @@ __device__ __forceinline__ void dma_block(const char *row_ptr, int q, char *dst)
                                    0, 0);
 }
 
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Eight ds_read_b64_tr_b16 (see the decode kernel) issued together, in one
+// asm statement that also waits for them: the compiler cannot tell that these
+// reads do not alias direct-to-LDS loads still in flight and would otherwise
+// wait for all of those (vmcnt(0)) before the builtin's read.  Outputs are
+// early-clobber, so no address register is reused while a read is pending.
+__device__ __forceinline__ void ds_read_tr8(bf16x4 (&v)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // wait for every outstanding direct-to-LDS load); the empty asm statements
 // keep the compiler from moving memory accesses across it.  Callers order

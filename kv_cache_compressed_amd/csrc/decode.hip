@@ -27,9 +27,9 @@
 //    frame: u = Sigmoid((g + b_hc) * Linear(pe_j)) * c, slot j = u (t mod s
 //    == 0) or slot j + u, RoPE key j = K^R_t, written to the cache and into
 //    its LDS copy before that row is attended.
-//  * Splits write (max, sum, O) partials; the last split of a sequence to
-//    finish (device-scope atomic counter) merges them by log-sum-exp in
-//    split order, so results are deterministic.
+//  * Splits write (max, sum, O) partials, merged by log-sum-exp in split
+//    order by a small second kernel (deterministic results); a sequence that
+//    fits one split is normalised and written directly.
 
 #include <math.h>
 
@@ -47,9 +47,11 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 template <typename T, int R, int DR, int NHB> struct DecCfg {
   static constexpr int RK = R + DR, ES = (int)sizeof(T), RB = RK * ES, NSEG = RB / 64;
   static constexpr int CS = R >= 512 ? 2 : 1;           // channel halves of O
-  static constexpr int TP = 4 / (NHB * CS), SROWS = 16 * TP;
-  static constexpr int TILE_B = 16 * RB, STAGE_B = TP * TILE_B;
-  static constexpr int NBLK = TP * NSEG, LPW = (NBLK + 3) / 4;
+  static constexpr int TP = 4 / (NHB * CS);               // tile streams
+  static constexpr int TPW = TP >= 2 ? 1 : 2;             // tiles per wave per stage
+  static constexpr int SROWS = 16 * TP * TPW;
+  static constexpr int TILE_B = 16 * RB, STAGE_B = TP * TPW * TILE_B;
+  static constexpr int NBLK = TP * TPW * NSEG, LPW = (NBLK + 3) / 4;
   static constexpr int KS = RK / 32, MT = R / 16, MTW = MT / CS, NU = (R + 255) / 256;
   static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
   static_assert(TP >= 1, "too many head blocks for this width");
@@ -98,9 +100,15 @@ __device__ __forceinline__ void attend16(WaveState<T, R, DR, NHB> &st, const cha
                                          int end, int half, float sl2) {
   using C = DecCfg<T, R, DR, NHB>;
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  // Two independent accumulation chains over the k-steps.
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) sc = mma_k32(s_frag<T>(tile, c, ks, g), st.q[ks], sc);
+  for (int ks = 0; ks + 1 < C::KS; ks += 2) {
+    s0 = mma_k32(s_frag<T>(tile, c, ks, g), st.q[ks], s0);
+    s1 = mma_k32(s_frag<T>(tile, c, ks + 1, g), st.q[ks + 1], s1);
+  }
+  if constexpr (C::KS % 2) s0 = mma_k32(s_frag<T>(tile, c, C::KS - 1, g), st.q[C::KS - 1], s0);
+  const f32x4 sc = s0 + s1;
   float v[4], mx = kNegInf;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -108,32 +116,49 @@ __device__ __forceinline__ void attend16(WaveState<T, R, DR, NHB> &st, const cha
     mx = fmaxf(mx, v[e]);
   }
   mx = fmaxf(mx, wave_xor(mx, 16));
-  mx = fmaxf(mx, wave_xor(mx, 32));
-  const float mn = fmaxf(st.m, mx);   // finite: key kbase is visible
-  const float alpha = exp2f(st.m - mn);
+  mx = fmaxf(mx, wave_xor(mx, 32));   // finite: key kbase is visible
+  // Lazy rescaling: the reference max m only moves when a score exceeds it
+  // by more than 8 (log2 units), so p = 2^(z - m) <= 2^8 and the rescale of O
+  // (a pass over all its registers) is skipped on almost every tile.
+  const bool up = mx > st.m + 8.0f;
+  if (__builtin_amdgcn_ballot_w64(up)) {
+    const float mn = up ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < C::MTW; ++mt) st.o[mt] *= alpha;
+    st.m = mn;
+  }
   typename Frag4<T>::type pf;
   float ps = 0.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float p = exp2f(v[e] - mn);
+    const float p = __builtin_amdgcn_exp2f(v[e] - st.m);
     ps += p;
     pf[e] = from_f32<T>(p);
   }
-  st.l = st.l * alpha + ps;
-  st.m = mn;
-  // Channel blocks in groups of 8, so the compiler does not hoist every
-  // transposing read of the tile ahead of the products (register pressure).
+  st.l += ps;
+  // Channel blocks in groups of 8: the transposing reads of a group are
+  // issued together, then its 8 products.
   const int cb = half * C::MTW;
+  static_assert(C::MTW % 8 == 0, "channel blocks come in groups of 8");
 #pragma unroll
   for (int m0 = 0; m0 < C::MTW; m0 += 8) {
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (sizeof(T) == 2) {
+      uint32_t ad[8];
+      bf16x4 vv[8];
 #pragma unroll
-    for (int mt = m0; mt < m0 + 8 && mt < C::MTW; ++mt) {
-      st.o[mt] *= alpha;
-      st.o[mt] = mma_k16(v_frag<T>(tile, 16 * (cb + mt), g, c), pf, st.o[mt]);
+      for (int j = 0; j < 8; ++j)
+        ad[j] = lds_addr(tile + tile_off(4 * g + (c >> 2), (16 * (cb + m0 + j) + 4 * (c & 3)) * 2));
+      ds_read_tr8(vv, ad);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.o[m0 + j] = mma_k16(vv[j], pf, st.o[m0 + j]);
+    } else {
+#pragma unroll
+      for (int mt = m0; mt < m0 + 8; ++mt)
+        st.o[mt] = mma_k16(v_frag<T>(tile, 16 * (cb + mt), g, c), pf, st.o[mt]);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait until at most `after` stages issued after the current one are still
@@ -164,7 +189,6 @@ struct DecodeArgs {
   const float *gate_pos;
   float *part_o;       // [B, splits, H, R]
   float *part_ml;      // [B, splits, H, 2]
-  int *counters;       // [B], zero on entry
   void *o;             // [B, H, R]
   int H, s, chunk, splits, nst;
   float sl2;
@@ -174,8 +198,6 @@ template <typename T, int R, int DR, int NHB>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   using C = DecCfg<T, R, DR, NHB>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  __shared__ int s_last;
-
   const int b = blockIdx.y, split = blockIdx.x;
   const int t = a.pos[b], s = a.s, jn = t / s, n = jn + 1;
   const int start = split * a.chunk;
@@ -281,8 +303,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       wait_lgkm0();
       bar();
     }
-    const int kb = row0 + tt * 16;
-    if (kb < end) attend16<T, R, DR, NHB>(st, sb + tt * C::TILE_B, kb, end, half, a.sl2);
+#pragma unroll
+    for (int i = 0; i < C::TPW; ++i) {
+      const int ti = tt + C::TP * i, kb = row0 + ti * 16;
+      if (kb < end) attend16<T, R, DR, NHB>(st, sb + ti * C::TILE_B, kb, end, half, a.sl2);
+    }
     if (k + a.nst < nstage) {
       wait_lgkm0();
       bar();
@@ -331,30 +356,50 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       }
     }
   }
-  if (ns == 1) return;
+}
 
-  // The last split of this sequence to finish combines all of them.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == ns - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t base = (size_t)b * a.splits * H;
-  for (int idx = tid; idx < H * R; idx += 256) {
-    const int h = idx / R, ch = idx % R;
-    float M = kNegInf;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.part_ml[(base + (size_t)k * H + h) * 2]);
-    float acc = 0.0f, L = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const size_t i = base + (size_t)k * H + h;
-      const float w = exp2f(a.part_ml[i * 2] - M);
-      L += w * a.part_ml[i * 2 + 1];
-      acc += w * a.part_o[i * R + ch];
+// Log-sum-exp merge of the splits of sequence b, head h into o[b, h, :]; one
+// workgroup of R/4 threads per (b, h), 4 channels per thread.  Sequences
+// that fit one split were written by the attention kernel itself.
+template <typename T, int R>
+__global__ __launch_bounds__(R / 4) void decode_combine_kernel(const int32_t *pos, int s, int chunk,
+                                                               int splits, int H,
+                                                               const float *part_o,
+                                                               const float *part_ml, T *o) {
+  const int b = blockIdx.x, h = blockIdx.y, ch = 4 * threadIdx.x;
+  const int n = pos[b] / s + 1, ns = (n + chunk - 1) / chunk;
+  if (ns == 1) return;
+  const size_t base = (size_t)b * splits * H + h;
+  float M = kNegInf, L = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < ns; k0 += 8) {
+    float pm[8], pl[8];
+    f32x4 po[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t i = base + (size_t)min(k0 + j, ns - 1) * H;
+      pm[j] = part_ml[i * 2];
+      pl[j] = part_ml[i * 2 + 1];
+      po[j] = *(const f32x4 *)(part_o + i * R + ch);
     }
-    ((T *)a.o)[((size_t)b * H + h) * R + ch] = from_f32<T>(acc / L);
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, pm[j]);
+    const float sc = exp2f(M - Mn);
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = (k0 + j < ns) ? exp2f(pm[j] - Mn) : 0.0f;
+      L += w * pl[j];
+      acc += w * po[j];
+    }
+    M = Mn;
   }
-  if (tid == 0) a.counters[b] = 0;
+  const float inv = 1.0f / L;
+  T *dst = o + ((size_t)b * H + h) * R + ch;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[e] * inv);
 }
 
 // Stand-alone merge-append: one workgroup per sequence.
@@ -406,7 +451,7 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
   const int cs = r >= 512 ? 2 : 1;
   if (p.nhb * cs > 4) return false;
-  const int tp = 4 / (p.nhb * cs), srows = 16 * tp;
+  const int tp = 4 / (p.nhb * cs), tpw = tp >= 2 ? 1 : 2, srows = 16 * tp * tpw;
   const size_t stage = (size_t)srows * (r + dR) * esz;
   if (stage + 1024 > 160 * 1024) return false;
   const int64_t nmax = max_pos / s + 1;
@@ -436,19 +481,41 @@ hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int
                                    int s, float scale, const int32_t *pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
-                                   const float *gate_pos, float *part_o, float *part_ml,
-                                   int *counters, void *o, hipStream_t stream) {
+                                   const float *gate_pos, float *part_o, float *part_ml, void *o,
+                                   hipStream_t stream) {
   const int esz = dtype == 1 ? 2 : 4;
-  DecodeArgs args{pos,     (char *)cache, batch_stride * esz, qt,   QR,         KR_t,
-                  cg,      b_hc,          gate_pos,           part_o, part_ml, counters,
-                  o,       H,             s,                  plan.chunk, plan.splits, plan.nst,
-                  scale * kLog2e};
+  DecodeArgs args{pos,    (char *)cache, batch_stride * esz, qt,         QR,          KR_t,     cg,
+                  b_hc,   gate_pos,      part_o,             part_ml,    o,           H,        s,
+                  plan.chunk, plan.splits, plan.nst,         scale * kLog2e};
   if (dtype == 1) {
     if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream);
     return decode_attn_h<bf16, 512, 64>(plan, B, args, stream);
   }
   if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, args, stream);
   return decode_attn_h<float, 512, 64>(plan, B, args, stream);
+}
+
+hipError_t launch_decode_combine(int dtype, const DecodePlan &plan, int B, int H, int r, int s,
+                                 const int32_t *pos, const float *part_o, const float *part_ml,
+                                 void *o, hipStream_t stream) {
+  if (plan.splits == 1) return hipSuccess;
+  const dim3 grid(B, H);
+  if (dtype == 1) {
+    if (r == 256)
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, 256>), grid, dim3(64), 0, stream, pos, s,
+                         plan.chunk, plan.splits, H, part_o, part_ml, (bf16 *)o);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), grid, dim3(128), 0, stream, pos, s,
+                         plan.chunk, plan.splits, H, part_o, part_ml, (bf16 *)o);
+  } else {
+    if (r == 256)
+      hipLaunchKernelGGL((decode_combine_kernel<float, 256>), grid, dim3(64), 0, stream, pos, s,
+                         plan.chunk, plan.splits, H, part_o, part_ml, (float *)o);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<float, 512>), grid, dim3(128), 0, stream, pos, s,
+                         plan.chunk, plan.splits, H, part_o, part_ml, (float *)o);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,

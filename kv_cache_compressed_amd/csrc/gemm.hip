@@ -12,9 +12,8 @@
 //    product is bound by reading B once, so each workgroup owns a narrow
 //    column strip (16 or 32 columns) over all rows, and streams its A and B
 //    tiles through a ring of LDS stages by direct global->LDS loads, several
-//    stages in flight.  K may be split over workgroups; the partial tiles are
-//    then summed, in split order, by the last workgroup of the strip to
-//    finish (device-scope atomic counter).
+//    stages in flight.  K may be split over workgroups; the fp32 partial
+//    tiles are then summed, in split order, by a second small kernel.
 //
 // B may consist of three row segments (rows < N1 from B1, < N2 from B2, the
 // rest from B3), so that one pass over X yields the latent c = X W_dkv^T, the
@@ -157,9 +156,6 @@ struct SkinnyArgs {
   int M, N, KS;         // KS = K / 32
   int kps, ksplit, nst; // k-steps per split, splits, ring stages
   float *part;          // [ksplit, M, N] fp32 when ksplit > 1
-  int *counters;        // [n strips], zero on entry when ksplit > 1
-  int *zero;            // counters to clear before anything else (first workgroup)
-  int nzero;
 };
 
 template <typename T, int BM, int NT, class Epi>
@@ -171,14 +167,11 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi)
   constexpr int NBLK = (XG + NG) * C::NSEG, LPW = (NBLK + 3) / 4;
   static_assert(OT >= 4 ? OT % 4 == 0 : 4 % OT == 0, "tile split");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int strip = blockIdx.x, split = blockIdx.y;
   const int n0 = strip * NT;
-  if (a.nzero && strip == 0 && split == 0)
-    for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
   const int ks0 = split * a.kps, ks1 = min(a.KS, ks0 + a.kps);
   const int nstage = (ks1 - ks0 + C::SK - 1) / C::SK;
   char *dummy = smem + a.nst * STAGE_B;
@@ -294,20 +287,25 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi)
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[strip], 1) == a.ksplit - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int idx = tid; idx < BM * NT; idx += 256) {
-    const int m = idx / NT, n = n0 + idx % NT;
-    if (m >= a.M || n >= a.N) continue;
-    float v = 0.0f;
-    for (int k = 0; k < a.ksplit; ++k) v += a.part[((size_t)k * a.M + m) * a.N + n];
-    epi(m, n, v);
+}
+
+// Sum of the K-split partials [ksplit, M, N], in split order, into the epilogue.
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, int ksplit, int M,
+                                                            int N, Epi epi) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * N) return;
+  const int m = (int)(idx / N), n = (int)(idx % N);
+  float v = 0.0f;
+  for (int k0 = 0; k0 < ksplit; k0 += 8) {
+    float pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pv[j] = part[((size_t)min(k0 + j, ksplit - 1) * M + m) * N + n];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += (k0 + j < ksplit) ? pv[j] : 0.0f;
   }
-  if (tid == 0) a.counters[strip] = 0;
+  epi(m, n, v);
 }
 
 // ---- epilogues ---------------------------------------------------------------
@@ -340,11 +338,6 @@ template <typename T> struct EpiProj {
     else qt[(size_t)m * HR + (n - r2)] = from_f32<T>(v);
   }
 };
-
-__global__ __launch_bounds__(256) void zero_kernel(int *p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
-}
 
 // W_gate[i, k] = sum_j W_hc[i, j] W_dkv[j, k], accumulated in fp32.
 template <typename T>
@@ -394,11 +387,11 @@ hipError_t skinny_t(SkinnyArgs a, int strips, Epi epi, hipStream_t stream) {
 }
 
 // Skinny product of M <= 128 rows: picks the row tile and column strip and,
-// when `ksplit` > 1, splits K (partials in `part`, counters per strip).
+// when `ksplit` > 1 and `part` is given, splits K over workgroups (fp32
+// partials in `part`, summed by a second kernel).
 template <typename T, class Epi>
 hipError_t run_skinny(const T *X, int ldx, const BSeg &bs, int M, int N, int K, int ksplit,
-                      float *part, int *counters, int *zero, int nzero, Epi epi,
-                      hipStream_t stream) {
+                      float *part, Epi epi, hipStream_t stream) {
   SkinnyArgs a;
   a.X = X;
   a.ldx = ldx;
@@ -406,36 +399,31 @@ hipError_t run_skinny(const T *X, int ldx, const BSeg &bs, int M, int N, int K, 
   a.M = M;
   a.N = N;
   a.KS = K / 32;
-  if (ksplit < 1 || !part || !counters) ksplit = 1;
+  if (ksplit < 1 || !part) ksplit = 1;
   if (ksplit > a.KS) ksplit = a.KS;
   a.kps = (a.KS + ksplit - 1) / ksplit;
   a.ksplit = (a.KS + a.kps - 1) / a.kps;
   a.nst = 1;
   a.part = part;
-  a.counters = counters;
-  a.zero = zero;
-  a.nzero = zero ? nzero : 0;
-  if (M <= 16) return skinny_t<T, 16, 16>(a, (N + 15) / 16, epi, stream);
-  if (M <= 32) return skinny_t<T, 32, 16>(a, (N + 15) / 16, epi, stream);
-  if (M <= 64) return skinny_t<T, 64, 16>(a, (N + 15) / 16, epi, stream);
-  return skinny_t<T, 128, 32>(a, (N + 31) / 32, epi, stream);
+  hipError_t e;
+  if (M <= 16) e = skinny_t<T, 16, 16>(a, (N + 15) / 16, epi, stream);
+  else if (M <= 32) e = skinny_t<T, 32, 16>(a, (N + 15) / 16, epi, stream);
+  else if (M <= 64) e = skinny_t<T, 64, 16>(a, (N + 15) / 16, epi, stream);
+  else e = skinny_t<T, 128, 32>(a, (N + 31) / 32, epi, stream);
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  const int64_t total = (int64_t)M * N;
+  hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, part, a.ksplit, M, N, epi);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_gate, int r,
-                  const void *A, int HR, float *cg, void *qt, int *zero, int nzero,
-                  hipStream_t stream) {
+                  const void *A, int HR, float *cg, void *qt, hipStream_t stream) {
   EpiProj<T> epi{cg, (T *)qt, 2 * r, HR};
   BSeg bs{W_dkv, W_gate, A, r, 2 * r, d};
   const int N = 2 * r + (A ? HR : 0);
-  if (M <= 128)
-    return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, nullptr, zero, nzero, epi,
-                         stream);
-  if (zero && nzero > 0) {
-    hipLaunchKernelGGL(zero_kernel, dim3((nzero + 255) / 256), dim3(256), 0, stream, zero, nzero);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (M <= 128) return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, epi, stream);
   return run_gemm<T>((const T *)X, d, bs, M, N, d, epi, stream);
 }
 
@@ -446,12 +434,10 @@ int out_proj_splits(int M, int N, int K) {
   const int strips = M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
   int ks = (256 + strips - 1) / strips;   // aim at about 256 workgroups
   const int KS = K / 32;
-  if (ks > KS / 4) ks = KS / 4 > 0 ? KS / 4 : 1;   // at least 4 k-steps per split
+  if (ks > KS / 8) ks = KS / 8 > 0 ? KS / 8 : 1;   // at least 8 k-steps per split
   if (ks < 1) ks = 1;
   return ks;
 }
-
-int out_proj_strips(int M, int N) { return M <= 64 ? (N + 15) / 16 : (N + 31) / 32; }
 
 hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, int ldb, int M,
                              int N, int K, void *out, int ldc, hipStream_t stream) {
@@ -464,14 +450,14 @@ hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, 
 }
 
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
-                           float *part, int *counters, hipStream_t stream) {
+                           float *part, hipStream_t stream) {
   if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);
-  const int ks = out_proj_splits(M, N, K);
+  const int ks = part ? out_proj_splits(M, N, K) : 1;
   BSeg bs{Bvo, Bvo, Bvo, N, N, K};
   if (dtype == 1)
-    return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
+    return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part,
                             EpiStore<bf16>{(bf16 *)Y, N}, stream);
-  return run_skinny<float>((const float *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
+  return run_skinny<float>((const float *)O, K, bs, M, N, K, ks, part,
                            EpiStore<float>{(float *)Y, N}, stream);
 }
 
@@ -497,10 +483,9 @@ hipError_t launch_gate_map(int dtype, const void *W_hc, const void *W_dkv, int r
 
 hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv,
                        const void *W_gate, int r, const void *A, int HR, float *cg, void *qt,
-                       int *zero, int nzero, hipStream_t stream) {
-  if (dtype == 1)
-    return proj_t<bf16>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
-  return proj_t<float>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
+                       hipStream_t stream) {
+  if (dtype == 1) return proj_t<bf16>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, stream);
+  return proj_t<float>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, stream);
 }
 
 }  // namespace mtla
