@@ -8,21 +8,27 @@
 // decoupled RoPE with temporal compression (the Y formula).
 // [Fig2] = "Multi-head Temporal Latent Attention" (sciencestack.ai), Fig. 2 (a).
 //
-// Attention kernel, one workgroup per (sequence b, split of `chunk` slots):
-//  * The cache rows of the split stream from HBM into a ring of LDS stages by
-//    direct global->LDS loads (global_load_lds_dwordx4, no register staging),
-//    up to `nst` stages in flight; a stage is 16*TP rows (TP 16-row tiles).
-//  * Every head of the sequence reads the same rows (one latent cache shared
-//    by all heads), so each byte is fetched once.  The 4 waves split the work
-//    as head block (16 heads) x tile of the stage x half of the latent
-//    channels of O (halves only for r = 512, where all of O would not fit the
-//    registers of one wave; both halves then compute the same scores).
-//  * Per 16-row tile a wave computes S^T (16 keys x 16 heads) = K . Q^T with
-//    K from LDS as the MFMA A operand (K = latent ++ RoPE key, r + d_hR
-//    wide), applies the online softmax in log2 units, and accumulates
-//    O^T (r x 16 heads) += C^T . P^T, reading C^T from the row-major tile with
-//    ds_read_tr16_b64 (the K=16 bf16 MFMA's A layout) and P^T straight from
-//    the score registers (the score layout is the B layout).
+// Attention kernel, one workgroup (4 waves) per (sequence b, split of `chunk`
+// slots).  All heads of a sequence read the same compressed rows (one latent
+// cache shared by every head), so each row is fetched from HBM once:
+//  * The split's rows stream into a ring of LDS stages by direct
+//    global->LDS loads (global_load_lds_dwordx4, no register staging), up to
+//    `nst` stages in flight.  A stage is TPS 16-row tiles, TPS = 4 / NHB for
+//    NHB blocks of 16 heads.
+//  * Scores: wave w takes one (tile, head block) pair of the stage and
+//    computes S^T (16 keys x 16 heads) = K . Q^T on the K=32 MFMA, K (latent
+//    ++ RoPE key, r + d_hR wide) from LDS as the A operand, Q^T from
+//    registers.
+//  * Softmax: the column maxima of all pairs meet in LDS, so every wave
+//    derives the same per-head reference max; it moves lazily (only when a
+//    score exceeds it by more than 2^8), which skips the rescale of O on
+//    almost every stage.  P = 2^(z - m) goes to LDS in bf16 (fp32 storage:
+//    fp32).
+//  * Values: wave w accumulates O^T for its quarter of the r latent channels,
+//    all heads, all tiles of the stage: O^T += C^T . P^T on the K=16 MFMA,
+//    C^T read from the row-major tile with ds_read_tr16_b64 (its A layout)
+//    and P^T from LDS (the score layout is the B layout).  O needs no
+//    cross-wave reduction at the end.
 //  * The split that owns the newest slot j = floor(t/s) first merges the new
 //    frame: u = Sigmoid((g + b_hc) * Linear(pe_j)) * c, slot j = u (t mod s
 //    == 0) or slot j + u, RoPE key j = K^R_t, written to the cache and into
@@ -46,15 +52,19 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 template <typename T, int R, int DR, int NHB> struct DecCfg {
   static constexpr int RK = R + DR, ES = (int)sizeof(T), RB = RK * ES, NSEG = RB / 64;
-  static constexpr int CS = R >= 512 ? 2 : 1;           // channel halves of O
-  static constexpr int TP = 4 / (NHB * CS);               // tile streams
-  static constexpr int TPW = TP >= 2 ? 1 : 2;             // tiles per wave per stage
-  static constexpr int SROWS = 16 * TP * TPW;
-  static constexpr int TILE_B = 16 * RB, STAGE_B = TP * TPW * TILE_B;
-  static constexpr int NBLK = TP * TPW * NSEG, LPW = (NBLK + 3) / 4;
-  static constexpr int KS = RK / 32, MT = R / 16, MTW = MT / CS, NU = (R + 255) / 256;
+  static constexpr int TPS = 4 / NHB;                    // 16-row tiles per stage
+  static constexpr int SROWS = 16 * TPS;
+  static constexpr int TILE_B = 16 * RB, STAGE_B = TPS * TILE_B;
+  static constexpr int NBLK = TPS * NSEG, LPW = (NBLK + 3) / 4;
+  static constexpr int KS = RK / 32;                     // k-steps of the scores
+  static constexpr int MQ = R / 64;                      // 16-channel blocks per wave
+  static constexpr int NU = (R + 255) / 256;
+  static constexpr int HW = 16 * NHB;                    // heads covered (padded)
+  // LDS after the ring: dummy block, per-pair column maxima, P tiles
+  static constexpr int SMAX_B = TPS * HW * 4;
+  static constexpr int P_B = TPS * NHB * 64 * 4 * ES;
   static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
-  static_assert(TP >= 1, "too many head blocks for this width");
+  static_assert(NHB * TPS == 4, "one (tile, head block) pair per wave");
 };
 
 // S operand: the 8 values of row `row`, k-step ks (32 values) that lane
@@ -70,95 +80,13 @@ __device__ __forceinline__ typename Frag<T>::type s_frag(const char *tile, int r
   }
 }
 
-// Transposed operand C^T for channels ch0..ch0+15 of the tile's keys
+// fp32 transposed operand C^T for channels ch0..ch0+15 of the tile's keys
 // 4g..4g+3: lane (g, j) receives channel ch0 + j of those four keys.
-template <typename T>
-__device__ __forceinline__ typename Frag4<T>::type v_frag(const char *tile, int ch0, int g, int j) {
-  if constexpr (sizeof(T) == 2) {
-    // ds_read_tr16_b64: in each 16-lane group, lane i returns element
-    // [4e + i/4][i%4] of the 16 x 4 block whose row k lane k addressed; lane
-    // k addresses key 4g + k/4, channels ch0 + 4(k%4) .. +3.
-    const char *p = tile + tile_off(4 * g + (j >> 2), (ch0 + 4 * (j & 3)) * 2);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
-  } else {
-    f32x4 v;
+__device__ __forceinline__ f32x4 v_frag_f32(const char *tile, int ch0, int g, int j) {
+  f32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + tile_off(4 * g + e, (ch0 + j) * 4));
-    return v;
-  }
-}
-
-template <typename T, int R, int DR, int NHB> struct WaveState {
-  typename Frag<T>::type q[DecCfg<T, R, DR, NHB>::KS];
-  f32x4 o[DecCfg<T, R, DR, NHB>::MTW];   // channels 16 (half*MTW + mt) + 4g + e
-  float m, l;
-};
-
-// One 16-key tile: key kbase + k is visible iff kbase + k < end.
-template <typename T, int R, int DR, int NHB>
-__device__ __forceinline__ void attend16(WaveState<T, R, DR, NHB> &st, const char *tile, int kbase,
-                                         int end, int half, float sl2) {
-  using C = DecCfg<T, R, DR, NHB>;
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  // Two independent accumulation chains over the k-steps.
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks + 1 < C::KS; ks += 2) {
-    s0 = mma_k32(s_frag<T>(tile, c, ks, g), st.q[ks], s0);
-    s1 = mma_k32(s_frag<T>(tile, c, ks + 1, g), st.q[ks + 1], s1);
-  }
-  if constexpr (C::KS % 2) s0 = mma_k32(s_frag<T>(tile, c, C::KS - 1, g), st.q[C::KS - 1], s0);
-  const f32x4 sc = s0 + s1;
-  float v[4], mx = kNegInf;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    v[e] = (kbase + 4 * g + e < end) ? sc[e] * sl2 : kNegInf;
-    mx = fmaxf(mx, v[e]);
-  }
-  mx = fmaxf(mx, wave_xor(mx, 16));
-  mx = fmaxf(mx, wave_xor(mx, 32));   // finite: key kbase is visible
-  // Lazy rescaling: the reference max m only moves when a score exceeds it
-  // by more than 8 (log2 units), so p = 2^(z - m) <= 2^8 and the rescale of O
-  // (a pass over all its registers) is skipped on almost every tile.
-  const bool up = mx > st.m + 8.0f;
-  if (__builtin_amdgcn_ballot_w64(up)) {
-    const float mn = up ? mx : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
-    st.l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < C::MTW; ++mt) st.o[mt] *= alpha;
-    st.m = mn;
-  }
-  typename Frag4<T>::type pf;
-  float ps = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float p = __builtin_amdgcn_exp2f(v[e] - st.m);
-    ps += p;
-    pf[e] = from_f32<T>(p);
-  }
-  st.l += ps;
-  // Channel blocks in groups of 8: the transposing reads of a group are
-  // issued together, then its 8 products.
-  const int cb = half * C::MTW;
-  static_assert(C::MTW % 8 == 0, "channel blocks come in groups of 8");
-#pragma unroll
-  for (int m0 = 0; m0 < C::MTW; m0 += 8) {
-    if constexpr (sizeof(T) == 2) {
-      uint32_t ad[8];
-      bf16x4 vv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        ad[j] = lds_addr(tile + tile_off(4 * g + (c >> 2), (16 * (cb + m0 + j) + 4 * (c & 3)) * 2));
-      ds_read_tr8(vv, ad);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st.o[m0 + j] = mma_k16(vv[j], pf, st.o[m0 + j]);
-    } else {
-#pragma unroll
-      for (int mt = m0; mt < m0 + 8; ++mt)
-        st.o[mt] = mma_k16(v_frag<T>(tile, 16 * (cb + mt), g, c), pf, st.o[mt]);
-    }
-  }
+  for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + tile_off(4 * g + e, (ch0 + j) * 4));
+  return v;
 }
 
 // Wait until at most `after` stages issued after the current one are still
@@ -197,7 +125,9 @@ struct DecodeArgs {
 template <typename T, int R, int DR, int NHB>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   using C = DecCfg<T, R, DR, NHB>;
+  typedef typename Frag4<T>::type P4;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
+
   const int b = blockIdx.y, split = blockIdx.x;
   const int t = a.pos[b], s = a.s, jn = t / s, n = jn + 1;
   const int start = split * a.chunk;
@@ -208,30 +138,33 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   const int nstage = (end - start + C::SROWS - 1) / C::SROWS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int hb = wave / (C::TP * C::CS), tt = (wave / C::CS) % C::TP, half = wave % C::CS;
-  const int H = a.H, head = hb * 16 + c;
+  const int st_tile = wave % C::TPS, st_hb = wave / C::TPS;   // score pair of this wave
+  const int H = a.H, shead = st_hb * 16 + c;
   char *seq = a.cache + (size_t)b * a.bstride_bytes;
   char *dummy = smem + a.nst * C::STAGE_B;
+  float *smax = (float *)(dummy + 1024);                       // [TPS][HW]
+  char *pbuf = (char *)smax + C::SMAX_B;                       // [TPS][NHB][64][4]
 
   // Everything read from global memory besides the stream is fetched first,
   // so that later waits for it never wait for the cache loads behind it.
-  WaveState<T, R, DR, NHB> st;
+  typename Frag<T>::type q[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const int k = 32 * ks + 8 * g;
-    if (head < H) {
-      if (k < R) load8(st.q[ks], (const T *)a.qt + ((size_t)b * H + head) * R + k);
-      else load8(st.q[ks], (const T *)a.QR + ((size_t)b * H + head) * DR + (k - R));
+    if (shead < H) {
+      if (k < R) load8(q[ks], (const T *)a.qt + ((size_t)b * H + shead) * R + k);
+      else load8(q[ks], (const T *)a.QR + ((size_t)b * H + shead) * DR + (k - R));
     } else {
-      st.q[ks] = zero_frag<T>();
+      q[ks] = zero_frag<T>();
     }
   }
   float mc[C::NU], mg[C::NU], mb[C::NU], mp[C::NU], mkr = 0.0f;
+#pragma unroll
+  for (int i = 0; i < C::NU; ++i) mc[i] = mg[i] = mb[i] = mp[i] = 0.0f;
   if (owner) {
 #pragma unroll
     for (int i = 0; i < C::NU; ++i) {
       const int ch = tid + 256 * i;
-      mc[i] = mg[i] = mb[i] = mp[i] = 0.0f;
       if (ch < R) {
         mc[i] = a.cg[(size_t)b * 2 * R + ch];
         mg[i] = a.cg[(size_t)b * 2 * R + R + ch];
@@ -250,22 +183,32 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     for (int i = 0; i < C::LPW; ++i) {
       const int blk = wave + 4 * i;
       const bool real = (C::NBLK % 4 == 0) || blk < C::NBLK;
-      const int tl = real ? blk / C::NSEG : 0, q = real ? blk % C::NSEG : 0;
+      const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
       const int slot = min(row0 + tl * 16 + (lane >> 2), end - 1);
-      dma_block(seq + (size_t)slot * C::RB, q, real ? sb + tl * C::TILE_B + q * 1024 : dummy);
+      dma_block(seq + (size_t)slot * C::RB, qq, real ? sb + tl * C::TILE_B + qq * 1024 : dummy);
     }
   };
   const int pro = min(a.nst, nstage);
   for (int k = 0; k < pro; ++k) issue(k);
 
-  st.m = kNegInf;
-  st.l = 0.0f;
+  // o[hb][qb]: O^T block of channels 16 (wave * MQ + qb) + 4g + e, head
+  // hb * 16 + c.  m[hb]: reference max of head hb * 16 + c (same in every
+  // wave).  lp: partial sum of P over this wave's score pairs.
+  f32x4 o[NHB][C::MQ];
+  float m[NHB];
 #pragma unroll
-  for (int mt = 0; mt < C::MTW; ++mt) st.o[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int hb = 0; hb < NHB; ++hb) {
+    m[hb] = kNegInf;
+#pragma unroll
+    for (int qb = 0; qb < C::MQ; ++qb) o[hb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  float lp = 0.0f;
 
   for (int k = 0; k < nstage; ++k) {
     wait_stages<C::LPW>(min(a.nst - 1, nstage - 1 - k));
     bar();
+    // Every wave is past stage k-1 here: its ring slot can be refilled.
+    if (k >= 1 && k - 1 + a.nst < nstage) issue(k - 1 + a.nst);
     char *sb = smem + (k % a.nst) * C::STAGE_B;
     const int row0 = start + k * C::SROWS;
     if (k == nstage - 1) {
@@ -287,10 +230,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
         for (int i = 0; i < C::NU; ++i) {
           const int ch = tid + 256 * i;
           if (ch < R) {
-            T *lp = (T *)(trow + tile_off(rr & 15, ch * C::ES));
+            T *lpnt = (T *)(trow + tile_off(rr & 15, ch * C::ES));
             const float u = sigmoidf((mg[i] + mb[i]) * mp[i]) * mc[i];
-            const T v = from_f32<T>(open ? u : to_f32(*lp) + u);
-            *lp = v;
+            const T v = from_f32<T>(open ? u : to_f32(*lpnt) + u);
+            *lpnt = v;
             grow[ch] = v;
           }
         }
@@ -303,57 +246,130 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       wait_lgkm0();
       bar();
     }
+
+    // Scores of this wave's (tile, head block) pair.
+    const char *stile = sb + st_tile * C::TILE_B;
+    const int kb = row0 + st_tile * 16;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < C::TPW; ++i) {
-      const int ti = tt + C::TP * i, kb = row0 + ti * 16;
-      if (kb < end) attend16<T, R, DR, NHB>(st, sb + ti * C::TILE_B, kb, end, half, a.sl2);
+    for (int ks = 0; ks + 1 < C::KS; ks += 2) {
+      s0 = mma_k32(s_frag<T>(stile, c, ks, g), q[ks], s0);
+      s1 = mma_k32(s_frag<T>(stile, c, ks + 1, g), q[ks + 1], s1);
     }
-    if (k + a.nst < nstage) {
-      wait_lgkm0();
-      bar();
-      issue(k + a.nst);
+    if constexpr (C::KS % 2) s0 = mma_k32(s_frag<T>(stile, c, C::KS - 1, g), q[C::KS - 1], s0);
+    float z[4], mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      z[e] = (kb + 4 * g + e < end) ? (s0[e] + s1[e]) * a.sl2 : kNegInf;
+      mx = fmaxf(mx, z[e]);
+    }
+    mx = fmaxf(mx, wave_xor(mx, 16));
+    mx = fmaxf(mx, wave_xor(mx, 32));   // -inf only for a tile wholly past the split
+    if (g == 0) smax[st_tile * C::HW + shead] = mx;
+    wait_lgkm0();
+    bar();
+
+    // Reference max per head, identical in every wave; rescale when it moves.
+    float mnew[NHB];
+    bool up_any = false;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      float sm = kNegInf;
+#pragma unroll
+      for (int tl = 0; tl < C::TPS; ++tl) sm = fmaxf(sm, smax[tl * C::HW + hb * 16 + c]);
+      const bool up = sm > m[hb] + 8.0f;
+      mnew[hb] = up ? sm : m[hb];
+      up_any |= up;
+    }
+    if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const float alpha = __builtin_amdgcn_exp2f(m[hb] - mnew[hb]);
+#pragma unroll
+        for (int qb = 0; qb < C::MQ; ++qb) o[hb][qb] *= alpha;
+        if (hb == st_hb) lp *= alpha;
+        m[hb] = mnew[hb];
+      }
+    }
+    float mref = m[0];
+#pragma unroll
+    for (int hb = 1; hb < NHB; ++hb)
+      if (hb == st_hb) mref = m[hb];
+    P4 pf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __builtin_amdgcn_exp2f(z[e] - mref);
+      lp += p;
+      pf[e] = from_f32<T>(p);
+    }
+    *(P4 *)(pbuf + ((st_tile * NHB + st_hb) * 64 + lane) * 4 * C::ES) = pf;
+    wait_lgkm0();
+    bar();
+
+    // O^T += C^T P^T for this wave's channel quarter, every pair of the stage.
+#pragma unroll
+    for (int tl = 0; tl < C::TPS; ++tl) {
+      if (row0 + tl * 16 >= end) continue;
+      const char *tile = sb + tl * C::TILE_B;
+      P4 pp[NHB];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        pp[hb] = *(const P4 *)(pbuf + ((tl * NHB + hb) * 64 + lane) * 4 * C::ES);
+#pragma unroll
+      for (int q0 = 0; q0 < C::MQ; q0 += 8) {
+        constexpr int QN = C::MQ < 8 ? C::MQ : 8;
+        typename Frag4<T>::type vv[8];
+        if constexpr (sizeof(T) == 2) {
+          uint32_t ad[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int ch0 = 16 * (wave * C::MQ + q0 + (j < QN ? j : 0));
+            ad[j] = lds_addr(tile + tile_off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
+          }
+          ds_read_tr8(vv, ad);
+        } else {
+#pragma unroll
+          for (int j = 0; j < QN; ++j) vv[j] = v_frag_f32(tile, 16 * (wave * C::MQ + q0 + j), g, c);
+        }
+#pragma unroll
+        for (int j = 0; j < QN; ++j)
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) o[hb][q0 + j] = mma_k16(vv[j], pp[hb], o[hb][q0 + j]);
+      }
     }
   }
 
-  // Merge the TP tile streams of each head block through LDS.
-  float lt = st.l + wave_xor(st.l, 16);
+  // Row sums: lane partials -> per head, over the waves of each head block.
+  float lt = lp + wave_xor(lp, 16);
   lt += wave_xor(lt, 32);
   wait_lgkm0();
   bar();
-  float *red = (float *)smem;                        // [TP][H][R]
-  float *redm = red + (size_t)C::TP * H * R;         // [TP][H]
-  float *redl = redm + C::TP * H;                    // [TP][H]
-  if (head < H) {
-#pragma unroll
-    for (int mt = 0; mt < C::MTW; ++mt)
-      *(f32x4 *)(red + ((size_t)tt * H + head) * R + 16 * (half * C::MTW + mt) + 4 * g) = st.o[mt];
-    if (g == 0 && half == 0) {
-      redm[tt * H + head] = st.m;
-      redl[tt * H + head] = lt;
-    }
-  }
-  __syncthreads();
+  if (g == 0) smax[st_tile * C::HW + shead] = lt;
+  wait_lgkm0();
+  bar();
   const size_t pbase = ((size_t)b * a.splits + split) * H;
-  for (int idx = tid; idx < H * R; idx += 256) {
-    const int h = idx / R, ch = idx % R;
-    float M = kNegInf;
 #pragma unroll
-    for (int k = 0; k < C::TP; ++k) M = fmaxf(M, redm[k * H + h]);
-    float acc = 0.0f, L = 0.0f;
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int head = hb * 16 + c;
+    if (head >= H) continue;
+    float L = 0.0f;
 #pragma unroll
-    for (int k = 0; k < C::TP; ++k) {
-      const float w = exp2f(redm[k * H + h] - M);
-      acc += w * red[((size_t)k * H + h) * R + ch];
-      L += w * redl[k * H + h];
-    }
-    if (ns == 1) {
-      ((T *)a.o)[((size_t)b * H + h) * R + ch] = from_f32<T>(acc / L);
-    } else {
-      a.part_o[(pbase + h) * R + ch] = acc;
-      if (ch == 0) {
-        a.part_ml[(pbase + h) * 2] = M;
-        a.part_ml[(pbase + h) * 2 + 1] = L;
+    for (int tl = 0; tl < C::TPS; ++tl) L += smax[tl * C::HW + head];
+#pragma unroll
+    for (int qb = 0; qb < C::MQ; ++qb) {
+      const int ch = 16 * (wave * C::MQ + qb) + 4 * g;
+      if (ns == 1) {
+        T *dst = (T *)a.o + ((size_t)b * H + head) * R + ch;
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[hb][qb][e] * inv);
+      } else {
+        *(f32x4 *)(a.part_o + (pbase + head) * R + ch) = o[hb][qb];
       }
+    }
+    if (ns > 1 && wave == 0 && g == 0) {
+      a.part_ml[(pbase + head) * 2] = m[hb];
+      a.part_ml[(pbase + head) * 2 + 1] = L;
     }
   }
 }
@@ -433,8 +449,7 @@ template <typename T, int R, int DR>
 hipError_t decode_attn_h(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream) {
   if (p.nhb == 1) return decode_attn_t<T, R, DR, 1>(p, B, args, stream);
   if (p.nhb == 2) return decode_attn_t<T, R, DR, 2>(p, B, args, stream);
-  if constexpr (R < 512) return decode_attn_t<T, R, DR, 4>(p, B, args, stream);
-  return hipErrorInvalidValue;   // decode_plan rejects this case
+  return decode_attn_t<T, R, DR, 4>(p, B, args, stream);
 }
 
 }  // namespace
@@ -449,11 +464,9 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   const int esz = dtype == 1 ? 2 : 4;
   DecodePlan p;
   p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
-  const int cs = r >= 512 ? 2 : 1;
-  if (p.nhb * cs > 4) return false;
-  const int tp = 4 / (p.nhb * cs), tpw = tp >= 2 ? 1 : 2, srows = 16 * tp * tpw;
+  const int tps = 4 / p.nhb, srows = 16 * tps;
   const size_t stage = (size_t)srows * (r + dR) * esz;
-  if (stage + 1024 > 160 * 1024) return false;
+  const size_t extra = 1024 + (size_t)tps * 16 * p.nhb * 4 + (size_t)tps * p.nhb * 64 * 4 * esz;
   const int64_t nmax = max_pos / s + 1;
   const int64_t total = (int64_t)B * nmax;
   int64_t chunk = (total + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS;
@@ -469,9 +482,7 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   if (nst > chunk / srows) nst = (int)(chunk / srows);
   if (nst < 1) nst = 1;
   p.nst = nst;
-  const size_t ring = nst * stage + 1024;
-  const size_t reduce = (size_t)tp * H * r * 4 + (size_t)2 * tp * H * 4;
-  p.lds = ring > reduce ? ring : reduce;
+  p.lds = nst * stage + extra;
   if (p.lds > 159 * 1024) return false;
   *plan = p;
   return true;

@@ -430,7 +430,10 @@ hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_
 }  // namespace
 
 int out_proj_splits(int M, int N, int K) {
+  (void)N;
+  (void)K;
   if (M > 128) return 1;
+  return 1;
   const int strips = M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
   int ks = (256 + strips - 1) / strips;   // aim at about 256 workgroups
   const int KS = K / 32;
