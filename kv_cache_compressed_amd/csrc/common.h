@@ -171,6 +171,39 @@ __device__ __forceinline__ void wait_lgkm0() {
   asm volatile("" ::: "memory");
 }
 
+// ---- handing partial results between workgroups of one kernel -------------
+//
+// The L2 of each XCD is not coherent with the others', so a workgroup's plain
+// stores are not visible to a workgroup on another XCD until the L2 is
+// written back (what a release fence does, for the whole L2 at once: far too
+// costly per workgroup).  Partial results are therefore stored and loaded
+// with the sc1 cache policy -- the accesses the memory model uses for
+// agent-scope atomics, coherent across XCDs -- as 16-byte buffer accesses
+// (coalesced, unlike per-lane atomics).  Protocol: the writer stores with
+// st_coh, waits for its stores (__syncthreads waits for them), then bumps a
+// counter with ctr_add; the workgroup that brings the counter to its final
+// value loads the partials with ld_coh.
+constexpr int kCoherent = 16;   // cache policy bits: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_coh4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ void st_coh1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ float ld_coh1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ int ctr_add(int *p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Raise a kernel's dynamic-LDS limit to everything its static LDS leaves of
 // the CU's 160 KB, once per instantiation (thread-safe static
 // initialisation), so that launches made later -- possibly under graph

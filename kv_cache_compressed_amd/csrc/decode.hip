@@ -33,8 +33,9 @@
 //    frame: u = Sigmoid((g + b_hc) * Linear(pe_j)) * c, slot j = u (t mod s
 //    == 0) or slot j + u, RoPE key j = K^R_t, written to the cache and into
 //    its LDS copy before that row is attended.
-//  * Splits write (max, sum, O) partials, merged by log-sum-exp in split
-//    order by a small second kernel (deterministic results); a sequence that
+//  * Splits store (max, sum, O) partials with XCD-coherent accesses; the
+//    last split of a sequence to finish (atomic counter) merges them by
+//    log-sum-exp in split order (deterministic results).  A sequence that
 //    fits one split is normalised and written directly.
 
 #include <math.h>
@@ -62,7 +63,7 @@ template <typename T, int R, int DR, int NHB> struct DecCfg {
   static constexpr int HW = 16 * NHB;                    // heads covered (padded)
   // LDS after the ring: dummy block, per-pair column maxima, P tiles
   static constexpr int SMAX_B = TPS * HW * 4;
-  static constexpr int P_B = TPS * NHB * 64 * 4 * ES;
+  static constexpr int P_B = TPS * NHB * 64 * 4 * ES;   // then one int (last-split flag)
   static_assert(RB % 64 == 0, "row bytes must be a multiple of 64");
   static_assert(NHB * TPS == 4, "one (tile, head block) pair per wave");
 };
@@ -117,6 +118,7 @@ struct DecodeArgs {
   const float *gate_pos;
   float *part_o;       // [B, splits, H, R]
   float *part_ml;      // [B, splits, H, 2]
+  int *counters;       // [B], zero on entry (zero again on exit)
   void *o;             // [B, H, R]
   int H, s, chunk, splits, nst;
   float sl2;
@@ -348,6 +350,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   wait_lgkm0();
   bar();
   const size_t pbase = ((size_t)b * a.splits + split) * H;
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(a.part_o, (uint32_t)((size_t)gridDim.y * a.splits * H * R * 4));
+  const __amdgpu_buffer_rsrc_t rml =
+      make_rsrc(a.part_ml, (uint32_t)((size_t)gridDim.y * a.splits * H * 8));
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int head = hb * 16 + c;
@@ -364,58 +370,79 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[hb][qb][e] * inv);
       } else {
-        *(f32x4 *)(a.part_o + (pbase + head) * R + ch) = o[hb][qb];
+        st_coh4(ro, (uint32_t)(((pbase + head) * R + ch) * 4), o[hb][qb]);
       }
     }
     if (ns > 1 && wave == 0 && g == 0) {
-      a.part_ml[(pbase + head) * 2] = m[hb];
-      a.part_ml[(pbase + head) * 2 + 1] = L;
+      st_coh1(rml, (uint32_t)((pbase + head) * 8), m[hb]);
+      st_coh1(rml, (uint32_t)((pbase + head) * 8 + 4), L);
     }
   }
-}
-
-// Log-sum-exp merge of the splits of sequence b, head h into o[b, h, :]; one
-// workgroup of R/4 threads per (b, h), 4 channels per thread.  Sequences
-// that fit one split were written by the attention kernel itself.
-template <typename T, int R>
-__global__ __launch_bounds__(R / 4) void decode_combine_kernel(const int32_t *pos, int s, int chunk,
-                                                               int splits, int H,
-                                                               const float *part_o,
-                                                               const float *part_ml, T *o) {
-  const int b = blockIdx.x, h = blockIdx.y, ch = 4 * threadIdx.x;
-  const int n = pos[b] / s + 1, ns = (n + chunk - 1) / chunk;
   if (ns == 1) return;
-  const size_t base = (size_t)b * splits * H + h;
-  float M = kNegInf, L = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < ns; k0 += 8) {
-    float pm[8], pl[8];
-    f32x4 po[8];
+
+  // The last split of this sequence to finish merges all of them (log-sum-
+  // exp in split order: deterministic).  Four 4-channel chunks by four splits
+  // per batch keep 48 loads in flight per thread.
+  int *last = (int *)(pbuf + C::P_B);
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (tid == 0) *last = ctr_add(&a.counters[b], 1) == ns - 1;
+  __syncthreads();
+  if (!*last) return;
+  constexpr int QC = R / 4;   // 4-channel chunks per head
+  const int nch = H * QC;
+  const size_t base = (size_t)b * a.splits * H;
+  for (int c0 = tid; c0 < nch; c0 += 4 * 256) {
+    float M[4], L[4];
+    f32x4 acc[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const size_t i = base + (size_t)min(k0 + j, ns - 1) * H;
-      pm[j] = part_ml[i * 2];
-      pl[j] = part_ml[i * 2 + 1];
-      po[j] = *(const f32x4 *)(part_o + i * R + ch);
+    for (int u = 0; u < 4; ++u) {
+      M[u] = kNegInf;
+      L[u] = 0.0f;
+      acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    float Mn = M;
+    for (int k0 = 0; k0 < ns; k0 += 4) {
+      float pm[4][4], pl[4][4];
+      f32x4 po[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, pm[j]);
-    const float sc = exp2f(M - Mn);
-    L *= sc;
-    acc *= sc;
+      for (int u = 0; u < 4; ++u) {
+        const int ci = min(c0 + 256 * u, nch - 1), h = ci / QC, ch = (ci % QC) * 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = (k0 + j < ns) ? exp2f(pm[j] - Mn) : 0.0f;
-      L += w * pl[j];
-      acc += w * po[j];
+        for (int j = 0; j < 4; ++j) {
+          const size_t i = base + (size_t)min(k0 + j, ns - 1) * H + h;
+          pm[u][j] = ld_coh1(rml, (uint32_t)(i * 8));
+          pl[u][j] = ld_coh1(rml, (uint32_t)(i * 8 + 4));
+          po[u][j] = ld_coh4(ro, (uint32_t)((i * R + ch) * 4));
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float Mn = M[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mn = fmaxf(Mn, pm[u][j]);
+        const float sc = __builtin_amdgcn_exp2f(M[u] - Mn);
+        L[u] *= sc;
+        acc[u] *= sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float w = (k0 + j < ns) ? __builtin_amdgcn_exp2f(pm[u][j] - Mn) : 0.0f;
+          L[u] += w * pl[u][j];
+          acc[u] += w * po[u][j];
+        }
+        M[u] = Mn;
+      }
     }
-    M = Mn;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ci = c0 + 256 * u;
+      if (ci >= nch) continue;
+      const int h = ci / QC, ch = (ci % QC) * 4;
+      T *dst = (T *)a.o + ((size_t)b * H + h) * R + ch;
+      const float inv = 1.0f / L[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[u][e] * inv);
+    }
   }
-  const float inv = 1.0f / L;
-  T *dst = o + ((size_t)b * H + h) * R + ch;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[e] * inv);
+  if (tid == 0) __hip_atomic_store(&a.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stand-alone merge-append: one workgroup per sequence.
@@ -466,7 +493,8 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
   const int tps = 4 / p.nhb, srows = 16 * tps;
   const size_t stage = (size_t)srows * (r + dR) * esz;
-  const size_t extra = 1024 + (size_t)tps * 16 * p.nhb * 4 + (size_t)tps * p.nhb * 64 * 4 * esz;
+  const size_t extra =
+      1024 + (size_t)tps * 16 * p.nhb * 4 + (size_t)tps * p.nhb * 64 * 4 * esz + 16;
   const int64_t nmax = max_pos / s + 1;
   const int64_t total = (int64_t)B * nmax;
   int64_t chunk = (total + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS;
@@ -492,41 +520,19 @@ hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int
                                    int s, float scale, const int32_t *pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
-                                   const float *gate_pos, float *part_o, float *part_ml, void *o,
-                                   hipStream_t stream) {
+                                   const float *gate_pos, float *part_o, float *part_ml,
+                                   int *counters, void *o, hipStream_t stream) {
   const int esz = dtype == 1 ? 2 : 4;
-  DecodeArgs args{pos,    (char *)cache, batch_stride * esz, qt,         QR,          KR_t,     cg,
-                  b_hc,   gate_pos,      part_o,             part_ml,    o,           H,        s,
-                  plan.chunk, plan.splits, plan.nst,         scale * kLog2e};
+  DecodeArgs args{pos,      (char *)cache, batch_stride * esz, qt,         QR,
+                  KR_t,     cg,            b_hc,               gate_pos,   part_o,
+                  part_ml,  counters,      o,                  H,          s,
+                  plan.chunk, plan.splits, plan.nst,           scale * kLog2e};
   if (dtype == 1) {
     if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream);
     return decode_attn_h<bf16, 512, 64>(plan, B, args, stream);
   }
   if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, args, stream);
   return decode_attn_h<float, 512, 64>(plan, B, args, stream);
-}
-
-hipError_t launch_decode_combine(int dtype, const DecodePlan &plan, int B, int H, int r, int s,
-                                 const int32_t *pos, const float *part_o, const float *part_ml,
-                                 void *o, hipStream_t stream) {
-  if (plan.splits == 1) return hipSuccess;
-  const dim3 grid(B, H);
-  if (dtype == 1) {
-    if (r == 256)
-      hipLaunchKernelGGL((decode_combine_kernel<bf16, 256>), grid, dim3(64), 0, stream, pos, s,
-                         plan.chunk, plan.splits, H, part_o, part_ml, (bf16 *)o);
-    else
-      hipLaunchKernelGGL((decode_combine_kernel<bf16, 512>), grid, dim3(128), 0, stream, pos, s,
-                         plan.chunk, plan.splits, H, part_o, part_ml, (bf16 *)o);
-  } else {
-    if (r == 256)
-      hipLaunchKernelGGL((decode_combine_kernel<float, 256>), grid, dim3(64), 0, stream, pos, s,
-                         plan.chunk, plan.splits, H, part_o, part_ml, (float *)o);
-    else
-      hipLaunchKernelGGL((decode_combine_kernel<float, 512>), grid, dim3(128), 0, stream, pos, s,
-                         plan.chunk, plan.splits, H, part_o, part_ml, (float *)o);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,

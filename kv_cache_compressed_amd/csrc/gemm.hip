@@ -13,7 +13,8 @@
 //    column strip (16 or 32 columns) over all rows, and streams its A and B
 //    tiles through a ring of LDS stages by direct global->LDS loads, several
 //    stages in flight.  K may be split over workgroups; the fp32 partial
-//    tiles are then summed, in split order, by a second small kernel.
+//    tiles (XCD-coherent stores) are then summed, in split order, by the
+//    last workgroup of the strip to finish (atomic counter).
 //
 // B may consist of three row segments (rows < N1 from B1, < N2 from B2, the
 // rest from B3), so that one pass over X yields the latent c = X W_dkv^T, the
@@ -155,7 +156,10 @@ struct SkinnyArgs {
   BSeg bs;
   int M, N, KS;         // KS = K / 32
   int kps, ksplit, nst; // k-steps per split, splits, ring stages
-  float *part;          // [ksplit, M, N] fp32 when ksplit > 1
+  float *part;          // split partials when ksplit > 1: [ksplit][strip][tile][lane] f32x4
+  int *counters;        // [strips], zero on entry when ksplit > 1 (zero again on exit)
+  int *zero;            // ints cleared by workgroup (0, 0) before anything else
+  int nzero;
 };
 
 template <typename T, int BM, int NT, class Epi>
@@ -172,6 +176,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi)
   const int g = lane >> 4, c = lane & 15;
   const int strip = blockIdx.x, split = blockIdx.y;
   const int n0 = strip * NT;
+  if (a.nzero && strip == 0 && split == 0)
+    for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
   const int ks0 = split * a.kps, ks1 = min(a.KS, ks0 + a.kps);
   const int nstage = (ks1 - ks0 + C::SK - 1) / C::SK;
   char *dummy = smem + a.nst * STAGE_B;
@@ -275,37 +281,46 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi)
     }
     return;
   }
+  // K split: partials in fragment order, XCD-coherent; the last workgroup of
+  // the strip to finish adds them in split order and applies the epilogue.
+  const int strips = gridDim.x;
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(a.part, (uint32_t)((size_t)a.ksplit * strips * OT * 64 * 16));
   if (writer) {
 #pragma unroll
     for (int i = 0; i < OTW; ++i) {
-      const int ot = ot0 + 4 * i, xi = ot / NG, ni = ot % NG;
-      const int n = n0 + 16 * ni + c;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * xi + 4 * g + e;
-        if (m < a.M && n < a.N) a.part[((size_t)split * a.M + m) * a.N + n] = acc[i][e];
-      }
+      const int ot = ot0 + 4 * i;
+      st_coh4(rp, (uint32_t)(((((size_t)split * strips + strip) * OT + ot) * 64 + lane) * 16),
+              acc[i]);
     }
   }
-}
-
-// Sum of the K-split partials [ksplit, M, N], in split order, into the epilogue.
-template <class Epi>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, int ksplit, int M,
-                                                            int N, Epi epi) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * N) return;
-  const int m = (int)(idx / N), n = (int)(idx % N);
-  float v = 0.0f;
-  for (int k0 = 0; k0 < ksplit; k0 += 8) {
-    float pv[8];
+  int *last = (int *)smem;
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (tid == 0) *last = ctr_add(&a.counters[strip], 1) == a.ksplit - 1;
+  __syncthreads();
+  if (!*last) return;
+  for (int it = tid; it < OT * 64; it += 256) {
+    const int ot = it / 64, ln = it % 64, xi = ot / NG, ni = ot % NG;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
+      f32x4 pv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      pv[j] = part[((size_t)min(k0 + j, ksplit - 1) * M + m) * N + n];
+      for (int j = 0; j < 8; ++j) {
+        const int kk = min(k0 + j, a.ksplit - 1);
+        pv[j] = ld_coh4(rp, (uint32_t)(((((size_t)kk * strips + strip) * OT + ot) * 64 + ln) * 16));
+      }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v += (k0 + j < ksplit) ? pv[j] : 0.0f;
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < a.ksplit) v += pv[j];
+    }
+    const int n = n0 + 16 * ni + (ln & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * xi + 4 * (ln >> 4) + e;
+      if (m < a.M && n < a.N) epi(m, n, v[e]);
+    }
   }
-  epi(m, n, v);
+  if (tid == 0) __hip_atomic_store(&a.counters[strip], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- epilogues ---------------------------------------------------------------
@@ -387,11 +402,12 @@ hipError_t skinny_t(SkinnyArgs a, int strips, Epi epi, hipStream_t stream) {
 }
 
 // Skinny product of M <= 128 rows: picks the row tile and column strip and,
-// when `ksplit` > 1 and `part` is given, splits K over workgroups (fp32
-// partials in `part`, summed by a second kernel).
+// when `ksplit` > 1 and `part`/`counters` are given, splits K over
+// workgroups.  `zero`: ints cleared at the start (may be null).
 template <typename T, class Epi>
 hipError_t run_skinny(const T *X, int ldx, const BSeg &bs, int M, int N, int K, int ksplit,
-                      float *part, Epi epi, hipStream_t stream) {
+                      float *part, int *counters, int *zero, int nzero, Epi epi,
+                      hipStream_t stream) {
   SkinnyArgs a;
   a.X = X;
   a.ldx = ldx;
@@ -399,42 +415,54 @@ hipError_t run_skinny(const T *X, int ldx, const BSeg &bs, int M, int N, int K, 
   a.M = M;
   a.N = N;
   a.KS = K / 32;
-  if (ksplit < 1 || !part) ksplit = 1;
+  if (ksplit < 1 || !part || !counters) ksplit = 1;
   if (ksplit > a.KS) ksplit = a.KS;
   a.kps = (a.KS + ksplit - 1) / ksplit;
   a.ksplit = (a.KS + a.kps - 1) / a.kps;
   a.nst = 1;
   a.part = part;
-  hipError_t e;
-  if (M <= 16) e = skinny_t<T, 16, 16>(a, (N + 15) / 16, epi, stream);
-  else if (M <= 32) e = skinny_t<T, 32, 16>(a, (N + 15) / 16, epi, stream);
-  else if (M <= 64) e = skinny_t<T, 64, 16>(a, (N + 15) / 16, epi, stream);
-  else e = skinny_t<T, 128, 32>(a, (N + 31) / 32, epi, stream);
-  if (e != hipSuccess || a.ksplit == 1) return e;
-  const int64_t total = (int64_t)M * N;
-  hipLaunchKernelGGL(splitk_reduce_kernel<Epi>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, part, a.ksplit, M, N, epi);
-  return hipGetLastError();
+  a.counters = counters;
+  a.zero = zero;
+  a.nzero = zero ? nzero : 0;
+  if (M <= 16) return skinny_t<T, 16, 16>(a, (N + 15) / 16, epi, stream);
+  if (M <= 32) return skinny_t<T, 32, 16>(a, (N + 15) / 16, epi, stream);
+  if (M <= 64) return skinny_t<T, 64, 16>(a, (N + 15) / 16, epi, stream);
+  return skinny_t<T, 128, 32>(a, (N + 31) / 32, epi, stream);
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(int *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 template <typename T>
 hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_gate, int r,
-                  const void *A, int HR, float *cg, void *qt, hipStream_t stream) {
+                  const void *A, int HR, float *cg, void *qt, int *zero, int nzero,
+                  hipStream_t stream) {
   EpiProj<T> epi{cg, (T *)qt, 2 * r, HR};
   BSeg bs{W_dkv, W_gate, A, r, 2 * r, d};
   const int N = 2 * r + (A ? HR : 0);
-  if (M <= 128) return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, epi, stream);
+  if (M <= 128)
+    return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, nullptr, zero, nzero, epi,
+                         stream);
+  if (zero && nzero > 0) {
+    hipLaunchKernelGGL(zero_kernel, dim3((nzero + 255) / 256), dim3(256), 0, stream, zero, nzero);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return run_gemm<T>((const T *)X, d, bs, M, N, d, epi, stream);
 }
 
 }  // namespace
 
+int out_proj_strips(int M, int N) {
+  if (M > 128) return 0;
+  return M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
+}
+
 int out_proj_splits(int M, int N, int K) {
-  (void)N;
-  (void)K;
   if (M > 128) return 1;
-  return 1;
-  const int strips = M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
+  const int strips = out_proj_strips(M, N);
   int ks = (256 + strips - 1) / strips;   // aim at about 256 workgroups
   const int KS = K / 32;
   if (ks > KS / 8) ks = KS / 8 > 0 ? KS / 8 : 1;   // at least 8 k-steps per split
@@ -453,14 +481,14 @@ hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, 
 }
 
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
-                           float *part, hipStream_t stream) {
+                           float *part, int *counters, hipStream_t stream) {
   if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);
-  const int ks = part ? out_proj_splits(M, N, K) : 1;
+  const int ks = (part && counters) ? out_proj_splits(M, N, K) : 1;
   BSeg bs{Bvo, Bvo, Bvo, N, N, K};
   if (dtype == 1)
-    return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part,
+    return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
                             EpiStore<bf16>{(bf16 *)Y, N}, stream);
-  return run_skinny<float>((const float *)O, K, bs, M, N, K, ks, part,
+  return run_skinny<float>((const float *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
                            EpiStore<float>{(float *)Y, N}, stream);
 }
 
@@ -486,9 +514,9 @@ hipError_t launch_gate_map(int dtype, const void *W_hc, const void *W_dkv, int r
 
 hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv,
                        const void *W_gate, int r, const void *A, int HR, float *cg, void *qt,
-                       hipStream_t stream) {
-  if (dtype == 1) return proj_t<bf16>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, stream);
-  return proj_t<float>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, stream);
+                       int *zero, int nzero, hipStream_t stream) {
+  if (dtype == 1) return proj_t<bf16>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
+  return proj_t<float>(X, M, d, W_dkv, W_gate, r, A, HR, cg, qt, zero, nzero, stream);
 }
 
 }  // namespace mtla

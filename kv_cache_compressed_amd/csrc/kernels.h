@@ -23,17 +23,22 @@ hipError_t launch_gate_map(int dtype, const void *W_hc, const void *W_dkv, int r
                            void *W_gate, hipStream_t stream);
 
 // One pass over X [M, d]: cg [M, 2r] (fp32) = (X W_dkv^T, X W_gate^T), and,
-// when A != nullptr, qt [M, HR] (storage type) = X A^T with A [HR, d].
+// when A != nullptr, qt [M, HR] (storage type) = X A^T with A [HR, d].  When
+// `zero` is given its first `nzero` ints are cleared first (the counters of
+// the kernels that follow in a decoding step).
 hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv,
                        const void *W_gate, int r, const void *A, int HR, float *cg, void *qt,
-                       hipStream_t stream);
+                       int *zero, int nzero, hipStream_t stream);
 
-// Y [M, N] = O [M, K] Bvo [N, K]^T.  For M <= 128 and `part` given, the
-// product is split over K (out_proj_splits) with fp32 partials in `part`
-// [splits, M, N], summed by a second kernel.
+// Y [M, N] = O [M, K] Bvo [N, K]^T.  For M <= 128 with `part` and `counters`
+// given, K is split over workgroups (out_proj_splits) with fp32 partials in
+// `part` (out_proj_splits * M_pad * N floats at most, M_pad = M rounded up
+// to the row tile of 16, 32, 64 or 128) and one counter per column strip
+// (out_proj_strips), zero on entry (zero again on exit).
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
-                           float *part, hipStream_t stream);
+                           float *part, int *counters, hipStream_t stream);
 int out_proj_splits(int M, int N, int K);
+int out_proj_strips(int M, int N);
 
 // ---- incremental decoding ---------------------------------------------------
 
@@ -52,21 +57,16 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
 
 // Merge of frame pos[b] into slot floor(pos[b]/s) of every sequence (from
 // cg = (c, gate pre-activation) and the tables), then attention over slots
-// 0..floor(pos[b]/s): sequences that fit one split are written to o [B, H, r]
-// (storage type), the others leave partials part_o [B, splits, H, r] and
-// part_ml [B, splits, H, 2] (fp32) for launch_decode_combine.  qt [B, H, r],
-// QR [B, H, dR], KR_t [B, dR].
+// 0..floor(pos[b]/s) into o [B, H, r] (storage type).  qt [B, H, r], QR
+// [B, H, dR], KR_t [B, dR]; split partials part_o [B, splits, H, r] and
+// part_ml [B, splits, H, 2] fp32; counters [B], zero on entry (zero again on
+// exit).
 hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
                                    int s, float scale, const int32_t *pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
-                                   const float *gate_pos, float *part_o, float *part_ml, void *o,
-                                   hipStream_t stream);
-
-// Log-sum-exp merge of the splits into o (nothing to do when plan.splits == 1).
-hipError_t launch_decode_combine(int dtype, const DecodePlan &plan, int B, int H, int r, int s,
-                                 const int32_t *pos, const float *part_o, const float *part_ml,
-                                 void *o, hipStream_t stream);
+                                   const float *gate_pos, float *part_o, float *part_ml,
+                                   int *counters, void *o, hipStream_t stream);
 
 // Merge alone (no attention), one workgroup per sequence.
 hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,

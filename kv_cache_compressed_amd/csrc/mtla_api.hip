@@ -97,7 +97,8 @@ mtla_status launched(hipError_t e, const char *what) {
   } while (0)
 
 struct DecodeWs {
-  size_t cg, qt, part_o, part_ml, o, ypart, total;
+  size_t cg, qt, part_o, part_ml, o, ypart, counters, total;
+  int ncount;
 };
 
 // Workspace of one decoding step (plan != nullptr) or of a merge-append.
@@ -106,14 +107,18 @@ DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
   const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r;
   size_t off = 0;
   w.cg = off; off += align_up(B * 2 * r * 4);
-  w.qt = w.part_o = w.part_ml = w.o = w.ypart = 0;
+  w.qt = w.part_o = w.part_ml = w.o = w.ypart = w.counters = 0;
+  w.ncount = 0;
   if (plan) {
     const int ks = mtla::out_proj_splits(B, d->d, (int)HR);
+    const size_t mpad = B <= 16 ? 16 : B <= 32 ? 32 : B <= 64 ? 64 : 128;
+    w.ncount = B + mtla::out_proj_strips(B, d->d);
     w.qt = off;       off += align_up(B * HR * e);
     w.part_o = off;   off += align_up((size_t)B * plan->splits * HR * 4);
     w.part_ml = off;  off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
     w.o = off;        off += align_up(B * HR * e);
-    w.ypart = off;    off += align_up((size_t)ks * B * d->d * 4);
+    w.ypart = off;    off += align_up((size_t)ks * mpad * (d->d + 32) * 4);
+    w.counters = off; off += align_up((size_t)w.ncount * 4);
   }
   w.total = off;
   return w;
@@ -233,7 +238,7 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
   hipStream_t s = (hipStream_t)stream;
   float *cg = (float *)((char *)workspace + ws.cg);
   LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, nullptr, 0,
-                           cg, nullptr, s),
+                           cg, nullptr, nullptr, 0, s),
          "latent and gate projection");
   LAUNCH(mtla::launch_merge(dims->dtype, B, dims->r, dims->d_hR, dims->s, pos, cg, w->b_hc,
                             w->gate_pos, KR_t, cache->slots, cache->batch_stride, s),
@@ -276,20 +281,19 @@ mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const
   void *qt = base + ws.qt, *o = base + ws.o;
   float *part_o = (float *)(base + ws.part_o), *part_ml = (float *)(base + ws.part_ml);
   float *ypart = (float *)(base + ws.ypart);
+  int *counters = (int *)(base + ws.counters);
   const int HR = dims->H * dims->r;
   LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
-                           qt, s),
+                           qt, counters, ws.ncount, s),
          "latent, gate and query projection");
   if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
                                        eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
-                                       QR_t, KR_t, cg, w->b_hc, w->gate_pos, part_o, part_ml, o, s),
+                                       QR_t, KR_t, cg, w->b_hc, w->gate_pos, part_o, part_ml,
+                                       counters, o, s),
          "merge and decode attention");
   if ((st = record(events, 1, s)) != MTLA_OK) return st;
-  LAUNCH(mtla::launch_decode_combine(dims->dtype, plan, B, dims->H, dims->r, dims->s, pos, part_o,
-                                     part_ml, o, s),
-         "split combine");
-  LAUNCH(mtla::launch_out_proj(dims->dtype, o, B, HR, w->Bvo, dims->d, Y, ypart, s),
+  LAUNCH(mtla::launch_out_proj(dims->dtype, o, B, HR, w->Bvo, dims->d, Y, ypart, counters + B, s),
          "output projection");
   return ok();
 }
@@ -330,7 +334,7 @@ mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const voi
   void *Cp = Cprime_out ? Cprime_out : (void *)(base + ws.Cp);
   const int M = B * T, HR = dims->H * dims->r;
   LAUNCH(mtla::launch_proj(dims->dtype, X, M, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
-                           qt, s),
+                           qt, nullptr, 0, s),
          "latent, gate and query projection");
   LAUNCH(mtla::launch_group_scan(dims->dtype, cg, w->b_hc, w->gate_pos, KR, B, T, dims->r,
                                  dims->d_hR, dims->s, Cp, keys, ws.keys_stride,
@@ -342,7 +346,7 @@ mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const voi
                                         eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s),
          "strided attention");
   if ((st = record(events, 1, s)) != MTLA_OK) return st;
-  LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HR, w->Bvo, dims->d, Y, nullptr, s),
+  LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HR, w->Bvo, dims->d, Y, nullptr, nullptr, s),
          "output projection");
   return ok();
 }
