@@ -163,11 +163,12 @@ mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, c
                                  size_t ws_bytes, void *stream);
 
 /* Profiling variants of mtla_decode_step and mtla_prefill_strided: the same
- * computation, and in addition events[0] is recorded on `stream` just before
- * the attention kernel (the split-K decode attention, resp. the strided
- * prefill attention) and events[1] just after it, so the caller can time that
- * kernel alone with hipEventElapsedTime.  `events` points to two hipEvent_t
- * handles owned by the caller; a missing handle is MTLA_ERR_ARG. */
+ * computation, and in addition the attention kernel (the split-K decode
+ * attention, resp. the strided prefill attention) is launched so that the
+ * runtime stamps events[0] with its start and events[1] with its end
+ * (hipExtLaunchKernel; no extra marker packets), for hipEventElapsedTime.
+ * `events` points to two hipEvent_t handles (created with timing enabled)
+ * owned by the caller; a missing handle is MTLA_ERR_ARG. */
 mtla_status mtla_decode_step_timed(const mtla_dims *dims, const mtla_weights *w,
                                    const mtla_cache *cache, const void *X_t, const void *QR_t,
                                    const void *KR_t, const int32_t *pos, int32_t B, int32_t max_pos,

@@ -319,7 +319,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
 template <typename T, int R, int DR>
 hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void *qt,
                           const void *QR, const void *keys, int64_t kstride, const void *Cp,
-                          const void *KR, void *O, hipStream_t stream) {
+                          const void *KR, void *O, hipStream_t stream, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   constexpr int NQ = R <= 256 ? 2 : 1;
   constexpr bool PF = sizeof(T) == 2;
   constexpr int ROWS = 64 * NQ;
@@ -328,8 +329,7 @@ hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void 
   auto kern = prefill_attn_kernel<T, R, DR, NQ, PF>;
   allow_lds<prefill_attn_kernel<T, R, DR, NQ, PF>>();
   PrefillArgs args{qt, QR, keys, kstride, Cp, KR, O, B, T_len, H, s, tiles, sl2};
-  hipLaunchKernelGGL(kern, dim3(tiles * B), dim3(256), lds, stream, args);
-  return hipGetLastError();
+  return launch_timed((const void *)kern, dim3(tiles * B), dim3(256), lds, stream, &args, ev0, ev1);
 }
 
 }  // namespace
@@ -361,14 +361,14 @@ bool prefill_attention_supported(int dtype, int H, int r, int dR) {
 hipError_t launch_prefill_attention(int dtype, int B, int T, int H, int r, int dR, int s,
                                     float scale, const void *qt, const void *QR, const void *keys,
                                     int64_t keys_stride, const void *Cp, const void *KR, void *O,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const float sl2 = scale * kLog2e;
   if (dtype == 1) {
-    if (r == 256) return prefill_attn_t<bf16, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream);
-    return prefill_attn_t<bf16, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream);
+    if (r == 256) return prefill_attn_t<bf16, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
+    return prefill_attn_t<bf16, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
   }
-  if (r == 256) return prefill_attn_t<float, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream);
-  return prefill_attn_t<float, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream);
+  if (r == 256) return prefill_attn_t<float, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
+  return prefill_attn_t<float, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
 }
 
 }  // namespace mtla

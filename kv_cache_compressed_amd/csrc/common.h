@@ -12,6 +12,7 @@
 // written once over the storage type T.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -220,6 +221,23 @@ template <auto Kernel> void allow_lds() {
     return true;
   }();
   (void)once;
+}
+
+// Launch a kernel taking one argument struct; when ev0/ev1 are given, the
+// runtime stamps them with the kernel's own start and end (hipExtLaunchKernel:
+// no separate marker packets, so nothing is added between kernels).
+template <class Args>
+hipError_t launch_timed(const void *kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                        Args *args, hipEvent_t ev0, hipEvent_t ev1) {
+  void *argv[] = {(void *)args};
+  if (ev0 || ev1) {
+    const hipError_t e = hipExtLaunchKernel(kernel, grid, block, argv, lds, stream, ev0, ev1, 0);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+  }
+  const hipError_t e = hipLaunchKernel(kernel, grid, block, argv, lds, stream);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
 }
 
 }  // namespace mtla

@@ -465,18 +465,20 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *pos, int s, i
 
 
 template <typename T, int R, int DR, int NHB>
-hipError_t decode_attn_t(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream) {
+hipError_t decode_attn_t(const DecodePlan &p, int B, DecodeArgs args, hipStream_t stream,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  auto kern = decode_attn_kernel<T, R, DR, NHB>;
   allow_lds<decode_attn_kernel<T, R, DR, NHB>>();
-  hipLaunchKernelGGL((decode_attn_kernel<T, R, DR, NHB>), dim3(p.splits, B), dim3(256), p.lds,
-                     stream, args);
-  return hipGetLastError();
+  return launch_timed((const void *)kern, dim3(p.splits, B), dim3(256), p.lds, stream, &args,
+                      ev0, ev1);
 }
 
 template <typename T, int R, int DR>
-hipError_t decode_attn_h(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream) {
-  if (p.nhb == 1) return decode_attn_t<T, R, DR, 1>(p, B, args, stream);
-  if (p.nhb == 2) return decode_attn_t<T, R, DR, 2>(p, B, args, stream);
-  return decode_attn_t<T, R, DR, 4>(p, B, args, stream);
+hipError_t decode_attn_h(const DecodePlan &p, int B, const DecodeArgs &args, hipStream_t stream,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  if (p.nhb == 1) return decode_attn_t<T, R, DR, 1>(p, B, args, stream, ev0, ev1);
+  if (p.nhb == 2) return decode_attn_t<T, R, DR, 2>(p, B, args, stream, ev0, ev1);
+  return decode_attn_t<T, R, DR, 4>(p, B, args, stream, ev0, ev1);
 }
 
 }  // namespace
@@ -521,18 +523,19 @@ hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
                                    const float *gate_pos, float *part_o, float *part_ml,
-                                   int *counters, void *o, hipStream_t stream) {
+                                   int *counters, void *o, hipStream_t stream, hipEvent_t ev0,
+                                   hipEvent_t ev1) {
   const int esz = dtype == 1 ? 2 : 4;
   DecodeArgs args{pos,      (char *)cache, batch_stride * esz, qt,         QR,
                   KR_t,     cg,            b_hc,               gate_pos,   part_o,
                   part_ml,  counters,      o,                  H,          s,
                   plan.chunk, plan.splits, plan.nst,           scale * kLog2e};
   if (dtype == 1) {
-    if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream);
-    return decode_attn_h<bf16, 512, 64>(plan, B, args, stream);
+    if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream, ev0, ev1);
+    return decode_attn_h<bf16, 512, 64>(plan, B, args, stream, ev0, ev1);
   }
-  if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, args, stream);
-  return decode_attn_h<float, 512, 64>(plan, B, args, stream);
+  if (r == 256) return decode_attn_h<float, 256, 32>(plan, B, args, stream, ev0, ev1);
+  return decode_attn_h<float, 512, 64>(plan, B, args, stream, ev0, ev1);
 }
 
 hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,

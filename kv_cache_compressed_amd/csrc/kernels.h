@@ -1,5 +1,7 @@
 // Launchers of the MTLA kernels; every launcher enqueues on `stream` and
-// returns hipGetLastError() of its launch.  Pointers are device pointers in
+// returns hipGetLastError() of its launch.  Attention launchers take an
+// optional pair of events that the runtime stamps with the kernel's own
+// start and end.  Pointers are device pointers in
 // the storage type selected by `dtype` (0 fp32, 1 bf16) unless typed.
 #pragma once
 
@@ -66,7 +68,8 @@ hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
                                    const float *gate_pos, float *part_o, float *part_ml,
-                                   int *counters, void *o, hipStream_t stream);
+                                   int *counters, void *o, hipStream_t stream,
+                                   hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Merge alone (no attention), one workgroup per sequence.
 hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,
@@ -91,7 +94,8 @@ hipError_t launch_group_scan(int dtype, const float *cg, const void *b_hc, const
 hipError_t launch_prefill_attention(int dtype, int B, int T, int H, int r, int dR, int s,
                                     float scale, const void *qt, const void *QR, const void *keys,
                                     int64_t keys_stride, const void *Cp, const void *KR, void *O,
-                                    hipStream_t stream);
+                                    hipStream_t stream,
+                                    hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 bool prefill_attention_supported(int dtype, int H, int r, int dR);
 

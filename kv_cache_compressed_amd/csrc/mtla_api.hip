@@ -250,10 +250,9 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
 
 namespace {
 
-mtla_status record(void *const *events, int i, hipStream_t s) {
-  if (!events) return MTLA_OK;
-  return launched(hipEventRecord((hipEvent_t)events[i], s), "event record");
-}
+hipEvent_t ev0(void *const *events) { return events ? (hipEvent_t)events[0] : nullptr; }
+hipEvent_t ev1(void *const *events) { return events ? (hipEvent_t)events[1] : nullptr; }
+
 
 mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                              const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
@@ -286,13 +285,11 @@ mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const
   LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
                            qt, counters, ws.ncount, s),
          "latent, gate and query projection");
-  if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
                                        eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
                                        QR_t, KR_t, cg, w->b_hc, w->gate_pos, part_o, part_ml,
-                                       counters, o, s),
+                                       counters, o, s, ev0(events), ev1(events)),
          "merge and decode attention");
-  if ((st = record(events, 1, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_out_proj(dims->dtype, o, B, HR, w->Bvo, dims->d, Y, ypart, counters + B, s),
          "output projection");
   return ok();
@@ -341,11 +338,10 @@ mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const voi
                                  cache_out ? cache_out->slots : nullptr,
                                  cache_out ? cache_out->batch_stride : 0, s),
          "gate and group scan");
-  if ((st = record(events, 0, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_prefill_attention(dims->dtype, B, T, dims->H, dims->r, dims->d_hR, dims->s,
-                                        eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s),
+                                        eff_scale(dims), qt, QR, keys, ws.keys_stride, Cp, KR, O, s,
+                                        ev0(events), ev1(events)),
          "strided attention");
-  if ((st = record(events, 1, s)) != MTLA_OK) return st;
   LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HR, w->Bvo, dims->d, Y, nullptr, nullptr, s),
          "output projection");
   return ok();
