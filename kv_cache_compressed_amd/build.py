@@ -16,8 +16,13 @@ SOURCES = ["gemm.hip", "decode.hip", "attention.hip", "mtla_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs (gfx950 reads C
+# and writes D there), instead of copying every accumulator through AGPRs
+# around each product; the attention kernels keep their O accumulators live
+# across VALU rescaling, which the copies otherwise make expensive.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", INCLUDE, "-I", CSRC]
 
 

@@ -2,25 +2,26 @@
 // group scan that build the intermediate states C', and the stride-aware
 // masked attention kernel.
 //
-// The attention kernel's wave-level step (attend32): a tile of 32
-// compressed rows (latent r values followed by the RoPE key) sits in LDS, and
-// a wave scores it against 16*NQ query columns held in registers:
-//
-//   S^T (32 keys x 16 cols) = K_tile (32 x (r+d_hR)) . Q^T     A = keys from LDS
-//   O^T (r x 16 cols)     += C_tile^T (r x 32) . P^T          A = keys, read transposed
-//
-// Keys are the MFMA A operand in both products.  For the second one each lane
-// needs 8 keys of one latent channel; gfx950's ds_read_tr16_b64 delivers them
-// from the row-major tile (two reads per 16x16x32 MFMA).  The k index of the
-// P.V product runs over the keys in the order {4g..4g+3, 16+4g..16+4g+3},
-// which is exactly the order in which each lane already holds its
-// probabilities after the score MFMA, so P needs no cross-lane movement.
-// Softmax runs online in log2 units; a column's running max is shared by the
-// four lane groups, the running sum stays per lane and is reduced at the end.
-//
 // [Notes] = "Multi-head Temporal Latent Attention" paper notes (zhaoyang97
-// Paper-Notes): key designs / stride-aware causal mask and decoupled RoPE
-// (the Y formula); [Fig2] = sciencestack.ai page, Figure 2.
+// Paper-Notes): key designs / hyper-network temporal merging, stride-aware
+// causal mask and decoupled RoPE (the Y formula); [Fig2] = sciencestack.ai
+// page, Figure 2 (c).
+//
+// Attention kernel.  Query rows are (frame m, head h) pairs, row = m*H + h.
+// Row (m, h) sees the compact keys j < floor(m/s) -- the group-final states of
+// the groups that ended before m, i.e. the stride-aware mask's columns
+// n < m with n mod s = s-1 -- plus its own state C'_m, which seeds the online
+// softmax.  A workgroup owns 4 * 16 * NQ consecutive rows; each wave holds
+// 16 * NQ of them (NQ 16-row tiles) with their queries in registers and
+// their O^T (r x rows) accumulators in AGPRs.  The compact keys stream
+// through a ring of LDS stages (32 keys each) by direct global->LDS loads,
+// in the swizzled 16-row tile layout; the loop ends at the workgroup's causal
+// frontier, so masked tiles are never visited.  Per 16-key tile a wave:
+//   S^T (16 keys x 16 rows) = K . Q^T        K from LDS, A operand, K=32 MFMA
+//   online softmax in log2 units, reference max moved lazily (by > 2^8)
+//   O^T (r x 16 rows)     += C^T . P^T      C^T by ds_read_tr16_b64, K=16 MFMA
+// Each K fragment read from LDS feeds NQ MFMAs and each C^T fragment NQ more,
+// which keeps LDS traffic below what the matrix cores consume.
 
 #include <math.h>
 
@@ -32,102 +33,6 @@ namespace mtla {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-template <typename T, int R, int DR, int NQ> struct AttnState {
-  static constexpr int RK = R + DR, KS = RK / 32, MT = R / 16;
-  typename Frag<T>::type q[NQ][KS];
-  f32x4 o[NQ][MT];
-  float m[NQ];
-  float l[NQ];
-};
-
-// A operand of O^T += C^T P^T for latent channels ch0..ch0+15: lane (g, j)
-// receives channel ch0 + j of keys {4g+e} (e < 4) and {16+4g+e-4} (e >= 4).
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type pv_frag(const char *kt, int stride, int ch0,
-                                                          int g, int j) {
-  if constexpr (sizeof(T) == 2) {
-    // ds_read_tr16_b64: within a 16-lane group, lane i returns element
-    // [4e + i/4][i%4] of the 16 x 4 block whose row k lane k addressed.
-    const char *p0 = kt + (4 * g + (j >> 2)) * stride + (ch0 + 4 * (j & 3)) * 2;
-    const char *p1 = p0 + 16 * stride;
-    bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
-    bf16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
-    return (bf16x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  } else {
-    f32x8 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = *(const float *)(kt + (4 * g + e) * stride + (ch0 + j) * 4);
-      v[4 + e] = *(const float *)(kt + (16 + 4 * g + e) * stride + (ch0 + j) * 4);
-    }
-    return v;
-  }
-}
-
-// One 32-key tile: key kbase + k is visible to column q iff kbase + k < lim[q].
-template <typename T, int R, int DR, int NQ>
-__device__ __forceinline__ void attend32(AttnState<T, R, DR, NQ> &st, const char *kt, int stride,
-                                         int kbase, const int (&lim)[NQ], float sl2) {
-  constexpr int KS = AttnState<T, R, DR, NQ>::KS, MT = AttnState<T, R, DR, NQ>::MT;
-  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  f32x4 s0[NQ], s1[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) s0[q] = s1[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    typename Frag<T>::type a0, a1;
-    load8(a0, (const T *)(kt + c * stride + (32 * ks + 8 * g) * (int)sizeof(T)));
-    load8(a1, (const T *)(kt + (16 + c) * stride + (32 * ks + 8 * g) * (int)sizeof(T)));
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      s0[q] = mma_k32(a0, st.q[q][ks], s0[q]);
-      s1[q] = mma_k32(a1, st.q[q][ks], s1[q]);
-    }
-  }
-  typename Frag<T>::type pf[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    float mx = kNegInf;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int k0 = kbase + 4 * g + e;
-      const float v0 = k0 < lim[q] ? s0[q][e] * sl2 : kNegInf;
-      const float v1 = k0 + 16 < lim[q] ? s1[q][e] * sl2 : kNegInf;
-      s0[q][e] = v0;
-      s1[q][e] = v1;
-      mx = fmaxf(mx, fmaxf(v0, v1));
-    }
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float mn = fmaxf(st.m[q], mx);
-    const bool none = (mn == kNegInf);
-    const float alpha = none ? 1.0f : exp2f(st.m[q] - mn);
-    float ps = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = none ? 0.0f : exp2f(s0[q][e] - mn);
-      const float p1 = none ? 0.0f : exp2f(s1[q][e] - mn);
-      ps += p0 + p1;
-      pf[q][e] = (T)p0;
-      pf[q][4 + e] = (T)p1;
-    }
-    st.l[q] = st.l[q] * alpha + ps;
-    st.m[q] = mn;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) st.o[q][mt] *= alpha;
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const typename Frag<T>::type a = pv_frag<T>(kt, stride, 16 * mt, g, c);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) st.o[q][mt] = mma_k32(a, pf[q], st.o[q][mt]);
-  }
-}
-
-template <typename T> constexpr int row_stride(int rk) { return rk * (int)sizeof(T) + 16; }
 
 // ---------------------------------------------------------------------------
 // parallel form ([Notes] stride-aware causal mask; [Fig2] (c))
@@ -167,30 +72,32 @@ __global__ __launch_bounds__(256) void group_scan_kernel(const float *cg, const 
 }
 
 struct PrefillArgs {
-  const void *qt;
-  const void *QR;
-  const void *keys;
-  int64_t kstride;
-  const void *Cp;
-  const void *KR;
-  void *O;
-  int B, T, H, s, tiles;
+  const void *qt;        // [B, T, H, R]
+  const void *QR;        // [B, T, H, DR]
+  const char *keys;      // [B] x keys_stride: ceil(T/s) compact rows of R + DR values
+  int64_t kstride_bytes;
+  const void *Cp;        // [B, T, R]
+  const void *KR;        // [B, T, DR]
+  void *O;               // [B, T, H, R]
+  int B, T, H, s, tiles, nst;
   float sl2;
 };
 
-// Rows of the query side are (frame m, head h) pairs, row = m*H + h; a
-// workgroup owns 128 consecutive rows, each wave 32*NQ/2 of them (NQ tiles of
-// 16).  Row (m, h) sees the compressed rows j < floor(m/s) -- the group-final
-// states of the groups that ended before m -- plus its own state C'_m, which
-// seeds the online softmax (score, weight 1, value C'_m) before the key loop.
-template <typename T, int R, int DR, int NQ, bool PREFETCH>
+template <typename T, int R, int DR, int NQ> struct PreCfg {
+  static constexpr int RK = R + DR, ES = (int)sizeof(T), RB = RK * ES, NSEG = RB / 64;
+  static constexpr int KS = RK / 32, MT = R / 16;
+  static constexpr int ROWS_W = 16 * NQ, ROWS = 4 * ROWS_W;
+  static constexpr int TPS = 2, SROWS = 16 * TPS;          // 32 keys per stage
+  static constexpr int TILE_B = 16 * RB, STAGE_B = TPS * TILE_B;
+  static constexpr int NBLK = TPS * NSEG, LPW = (NBLK + 3) / 4;
+  static_assert(MT % 8 == 0, "channel blocks come in groups of 8");
+};
+
+template <typename T, int R, int DR, int NQ>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
-  constexpr int RK = R + DR, STRIDE = row_stride<T>(RK);
-  constexpr int CH = RK * (int)sizeof(T) / 16, EPC = 16 / (int)sizeof(T);
-  constexpr int KBLK = 64, NCH = KBLK * CH, NLD = (NCH + 255) / 256;
-  constexpr int KS = RK / 32, MT = R / 16;
-  constexpr int ROWS = 64 * NQ;                // rows per workgroup
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  using C = PreCfg<T, R, DR, NQ>;
+  typedef typename Frag4<T>::type P4;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -211,124 +118,178 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
     }
   }
   const int nrows = Tn * H;
-  const int rw = qtile * ROWS + wave * 16 * NQ;
+  const int rw = qtile * C::ROWS + wave * C::ROWS_W;   // first row of this wave
 
-  AttnState<T, R, DR, NQ> st;
+  // Queries, the self term and the initial state of every row of the wave.
+  typename Frag<T>::type q[NQ][C::KS];
+  f32x4 o[NQ][C::MT];
+  float m[NQ], l[NQ];
   int lim[NQ];
-  int wlim = 0;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int row = rw + 16 * q + c;
+  for (int qi = 0; qi < NQ; ++qi) {
+    // Rows past the end read row 0 (valid memory) and are never written back.
+    const int row = rw + 16 * qi + c;
     const bool ok = row < nrows;
-    const int m = ok ? row / H : 0, h = ok ? row % H : 0;
-    lim[q] = ok ? m / s : 0;
-    const size_t qoff = ((size_t)b * Tn + m) * H + h;
+    const int rr = ok ? row : 0;
+    const int mf = rr / H, h = rr % H;
+    lim[qi] = ok ? mf / s : 0;
+    const size_t qoff = ((size_t)b * Tn + mf) * H + h;
+    const size_t coff = (size_t)b * Tn + mf;
     float dot = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
       const int k = 32 * ks + 8 * g;
       typename Frag<T>::type d;
-      if (ok) {
-        if (k < R) {
-          load8(st.q[q][ks], (const T *)a.qt + qoff * R + k);
-          load8(d, (const T *)a.Cp + ((size_t)b * Tn + m) * R + k);
-        } else {
-          load8(st.q[q][ks], (const T *)a.QR + qoff * DR + (k - R));
-          load8(d, (const T *)a.KR + ((size_t)b * Tn + m) * DR + (k - R));
-        }
+      if (k < R) {
+        load8(q[qi][ks], (const T *)a.qt + qoff * R + k);
+        load8(d, (const T *)a.Cp + coff * R + k);
       } else {
-        st.q[q][ks] = zero_frag<T>();
-        d = zero_frag<T>();
+        load8(q[qi][ks], (const T *)a.QR + qoff * DR + (k - R));
+        load8(d, (const T *)a.KR + coff * DR + (k - R));
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot += to_f32(st.q[q][ks][e]) * to_f32(d[e]);
+      for (int e = 0; e < 8; ++e) dot += to_f32(q[qi][ks][e]) * to_f32(d[e]);
     }
-    dot += wave_xor(dot, 16);
-    dot += wave_xor(dot, 32);
-    st.m[q] = dot * a.sl2;
-    st.l[q] = (g == 0) ? 1.0f : 0.0f;
+    m[qi] = sum_g(dot) * a.sl2;
+    l[qi] = (g == 0) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        st.o[q][mt][e] = ok ? to_f32(((const T *)a.Cp)[((size_t)b * Tn + m) * R + 16 * mt + 4 * g + e]) : 0.0f;
-    }
+    for (int mt = 0; mt < C::MT; ++mt) o[qi][mt] = load4f((const T *)a.Cp + coff * R + 16 * mt + 4 * g);
   }
-  // Largest key count any row of this wave / workgroup can see.
-  {
-    const int last = min(rw + 16 * NQ, nrows) - 1;
-    wlim = last >= 0 ? (last / H) / s : 0;
-  }
-  const int last_wg = min(qtile * ROWS + ROWS, nrows) - 1;
-  const int kmax = (last_wg / H) / s;
+  asm volatile("" ::: "memory");
 
-  const T *src = (const T *)a.keys + (size_t)b * a.kstride;
-  u32x4 pre[NLD];
-  auto fetch = [&](int kb0) {
+  // Keys this wave / workgroup can see at most (row limits grow with the row).
+  const int wlast = min(rw + C::ROWS_W, nrows) - 1;
+  const int wlim = wlast >= rw ? (wlast / H) / s : 0;
+  const int glast = min(qtile * C::ROWS + C::ROWS, nrows) - 1;
+  const int kmax = (glast / H) / s;
+  const int nstage = (kmax + C::SROWS - 1) / C::SROWS;
+  const char *src = a.keys + (size_t)b * a.kstride_bytes;
+  char *dummy = smem + a.nst * C::STAGE_B;
+
+  auto issue = [&](int sidx) {
+    char *sb = smem + (sidx % a.nst) * C::STAGE_B;
+    const int row0 = sidx * C::SROWS;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / CH, ch = idx % CH;
-      pre[i] = (u32x4){0u, 0u, 0u, 0u};
-      if (idx < NCH && kb0 + row < kmax) pre[i] = ldg16(src + (size_t)(kb0 + row) * RK + ch * EPC);
+    for (int i = 0; i < C::LPW; ++i) {
+      const int blk = wave + 4 * i;
+      const bool real = (C::NBLK % 4 == 0) || blk < C::NBLK;
+      const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
+      const int key = min(row0 + tl * 16 + (lane >> 2), kmax - 1);
+      dma_block(src + (size_t)key * C::RB, qq, real ? sb + tl * C::TILE_B + qq * 1024 : dummy);
     }
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int idx = tid + 256 * i;
-      if (idx < NCH) sts16(smem + (idx / CH) * STRIDE + (idx % CH) * 16, pre[i]);
-    }
-  };
+  const int pro = min(a.nst, nstage);
+  for (int k = 0; k < pro; ++k) issue(k);
 
-  if (PREFETCH && kmax > 0) fetch(0);
-  for (int kb0 = 0; kb0 < kmax; kb0 += KBLK) {
-    if (!PREFETCH) fetch(kb0);
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (PREFETCH && kb0 + KBLK < kmax) fetch(kb0 + KBLK);
+  for (int k = 0; k < nstage; ++k) {
+    wait_stages<C::LPW>(min(a.nst - 1, nstage - 1 - k));
+    bar();
+    // Every wave is past stage k-1 here: its ring slot can be refilled.
+    if (k >= 1 && k - 1 + a.nst < nstage) issue(k - 1 + a.nst);
+    const char *sb = smem + (k % a.nst) * C::STAGE_B;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kt = kb0 + 32 * half;
-      if (kt < wlim) attend32<T, R, DR, NQ>(st, smem + 32 * half * STRIDE, STRIDE, kt, lim, a.sl2);
+    for (int tl = 0; tl < C::TPS; ++tl) {
+      const int kb = k * C::SROWS + tl * 16;
+      if (kb >= wlim) continue;
+      const char *tile = sb + tl * C::TILE_B;
+      // S^T for the NQ row tiles; each K fragment feeds NQ products.
+      f32x4 sc[NQ];
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) sc[qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const typename Frag<T>::type af = s_frag<T>(tile, c, ks, g);
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) sc[qi] = mma_k32(af, q[qi][ks], sc[qi]);
+      }
+      // Online softmax per row; the reference max moves only by steps > 2^8.
+      float z[NQ][4];
+      bool up_any = false;
+      float mnew[NQ];
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[qi][e] = (kb + 4 * g + e < lim[qi]) ? sc[qi][e] * a.sl2 : kNegInf;
+          mx = fmaxf(mx, z[qi][e]);
+        }
+        mx = max_g(mx);
+        const bool up = mx > m[qi] + 8.0f;
+        mnew[qi] = up ? mx : m[qi];
+        up_any |= up;
+      }
+      if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+          const float alpha = __builtin_amdgcn_exp2f(m[qi] - mnew[qi]);
+          l[qi] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < C::MT; ++mt) o[qi][mt] *= alpha;
+          m[qi] = mnew[qi];
+        }
+      }
+      P4 pf[NQ];
+#pragma unroll
+      for (int qi = 0; qi < NQ; ++qi) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(z[qi][e] - m[qi]);
+          l[qi] += p;
+          pf[qi][e] = from_f32<T>(p);
+        }
+      }
+      // O^T += C^T P^T; each C^T fragment feeds NQ products.
+#pragma unroll
+      for (int m0 = 0; m0 < C::MT; m0 += 8) {
+        typename Frag4<T>::type vv[8];
+        if constexpr (sizeof(T) == 2) {
+          uint32_t ad[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            ad[j] = lds_addr(tile + tile_off(4 * g + (c >> 2), (16 * (m0 + j) + 4 * (c & 3)) * 2));
+          ds_read_tr8(vv, ad);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vv[j] = v_frag_f32(tile, 16 * (m0 + j), g, c);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int qi = 0; qi < NQ; ++qi) o[qi][m0 + j] = mma_k16(vv[j], pf[qi], o[qi][m0 + j]);
+      }
     }
   }
 
   // O = O^T / l, written back row-major [B, T, H, R].
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    float lt = st.l[q] + wave_xor(st.l[q], 16);
-    lt += wave_xor(lt, 32);
-    const int row = rw + 16 * q + c;
+  for (int qi = 0; qi < NQ; ++qi) {
+    const float lt = sum_g(l[qi]);
+    const int row = rw + 16 * qi + c;
     if (row < nrows) {
       const float inv = 1.0f / lt;
-      T *dst = (T *)a.O + ((size_t)b * nrows + row) * R;
+      T *dst = (T *)a.O + ((size_t)b * nrows + row) * R + 4 * g;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[16 * mt + 4 * g + e] = from_f32<T>(st.o[q][mt][e] * inv);
+      for (int mt = 0; mt < C::MT; ++mt) store4f(dst + 16 * mt, o[qi][mt] * inv);
     }
   }
 }
 
-// Raise the dynamic-LDS limit of a kernel to the full 160 KB once per
-// instantiation (thread-safe static initialisation), so that launches made
-// later -- possibly under graph capture -- issue nothing but the launch.
-
-template <typename T, int R, int DR>
+template <typename T, int R, int DR, int NQ>
 hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void *qt,
                           const void *QR, const void *keys, int64_t kstride, const void *Cp,
                           const void *KR, void *O, hipStream_t stream, hipEvent_t ev0,
                           hipEvent_t ev1) {
-  constexpr int NQ = R <= 256 ? 2 : 1;
-  constexpr bool PF = sizeof(T) == 2;
-  constexpr int ROWS = 64 * NQ;
-  const int tiles = (T_len * H + ROWS - 1) / ROWS;
-  const size_t lds = (size_t)64 * row_stride<T>(R + DR);
-  auto kern = prefill_attn_kernel<T, R, DR, NQ, PF>;
-  allow_lds<prefill_attn_kernel<T, R, DR, NQ, PF>>();
-  PrefillArgs args{qt, QR, keys, kstride, Cp, KR, O, B, T_len, H, s, tiles, sl2};
+  using C = PreCfg<T, R, DR, NQ>;
+  const int tiles = (T_len * H + C::ROWS - 1) / C::ROWS;
+  int nst = (int)(144 * 1024 / C::STAGE_B);
+  if (nst > 4) nst = 4;
+  if (nst < 1) nst = 1;
+  const size_t lds = (size_t)nst * C::STAGE_B + 1024;
+  auto kern = prefill_attn_kernel<T, R, DR, NQ>;
+  allow_lds<prefill_attn_kernel<T, R, DR, NQ>>();
+  PrefillArgs args{qt, QR, (const char *)keys, kstride * C::ES, Cp, KR, O, B, T_len, H, s, tiles,
+                   nst, sl2};
   return launch_timed((const void *)kern, dim3(tiles * B), dim3(256), lds, stream, &args, ev0, ev1);
 }
 
@@ -364,11 +325,17 @@ hipError_t launch_prefill_attention(int dtype, int B, int T, int H, int r, int d
                                     hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const float sl2 = scale * kLog2e;
   if (dtype == 1) {
-    if (r == 256) return prefill_attn_t<bf16, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
-    return prefill_attn_t<bf16, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
+    if (r == 256)
+      return prefill_attn_t<bf16, 256, 32, 3>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O,
+                                              stream, ev0, ev1);
+    return prefill_attn_t<bf16, 512, 64, 1>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O,
+                                            stream, ev0, ev1);
   }
-  if (r == 256) return prefill_attn_t<float, 256, 32>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
-  return prefill_attn_t<float, 512, 64>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O, stream, ev0, ev1);
+  if (r == 256)
+    return prefill_attn_t<float, 256, 32, 2>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O,
+                                             stream, ev0, ev1);
+  return prefill_attn_t<float, 512, 64, 1>(B, T, H, s, sl2, qt, QR, keys, keys_stride, Cp, KR, O,
+                                           stream, ev0, ev1);
 }
 
 }  // namespace mtla

@@ -71,6 +71,17 @@ __device__ __forceinline__ void load8(f32x8 &v, const float *p) {
   v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// 4 consecutive elements (8- or 16-byte aligned) <-> fp32.
+__device__ __forceinline__ f32x4 load4f(const bf16 *p) {
+  const bf16x4 v = *(const bf16x4 *)p;
+  return (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 load4f(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ void store4f(bf16 *p, f32x4 v) {
+  *(bf16x4 *)p = (bf16x4){(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void store4f(float *p, f32x4 v) { *(f32x4 *)p = v; }
+
 template <typename T> __device__ __forceinline__ typename Frag<T>::type zero_frag() {
   typename Frag<T>::type v;
 #pragma unroll
@@ -86,7 +97,32 @@ __device__ __forceinline__ void sts16(void *p, u32x4 v) { *(u32x4 *)p = v; }
 
 __device__ __forceinline__ float sigmoidf(float g) { return 1.0f / (1.0f + expf(-g)); }
 
-__device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// Max / sum over the four lanes c, c+16, c+32, c+48 (the lane groups that
+// share an MFMA output column), with gfx950's cross-row swaps
+// v_permlane16_swap / v_permlane32_swap: VALU operations, no LDS round trip
+// (a shuffle through ds_bpermute waits on the LDS pipe every time).  Written
+// in asm to obtain both registers the swap writes; s_nop pads the VALU
+// hazards around them.
+__device__ __forceinline__ void perm_swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void perm_swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_g(float v) {
+  float a = v, b = v;
+  perm_swap16(a, b);
+  float c = fmaxf(a, b), d = c;
+  perm_swap32(c, d);
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float sum_g(float v) {
+  float a = v, b = v;
+  perm_swap16(a, b);
+  float c = a + b, d = c;
+  perm_swap32(c, d);
+  return c + d;
+}
 
 // ---- 16-row LDS tiles filled by direct global->LDS loads ------------------
 //
@@ -170,6 +206,46 @@ __device__ __forceinline__ void wait_lgkm0() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
+}
+
+// ---- reading MFMA operands from 16-row tiles --------------------------------
+
+// S operand: the 8 values of row `row`, k-step ks (32 values) that lane
+// group g feeds to the K=32 MFMA.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type s_frag(const char *tile, int row, int ks, int g) {
+  if constexpr (sizeof(T) == 2) {
+    return *(const bf16x8 *)(tile + tile_off(row, ks * 64 + g * 16));
+  } else {
+    const f32x4 x = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32));
+    const f32x4 y = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32 + 16));
+    return (f32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+
+// fp32 transposed operand C^T for channels ch0..ch0+15 of the tile's keys
+// 4g..4g+3: lane (g, j) receives channel ch0 + j of those four keys.
+__device__ __forceinline__ f32x4 v_frag_f32(const char *tile, int ch0, int g, int j) {
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + tile_off(4 * g + e, (ch0 + j) * 4));
+  return v;
+}
+
+// Wait until at most `after` stages issued after the current one are still
+// in flight (each wave issues LPW loads per stage; loads complete in order).
+template <int N> constexpr int capped() { return N < 63 ? N : 63; }
+template <int LPW> __device__ __forceinline__ void wait_stages(int after) {
+  switch (after) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<capped<LPW>()>(); break;
+    case 2: wait_vm<capped<2 * LPW>()>(); break;
+    case 3: wait_vm<capped<3 * LPW>()>(); break;
+    case 4: wait_vm<capped<4 * LPW>()>(); break;
+    case 5: wait_vm<capped<5 * LPW>()>(); break;
+    case 6: wait_vm<capped<6 * LPW>()>(); break;
+    default: wait_vm<capped<7 * LPW>()>(); break;
+  }
 }
 
 // ---- handing partial results between workgroups of one kernel -------------

@@ -68,44 +68,6 @@ template <typename T, int R, int DR, int NHB> struct DecCfg {
   static_assert(NHB * TPS == 4, "one (tile, head block) pair per wave");
 };
 
-// S operand: the 8 values of row `row`, k-step ks (32 values) that lane
-// group g feeds to the K=32 MFMA.
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type s_frag(const char *tile, int row, int ks, int g) {
-  if constexpr (sizeof(T) == 2) {
-    return *(const bf16x8 *)(tile + tile_off(row, ks * 64 + g * 16));
-  } else {
-    const f32x4 x = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32));
-    const f32x4 y = *(const f32x4 *)(tile + tile_off(row, ks * 128 + g * 32 + 16));
-    return (f32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  }
-}
-
-// fp32 transposed operand C^T for channels ch0..ch0+15 of the tile's keys
-// 4g..4g+3: lane (g, j) receives channel ch0 + j of those four keys.
-__device__ __forceinline__ f32x4 v_frag_f32(const char *tile, int ch0, int g, int j) {
-  f32x4 v;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + tile_off(4 * g + e, (ch0 + j) * 4));
-  return v;
-}
-
-// Wait until at most `after` stages issued after the current one are still
-// in flight (each wave issues LPW loads per stage; loads complete in order).
-template <int N> constexpr int capped() { return N < 63 ? N : 63; }
-template <int LPW> __device__ __forceinline__ void wait_stages(int after) {
-  switch (after) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<capped<LPW>()>(); break;
-    case 2: wait_vm<capped<2 * LPW>()>(); break;
-    case 3: wait_vm<capped<3 * LPW>()>(); break;
-    case 4: wait_vm<capped<4 * LPW>()>(); break;
-    case 5: wait_vm<capped<5 * LPW>()>(); break;
-    case 6: wait_vm<capped<6 * LPW>()>(); break;
-    default: wait_vm<capped<7 * LPW>()>(); break;
-  }
-}
-
 struct DecodeArgs {
   const int32_t *pos;
   char *cache;
@@ -265,8 +227,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       z[e] = (kb + 4 * g + e < end) ? (s0[e] + s1[e]) * a.sl2 : kNegInf;
       mx = fmaxf(mx, z[e]);
     }
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));   // -inf only for a tile wholly past the split
+    mx = max_g(mx);   // -inf only for a tile wholly past the split
     if (g == 0) smax[st_tile * C::HW + shead] = mx;
     wait_lgkm0();
     bar();
@@ -342,8 +303,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   }
 
   // Row sums: lane partials -> per head, over the waves of each head block.
-  float lt = lp + wave_xor(lp, 16);
-  lt += wave_xor(lt, 32);
+  const float lt = sum_g(lp);
   wait_lgkm0();
   bar();
   if (g == 0) smax[st_tile * C::HW + shead] = lt;
