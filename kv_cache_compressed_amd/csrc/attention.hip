@@ -7,24 +7,28 @@
 // causal mask and decoupled RoPE (the Y formula); [Fig2] = sciencestack.ai
 // page, Figure 2 (c).
 //
-// Attention kernel.  Query rows are (frame m, head h) pairs, row = m*H + h.
+// Attention kernels.  Query rows are (frame m, head h) pairs, row = m*H + h.
 // Row (m, h) sees the compact keys j < floor(m/s) -- the group-final states of
 // the groups that ended before m, i.e. the stride-aware mask's columns
 // n < m with n mod s = s-1 -- plus its own state C'_m, which seeds the online
-// softmax.  A workgroup owns 4 * 16 * NQ consecutive rows; each wave holds
-// 16 * NQ of them (NQ 16-row tiles) with their queries in registers and
-// their O^T (r x rows) accumulators in AGPRs.  The compact keys stream
-// through a ring of LDS stages (32 keys each) by direct global->LDS loads,
-// in the swizzled 16-row tile layout; the loop ends at the workgroup's causal
-// frontier, so masked tiles are never visited.  Per 16-key tile a wave:
-//   S^T (16 keys x 16 rows) = K . Q^T        K from LDS, A operand, K=32 MFMA
-//   online softmax in log2 units, reference max moved lazily (by > 2^8)
-//   O^T (r x 16 rows)     += C^T . P^T      C^T by ds_read_tr16_b64, K=16 MFMA
-// Each K fragment read from LDS feeds NQ MFMAs and each C^T fragment NQ more,
-// which keeps LDS traffic below what the matrix cores consume.
+// softmax.  The compact keys stream through a ring of LDS stages (32 keys
+// each) by direct global->LDS loads, in the swizzled 16-row tile layout; the
+// loop ends at the workgroup's causal frontier, so masked tiles are never
+// visited.  Two kernels:
+//   * prefill_attn_kernel (fp32 storage, and r = 512): a workgroup owns
+//     4 * 16 * NQ consecutive rows, each wave 16 * NQ of them with their
+//     queries and O^T (r x rows) accumulators in registers.  Per 16-key tile
+//     a wave computes S^T = K . Q^T (K from LDS, K=32 MFMA), the online
+//     softmax in log2 units (reference max moved lazily, by > 2^8), and
+//     O^T += C^T . P^T (C^T by transposing LDS reads, K=16 MFMA).  Each K
+//     fragment read from LDS feeds NQ products and each C^T fragment NQ more.
+//   * prefill_ws_kernel (bf16, r = 256): the warp-specialised form described
+//     above its definition.
 
 #include <float.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -296,19 +300,27 @@ hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void 
 
 // ---------------------------------------------------------------------------
 // Warp-specialised attention for bf16 latents with r = 256, d_hR = 32: eight
-// waves, two per SIMD.  Waves 0-3 ("score waves") own 48 rows each: they
-// hold the queries, compute S^T for the 32 keys of a stage, run the online
-// softmax and pass the bf16 probabilities P^T and the per-row rescale
-// factors to their partner through LDS.  Waves 4-7 ("value waves") hold the
-// O^T accumulators of the same rows and add C^T P^T over the stage's 32 keys
-// with K=32 products (gfx950's 16x16x32 bf16 MFMA runs at twice the rate of
-// the 16x16x16 form).  A score wave and its partner share a SIMD, so the
-// softmax arithmetic of one overlaps the matrix products of the other and
-// each hides the other's LDS latency; splitting the roles also splits the
-// register state (queries vs accumulators) so each wave fits in half the
-// SIMD's register file.  One workgroup barrier per stage orders the
-// handoff: at iteration k the score waves process stage k while the value
-// waves consume stage k-1.
+// waves, two per SIMD, over the same LDS ring of compact keys.
+//   Score waves 0-3 own 48 rows each (three 16-row tiles): they hold the
+//   queries, compute S^T for the 32 keys of a stage (K=32 MFMAs, each K^T
+//   fragment feeding three products), run the online softmax and pass the
+//   bf16 probabilities P^T, the per-row rescale factors and a per-wave
+//   rescale flag to the value waves through LDS.
+//   Value wave v holds O^T for all 192 rows of the workgroup and the channel
+//   quarter [64 v, 64 v + 64): each C^T fragment, fetched with gfx950's
+//   transposing LDS read (half the bandwidth of a 16-byte read), feeds twelve
+//   products, and the P^T fragments come with full-rate 16-byte reads.
+// Splitting the roles splits the register state (queries vs accumulators),
+// so each wave fits in half the SIMD's register file and a score wave and a
+// value wave share each SIMD: one's VALU work overlaps the other's matrix
+// products and each covers the other's LDS latency.  Two workgroup barriers
+// per stage order the handoff and split the stage into two phases: in phase
+// A the score waves run the products S^T of stage k (and tile 0's
+// exponentials, threaded between tile 1's products), in phase B the rest of
+// the softmax of stage k, while tile 0's K^T fragments of stage k+1 are
+// fetched; the value waves spread their products for stage k-1 over both
+// phases (half the row tiles each).  The 16x16x32 bf16 MFMA is used
+// throughout: gfx950 runs the 16x16x16 form at half its rate.
 // ---------------------------------------------------------------------------
 struct WsCfg {
   static constexpr int R = 256, DR = 32, RK = R + DR, RB = RK * 2, NSEG = RB / 64;
@@ -316,10 +328,14 @@ struct WsCfg {
   static constexpr int ROWS_W = 16 * NQ, ROWS = 4 * ROWS_W;
   static constexpr int SROWS = 32, TILE_B = 16 * RB, STAGE_B = 2 * TILE_B;
   static constexpr int NBLK = 2 * NSEG, LPW = (NBLK + 3) / 4;
-  static constexpr int P_B = 4 * NQ * 64 * 16;   // P slot: 4 waves x NQ fragments x 64 lanes x 16 B
-  static constexpr int A_B = 4 * ROWS_W * 4;     // rescale-factor slot (also the row sums)
-  static constexpr int EXTRA = 2 * P_B + 3 * A_B + 1024;
+  static constexpr int NRT = 4 * NQ;            // 16-row tiles per workgroup
+  static constexpr int NB = MT / 4;              // channel blocks per value wave
+  static constexpr int P_B = NRT * 64 * 16;      // P slot: row tiles x 64 lanes x 16 B
+  static constexpr int A_B = 16 * NRT * 4;       // per-row floats [lane row c][row tile]
+  static constexpr int F_B = 16;                 // rescale flags of the 4 score waves
+  static constexpr int EXTRA = 2 * P_B + 3 * A_B + 2 * F_B + 1024;
   static constexpr int MAX_NST = 6;
+  static_assert(KS == NSEG, "a K^T fragment row spans one 1 KB block per k-step");
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -355,9 +371,10 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
   const int nstage = (kmax + C::SROWS - 1) / C::SROWS;
 
   char *pbase = smem + nst * C::STAGE_B;
-  float *abase = (float *)(pbase + 2 * C::P_B);
-  float *lbuf = abase + 2 * (C::A_B / 4);
-  char *dummy = (char *)(lbuf + C::A_B / 4);
+  float *abase = (float *)(pbase + 2 * C::P_B);   // rescale factors, two slots
+  float *lbuf = abase + 2 * (C::A_B / 4);          // row sums
+  float *fbase = lbuf + C::A_B / 4;                // rescale flags, two slots
+  char *dummy = (char *)(fbase + 2 * (C::F_B / 4));
 
   if (wave < 4) {
     // ---------------- score wave ----------------
@@ -416,6 +433,18 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
     int last = pro - 1;
     if (nstage > 0) wait_stages<C::LPW>(last);
 
+    // K^T fragments of the stage about to be processed: row c of each tile,
+    // this lane group's 16-byte chunk of every k-step.  Tile 0's are read one
+    // phase ahead (during the previous stage's softmax) and tile 1's at the
+    // start of phase A, behind tile 0's products, so that phase A issues
+    // matrix products without waiting on LDS.
+    bf16x8 kf0[C::KS];
+    auto krow = [&](int k) { return smem + (k % nst) * C::STAGE_B + tile_off(c, g * 16); };
+    auto read_k0 = [&](int k) {
+      const char *row = krow(k);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kf0[ks] = *(const bf16x8 *)(row + ks * 1024);
+    };
     for (int k = 0; k <= nstage; ++k) {
       bar();
       // Stage k-2 has been consumed by both roles: refill its slot.
@@ -423,25 +452,69 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
         issue(k - 2 + nst);
         last = k - 2 + nst;
       }
-      if (k < nstage && k * C::SROWS < wlim) {
-        const char *sb = smem + (k % nst) * C::STAGE_B;
-        const int kb = k * C::SROWS;
-        f32x4 sc[2][C::NQ];
+      const bool act = k < nstage && k * C::SROWS < wlim;
+      const int kb = k * C::SROWS;
+      f32x4 sc[2][C::NQ];
+      // Online softmax in log2 units with a lazily moved reference max m
+      // per row: p = 2^(s sl2 - m) against the current m, and only when some
+      // p of the wave exceeds 2^8 (a row's maximum rose by more than 8) are
+      // the exact row maxima taken and m moved to those that did.  pr holds
+      // tile 0's p in [0, 4) and tile 1's in [4, 8).
+      float pr[C::NQ][8];
+      float pmax = 0.0f;
+      bool moved = false;
+      // Phase A: the products S^T of stage k, and tile 0's p while tile 1's
+      // products run (needing no row maximum, they only wait for tile 0's).
+      if (act) {
+        if (k == 0) read_k0(0);
+        bf16x8 kf1[C::KS];
+        const char *row1 = krow(k) + C::TILE_B;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const char *tile = sb + t * C::TILE_B;
-          bf16x8 kf[C::KS];
+        for (int ks = 0; ks < C::KS; ++ks) kf1[ks] = *(const bf16x8 *)(row1 + ks * 1024);
+        // Keep the nine reads ahead of tile 0's products (the compiler would
+        // otherwise spread them out, each behind a full wait).
+        asm volatile("" ::: "memory");
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks)
-            kf[ks] = *(const bf16x8 *)(tile + tile_off(c, ks * 64 + g * 16));
-#pragma unroll
-          for (int qi = 0; qi < C::NQ; ++qi) sc[t][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int qi = 0; qi < C::NQ; ++qi) sc[t][qi] = mma_k32(kf[ks], q[qi][ks], sc[t][qi]);
+        for (int qi = 0; qi < C::NQ; ++qi) {
+          sc[0][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          sc[1][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int qi = 0; qi < C::NQ; ++qi) sc[0][qi] = mma_k32(kf0[ks], q[qi][ks], sc[0][qi]);
+        // Tile 0's products first: nothing is scheduled across this point.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int qi = 0; qi < C::NQ; ++qi) sc[1][qi] = mma_k32(kf1[ks], q[qi][ks], sc[1][qi]);
+#pragma unroll
+        for (int qi = 0; qi < C::NQ; ++qi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pr[qi][e] = __builtin_amdgcn_exp2f(fmaf(sc[0][qi][e], a.sl2, -m[qi]));
+            pmax = fmaxf(pmax, pr[qi][e]);
+          }
+        // Tile 1's products with tile 0's exponentials threaded between them.
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      }
+      // Stage k+1 resident before the next barrier, so that it can be read
+      // during phase B.
+      if (k + 1 < nstage) wait_stages<C::LPW>(last - (k + 1));
+      bar();
+      // Phase B: softmax of stage k on the VALU while the value waves'
+      // products of stage k-1 occupy the matrix cores; tile 0's K^T
+      // fragments of stage k+1 are read meanwhile.
+      if (k + 1 < nstage && (k + 1) * C::SROWS < wlim) read_k0(k + 1);
+      if (act) {
         if (kb + C::SROWS > wmin) {
+          // Diagonal stage: mask the keys a row cannot see and redo tile 0.
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -449,123 +522,172 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (kb + 16 * t + 4 * g + e >= lim[qi]) sc[t][qi][e] = kNegInf;
+          pmax = 0.0f;
+#pragma unroll
+          for (int qi = 0; qi < C::NQ; ++qi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pr[qi][e] = __builtin_amdgcn_exp2f(fmaf(sc[0][qi][e], a.sl2, -m[qi]));
+              pmax = fmaxf(pmax, pr[qi][e]);
+            }
         }
-        // Online softmax in log2 units (sl2 > 0, so the max commutes with
-        // the scaling); the reference max moves only by steps > 2^8.
-        float mnew[C::NQ];
-        bool up_any = false;
 #pragma unroll
-        for (int qi = 0; qi < C::NQ; ++qi) {
-          float v = kNegInf;
+        for (int qi = 0; qi < C::NQ; ++qi)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v = fmaxf(v, sc[t][qi][e]);
-          const float mx = max_g(v) * a.sl2;
-          const bool up = mx > m[qi] + 8.0f;
-          mnew[qi] = up ? mx : m[qi];
-          up_any |= up;
-        }
+          for (int e = 0; e < 4; ++e) {
+            pr[qi][4 + e] = __builtin_amdgcn_exp2f(fmaf(sc[1][qi][e], a.sl2, -m[qi]));
+            pmax = fmaxf(pmax, pr[qi][4 + e]);
+          }
         float alpha[C::NQ];
 #pragma unroll
         for (int qi = 0; qi < C::NQ; ++qi) alpha[qi] = 1.0f;
-        if (__builtin_amdgcn_ballot_w64(up_any)) {
+        moved = __builtin_amdgcn_ballot_w64(!(pmax <= 256.0f)) != 0;
+        if (moved) {
 #pragma unroll
           for (int qi = 0; qi < C::NQ; ++qi) {
-            alpha[qi] = __builtin_amdgcn_exp2f(m[qi] - mnew[qi]);
-            l[qi] *= alpha[qi];
-            m[qi] = mnew[qi];
+            float v = kNegInf;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v = fmaxf(v, sc[t][qi][e]);
+            // sl2 > 0, so the maximum commutes with the scaling.
+            const float mx = max_g(v) * a.sl2;
+            if (mx > m[qi] + 8.0f) {
+              alpha[qi] = __builtin_amdgcn_exp2f(m[qi] - mx);
+              l[qi] *= alpha[qi];
+              m[qi] = mx;
+#pragma unroll
+              for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  pr[qi][4 * t + e] = __builtin_amdgcn_exp2f(fmaf(sc[t][qi][e], a.sl2, -m[qi]));
+            }
           }
         }
         char *pb = pbase + (k & 1) * C::P_B + w * (C::NQ * 1024);
-        float *ab = abase + (k & 1) * (C::A_B / 4) + w * C::ROWS_W;
+        float *ab = abase + (k & 1) * (C::A_B / 4) + c * C::NRT + C::NQ * w;
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
         for (int qi = 0; qi < C::NQ; ++qi) {
           // P^T fragment: k index 8g+e holds key 4g+e of tile 0 (e < 4) and
           // key 4g+e-4 of tile 1 (e >= 4) -- the same order in which the
-          // value wave assembles C^T from its two transposing reads.
+          // value wave assembles C^T from its two transposing reads.  The
+          // row sum accumulates the bf16 values the products use.
           bf16x8 pf;
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+          for (int e = 0; e < 8; ++e) pf[e] = (bf16)pr[qi][e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][qi][e], a.sl2, -m[qi]));
-              l[qi] += p;
-              pf[4 * t + e] = (bf16)p;
-            }
+          for (int e = 0; e < 8; e += 2)
+            l[qi] = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[e], pf[e + 1]}, ones, l[qi], false);
           *(bf16x8 *)(pb + qi * 1024 + lane * 16) = pf;
-          if (g == 0) ab[qi * 16 + c] = alpha[qi];
+          if (g == 0) ab[qi] = alpha[qi];
         }
       }
-      // Stage k+1 resident and this wave's P / alpha written before the
-      // next barrier.
-      if (k + 1 < nstage) wait_stages<C::LPW>(last - (k + 1));
+      // Whether this wave moved its reference maxima (the value waves then
+      // rescale its rows); a wave with no keys left in this stage writes 0.
+      if (k < nstage && lane == 0) fbase[(k & 1) * 4 + w] = moved ? 1.0f : 0.0f;
+      // This wave's P / alpha written before the next barrier.
       wait_lgkm0();
     }
 #pragma unroll
     for (int qi = 0; qi < C::NQ; ++qi) {
       const float lt = sum_g(l[qi]);
-      if (g == 0) lbuf[w * C::ROWS_W + qi * 16 + c] = lt;
+      if (g == 0) lbuf[c * C::NRT + C::NQ * w + qi] = lt;
     }
     wait_lgkm0();
     bar();
   } else {
     // ---------------- value wave ----------------
-    f32x4 o[C::NQ][C::MT];
+    // Value wave v holds O^T for all NRT row tiles of the workgroup and the
+    // channel quarter [64 v, 64 v + 64) (NB blocks of 16): each C^T fragment
+    // it reads with the half-rate transposing reads then feeds NRT products,
+    // while the P^T fragments come with full-rate 16-byte reads.
+    const int v = w;
+    f32x4 o[C::NRT][C::NB];
+    int wl[4];   // key limit of each score wave's rows
 #pragma unroll
-    for (int qi = 0; qi < C::NQ; ++qi) {
-      const int row = rw + 16 * qi + c;
+    for (int u = 0; u < 4; ++u) {
+      const int r0 = qtile * C::ROWS + u * C::ROWS_W, r1 = min(r0 + C::ROWS_W, nrows) - 1;
+      wl[u] = r1 >= r0 ? (r1 / H) / s : 0;
+    }
+#pragma unroll
+    for (int rt = 0; rt < C::NRT; ++rt) {
+      const int row = qtile * C::ROWS + 16 * rt + c;
       const int rr = row < nrows ? row : 0;
       const size_t coff = (size_t)b * Tn + rr / H;
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
-        o[qi][mt] = load4f((const bf16 *)a.Cp + coff * C::R + 16 * mt + 4 * g);
+      for (int mb = 0; mb < C::NB; ++mb)
+        o[rt][mb] = load4f((const bf16 *)a.Cp + coff * C::R + 64 * v + 16 * mb + 4 * g);
     }
+    // O^T += C^T P^T for row tiles [r0, r1) of stage kk.
+    auto pv = [&](int kk, const bf16x8 (&vf)[C::NB], auto r0c, auto r1c) {
+      constexpr int r0 = decltype(r0c)::value, r1 = decltype(r1c)::value;
+      const char *pb = pbase + (kk & 1) * C::P_B;
+#pragma unroll
+      for (int rt = r0; rt < r1; ++rt) {
+        if (kk * C::SROWS >= wl[rt / C::NQ]) continue;   // that score wave had no keys
+        const bf16x8 pf = *(const bf16x8 *)(pb + rt * 1024 + lane * 16);
+#pragma unroll
+        for (int mb = 0; mb < C::NB; ++mb) o[rt][mb] = mma_k32(vf[mb], pf, o[rt][mb]);
+      }
+    };
+    using Half = std::integral_constant<int, C::NRT / 2>;
+    using Zero = std::integral_constant<int, 0>;
+    using Full = std::integral_constant<int, C::NRT>;
     for (int k = 0; k <= nstage; ++k) {
       bar();
       const int kk = k - 1;
-      if (kk >= 0 && kk * C::SROWS < wlim) {
+      const bool act = kk >= 0;
+      bf16x8 vf[C::NB];
+      // Phase A: rescale if a score wave moved its maxima, read this
+      // quarter's C^T fragments of stage k-1 and do the first half of the
+      // row tiles (alongside the score waves' products).
+      if (act) {
+        const f32x4 fl = *(const f32x4 *)(fbase + (kk & 1) * 4);
+        if (fl[0] + fl[1] + fl[2] + fl[3] != 0.0f) {
+          const float *ab = abase + (kk & 1) * (C::A_B / 4) + c * C::NRT;
+          float al[C::NRT];
+#pragma unroll
+          for (int i = 0; i < C::NRT; i += 4) {
+            const f32x4 x = *(const f32x4 *)(ab + i);
+            al[i] = x[0]; al[i + 1] = x[1]; al[i + 2] = x[2]; al[i + 3] = x[3];
+          }
+#pragma unroll
+          for (int rt = 0; rt < C::NRT; ++rt) {
+            // Rows of a wave without a flag keep their factor of 1.
+            const float f = fl[rt / C::NQ] != 0.0f ? al[rt] : 1.0f;
+#pragma unroll
+            for (int mb = 0; mb < C::NB; ++mb) o[rt][mb] *= f;
+          }
+        }
         const char *sb = smem + (kk % nst) * C::STAGE_B;
-        const char *pb = pbase + (kk & 1) * C::P_B + w * (C::NQ * 1024);
-        const float *ab = abase + (kk & 1) * (C::A_B / 4) + w * C::ROWS_W;
-        float al[C::NQ];
-        bool resc = false;
 #pragma unroll
-        for (int qi = 0; qi < C::NQ; ++qi) {
-          al[qi] = ab[qi * 16 + c];
-          resc |= al[qi] != 1.0f;
-        }
-        if (__builtin_amdgcn_ballot_w64(resc)) {
-#pragma unroll
-          for (int qi = 0; qi < C::NQ; ++qi)
-#pragma unroll
-            for (int mt = 0; mt < C::MT; ++mt) o[qi][mt] *= al[qi];
-        }
-        bf16x8 pf[C::NQ];
-#pragma unroll
-        for (int qi = 0; qi < C::NQ; ++qi) pf[qi] = *(const bf16x8 *)(pb + qi * 1024 + lane * 16);
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) {
-          // Lane (g, c) addresses row 4g + c/4, channels 16mt + 4(c%4)..+3;
-          // the transposing read hands it channel 16mt + c of keys 4g..4g+3.
-          const char *p0 = sb + tile_off(4 * g + (c >> 2), (16 * mt + 4 * (c & 3)) * 2);
+        for (int mb = 0; mb < C::NB; ++mb) {
+          // Lane (g, c) addresses row 4g + c/4, channels 16m + 4(c%4)..+3 of
+          // block m; the transposing read hands it channel 16m + c of keys
+          // 4g..4g+3 (tile 0, low half) and of tile 1 (high half).
+          const int m = 4 * v + mb;
+          const char *p0 = sb + tile_off(4 * g + (c >> 2), (16 * m + 4 * (c & 3)) * 2);
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
           const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + C::TILE_B));
-          const bf16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qi = 0; qi < C::NQ; ++qi) o[qi][mt] = mma_k32(v, pf[qi], o[qi][mt]);
+          vf[mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+        pv(kk, vf, Zero(), Half());
       }
+      bar();
+      // Phase B: the second half (alongside the score waves' softmax).
+      if (act) pv(kk, vf, Half(), Full());
     }
     bar();
+    const float *lb = lbuf + c * C::NRT;
 #pragma unroll
-    for (int qi = 0; qi < C::NQ; ++qi) {
-      const int row = rw + 16 * qi + c;
+    for (int rt = 0; rt < C::NRT; ++rt) {
+      const int row = qtile * C::ROWS + 16 * rt + c;
       if (row < nrows) {
-        const float inv = 1.0f / lbuf[w * C::ROWS_W + qi * 16 + c];
-        bf16 *dst = (bf16 *)a.O + ((size_t)b * nrows + row) * C::R + 4 * g;
+        const float inv = 1.0f / lb[rt];
+        bf16 *dst = (bf16 *)a.O + ((size_t)b * nrows + row) * C::R + 64 * v + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) store4f(dst + 16 * mt, o[qi][mt] * inv);
+        for (int mb = 0; mb < C::NB; ++mb) store4f(dst + 16 * mb, o[rt][mb] * inv);
       }
     }
   }
