@@ -44,6 +44,14 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc")
+# Sources that define each timed kernel: a counter summary under profiles/
+# applies only while these files are unchanged.
+KERNEL_SOURCES = {
+    "decode_attn_kernel": ("decode.hip", "common.h", "kernels.h"),
+    "prefill_ws_kernel": ("attention.hip", "common.h", "kernels.h"),
+}
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "decode tokens/s + achieved HBM GB/s (compressed cache); prefill TFLOP/s, 1 GPU"
 
@@ -84,6 +92,49 @@ class HipEvents:
 
     def destroy(self, e):
         self.lib.hipEventDestroy(e)
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the counter summary
+    profiles/<workload>_traffic.md (rocprofv3 FETCH_SIZE and WRITE_SIZE,
+    scaled by the factor a plain copy of known size gave in the same runs),
+    or None when there is no summary or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_record: "):
+                rec = json.loads(line[len("traffic_record: "):])
+    if not rec or rec.get("kernel") != kernel or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec
+
+
+def calib_copy(mib: int):
+    """A plain elementwise pass of known size for counter calibration: reads
+    `mib` MiB and writes `mib` MiB (bf16 negation into a second buffer, both
+    larger than the 256 MB Infinity Cache)."""
+    import torch
+    n = (mib << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def _decode_setup(cfg: int, seed_pos=None):
@@ -279,6 +330,9 @@ def main():
     ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
                                        "llm_decode_b128_ctx32768", "prefill_b16_t4096"],
                     help="time one workload alone and print its record (for profiling runs)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise pass reading and writing MIB MiB each "
+                         "(the reference for scaling memory counters in profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the MTLA hot path here has no multi-GPU path "
@@ -290,6 +344,8 @@ def main():
         sys.exit(1)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
+    if args.calib_copy:
+        calib_copy(args.calib_copy)
     if args.only:
         cfg = {"decode_b32_ctx2048": 2, "ragged_decode_b64_s4": 3,
                "llm_decode_b128_ctx32768": 5, "prefill_b16_t4096": 4}[args.only]
@@ -323,6 +379,12 @@ def main():
         log("cpu baseline ...")
         cpu = cpu_baseline(args.cpu_seconds)
         cpu["value"] = round(cpu["value"], 2)
+    tr = measured_traffic("decode_b32_ctx2048", "decode_attn_kernel")
+    traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None
+    ptr = measured_traffic("prefill_b16_t4096", "prefill_ws_kernel")
+    if ptr:
+        extra["prefill_b16_t4096"]["attn_hbm_traffic_bytes"] = round(
+            ptr["fetch_bytes_per_launch"] + ptr["write_bytes_per_launch"])
     out = {
         "metric": METRIC,
         "value": round(head["tokens_per_s"], 1),
@@ -341,7 +403,7 @@ def main():
                    "cache_replicas": head["replicas"]},
         "roofline": {"bound": "hbm", "kernel": "decode_attn_kernel",
                      "achieved": round(head["attn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": head["cache_bytes"],
                      "avg_kernel_us": round(head["attn_ms"] * 1e3, 3)},
         "cpu_baseline": cpu,
