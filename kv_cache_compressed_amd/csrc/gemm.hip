@@ -58,7 +58,21 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+  // L2.  When the tile count allows, XCD x takes a contiguous run of tiles in
+  // row-major order, so the column tiles that share one A row block run at
+  // about the same time on one L2 instead of fetching it once per XCD.
+  int tm = blockIdx.y, tn = blockIdx.x;
+  {
+    const int nT = gridDim.x * gridDim.y;
+    if (nT % 8 == 0) {
+      const int id = blockIdx.y * gridDim.x + blockIdx.x;
+      const int t = (id % 8) * (nT / 8) + id / 8;
+      tm = t / gridDim.x;
+      tn = t % gridDim.x;
+    }
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const T *brow[BLD];
 #pragma unroll
