@@ -122,9 +122,15 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       q[ks] = zero_frag<T>();
     }
   }
-  float mc[C::NU], mg[C::NU], mb[C::NU], mp[C::NU], mkr = 0.0f;
+  // b_hc and K^R stay in the storage type until used, so that no wait for
+  // these loads (and for every load issued before them) precedes the stream.
+  float mc[C::NU], mg[C::NU], mp[C::NU];
+  T mb[C::NU], mkr = from_f32<T>(0.0f);
 #pragma unroll
-  for (int i = 0; i < C::NU; ++i) mc[i] = mg[i] = mb[i] = mp[i] = 0.0f;
+  for (int i = 0; i < C::NU; ++i) {
+    mc[i] = mg[i] = mp[i] = 0.0f;
+    mb[i] = from_f32<T>(0.0f);
+  }
   if (owner) {
 #pragma unroll
     for (int i = 0; i < C::NU; ++i) {
@@ -132,11 +138,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       if (ch < R) {
         mc[i] = a.cg[(size_t)b * 2 * R + ch];
         mg[i] = a.cg[(size_t)b * 2 * R + R + ch];
-        mb[i] = to_f32(((const T *)a.b_hc)[ch]);
+        mb[i] = ((const T *)a.b_hc)[ch];
         mp[i] = a.gate_pos[(size_t)jn * R + ch];
       }
     }
-    if (tid < DR) mkr = to_f32(((const T *)a.KR)[(size_t)b * DR + tid]);
+    if (tid < DR) mkr = ((const T *)a.KR)[(size_t)b * DR + tid];
   }
   asm volatile("" ::: "memory");
 
@@ -195,14 +201,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
           const int ch = tid + 256 * i;
           if (ch < R) {
             T *lpnt = (T *)(trow + tile_off(rr & 15, ch * C::ES));
-            const float u = sigmoidf((mg[i] + mb[i]) * mp[i]) * mc[i];
+            const float u = sigmoidf((mg[i] + to_f32(mb[i])) * mp[i]) * mc[i];
             const T v = from_f32<T>(open ? u : to_f32(*lpnt) + u);
             *lpnt = v;
             grow[ch] = v;
           }
         }
         if (tid < DR) {
-          const T v = from_f32<T>(mkr);
+          const T v = mkr;
           *(T *)(trow + tile_off(rr & 15, (R + tid) * C::ES)) = v;
           grow[R + tid] = v;
         }
@@ -341,49 +347,56 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   if (ns == 1) return;
 
   // The last split of this sequence to finish merges all of them (log-sum-
-  // exp in split order: deterministic).  Four 4-channel chunks by four splits
-  // per batch keep 48 loads in flight per thread.
+  // exp in split order: deterministic).  A thread takes two 4-channel chunks
+  // at a time and loads up to eight splits' partials of both in one batch,
+  // so a merge of up to eight splits waits for one round trip.
   int *last = (int *)(pbuf + C::P_B);
   __syncthreads();   // this workgroup's partial stores have completed
   if (tid == 0) *last = ctr_add(&a.counters[b], 1) == ns - 1;
   __syncthreads();
   if (!*last) return;
   constexpr int QC = R / 4;   // 4-channel chunks per head
+  constexpr int UB = 2, SB = 8;
   const int nch = H * QC;
   const size_t base = (size_t)b * a.splits * H;
-  for (int c0 = tid; c0 < nch; c0 += 4 * 256) {
-    float M[4], L[4];
-    f32x4 acc[4];
+  for (int c0 = tid; c0 < nch; c0 += UB * 256) {
+    float M[UB], L[UB];
+    f32x4 acc[UB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UB; ++u) {
       M[u] = kNegInf;
       L[u] = 0.0f;
       acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    for (int k0 = 0; k0 < ns; k0 += 4) {
-      float pm[4][4], pl[4][4];
-      f32x4 po[4][4];
+    for (int k0 = 0; k0 < ns; k0 += SB) {
+      float pm[UB][SB], pl[UB][SB];
+      f32x4 po[UB][SB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < UB; ++u) {
         const int ci = min(c0 + 256 * u, nch - 1), h = ci / QC, ch = (ci % QC) * 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const size_t i = base + (size_t)min(k0 + j, ns - 1) * H + h;
-          pm[u][j] = ld_coh1(rml, (uint32_t)(i * 8));
-          pl[u][j] = ld_coh1(rml, (uint32_t)(i * 8 + 4));
-          po[u][j] = ld_coh4(ro, (uint32_t)((i * R + ch) * 4));
+        for (int j = 0; j < SB; ++j) {
+          pm[u][j] = kNegInf;
+          pl[u][j] = 0.0f;
+          po[u][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          if (k0 + j < ns) {
+            const size_t i = base + (size_t)(k0 + j) * H + h;
+            pm[u][j] = ld_coh1(rml, (uint32_t)(i * 8));
+            pl[u][j] = ld_coh1(rml, (uint32_t)(i * 8 + 4));
+            po[u][j] = ld_coh4(ro, (uint32_t)((i * R + ch) * 4));
+          }
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < UB; ++u) {
         float Mn = M[u];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Mn = fmaxf(Mn, pm[u][j]);
+        for (int j = 0; j < SB; ++j) Mn = fmaxf(Mn, pm[u][j]);
         const float sc = __builtin_amdgcn_exp2f(M[u] - Mn);
         L[u] *= sc;
         acc[u] *= sc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < SB; ++j) {
           const float w = (k0 + j < ns) ? __builtin_amdgcn_exp2f(pm[u][j] - Mn) : 0.0f;
           L[u] += w * pl[u][j];
           acc[u] += w * po[u][j];
@@ -392,7 +405,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < UB; ++u) {
       const int ci = c0 + 256 * u;
       if (ci >= nch) continue;
       const int h = ci / QC, ch = (ci % QC) * 4;
