@@ -40,9 +40,19 @@ struct BSeg {
   }
 };
 
+// K split over blockIdx.z: split z covers k in [z kchunk, (z+1) kchunk).
+// With more than one split the fp32 partial tiles go to `part` (coherent
+// stores) and the last split of a tile to finish (counter per tile, zero on
+// entry and again on exit) adds them in split order and applies the epilogue.
+struct KSplit {
+  int kchunk;
+  float *part;
+  int *counters;
+};
+
 template <typename T, int BM, int BN, int WGM, int WGN, class Epi>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, int lda, BSeg bs,
-                                                      int M, int N, int K, Epi epi) {
+                                                      int M, int N, int K, Epi epi, KSplit ksp) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
@@ -119,12 +129,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
+  const int nsplit = gridDim.z;
+  const int kb = blockIdx.z * ksp.kchunk, ke = min(K, kb + ksp.kchunk);
+  fetch(kb);
   stash(0);
   __syncthreads();
   int buf = 0;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool more = k0 + BK < K;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    const bool more = k0 + BK < ke;
     if (more) fetch(k0 + BK);
     const char *base = smem[buf];
     typename Frag<T>::type fa[TM], fb[TN];
@@ -143,17 +155,53 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const T *__restrict__ A, i
     buf ^= 1;
   }
 
+  auto apply = [&](int i, int j, f32x4 v) {
+    const int n = n0 + wn0 + 16 * j + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = m0 + wm0 + 16 * i + 4 * g + e;
+      if (m < M && n < N) epi(m, n, v[e]);
+    }
+  };
+  if (nsplit == 1) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) apply(i, j, acc[i][j]);
+    return;
+  }
+  // Partials in fragment order: [split][tile][wave][i][j][lane] x 16 bytes.
+  const int ntile = gridDim.x * gridDim.y, tile = tm * gridDim.x + tn;
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(ksp.part, (uint32_t)((size_t)nsplit * ntile * BM * BN * 4));
+  auto poff = [&](int sp, int i, int j) {
+    return (uint32_t)((((((size_t)sp * ntile + tile) * 4 + wave) * TM + i) * TN + j) * 64 + lane) * 16;
+  };
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) st_coh4(rp, poff(blockIdx.z, i, j), acc[i][j]);
+  __shared__ int last;
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (tid == 0) last = ctr_add(&ksp.counters[tile], 1) == nsplit - 1;
+  __syncthreads();
+  if (!last) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + 16 * j + c;
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        f32x4 pv[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm0 + 16 * i + 4 * g + e;
-        if (m < M && n < N) epi(m, n, acc[i][j][e]);
+        for (int u = 0; u < 8; ++u) pv[u] = ld_coh4(rp, poff(min(s0 + u, nsplit - 1), i, j));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < nsplit) v += pv[u];
       }
+      apply(i, j, v);
     }
+  if (tid == 0) __hip_atomic_store(&ksp.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- skinny products (rows <= 128) -------------------------------------------
@@ -389,15 +437,48 @@ hipError_t run_gemm(const T *A, int lda, const BSeg &bs, int M, int N, int K, Ep
     // fp32 tiles of 128 x 128 would need more than 64 KB of static LDS.
     dim3 grid((N + 63) / 64, (M + 127) / 128);
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 64, 4, 1, Epi>), grid, dim3(256), 0, stream, A, lda,
-                       bs, M, N, K, epi);
+                       bs, M, N, K, epi, KSplit{K, nullptr, nullptr});
   } else {
     dim3 grid((N + 127) / 128, (M + 127) / 128);
     hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 128, 2, 2, Epi>), grid, dim3(256), 0, stream, A,
-                       lda, bs, M, N, K, epi);
+                       lda, bs, M, N, K, epi, KSplit{K, nullptr, nullptr});
   }
   return hipGetLastError();
 }
 
+
+// Tiled product of at most 128 rows with K split over about 256 workgroups
+// (BN = 128 for bf16, 64 for fp32); `part` holds tiled_splitk_part_bytes.
+struct TiledSplit {
+  int bn, tiles, splits, kchunk;
+};
+TiledSplit tiled_splitk_plan(int esz, int N, int K) {
+  TiledSplit t;
+  t.bn = esz == 2 ? 128 : 64;
+  t.tiles = (N + t.bn - 1) / t.bn;
+  int sp = 256 / t.tiles;
+  if (sp > 8) sp = 8;
+  if (sp > K / 256) sp = K / 256;   // at least 8 k-steps per split
+  if (sp < 1) sp = 1;
+  t.kchunk = ((K + sp - 1) / sp + BK - 1) / BK * BK;
+  t.splits = (K + t.kchunk - 1) / t.kchunk;
+  return t;
+}
+
+template <typename T, class Epi>
+hipError_t run_gemm_splitk(const T *A, int lda, const BSeg &bs, int M, int N, int K, float *part,
+                           int *counters, Epi epi, hipStream_t stream) {
+  const TiledSplit t = tiled_splitk_plan((int)sizeof(T), N, K);
+  const KSplit ksp{t.kchunk, part, counters};
+  dim3 grid(t.tiles, 1, t.splits);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 128, 2, 2, Epi>), grid, dim3(256), 0, stream, A,
+                       lda, bs, M, N, K, epi, ksp);
+  else
+    hipLaunchKernelGGL((gemm_nt_kernel<T, 128, 64, 4, 1, Epi>), grid, dim3(256), 0, stream, A, lda,
+                       bs, M, N, K, epi, ksp);
+  return hipGetLastError();
+}
 
 template <typename T, int BM, int NT, class Epi>
 hipError_t skinny_t(SkinnyArgs a, int strips, Epi epi, hipStream_t stream) {
@@ -456,7 +537,12 @@ hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_
   EpiProj<T> epi{cg, (T *)qt, 2 * r, HR};
   BSeg bs{W_dkv, W_gate, A, r, 2 * r, d};
   const int N = 2 * r + (A ? HR : 0);
-  if (M <= 128)
+  // Up to 64 rows the strip-per-workgroup product streams the weights with
+  // little else; beyond that, re-reading all of X for every narrow strip and
+  // the per-tile fragment reads dominate (at 128 rows, d = 4096: 0.4 TB/s of
+  // weights against 2.0 TB/s for the tiled product), so the tiled kernel
+  // takes over.
+  if (M <= 64)
     return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, nullptr, zero, nzero, epi,
                          stream);
   if (zero && nzero > 0) {
@@ -472,6 +558,16 @@ hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_
 int out_proj_strips(int M, int N) {
   if (M > 128) return 0;
   return M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
+}
+
+size_t out_proj_part_bytes(int esz, int M, int N, int K) {
+  if (M > 128) return 0;
+  const int mpad = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+  if (M > 64) {
+    const TiledSplit t = tiled_splitk_plan(esz, N, K);
+    return t.splits > 1 ? (size_t)t.splits * t.tiles * 128 * t.bn * 4 : 0;
+  }
+  return (size_t)out_proj_splits(M, N, K) * mpad * (N + 32) * 4;
 }
 
 int out_proj_splits(int M, int N, int K) {
@@ -497,8 +593,18 @@ hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, 
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
                            float *part, int *counters, hipStream_t stream) {
   if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);
-  const int ks = (part && counters) ? out_proj_splits(M, N, K) : 1;
   BSeg bs{Bvo, Bvo, Bvo, N, N, K};
+  if (M > 64 && part && counters) {
+    // 65..128 rows: the tiled product (fragments reused across each wave's
+    // block of tiles) with K split, instead of narrow strips that each read
+    // all of O.
+    if (dtype == 1)
+      return run_gemm_splitk<bf16>((const bf16 *)O, K, bs, M, N, K, part, counters,
+                                   EpiStore<bf16>{(bf16 *)Y, N}, stream);
+    return run_gemm_splitk<float>((const float *)O, K, bs, M, N, K, part, counters,
+                                  EpiStore<float>{(float *)Y, N}, stream);
+  }
+  const int ks = (part && counters) ? out_proj_splits(M, N, K) : 1;
   if (dtype == 1)
     return run_skinny<bf16>((const bf16 *)O, K, bs, M, N, K, ks, part, counters, nullptr, 0,
                             EpiStore<bf16>{(bf16 *)Y, N}, stream);

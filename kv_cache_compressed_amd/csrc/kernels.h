@@ -33,13 +33,15 @@ hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv
                        int *zero, int nzero, hipStream_t stream);
 
 // Y [M, N] = O [M, K] Bvo [N, K]^T.  For M <= 128 with `part` and `counters`
-// given, K is split over workgroups (out_proj_splits) with fp32 partials in
-// `part` (out_proj_splits * M_pad * N floats at most, M_pad = M rounded up
-// to the row tile of 16, 32, 64 or 128) and one counter per column strip
-// (out_proj_strips), zero on entry (zero again on exit).
+// given, K is split over workgroups with fp32 partials in `part`
+// (out_proj_part_bytes) and counters (at most out_proj_strips of them), zero
+// on entry and zero again on exit: up to 64 rows as narrow column strips
+// (out_proj_splits splits), 65..128 rows as 128-row tiles.
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
                            float *part, int *counters, hipStream_t stream);
 int out_proj_splits(int M, int N, int K);
+// Bytes of fp32 partials launch_out_proj needs in `part` (esz: storage bytes).
+size_t out_proj_part_bytes(int esz, int M, int N, int K);
 int out_proj_strips(int M, int N);
 
 // ---- incremental decoding ---------------------------------------------------

@@ -110,14 +110,12 @@ DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
   w.qt = w.part_o = w.part_ml = w.o = w.ypart = w.counters = 0;
   w.ncount = 0;
   if (plan) {
-    const int ks = mtla::out_proj_splits(B, d->d, (int)HR);
-    const size_t mpad = B <= 16 ? 16 : B <= 32 ? 32 : B <= 64 ? 64 : 128;
     w.ncount = B + mtla::out_proj_strips(B, d->d);
     w.qt = off;       off += align_up(B * HR * e);
     w.part_o = off;   off += align_up((size_t)B * plan->splits * HR * 4);
     w.part_ml = off;  off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
     w.o = off;        off += align_up(B * HR * e);
-    w.ypart = off;    off += align_up((size_t)ks * mpad * (d->d + 32) * 4);
+    w.ypart = off;    off += align_up(mtla::out_proj_part_bytes((int)e, B, d->d, (int)HR));
     w.counters = off; off += align_up((size_t)w.ncount * 4);
   }
   w.total = off;

@@ -121,6 +121,19 @@ def test_decode_batch_above_128():
     _decode_case(dims, pos, "bf16", 7300, check=[0, 1, 67, 135])
 
 
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
+def test_decode_batch_between_64_and_128(storage):
+    """65..128 sequences: both projections take the tiled path -- the output
+    projection with K split over workgroups and combined by the last split of
+    each tile -- with the split counters cleared by their own kernel."""
+    needs_gpu()
+    dims = Dims(d=256, H=8, d_h=64, r=256, d_hR=32, s=3)
+    rng = np.random.default_rng(7350)
+    pos = rng.integers(0, 900, size=100)
+    say("decode B=100", storage)
+    _decode_case(dims, pos, storage, 7350, check=[0, 1, 50, 99])
+
+
 def test_decode_wide_latent_fp32():
     needs_gpu()
     dims = Dims(d=256, H=4, d_h=128, r=512, d_hR=64, s=2)
