@@ -392,6 +392,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
       }
     };
 
+    // The key stream goes out first, so that its round trip overlaps that of
+    // the queries (waiting for the queries then waits for the first stages
+    // too -- loads complete in order -- which the loop needs next anyway).
+    const int pro = min(nst, nstage);
+    for (int k = 0; k < pro; ++k) issue(k);
+
     bf16x8 q[C::NQ][C::KS];
     float m[C::NQ], l[C::NQ];
     int lim[C::NQ];
@@ -428,8 +434,6 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
 
     // Keys below wmin are visible to every row of the wave: no mask needed.
     const int wmin = rw < nrows ? ((rw / H) / s) : 0;
-    const int pro = min(nst, nstage);
-    for (int k = 0; k < pro; ++k) issue(k);
     int last = pro - 1;
     if (nstage > 0) wait_stages<C::LPW>(last);
 
