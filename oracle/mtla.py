@@ -274,6 +274,22 @@ def decode_sequence(X, QR, KR, W, s, scale, max_slots=None):
     return dict(Y=np.stack(Y), O=np.stack(O), cache_lat=lat[:n].copy(), cache_rope=rk[:n].copy())
 
 
+def merge_chunk(lat, rk, t0, Xc, KRc, W, s):
+    """Merge-append of L consecutive frames t0 .. t0+L-1 (``Xc`` [L, d],
+    ``KRc`` [L, d_hR]) into the cache in place: the incremental merge of
+    [Fig2] (a), one frame after the other.  A chunk that starts inside a group
+    (t0 mod s != 0) therefore continues that group's live temporary slot
+    instead of opening a new one, and each slot it touches ends holding the
+    newest state of its group and the RoPE key of the newest frame merged
+    into it.  Returns C' [L, r]: row i is the state of frame t0+i's slot right
+    after that frame was merged (the intermediate state of [Fig2] (c))."""
+    Cp = np.empty((Xc.shape[0], lat.shape[1]), dtype=lat.dtype)
+    for i in range(Xc.shape[0]):
+        j = merge_append(lat, rk, t0 + i, Xc[i], KRc[i], W, s)
+        Cp[i] = lat[j]
+    return Cp
+
+
 # ---------------------------------------------------------------------------
 # reference forms used only to pin the ones above
 # ---------------------------------------------------------------------------

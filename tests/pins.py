@@ -376,10 +376,73 @@ def pin_predownsampling_differs():
             assert e > 1e-3, (t, e)
 
 
+# ---------------------------------------------------------------------------
+# chunked (multi-frame) merge-append
+# ---------------------------------------------------------------------------
+
+
+def pin_chunked_append_equals_prefill():
+    """Merging a sequence chunk by chunk -- boundaries inside groups as well
+    as on them, empty chunks included -- leaves exactly the cache of the
+    parallel form, untouched rows stay untouched, and the chunks' states
+    concatenate to the parallel form's C' (bit for bit: both add the same
+    per-frame updates in the same order)."""
+    rng = np.random.default_rng(1101)
+    for s, T in ((1, 9), (2, 13), (3, 17), (4, 18), (5, 7)):
+        dims = Dims(**{**TINY.asdict(), "s": s})
+        W, X, QR, KR = _layer(dims, 1100 + s, T)
+        pf = om.prefill(X, QR, KR, W, s, dims.scale)
+        n = om.n_slots(T, s)
+        lat = np.full((n + 2, dims.r), np.nan)
+        rk = np.full((n + 2, dims.d_hR), np.nan)
+        cuts = {0, 1, min(s + 1, T), T - 2, T} | set(rng.integers(1, T, size=3).tolist())
+        cuts = sorted(c for c in cuts if 0 <= c <= T)
+        states = []
+        for a, b in zip(cuts[:-1] + [T], cuts[1:] + [T]):   # last pair is an empty chunk
+            states.append(om.merge_chunk(lat, rk, a, X[a:b], KR[a:b], W, s))
+        assert np.array_equal(np.concatenate(states), pf["Cp"]), (s, T)
+        assert np.array_equal(lat[:n], pf["cache_lat"]), (s, T)
+        assert np.array_equal(rk[:n], pf["cache_rope"]), (s, T)
+        assert np.all(np.isnan(lat[n:])) and np.all(np.isnan(rk[n:]))
+
+
+def pin_chunk_continues_live_slot():
+    """Closed form of a chunk over a cache the oracle did not write: with a
+    zero content branch every merge weight is 1/2, so a chunk starting inside
+    group j0 adds half of each of its latents to whatever slot j0 holds, and
+    a chunk starting on a group boundary discards it.  Latents are small
+    integers, so every sum is exact."""
+    r = d = 8
+    for s, t0, L in ((2, 3, 6), (3, 4, 7), (4, 8, 5), (3, 6, 2), (1, 5, 4)):
+        W = dict(W_dkv=np.eye(r, d), W_hc=np.zeros((r, r)), b_hc=np.zeros(r),
+                 P=np.ones((16, r)))
+        X = np.arange(1.0, L * d + 1.0).reshape(L, d) % 7.0 - 3.0
+        KRc = np.stack([np.array([t0 + i, 100.0 + i]) for i in range(L)])
+        j0 = t0 // s
+        v = np.arange(r, dtype=np.float64) * 0.25 - 1.0     # prior content of slot j0
+        lat = np.full((16, r), np.nan)
+        rk = np.full((16, 2), np.nan)
+        lat[j0] = v
+        rk[j0] = [-1.0, -1.0]
+        Cp = om.merge_chunk(lat, rk, t0, X, KRc, W, s)
+        for i in range(L):
+            f = t0 + i
+            j = f // s
+            first = max(t0, s * j)
+            expect = (v if first > s * j else 0.0) + 0.5 * X[first - t0: i + 1].sum(axis=0)
+            assert np.array_equal(Cp[i], expect), (s, t0, i)
+        for j in range(j0, (t0 + L - 1) // s + 1):
+            last = min(t0 + L - 1, s * j + s - 1)
+            assert np.array_equal(lat[j], Cp[last - t0]), (s, t0, j)
+            assert np.array_equal(rk[j], KRc[last - t0]), (s, t0, j)
+        assert np.all(np.isnan(lat[(t0 + L - 1) // s + 1:]))
+
+
 ALL_PINS = [
     pin_mask_printed_rule, pin_mask_double_loop, pin_slot_counts, pin_worked_example_s2,
     pin_cache_size_law, pin_latent_orientation, pin_gate_structure, pin_gate_bias_and_position,
     pin_absorbed_equals_unabsorbed, pin_decode_equals_prefill, pin_resume_from_partial_prefill,
     pin_s1_is_causal_mla, pin_any_s_matches_sdpa, pin_half_gate_group_mean, pin_large_s_limit,
     pin_uniform_softmax, pin_first_step, pin_predownsampling_differs,
+    pin_chunked_append_equals_prefill, pin_chunk_continues_live_slot,
 ]

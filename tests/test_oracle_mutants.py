@@ -110,11 +110,43 @@ def _mut_decode_excludes_newest(mp):
     mp.setattr(om, "decode_step", ds)
 
 
+def _mut_chunk_opens_fresh(mp):
+    orig = om.merge_chunk
+
+    def mc(lat, rk, t0, Xc, KRc, W, s):
+        if Xc.shape[0] and t0 % s:
+            lat[om.slot_of(t0, s)] = 0.0     # forgets the live partial slot
+        return orig(lat, rk, t0, Xc, KRc, W, s)
+    mp.setattr(om, "merge_chunk", mc)
+
+
+def _mut_chunk_relative_positions(mp):
+    def mc(lat, rk, t0, Xc, KRc, W, s):
+        Cp = np.empty((Xc.shape[0], lat.shape[1]))
+        for i in range(Xc.shape[0]):
+            j = om.merge_append(lat, rk, i, Xc[i], KRc[i], W, s) + om.slot_of(t0, s)
+            Cp[i] = lat[j]
+        return Cp
+    mp.setattr(om, "merge_chunk", mc)
+
+
+def _mut_chunk_state_before_merge(mp):
+    def mc(lat, rk, t0, Xc, KRc, W, s):
+        Cp = np.empty((Xc.shape[0], lat.shape[1]))
+        for i in range(Xc.shape[0]):
+            j = om.slot_of(t0 + i, s)
+            Cp[i] = lat[j] if (t0 + i) % s else 0.0
+            om.merge_append(lat, rk, t0 + i, Xc[i], KRc[i], W, s)
+        return Cp
+    mp.setattr(om, "merge_chunk", mc)
+
+
 MUTANTS = [
     _mut_group_final_zero, _mut_drop_rope, _mut_transpose_whc, _mut_position_by_frame,
     _mut_additive_gate, _mut_no_reset, _mut_rope_key_first_frame, _mut_plain_prefix_sum,
     _mut_bvo_transposed, _mut_a_transposed, _mut_latent_transposed,
     _mut_scale_with_rope_width, _mut_sigmoid_sign, _mut_decode_excludes_newest,
+    _mut_chunk_opens_fresh, _mut_chunk_relative_positions, _mut_chunk_state_before_merge,
 ]
 
 
