@@ -27,7 +27,7 @@ second pass.
 
 Also reported (same line): the ragged and LLM-scale decode workloads, the
 strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
-of the whole forward), and the CPU oracle timed on the host cores on a bounded
+of the whole forward), the chunked merge-append (frames/s), and the CPU oracle timed on the host cores on a bounded
 sample of the headline workload.
 
 All inputs are seeded synthetic tensors (no datasets or trained weights).
@@ -286,6 +286,47 @@ def run_prefill(steps: int = 10, warmup: int = 3) -> dict:
                 tokens_per_s=M / (fwd_ms * 1e-3))
 
 
+def run_append(steps: int = 20, warmup: int = 3) -> dict:
+    """Chunked merge-append on the speech-decoder shapes: 32 sequences take
+    512 new frames each, starting at seeded positions in 0..1535 (most inside
+    a group), into caches of 1024 slots.  One step is one mtla_append_chunk
+    call (latent and gate projection of the 16384 frames, then the chunk
+    merge); every step writes a different cache replica."""
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    _, dims, _ = synth.config(2)
+    B, Lc, ms = 32, 512, 1024
+    rng = np.random.default_rng(synth.seed_for(2) + 10)
+    pos0 = rng.integers(0, ms * dims.s - Lc + 1, size=B).astype(np.int32)
+    w = synth.make_weights(dims, synth.seed_for(2), "bf16", pe_rows=ms)
+    layer = MTLALayer.from_arrays(dims, w, MTLA_BF16)
+    ch = synth.make_chunk(dims, w, pos0, Lc, synth.seed_for(2) + 11, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    X, KR = dev(ch["X"]), dev(ch["KR"])
+    p0 = torch.from_numpy(pos0).cuda()
+    max_pos = int(pos0.max()) + Lc - 1
+    row = dims.r + dims.d_hR
+    n_rep = 4
+    caches = [torch.zeros(B, ms, row, dtype=torch.bfloat16, device="cuda") for _ in range(n_rep)]
+    one = lambda i: layer.append_chunk(caches[i % n_rep], X, KR, p0, max_pos)
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    step_ms = _timed_loop(one, steps) / steps
+    frames = B * Lc
+    slots = int(np.sum((pos0 + Lc - 1) // dims.s - pos0 // dims.s + 1))
+    # bytes the call cannot avoid: frames and rotary keys in, weights, the
+    # partial slots read back, every touched slot written
+    io_bytes = (frames * (dims.d + dims.d_hR) * 2 + 2 * dims.r * dims.d * 2
+                + int(np.sum(pos0 % dims.s != 0)) * dims.r * 2 + slots * row * 2)
+    proj_flops = 2 * frames * dims.d * 2 * dims.r
+    return dict(name="append_chunk_b32_l512", B=B, L=Lc, dims=dims.asdict(), steps=steps,
+                step_ms=step_ms, frames_per_s=frames / (step_ms * 1e-3), slots_written=slots,
+                io_bytes=io_bytes, io_gbs=io_bytes / (step_ms * 1e-3) / 1e9,
+                proj_flops=proj_flops, proj_tflops=proj_flops / (step_ms * 1e-3) / 1e12)
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The oracle (numpy, fp32) on the headline decode workload: full-batch
     decode steps repeated until `seconds` of wall time have passed."""
@@ -328,7 +369,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
-                                       "llm_decode_b128_ctx32768", "prefill_b16_t4096"],
+                                       "llm_decode_b128_ctx32768", "prefill_b16_t4096",
+                                       "append_chunk_b32_l512"],
                     help="time one workload alone and print its record (for profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise pass reading and writing MIB MiB each "
@@ -346,6 +388,9 @@ def main():
 
     if args.calib_copy:
         calib_copy(args.calib_copy)
+    if args.only == "append_chunk_b32_l512":
+        print(json.dumps(run_append(args.steps, args.warmup)), flush=True)
+        return
     if args.only:
         cfg = {"decode_b32_ctx2048": 2, "ragged_decode_b64_s4": 3,
                "llm_decode_b128_ctx32768": 5, "prefill_b16_t4096": 4}[args.only]
@@ -376,6 +421,9 @@ def main():
         p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
         log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
             f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
+        log("append_chunk_b32_l512 ...")
+        a = extra["append_chunk_b32_l512"] = run_append()
+        log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")
         log("cpu baseline ...")
         cpu = cpu_baseline(args.cpu_seconds)
         cpu["value"] = round(cpu["value"], 2)

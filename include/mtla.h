@@ -130,6 +130,34 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
                               const void *X_t, const void *KR_t, const int32_t *pos, int32_t B,
                               int32_t max_pos, void *workspace, size_t ws_bytes, void *stream);
 
+/* Chunked merge-append ([Notes] temporal merging; [Fig2] (a) applied frame
+ * after frame): sequence b merges frames t = pos0[b] .. pos0[b] + n_b - 1 in
+ * order, with the result of n_b successive mtla_merge_append calls, where
+ * n_b = lens[b] clamped to [0, L], or L when lens is NULL.  A chunk that
+ * starts inside a group (pos0[b] mod s != 0) continues the live partial slot
+ * floor(pos0[b]/s) from its stored value -- the hand-off from a prefill that
+ * ended inside a group, or from earlier chunks; every slot the chunk touches
+ * ends holding its group's newest state and the RoPE key of the newest frame
+ * merged into it.  No other cache row is read or written.
+ * X [B, L, d], KR [B, L, d_hR] (rotated at positions pos0[b] + i), pos0 [B]
+ * and lens [B] (nullable) device int32; pos0[b] >= 0.
+ * max_pos: host-side upper bound of every pos0[b] + n_b - 1 (the caller's
+ *   contract); floor(max_pos/s) must be < cache->max_slots and <
+ *   gate_pos_rows (else MTLA_ERR_CAPACITY).  The kernel itself skips slots at
+ *   or beyond either bound, so a broken contract drops frames but never
+ *   writes outside the cache.
+ * Cprime_out (nullable): [B, L, r]; row i of sequence b receives the state of
+ *   frame pos0[b] + i's slot right after that frame's merge (the intermediate
+ *   state C' of the parallel form); rows i >= n_b are not written.
+ * In bf16 storage a slot is rounded once per chunk, where per-frame calls
+ * round it once per frame.  L = 0 is a no-op that returns MTLA_OK (X, KR and
+ * the workspace may then be NULL).
+ * Workspace: mtla_workspace_bytes(op=3, B, L). */
+mtla_status mtla_append_chunk(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                              const void *X, const void *KR, const int32_t *pos0,
+                              const int32_t *lens, int32_t B, int32_t L, int32_t max_pos,
+                              void *Cprime_out, void *workspace, size_t ws_bytes, void *stream);
+
 /* One incremental decoding step ([Notes] stride-aware mask motivation and Y
  * formula; [Fig2] (a)): mtla_merge_append at pos[b], then for every head h
  *   q~_h = A[h] x_t
@@ -181,8 +209,9 @@ mtla_status mtla_prefill_strided_timed(const mtla_dims *dims, const mtla_weights
                                        void *const *events);
 
 /* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
- * T_or_max_pos = max_pos) or 2 (prefill, with T_or_max_pos = T).  Returns 0
- * for invalid arguments.  Pure host function. */
+ * T_or_max_pos = max_pos), 2 (prefill, with T_or_max_pos = T) or 3 (chunked
+ * merge-append, with T_or_max_pos = L).  Returns 0 for invalid arguments.
+ * Pure host function. */
 size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos);
 
 /* Static description of a status code.  Pure host function. */

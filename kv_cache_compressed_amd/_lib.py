@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtla.so"
 
 MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = range(5)
 MTLA_F32, MTLA_BF16 = 0, 1
-OP_MERGE, OP_DECODE, OP_PREFILL = 0, 1, 2
+OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK = 0, 1, 2, 3
 
-EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append", "mtla_decode_step", "mtla_prefill_strided",
+EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
+            "mtla_append_chunk", "mtla_decode_step", "mtla_prefill_strided",
             "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_workspace_bytes",
             "mtla_status_string", "mtla_last_error_detail")
 
@@ -65,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtla_gate_content_map.argtypes = [P(Dims), c_void_p, c_void_p, c_void_p, c_void_p]
     lib.mtla_merge_append.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
                                       c_int32, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.mtla_append_chunk.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]
     lib.mtla_decode_step.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t,
                                      c_void_p]
@@ -73,7 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_size_t, c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
-    for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append", "mtla_decode_step",
+    for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
+              "mtla_append_chunk", "mtla_decode_step",
               "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
@@ -167,6 +172,20 @@ def mtla_merge_append(dims: Dims, w: Weights, cache: Cache, X_t, KR_t, pos, max_
     _check(load_library().mtla_merge_append(ctypes.byref(dims), ctypes.byref(w),
                                             ctypes.byref(cache), _ptr(X_t), _ptr(KR_t), _ptr(pos),
                                             B, int(max_pos), _ptr(ws), ws.numel(), _stream()))
+
+
+def mtla_append_chunk(dims: Dims, w: Weights, cache: Cache, X, KR, pos0, max_pos: int, lens=None,
+                      Cprime=None, ws=None):
+    """Merge frames pos0[b] .. pos0[b] + n_b - 1 of X [B, L, d] into the cache
+    (n_b = lens[b] or L); ``max_pos`` bounds every sequence's last frame."""
+    B, Lc = X.shape[0], X.shape[1]
+    if ws is None and Lc > 0:
+        ws = workspace(dims, OP_CHUNK, B, Lc, X.device)
+    _check(load_library().mtla_append_chunk(ctypes.byref(dims), ctypes.byref(w),
+                                            ctypes.byref(cache), _ptr(X), _ptr(KR), _ptr(pos0),
+                                            _ptr(lens), B, Lc, int(max_pos), _ptr(Cprime),
+                                            _ptr(ws), ws.numel() if ws is not None else 0,
+                                            _stream()))
 
 
 def _events(events):

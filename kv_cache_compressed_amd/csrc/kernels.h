@@ -78,6 +78,18 @@ hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *p
                         const void *b_hc, const float *gate_pos, const void *KR_t, void *cache,
                         int64_t batch_stride, hipStream_t stream);
 
+// Chunked merge-append: sequence b folds frames pos0[b] .. pos0[b] + n_b - 1
+// (n_b = lens[b] clamped to [0, L], or L when lens is null) into its cache in
+// frame order, continuing a live partial slot, from cg [B, L, 2r]; KR
+// [B, L, dR].  Cp [B, L, r] (nullable) receives each frame's running slot
+// state.  Slots >= jlim are skipped.  chunk_slots(L, s) bounds the slots one
+// chunk of L frames can touch.
+hipError_t launch_chunk_merge(int dtype, int B, int L, int r, int dR, int s, const int32_t *pos0,
+                              const int32_t *lens, const float *cg, const void *b_hc,
+                              const float *table, int jlim, const void *KR, void *Cp, void *cache,
+                              int64_t batch_stride, hipStream_t stream);
+int chunk_slots(int L, int s);
+
 // ---- parallel form ----------------------------------------------------------
 
 // Hyper-network gate and segmented (per group of s frames) inclusive sum:

@@ -142,6 +142,11 @@ PrefillWs prefill_ws(const mtla_dims *d, int B, int T) {
   return w;
 }
 
+// Workspace of a chunked merge-append of L frames: cg [B*L, 2r] fp32.
+size_t chunk_ws(const mtla_dims *d, int B, int L) {
+  return align_up((size_t)B * L * 2 * d->r * 4);
+}
+
 mtla_status check_positions(const mtla_dims *d, const mtla_weights *w, const mtla_cache *c, int B,
                             int max_pos) {
   if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
@@ -186,6 +191,7 @@ size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_
     if (T_or_max_pos < 1) return 0;
     return prefill_ws(dims, B, T_or_max_pos).total;
   }
+  if (op == 3) return chunk_ws(dims, B, T_or_max_pos);
   return 0;
 }
 
@@ -241,6 +247,40 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
   LAUNCH(mtla::launch_merge(dims->dtype, B, dims->r, dims->d_hR, dims->s, pos, cg, w->b_hc,
                             w->gate_pos, KR_t, cache->slots, cache->batch_stride, s),
          "merge");
+  return ok();
+}
+
+mtla_status mtla_append_chunk(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
+                              const void *X, const void *KR, const int32_t *pos0,
+                              const int32_t *lens, int32_t B, int32_t L, int32_t max_pos,
+                              void *Cprime_out, void *workspace, size_t ws_bytes, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if ((st = check_weights(w, false)) != MTLA_OK) return st;
+  if ((st = check_cache(dims, cache)) != MTLA_OK) return st;
+  CHECK_PTR(pos0);
+  if (lens && !aligned16(lens)) return fail(MTLA_ERR_ARG, "lens is not 16-byte aligned");
+  if (Cprime_out && !aligned16(Cprime_out)) return fail(MTLA_ERR_ARG, "Cprime_out is not 16-byte aligned");
+  if (L < 0) return fail(MTLA_ERR_ARG, "L=%d < 0", L);
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (L == 0) return ok();   // nothing is read: X, KR and the workspace may be null
+  CHECK_PTR(X);
+  CHECK_PTR(KR);
+  CHECK_PTR(workspace);
+  if ((int64_t)B * L > 0x7fffffffLL / 4) return fail(MTLA_ERR_UNSUPPORTED, "B*L too large");
+  if ((st = check_positions(dims, w, cache, B, max_pos)) != MTLA_OK) return st;
+  const size_t need = chunk_ws(dims, B, L);
+  if (ws_bytes < need) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  float *cg = (float *)workspace;
+  const int jlim = cache->max_slots < w->gate_pos_rows ? cache->max_slots : w->gate_pos_rows;
+  LAUNCH(mtla::launch_proj(dims->dtype, X, B * L, dims->d, w->W_dkv, w->W_gate, dims->r, nullptr,
+                           0, cg, nullptr, nullptr, 0, s),
+         "latent and gate projection");
+  LAUNCH(mtla::launch_chunk_merge(dims->dtype, B, L, dims->r, dims->d_hR, dims->s, pos0, lens, cg,
+                                  w->b_hc, w->gate_pos, jlim, KR, Cprime_out, cache->slots,
+                                  cache->batch_stride, s),
+         "chunked merge");
   return ok();
 }
 

@@ -2,7 +2,8 @@
 
 Holds the device weights in the layouts the C ABI takes, the fp32
 position-branch table and the folded content-branch map (built once on the
-GPU by mtla_gate_pos_table and mtla_gate_content_map) and reusable workspaces, and forwards to the three hot-path entry points.  It
+GPU by mtla_gate_pos_table and mtla_gate_content_map) and reusable
+workspaces, and forwards to the hot-path entry points.  It
 only marshals arguments; all arithmetic runs in libmtla.so.
 """
 from __future__ import annotations
@@ -54,6 +55,11 @@ class MTLALayer:
     def merge_append(self, cache: torch.Tensor, X_t, KR_t, pos, max_pos: int):
         L.mtla_merge_append(self.dims, self.w, L.make_cache(cache), X_t, KR_t, pos, max_pos,
                             self.workspace(L.OP_MERGE, X_t.shape[0], max_pos))
+
+    def append_chunk(self, cache: torch.Tensor, X, KR, pos0, max_pos: int, lens=None, Cprime=None):
+        ws = self.workspace(L.OP_CHUNK, X.shape[0], X.shape[1]) if X.shape[1] > 0 else None
+        L.mtla_append_chunk(self.dims, self.w, L.make_cache(cache), X, KR, pos0, max_pos, lens,
+                            Cprime, ws)
 
     def decode_step(self, cache: torch.Tensor, X_t, QR_t, KR_t, pos, max_pos: int, Y=None,
                     events=None):

@@ -214,3 +214,20 @@ def make_step(dims: Dims, w: dict, pos: np.ndarray, seed: int, storage: str = "b
     qr = rope(qr, pos[:, None].astype(np.float64))
     kr = rope(x @ w["W_KR"].T, pos.astype(np.float64))
     return dict(x=x, QR=round_to(qr, storage), KR=round_to(kr, storage))
+
+
+def make_chunk(dims: Dims, w: dict, pos0: np.ndarray, L: int, seed: int,
+               storage: str = "bf16") -> dict:
+    """A chunk of L new frames per sequence starting at 0-based positions
+    ``pos0`` [B]: X [B, L, d] ~ N(0, 1), and QR [B, L, H, d_hR], KR [B, L, d_hR]
+    rotated at each frame's absolute position pos0[b] + i."""
+    pos0 = np.asarray(pos0)
+    B = len(pos0)
+    H, dR = dims.H, dims.d_hR
+    rng = np.random.default_rng(seed)
+    X = round_to(rng.normal(0.0, 1.0, size=(B, L, dims.d)), storage)
+    pos = (pos0[:, None] + np.arange(L)[None, :]).astype(np.float64)      # [B, L]
+    qr = (X @ w["W_QR"].reshape(H * dR, dims.d).T).reshape(B, L, H, dR)
+    QR = rope(qr, pos[:, :, None])
+    KR = rope(X @ w["W_KR"].T, pos)
+    return dict(X=X, QR=round_to(QR, storage), KR=round_to(KR, storage))

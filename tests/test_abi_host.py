@@ -155,3 +155,63 @@ def test_prefill_and_merge_reject_before_launch():
     assert st == L.MTLA_ERR_ARG
     st = lib.mtla_gate_pos_table(ctypes.byref(d), FAKE, 16, 500, FAKE, FAKE, FAKE, None)
     assert st == L.MTLA_ERR_UNSUPPORTED
+
+
+def _chunk(dims=None, w=None, cache=None, B=4, Lc=16, max_pos=100, ws_bytes=1 << 30, pos0=FAKE,
+           lens=None, cprime=None, ws=FAKE):
+    lib = K.load_library()
+    dims = dims if dims is not None else _dims()
+    w = w if w is not None else _weights()
+    cache = cache if cache is not None else _cache()
+    return lib.mtla_append_chunk(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache), FAKE,
+                                 FAKE, pos0, lens, B, Lc, max_pos, cprime, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("negative_length", L.MTLA_ERR_ARG),
+    ("null_pos0", L.MTLA_ERR_ARG),
+    ("misaligned_lens", L.MTLA_ERR_ARG),
+    ("misaligned_cprime", L.MTLA_ERR_ARG),
+    ("zero_batch", L.MTLA_ERR_ARG),
+    ("capacity_slots", L.MTLA_ERR_CAPACITY),
+    ("capacity_gate_table", L.MTLA_ERR_CAPACITY),
+    ("small_workspace", L.MTLA_ERR_ARG),
+    ("unsupported_r", L.MTLA_ERR_UNSUPPORTED),
+])
+def test_append_chunk_rejects(case, expect):
+    kw = {}
+    if case == "negative_length":
+        kw["Lc"] = -1
+    elif case == "null_pos0":
+        kw["pos0"] = None
+    elif case == "misaligned_lens":
+        kw["lens"] = FAKE + 4
+    elif case == "misaligned_cprime":
+        kw["cprime"] = FAKE + 2
+    elif case == "zero_batch":
+        kw["B"] = 0
+    elif case == "capacity_slots":
+        kw["max_pos"] = 2 * 1024
+    elif case == "capacity_gate_table":
+        kw["w"] = _weights(rows=50)
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 4 * 16 * 2 * 256 * 4 - 1
+    elif case == "unsupported_r":
+        kw["dims"] = _dims(r=128, d_hR=16)
+    st = _chunk(**kw)
+    assert st == expect, (case, st, K.load_library().mtla_last_error_detail())
+
+
+def test_append_chunk_empty_is_a_noop():
+    """L = 0 returns OK before any launch (nothing to merge)."""
+    assert _chunk(Lc=0, ws=None, ws_bytes=0) == L.MTLA_OK
+    lib = K.load_library()
+    d, w, c = _dims(), _weights(), _cache()
+    assert lib.mtla_append_chunk(ctypes.byref(d), ctypes.byref(w), ctypes.byref(c), None, None,
+                                 FAKE, None, 4, 0, 0, None, None, 0, None) == L.MTLA_OK
+
+
+def test_append_chunk_workspace():
+    d = _dims()
+    assert K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 16) >= 4 * 16 * 2 * 256 * 4
+    assert K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 16) < K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 17)
