@@ -291,7 +291,9 @@ def merge_chunk(lat, rk, t0, Xc, KRc, W, s):
 
 
 # ---------------------------------------------------------------------------
-# reference forms used only to pin the ones above
+# the per-head (unabsorbed) form ([Fig1] before absorption; [Notes] decoupled
+# RoPE: training may keep the RoPE keys uncompressed) -- also the pin of the
+# absorbed form above
 # ---------------------------------------------------------------------------
 
 
@@ -311,6 +313,11 @@ def mha_unabsorbed(X, QR, KR, Cp, W_Q, W_K, W_V, W_O, s, scale):
         z = np.where(M, z, -np.inf)
         Y += softmax_rows(z) @ V @ W_O[h]
     return Y
+
+
+# ---------------------------------------------------------------------------
+# reference forms used only to pin the ones above
+# ---------------------------------------------------------------------------
 
 
 def prefill_predownsampled(X, QR, KR, W, s, scale):

@@ -294,6 +294,34 @@ def pin_any_s_matches_sdpa():
         assert relerr(pf["O"], O) < 1e-12, (s, relerr(pf["O"], O))
 
 
+def pin_unabsorbed_matches_sdpa():
+    """The per-head form: for every head, torch's SDPA over the explicit
+    queries [X W_Q^(h) | Q^R_h], keys [C' W_K^(h) | K^R] and values C' W_V^(h)
+    under the printed-rule mask, mapped through W_O^(h) and summed."""
+    import torch
+    import torch.nn.functional as F
+    for s, T in ((2, 21), (3, 16), (1, 7)):
+        dims = Dims(**{**TINY.asdict(), "s": s})
+        W, X, QR, KR = _layer(dims, 520 + s, T)
+        Cp = om.prefill(X, QR, KR, W, s, dims.scale)["Cp"]
+        mask = np.zeros((T, T), dtype=bool)
+        for m1 in range(1, T + 1):
+            for n1 in range(1, T + 1):
+                mask[m1 - 1, n1 - 1] = (n1 == m1) or (n1 < m1 and n1 % s == 0)
+        Y = np.zeros((T, dims.d))
+        for h in range(dims.H):
+            q = torch.from_numpy(np.concatenate([X @ W["W_Q"][h], QR[:, h, :]], axis=-1))
+            k = torch.from_numpy(np.concatenate([Cp @ W["W_K"][h], KR], axis=-1))
+            v = torch.from_numpy(Cp @ W["W_V"][h])
+            o = F.scaled_dot_product_attention(q[None], k[None], v[None],
+                                               attn_mask=torch.from_numpy(mask)[None],
+                                               scale=dims.scale)[0].numpy()
+            Y += o @ W["W_O"][h]
+        ref = om.mha_unabsorbed(X, QR, KR, Cp, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], s,
+                                dims.scale)
+        assert relerr(ref, Y) < 1e-12, (s, T, relerr(ref, Y))
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
@@ -444,5 +472,5 @@ ALL_PINS = [
     pin_absorbed_equals_unabsorbed, pin_decode_equals_prefill, pin_resume_from_partial_prefill,
     pin_s1_is_causal_mla, pin_any_s_matches_sdpa, pin_half_gate_group_mean, pin_large_s_limit,
     pin_uniform_softmax, pin_first_step, pin_predownsampling_differs,
-    pin_chunked_append_equals_prefill, pin_chunk_continues_live_slot,
+    pin_chunked_append_equals_prefill, pin_chunk_continues_live_slot, pin_unabsorbed_matches_sdpa,
 ]

@@ -141,12 +141,29 @@ def _mut_chunk_state_before_merge(mp):
     mp.setattr(om, "merge_chunk", mc)
 
 
+def _mut_unabsorbed_values_from_keys(mp):
+    orig = om.mha_unabsorbed
+
+    def mha(X, QR, KR, Cp, W_Q, W_K, W_V, W_O, s, scale):
+        return orig(X, QR, KR, Cp, W_Q, W_K, W_K, W_O, s, scale)
+    mp.setattr(om, "mha_unabsorbed", mha)
+
+
+def _mut_unabsorbed_causal_mask(mp):
+    orig = om.mha_unabsorbed
+
+    def mha(X, QR, KR, Cp, W_Q, W_K, W_V, W_O, s, scale):
+        return orig(X, QR, KR, Cp, W_Q, W_K, W_V, W_O, 1, scale)   # plain causal mask
+    mp.setattr(om, "mha_unabsorbed", mha)
+
+
 MUTANTS = [
     _mut_group_final_zero, _mut_drop_rope, _mut_transpose_whc, _mut_position_by_frame,
     _mut_additive_gate, _mut_no_reset, _mut_rope_key_first_frame, _mut_plain_prefix_sum,
     _mut_bvo_transposed, _mut_a_transposed, _mut_latent_transposed,
     _mut_scale_with_rope_width, _mut_sigmoid_sign, _mut_decode_excludes_newest,
     _mut_chunk_opens_fresh, _mut_chunk_relative_positions, _mut_chunk_state_before_merge,
+    _mut_unabsorbed_values_from_keys, _mut_unabsorbed_causal_mask,
 ]
 
 
