@@ -27,7 +27,8 @@ second pass.
 
 Also reported (same line): the ragged and LLM-scale decode workloads, the
 strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
-of the whole forward), the chunked merge-append (frames/s), and the CPU oracle timed on the host cores on a bounded
+of the whole forward, in the absorbed form and in the per-head form), the
+chunked merge-append (frames/s), and the CPU oracle timed on the host cores on a bounded
 sample of the headline workload.
 
 All inputs are seeded synthetic tensors (no datasets or trained weights).
@@ -327,6 +328,50 @@ def run_append(steps: int = 20, warmup: int = 3) -> dict:
                 proj_flops=proj_flops, proj_tflops=proj_flops / (step_ms * 1e-3) / 1e12)
 
 
+def run_prefill_unabsorbed(steps: int = 10, warmup: int = 3) -> dict:
+    """The same prefill workload in the per-head form (mtla_prefill_unabsorbed):
+    attention at head width over explicit per-head keys and values."""
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    ms = -(-T // dims.s)
+    w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
+    layer = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    X, QR, KR = dev(seq["X"]), dev(seq["QR"]), dev(seq["KR"])
+    del seq
+    Y = torch.empty(B, T, dims.d, dtype=torch.bfloat16, device="cuda")
+    cache = layer.new_cache(B, ms)
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(steps)]
+    run = lambda i, e=None: layer.prefill_unabsorbed(X, QR, KR, Y, cache=cache, events=e)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    fwd_ms = _timed_loop(run, steps) / steps
+    _timed_loop(lambda i: run(i, ev[i]), steps)
+    attn_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    _, pairs = prefill_flops(B, T, dims.H, dims.r, dims.d_hR, dims.s)
+    dh, dR, H, M = dims.d_h, dims.d_hR, dims.H, B * T
+    attn_flops = B * H * pairs * (2 * (dh + dR) + 2 * dh)
+    proj_flops = (2 * M * dims.d * 2 * dims.r          # latent and gate
+                  + 2 * M * dims.d * H * dh            # per-head queries
+                  + 2 * M * dims.r * 2 * H * dh        # per-head keys and values
+                  + 2 * M * H * dh * dims.d)           # output
+    return dict(name=name + "_per_head", B=B, T=T, dims=dims.asdict(), steps=steps,
+                forward_ms=fwd_ms, attn_ms=attn_ms, visible_pairs=B * H * pairs,
+                attn_flops=attn_flops, proj_flops=proj_flops,
+                attn_tflops=attn_flops / (attn_ms * 1e-3) / 1e12,
+                forward_tflops=(attn_flops + proj_flops) / (fwd_ms * 1e-3) / 1e12,
+                tokens_per_s=M / (fwd_ms * 1e-3))
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The oracle (numpy, fp32) on the headline decode workload: full-batch
     decode steps repeated until `seconds` of wall time have passed."""
@@ -370,7 +415,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
                                        "llm_decode_b128_ctx32768", "prefill_b16_t4096",
-                                       "append_chunk_b32_l512"],
+                                       "append_chunk_b32_l512", "prefill_b16_t4096_per_head"],
                     help="time one workload alone and print its record (for profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise pass reading and writing MIB MiB each "
@@ -388,6 +433,9 @@ def main():
 
     if args.calib_copy:
         calib_copy(args.calib_copy)
+    if args.only == "prefill_b16_t4096_per_head":
+        print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup)), flush=True)
+        return
     if args.only == "append_chunk_b32_l512":
         print(json.dumps(run_append(args.steps, args.warmup)), flush=True)
         return
@@ -421,6 +469,11 @@ def main():
         p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
         log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
             f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
+        log("prefill_b16_t4096_per_head ...")
+        u = extra["prefill_b16_t4096_per_head"] = run_prefill_unabsorbed()
+        u["attn_mfma_frac"] = u["attn_tflops"] / BF16_PEAK_TFLOPS
+        log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
+            f"({u['attn_mfma_frac']:.1%}), forward {u['forward_ms']:.3f} ms")
         log("append_chunk_b32_l512 ...")
         a = extra["append_chunk_b32_l512"] = run_append()
         log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")

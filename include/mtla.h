@@ -190,7 +190,43 @@ mtla_status mtla_prefill_strided(const mtla_dims *dims, const mtla_weights *w, c
                                  const mtla_cache *cache_out, void *Cprime_out, void *workspace,
                                  size_t ws_bytes, void *stream);
 
-/* Profiling variants of mtla_decode_step and mtla_prefill_strided: the same
+/* Weights of the per-head (unabsorbed) form ([Fig1] (b): the maps W_Q, W_K,
+ * W_V, W_O of every head before they are absorbed into A and Bvo).  The
+ * hyper-network fields are those of mtla_weights. */
+typedef struct {
+  const void *W_dkv;      /* [r, d]     latent map */
+  const void *W_gate;     /* [r, d]     W_hc W_dkv (mtla_gate_content_map) */
+  const void *b_hc;       /* [r]        content-branch bias */
+  const float *gate_pos;  /* [gate_pos_rows, r] FP32 position-branch table */
+  int32_t gate_pos_rows;
+  const void *W_Q;        /* [H*d_h, d] rows h*d_h .. h*d_h+d_h-1 map x_m to the query Q_h[m] */
+  const void *W_K;        /* [H*d_h, r] rows of head h map C'_n to its key K_h[n] */
+  const void *W_V;        /* [H*d_h, r] rows of head h map C'_n to its value V_h[n] */
+  const void *W_O;        /* [d, H*d_h] Y[m] = W_O (o_0; ...; o_{H-1}) */
+} mtla_unabsorbed_weights;
+
+/* Parallel forward in the per-head form ([Notes] stride-aware causal mask,
+ * decoupled RoPE: training may use the uncompressed RoPE keys; [Fig1] before
+ * absorption).  Same frames, gate, intermediate states and optional cache
+ * and C' outputs as mtla_prefill_strided; the attention runs at head width:
+ *   Q_h[m] = W_Q^(h) x_m,  K_h[n] = W_K^(h) C'_n,  V_h[n] = W_V^(h) C'_n
+ *   z = (Q_h[m] . K_h[n] + QR[m, h] . KR[n]) * scale over the visible n
+ *   Y[m] = W_O (o_0; ...; o_{H-1}),  o_h = sum_n softmax(z)_n V_h[n]
+ * With Wq_h, Wk_h, Wv_h the row blocks of head h of W_Q, W_K, W_V and Wo_h
+ * the column block of head h of W_O, the absorbed maps A[h] = Wk_h^T Wq_h
+ * and Bvo[:, h, :] = Wo_h Wv_h make this exactly mtla_prefill_strided; the
+ * per-head form spends 2 (d_h + d_hR) + 2 d_h flops per visible pair and head
+ * on attention instead of 2 (r + d_hR) + 2 r.  Supported: bf16 storage, d_h = 64,
+ * d_hR = 32 (else MTLA_ERR_UNSUPPORTED).  Workspace:
+ * mtla_workspace_bytes(op=4, B, T). */
+mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                                    const void *X, const void *QR, const void *KR, int32_t B,
+                                    int32_t T, void *Y, const mtla_cache *cache_out,
+                                    void *Cprime_out, void *workspace, size_t ws_bytes,
+                                    void *stream);
+
+/* Profiling variants of mtla_decode_step, mtla_prefill_strided and
+ * mtla_prefill_unabsorbed: the same
  * computation, and in addition the attention kernel (the split-K decode
  * attention, resp. the strided prefill attention) is launched so that the
  * runtime stamps events[0] with its start and events[1] with its end
@@ -207,10 +243,17 @@ mtla_status mtla_prefill_strided_timed(const mtla_dims *dims, const mtla_weights
                                        void *Y, const mtla_cache *cache_out, void *Cprime_out,
                                        void *workspace, size_t ws_bytes, void *stream,
                                        void *const *events);
+mtla_status mtla_prefill_unabsorbed_timed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                                          const void *X, const void *QR, const void *KR,
+                                          int32_t B, int32_t T, void *Y,
+                                          const mtla_cache *cache_out, void *Cprime_out,
+                                          void *workspace, size_t ws_bytes, void *stream,
+                                          void *const *events);
 
 /* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
- * T_or_max_pos = max_pos), 2 (prefill, with T_or_max_pos = T) or 3 (chunked
- * merge-append, with T_or_max_pos = L).  Returns 0 for invalid arguments.
+ * T_or_max_pos = max_pos), 2 (prefill, with T_or_max_pos = T), 3 (chunked
+ * merge-append, with T_or_max_pos = L) or 4 (per-head prefill, with
+ * T_or_max_pos = T).  Returns 0 for invalid arguments.
  * Pure host function. */
 size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos);
 

@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtla.so"
 
 MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = range(5)
 MTLA_F32, MTLA_BF16 = 0, 1
-OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK = 0, 1, 2, 3
+OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK, OP_UNABSORBED = 0, 1, 2, 3, 4
 
 EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
             "mtla_append_chunk", "mtla_decode_step", "mtla_prefill_strided",
-            "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_workspace_bytes",
+            "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_prefill_unabsorbed",
+            "mtla_prefill_unabsorbed_timed", "mtla_workspace_bytes",
             "mtla_status_string", "mtla_last_error_detail")
 
 
@@ -42,6 +43,12 @@ class Weights(ctypes.Structure):
     _fields_ = [("W_dkv", c_void_p), ("W_gate", c_void_p), ("b_hc", c_void_p),
                 ("gate_pos", c_void_p), ("gate_pos_rows", c_int32), ("A", c_void_p),
                 ("Bvo", c_void_p)]
+
+
+class UnabsorbedWeights(ctypes.Structure):
+    _fields_ = [("W_dkv", c_void_p), ("W_gate", c_void_p), ("b_hc", c_void_p),
+                ("gate_pos", c_void_p), ("gate_pos_rows", c_int32), ("W_Q", c_void_p),
+                ("W_K", c_void_p), ("W_V", c_void_p), ("W_O", c_void_p)]
 
 
 class Cache(ctypes.Structure):
@@ -75,11 +82,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtla_prefill_strided.argtypes = [P(Dims), P(Weights), c_void_p, c_void_p, c_void_p,
                                          c_int32, c_int32, c_void_p, P(Cache), c_void_p, c_void_p,
                                          c_size_t, c_void_p]
+    lib.mtla_prefill_unabsorbed.argtypes = [P(Dims), P(UnabsorbedWeights), c_void_p, c_void_p,
+                                            c_void_p, c_int32, c_int32, c_void_p, P(Cache),
+                                            c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.mtla_prefill_unabsorbed_timed.argtypes = lib.mtla_prefill_unabsorbed.argtypes + [c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
     for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
               "mtla_append_chunk", "mtla_decode_step",
-              "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed"):
+              "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed",
+              "mtla_prefill_unabsorbed", "mtla_prefill_unabsorbed_timed"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
     lib.mtla_workspace_bytes.restype = c_size_t
@@ -124,6 +136,14 @@ def make_weights(W_dkv, W_gate, b_hc, gate_pos, A=None, Bvo=None) -> Weights:
     while the struct is used."""
     return Weights(_ptr(W_dkv), _ptr(W_gate), _ptr(b_hc), _ptr(gate_pos), int(gate_pos.shape[0]),
                    _ptr(A), _ptr(Bvo))
+
+
+def make_unabsorbed_weights(W_dkv, W_gate, b_hc, gate_pos, W_Q, W_K, W_V, W_O) -> UnabsorbedWeights:
+    """Per-head maps in the ABI layouts: W_Q [H*d_h, d], W_K and W_V
+    [H*d_h, r], W_O [d, H*d_h].  The tensors must stay alive while the struct
+    is used."""
+    return UnabsorbedWeights(_ptr(W_dkv), _ptr(W_gate), _ptr(b_hc), _ptr(gate_pos),
+                             int(gate_pos.shape[0]), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(W_O))
 
 
 def make_cache(slots: torch.Tensor) -> Cache:
@@ -238,6 +258,26 @@ def mtla_prefill_strided(dims: Dims, w: Weights, X, QR, KR, Y=None, cache: Cache
         _check(lib.mtla_prefill_strided(*args))
     else:
         _check(lib.mtla_prefill_strided_timed(*args, _events(events)))
+    return Y
+
+
+def mtla_prefill_unabsorbed(dims: Dims, w: UnabsorbedWeights, X, QR, KR, Y=None,
+                            cache: Cache | None = None, Cprime=None, ws=None, events=None):
+    """``events``: optional pair of torch.cuda.Event recorded around the
+    per-head attention kernel (the profiling entry point is used then)."""
+    B, T = X.shape[0], X.shape[1]
+    if Y is None:
+        Y = torch.empty(B, T, dims.d, dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(dims, OP_UNABSORBED, B, T, X.device)
+    cptr = ctypes.byref(cache) if cache is not None else None
+    lib = load_library()
+    args = [ctypes.byref(dims), ctypes.byref(w), _ptr(X), _ptr(QR), _ptr(KR), B, T, _ptr(Y), cptr,
+            _ptr(Cprime), _ptr(ws), ws.numel(), _stream()]
+    if events is None:
+        _check(lib.mtla_prefill_unabsorbed(*args))
+    else:
+        _check(lib.mtla_prefill_unabsorbed_timed(*args, _events(events)))
     return Y
 
 

@@ -185,12 +185,18 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   };
   const int pro = min(a.nst, nstage);
   for (int k = 0; k < pro; ++k) issue(k);
+  int last = pro - 1;   // newest stage issued so far
 
   for (int k = 0; k < nstage; ++k) {
-    wait_stages<C::LPW>(min(a.nst - 1, nstage - 1 - k));
+    // Stage k has landed once at most last - k stages issued after it are
+    // still in flight (this wave's loads complete in issue order).
+    wait_stages<C::LPW>(last - k);
     bar();
     // Every wave is past stage k-1 here: its ring slot can be refilled.
-    if (k >= 1 && k - 1 + a.nst < nstage) issue(k - 1 + a.nst);
+    if (k >= 1 && k - 1 + a.nst < nstage) {
+      issue(k - 1 + a.nst);
+      last = k - 1 + a.nst;
+    }
     const char *sb = smem + (k % a.nst) * C::STAGE_B;
 #pragma unroll
     for (int tl = 0; tl < C::TPS; ++tl) {
@@ -322,6 +328,9 @@ hipError_t prefill_attn_t(int B, int T_len, int H, int s, float sl2, const void 
 // phases (half the row tiles each).  The 16x16x32 bf16 MFMA is used
 // throughout: gfx950 runs the 16x16x16 form at half its rate.
 // ---------------------------------------------------------------------------
+#ifndef MTLA_WS_SPLIT
+#define MTLA_WS_SPLIT 6
+#endif
 struct WsCfg {
   static constexpr int R = 256, DR = 32, RK = R + DR, RB = RK * 2, NSEG = RB / 64;
   static constexpr int NQ = 3, KS = RK / 32, MT = R / 16;
@@ -635,7 +644,7 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
         for (int mb = 0; mb < C::NB; ++mb) o[rt][mb] = mma_k32(vf[mb], pf, o[rt][mb]);
       }
     };
-    using Half = std::integral_constant<int, C::NRT / 2>;
+    using Half = std::integral_constant<int, MTLA_WS_SPLIT>;
     using Zero = std::integral_constant<int, 0>;
     using Full = std::integral_constant<int, C::NRT>;
     for (int k = 0; k <= nstage; ++k) {

@@ -160,6 +160,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   };
   const int pro = min(a.nst, nstage);
   for (int k = 0; k < pro; ++k) issue(k);
+  int lastst = pro - 1;   // newest stage issued so far
 
   // o[hb][qb]: O^T block of channels 16 (wave * MQ + qb) + 4g + e, head
   // hb * 16 + c.  m[hb]: reference max of head hb * 16 + c (same in every
@@ -175,10 +176,15 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   float lp = 0.0f;
 
   for (int k = 0; k < nstage; ++k) {
-    wait_stages<C::LPW>(min(a.nst - 1, nstage - 1 - k));
+    // Stage k has landed once at most lastst - k stages issued after it are
+    // still in flight (this wave's loads complete in issue order).
+    wait_stages<C::LPW>(lastst - k);
     bar();
     // Every wave is past stage k-1 here: its ring slot can be refilled.
-    if (k >= 1 && k - 1 + a.nst < nstage) issue(k - 1 + a.nst);
+    if (k >= 1 && k - 1 + a.nst < nstage) {
+      issue(k - 1 + a.nst);
+      lastst = k - 1 + a.nst;
+    }
     char *sb = smem + (k % a.nst) * C::STAGE_B;
     const int row0 = start + k * C::SROWS;
     if (k == nstage - 1) {

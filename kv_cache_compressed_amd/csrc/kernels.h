@@ -16,6 +16,12 @@ namespace mtla {
 hipError_t launch_gemm_store(int dtype, const void *A, int lda, const void *Bm, int ldb, int M,
                              int N, int K, void *out, int ldc, hipStream_t stream);
 
+// out[M, N] = A[M, K] [B1; B2]^T: output columns < N1 from the rows of B1,
+// the others from the rows of B2 (both with row stride ldb).
+hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1, const void *B2,
+                              int N1, int ldb, int M, int N, int K, void *out, int ldc,
+                              hipStream_t stream);
+
 // table[rows, r] (fp32) = pe[rows, d_pe] W_hp[r, d_pe]^T + b_hp.
 hipError_t launch_pos_table(int dtype, const void *pe, int rows, int d_pe, const void *W_hp,
                             const void *b_hp, int r, float *table, hipStream_t stream);
@@ -112,5 +118,14 @@ hipError_t launch_prefill_attention(int dtype, int B, int T, int H, int r, int d
                                     hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 bool prefill_attention_supported(int dtype, int H, int r, int dR);
+
+// Per-head (unabsorbed) stride-aware masked attention, bf16, d_h = 64,
+// dR = 32: O [B*T, H*64] from q [B*T, H*64], QR [B*T, H, dR], KV
+// [B*T, 2*H*64] (K_h at column 64 h, V_h at 64 (H + h)) and KR [B*T, dR].
+hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const void *q,
+                                  const void *QR, const void *KV, const void *KR, void *O,
+                                  hipStream_t stream, hipEvent_t ev0 = nullptr,
+                                  hipEvent_t ev1 = nullptr);
+bool heads_attention_supported(int dtype, int H, int d_h, int dR);
 
 }  // namespace mtla

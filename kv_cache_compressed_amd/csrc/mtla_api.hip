@@ -142,6 +142,28 @@ PrefillWs prefill_ws(const mtla_dims *d, int B, int T) {
   return w;
 }
 
+// Workspace of the per-head (unabsorbed) parallel form.
+struct HeadsWs {
+  size_t cg, Cp, keys, q, KV, O, total;
+  int64_t keys_stride;
+};
+
+HeadsWs heads_ws(const mtla_dims *d, int B, int T) {
+  HeadsWs w;
+  const size_t e = esize(d), r = d->r, HD = (size_t)d->H * d->d_h, M = (size_t)B * T;
+  const int64_t nS = (T + d->s - 1) / d->s;
+  w.keys_stride = nS * (d->r + d->d_hR);
+  size_t off = 0;
+  w.cg = off;    off += align_up(M * 2 * r * 4);
+  w.Cp = off;    off += align_up(M * r * e);
+  w.keys = off;  off += align_up((size_t)B * w.keys_stride * e);
+  w.q = off;     off += align_up(M * HD * e);
+  w.KV = off;    off += align_up(M * 2 * HD * e);
+  w.O = off;     off += align_up(M * HD * e);
+  w.total = off;
+  return w;
+}
+
 // Workspace of a chunked merge-append of L frames: cg [B*L, 2r] fp32.
 size_t chunk_ws(const mtla_dims *d, int B, int L) {
   return align_up((size_t)B * L * 2 * d->r * 4);
@@ -192,6 +214,10 @@ size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_
     return prefill_ws(dims, B, T_or_max_pos).total;
   }
   if (op == 3) return chunk_ws(dims, B, T_or_max_pos);
+  if (op == 4) {
+    if (T_or_max_pos < 1) return 0;
+    return heads_ws(dims, B, T_or_max_pos).total;
+  }
   return 0;
 }
 
@@ -385,9 +411,93 @@ mtla_status prefill_impl(const mtla_dims *dims, const mtla_weights *w, const voi
   return ok();
 }
 
+mtla_status prefill_unabsorbed_impl(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                                   const void *X, const void *QR, const void *KR, int32_t B,
+                                   int32_t T, void *Y, const mtla_cache *cache_out,
+                                   void *Cprime_out, void *workspace, size_t ws_bytes,
+                                   void *stream, void *const *events) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if (!w) return fail(MTLA_ERR_ARG, "weights is null");
+  CHECK_PTR(w->W_dkv);
+  CHECK_PTR(w->W_gate);
+  CHECK_PTR(w->b_hc);
+  CHECK_PTR(w->gate_pos);
+  if (w->gate_pos_rows <= 0) return fail(MTLA_ERR_ARG, "gate_pos_rows=%d", w->gate_pos_rows);
+  CHECK_PTR(w->W_Q);
+  CHECK_PTR(w->W_K);
+  CHECK_PTR(w->W_V);
+  CHECK_PTR(w->W_O);
+  CHECK_PTR(X);
+  CHECK_PTR(QR);
+  CHECK_PTR(KR);
+  CHECK_PTR(Y);
+  CHECK_PTR(workspace);
+  if (Cprime_out && !aligned16(Cprime_out)) return fail(MTLA_ERR_ARG, "Cprime_out is not 16-byte aligned");
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (T < 1) return fail(MTLA_ERR_ARG, "T=%d < 1", T);
+  if ((int64_t)B * T * dims->H * dims->d_h > 0x7fffffffLL / 4)
+    return fail(MTLA_ERR_UNSUPPORTED, "B*T*H*d_h too large");
+  if (!mtla::heads_attention_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR))
+    return fail(MTLA_ERR_UNSUPPORTED, "per-head form needs bf16 storage, d_h = 64, d_hR = 32");
+  const int nS = (T + dims->s - 1) / dims->s;
+  if ((T - 1) / dims->s >= w->gate_pos_rows)
+    return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
+  if (cache_out) {
+    if ((st = check_cache(dims, cache_out)) != MTLA_OK) return st;
+    if (nS > cache_out->max_slots)
+      return fail(MTLA_ERR_CAPACITY, "ceil(T/s)=%d > max_slots %d", nS, cache_out->max_slots);
+  }
+  const HeadsWs ws = heads_ws(dims, B, T);
+  if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  float *cg = (float *)(base + ws.cg);
+  void *keys = base + ws.keys, *q = base + ws.q, *KV = base + ws.KV, *O = base + ws.O;
+  void *Cp = Cprime_out ? Cprime_out : (void *)(base + ws.Cp);
+  const int M = B * T, HD = dims->H * dims->d_h;
+  LAUNCH(mtla::launch_proj(dims->dtype, X, M, dims->d, w->W_dkv, w->W_gate, dims->r, w->W_Q, HD,
+                           cg, q, nullptr, 0, s),
+         "latent, gate and query projection");
+  LAUNCH(mtla::launch_group_scan(dims->dtype, cg, w->b_hc, w->gate_pos, KR, B, T, dims->r,
+                                 dims->d_hR, dims->s, Cp, keys, ws.keys_stride,
+                                 cache_out ? cache_out->slots : nullptr,
+                                 cache_out ? cache_out->batch_stride : 0, s),
+         "gate and group scan");
+  LAUNCH(mtla::launch_gemm_store2(dims->dtype, Cp, dims->r, w->W_K, w->W_V, HD, dims->r, M, 2 * HD,
+                                  dims->r, KV, 2 * HD, s),
+         "per-head key and value projection");
+  LAUNCH(mtla::launch_heads_attention(B, T, dims->H, dims->s, eff_scale(dims), q, QR, KV, KR, O, s,
+                                      ev0(events), ev1(events)),
+         "per-head strided attention");
+  LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HD, w->W_O, dims->d, Y, nullptr, nullptr, s),
+         "output projection");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                                    const void *X, const void *QR, const void *KR, int32_t B,
+                                    int32_t T, void *Y, const mtla_cache *cache_out,
+                                    void *Cprime_out, void *workspace, size_t ws_bytes,
+                                    void *stream) {
+  return prefill_unabsorbed_impl(dims, w, X, QR, KR, B, T, Y, cache_out, Cprime_out, workspace,
+                                 ws_bytes, stream, nullptr);
+}
+
+mtla_status mtla_prefill_unabsorbed_timed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                                          const void *X, const void *QR, const void *KR,
+                                          int32_t B, int32_t T, void *Y,
+                                          const mtla_cache *cache_out, void *Cprime_out,
+                                          void *workspace, size_t ws_bytes, void *stream,
+                                          void *const *events) {
+  if (!events || !events[0] || !events[1]) return fail(MTLA_ERR_ARG, "events must hold two handles");
+  return prefill_unabsorbed_impl(dims, w, X, QR, KR, B, T, Y, cache_out, Cprime_out, workspace,
+                                 ws_bytes, stream, events);
+}
 
 mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                              const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,

@@ -16,8 +16,10 @@ from . import _lib as L
 class MTLALayer:
     WEIGHTS = ("W_dkv", "W_hc", "b_hc", "W_hp", "b_hp", "pe", "A", "Bvo")
 
+    HEAD_MAPS = ("W_Qh", "W_Kh", "W_Vh", "W_Oh")
+
     def __init__(self, d, H, d_h, r, d_hR, s, dtype=L.MTLA_BF16, scale=0.0, *, W_dkv, W_hc, b_hc,
-                 W_hp, b_hp, pe, A, Bvo):
+                 W_hp, b_hp, pe, A, Bvo, W_Qh=None, W_Kh=None, W_Vh=None, W_Oh=None):
         self.dims = L.make_dims(d, H, d_h, r, d_hR, s, dtype, scale)
         self.dtype = L.torch_dtype(dtype)
         self.t = dict(W_dkv=W_dkv, W_hc=W_hc, b_hc=b_hc, W_hp=W_hp, b_hp=b_hp, pe=pe, A=A, Bvo=Bvo)
@@ -27,6 +29,15 @@ class MTLALayer:
         self.gate_pos = L.mtla_gate_pos_table(self.dims, pe, W_hp, b_hp)
         self.W_gate = L.mtla_gate_content_map(self.dims, W_hc, W_dkv)
         self.w = L.make_weights(W_dkv, self.W_gate, b_hc, self.gate_pos, A, Bvo)
+        # Optional per-head maps ([out, in] layouts) for the unabsorbed form.
+        self.heads = dict(W_Qh=W_Qh, W_Kh=W_Kh, W_Vh=W_Vh, W_Oh=W_Oh)
+        self.wu = None
+        if all(v is not None for v in self.heads.values()):
+            for k, v in self.heads.items():
+                if v.dtype != self.dtype or not v.is_cuda or not v.is_contiguous():
+                    raise ValueError(f"{k} must be a contiguous device tensor of {self.dtype}")
+            self.wu = L.make_unabsorbed_weights(W_dkv, self.W_gate, b_hc, self.gate_pos, W_Qh,
+                                                W_Kh, W_Vh, W_Oh)
         self._ws = {}
 
     @classmethod
@@ -35,6 +46,9 @@ class MTLALayer:
         the ABI layouts.  ``dims`` has attributes d, H, d_h, r, d_hR, s."""
         td = L.torch_dtype(dtype)
         t = {k: torch.as_tensor(arrays[k]).to(td).to(device).contiguous() for k in cls.WEIGHTS}
+        for k in cls.HEAD_MAPS:
+            if k in arrays:
+                t[k] = torch.as_tensor(arrays[k]).to(td).to(device).contiguous()
         return cls(dims.d, dims.H, dims.d_h, dims.r, dims.d_hR, dims.s, dtype, scale, **t)
 
     @property
@@ -73,3 +87,12 @@ class MTLALayer:
         return L.mtla_prefill_strided(self.dims, self.w, X, QR, KR, Y, c, Cprime,
                                       self.workspace(L.OP_PREFILL, X.shape[0], X.shape[1]),
                                       events)
+
+    def prefill_unabsorbed(self, X, QR, KR, Y=None, cache: torch.Tensor | None = None,
+                           Cprime=None, events=None):
+        if self.wu is None:
+            raise ValueError("the layer was built without the per-head maps W_Qh, W_Kh, W_Vh, W_Oh")
+        c = L.make_cache(cache) if cache is not None else None
+        return L.mtla_prefill_unabsorbed(self.dims, self.wu, X, QR, KR, Y, c, Cprime,
+                                         self.workspace(L.OP_UNABSORBED, X.shape[0], X.shape[1]),
+                                         events)

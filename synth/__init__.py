@@ -155,9 +155,23 @@ def make_weights(dims: Dims, seed: int, storage: str = "f64", pe_rows: int = 64)
     w["A"] = np.matmul(w["W_K"], np.transpose(w["W_Q"], (0, 2, 1)))          # [H, r, d]
     w["Bvo"] = np.transpose(np.matmul(w["W_V"], w["W_O"]), (2, 0, 1)).copy()  # [d, H, r]
     w["pe"] = sinusoidal_table(pe_rows, d_pe)
-    for k in ("W_dkv", "W_hc", "b_hc", "W_hp", "b_hp", "A", "Bvo", "pe"):
+    # The per-head factors are rounded after A and Bvo are formed from them.
+    for k in ("W_dkv", "W_hc", "b_hc", "W_hp", "b_hp", "A", "Bvo", "pe",
+              "W_Q", "W_K", "W_V", "W_O"):
         w[k] = round_to(w[k], storage)
     return w
+
+
+def head_maps(w: dict) -> dict:
+    """The per-head maps of ``w`` in the library's [out, in] layouts, same
+    values: W_Qh [H*d_h, d] (rows of head h map x to its query), W_Kh and
+    W_Vh [H*d_h, r], W_Oh [d, H*d_h] (columns of head h)."""
+    H, d, d_h = w["W_Q"].shape
+    r = w["W_K"].shape[1]
+    return dict(W_Qh=np.transpose(w["W_Q"], (0, 2, 1)).reshape(H * d_h, d).copy(),
+                W_Kh=np.transpose(w["W_K"], (0, 2, 1)).reshape(H * d_h, r).copy(),
+                W_Vh=np.transpose(w["W_V"], (0, 2, 1)).reshape(H * d_h, r).copy(),
+                W_Oh=np.transpose(w["W_O"], (2, 0, 1)).reshape(d, H * d_h).copy())
 
 
 def make_sequence(dims: Dims, w: dict, B: int, T: int, seed: int, storage: str = "f64",

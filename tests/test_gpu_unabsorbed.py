@@ -1,0 +1,116 @@
+"""GPU parity of mtla_prefill_unabsorbed (the per-head form of the parallel
+forward) against the oracle's per-head attention over its intermediate
+states."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.mtla as om
+import synth
+from synth import Dims
+from gpu_util import TOL, dev, host, needs_gpu, relerr, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(dims, seed, pe_rows):
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    w = synth.make_weights(dims, seed, "bf16", pe_rows=pe_rows)
+    W = om.with_position_table(w, pe_rows)
+    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    return w, W, L
+
+
+def _case(dims, B, T, seed):
+    ms = om.n_slots(T, dims.s) + 2
+    w, W, L = _layer(dims, seed, ms)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, "bf16")
+    cache = L.new_cache(B, ms, fill=float("nan"))
+    Cp = torch.empty(B, T, dims.r, dtype=L.dtype, device="cuda")
+    Y = L.prefill_unabsorbed(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"),
+                             dev(seq["KR"], "bf16"), cache=cache, Cprime=Cp)
+    torch.cuda.synchronize()
+    Yg, Cpg, cg = host(Y), host(Cp), host(cache)
+    n = om.n_slots(T, dims.s)
+    for b in range(B):
+        X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
+        ref = om.prefill(X, QR, KR, W, dims.s, dims.scale)
+        yref = om.mha_unabsorbed(X, QR, KR, ref["Cp"], W["W_Q"], W["W_K"], W["W_V"], W["W_O"],
+                                 dims.s, dims.scale)
+        ey, ec = relerr(Yg[b], yref), relerr(Cpg[b], ref["Cp"])
+        say(f"  b={b} Y relerr {ey:.3g}  C' relerr {ec:.3g}")
+        assert ey < TOL["bf16"], (b, ey)
+        assert ec < TOL["bf16"], (b, ec)
+        assert relerr(cg[b, :n, :dims.r], ref["cache_lat"]) < TOL["bf16"]
+        assert np.array_equal(cg[b, :n, dims.r:], ref["cache_rope"])
+        assert np.all(np.isnan(cg[b, n:]))
+
+
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 8, 1), (2, 300, 8, 2), (3, 257, 8, 1), (1, 64, 4, 2),
+                                       (4, 513, 8, 1), (80, 100, 2, 1), (2, 130, 16, 1),
+                                       (5, 96, 3, 3)])
+def test_unabsorbed_matches_oracle(s, T, H, B):
+    needs_gpu()
+    dims = Dims(d=512, H=H, d_h=64, r=256, d_hR=32, s=s)
+    say("prefill per-head", s, T, H, B)
+    _case(dims, B, T, 9000 + 13 * s + T + H)
+
+
+def test_unabsorbed_full_size_sampled():
+    """The benchmark's per-head launch (B=16, T=4096, s=2), checked on
+    sampled rows of two sequences against the oracle's per-head attention of
+    each sampled row."""
+    needs_gpu()
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    ms = om.n_slots(T, dims.s)
+    w, W, L = _layer(dims, synth.seed_for(4), ms)
+    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    Cp = torch.empty(B, T, dims.r, dtype=L.dtype, device="cuda")
+    Y = L.prefill_unabsorbed(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"),
+                             dev(seq["KR"], "bf16"), Cprime=Cp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9100)
+    for b in (0, B - 1):
+        X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
+        _, U = om.gated_latents(X, W, dims.s)
+        Cpr = om.intermediate_states(U, dims.s)
+        assert relerr(host(Cp[b]), Cpr) < TOL["bf16"]
+        rows = np.unique(np.concatenate([[0, 1, 2, 255, 256, T - 2, T - 1],
+                                         rng.integers(0, T, size=24)]))
+        Yg = host(Y[b])[rows]
+        Yr = []
+        for m in rows:
+            vis = [n for n in range(m + 1) if om.visible(m, n, dims.s)]
+            y = np.zeros(dims.d)
+            for h in range(dims.H):
+                q = X[m] @ W["W_Q"][h]
+                K = Cpr[vis] @ W["W_K"][h]
+                V = Cpr[vis] @ W["W_V"][h]
+                z = (K @ q + KR[vis] @ QR[m, h]) * dims.scale
+                p = np.exp(z - z.max())
+                y += (p / p.sum()) @ V @ W["W_O"][h]
+            Yr.append(y)
+        e = relerr(Yg, np.stack(Yr))
+        say(f"  b={b} sampled-row relerr {e:.3g}")
+        assert e < TOL["bf16"]
+
+
+def test_unabsorbed_equals_absorbed_form():
+    """The two forms of the parallel forward agree on the same layer (both
+    against their own oracle in the tests above; here directly, bf16 vs bf16,
+    within the bf16 tolerance)."""
+    needs_gpu()
+    dims = Dims(d=512, H=8, d_h=64, r=256, d_hR=32, s=2)
+    T, B = 700, 2
+    ms = om.n_slots(T, dims.s)
+    w, W, L = _layer(dims, 9200, ms)
+    seq = synth.make_sequence(dims, w, B, T, 9201, "bf16")
+    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
+    Ya = host(L.prefill(X, QR, KR))
+    Yu = host(L.prefill_unabsorbed(X, QR, KR))
+    torch.cuda.synchronize()
+    # the absorbed maps come from unrounded factors: compare at 2x the bf16 bar
+    e = relerr(Yu, Ya)
+    say(f"  absorbed vs per-head relerr {e:.3g}")
+    assert e < 2 * TOL["bf16"]
