@@ -55,20 +55,29 @@ struct HeadsArgs {
   float sl2;        // scale * log2(e)
 };
 
+#ifndef MTLA_HEADS_WAVES
+#define MTLA_HEADS_WAVES 4
+#endif
+#ifndef MTLA_HEADS_NST
+#define MTLA_HEADS_NST 5
+#endif
+
 struct HdCfg {
   static constexpr int DH = 64, DR = 32, QK = DH + DR;   // 96 score channels
   static constexpr int RB = (QK + DH) * 2;                // LDS key row K | K^R | V: 320 B
   static constexpr int NSEG = RB / 64;                    // 64-byte blocks per row
   static constexpr int VOFF = QK * 2;                     // byte offset of V in a key row
   static constexpr int KS = QK / 32, MB = DH / 16;        // 3 k-steps, 4 channel blocks
-  static constexpr int NQ = 4, ROWS_W = 16 * NQ, ROWS = 4 * ROWS_W;
+  static constexpr int NW = MTLA_HEADS_WAVES;            // waves per workgroup
+  static constexpr int NQ = 4, ROWS_W = 16 * NQ, ROWS = NW * ROWS_W;
   static constexpr int SROWS = 32, TILE_B = 16 * RB, STAGE_B = 2 * TILE_B;
-  static constexpr int NBLK = 2 * NSEG, LPW = (NBLK + 3) / 4;
-  static constexpr int NST = 5;        // ring stages (>= 3: slots k, k+1 and the refill)
+  static constexpr int NBLK = 2 * NSEG, LPW = (NBLK + NW - 1) / NW;
+  static constexpr int NST = MTLA_HEADS_NST;   // ring stages (>= 3: slots k, k+1 and the refill)
+  static_assert(NST >= 3, "the pipeline reads two stages while a third is refilled");
   static_assert(NSEG == 5 && VOFF == 192, "block map of the key rows");
 };
 
-__global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
+__global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kernel(HeadsArgs a) {
   using C = HdCfg;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
     const int row0 = sidx * C::SROWS;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
-      const int blk = wave + 4 * i;
+      const int blk = wave + C::NW * i;
       const bool real = blk < C::NBLK;
       const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
       const int key = min(row0 + tl * 16 + (lane >> 2), kmax - 1);
@@ -173,33 +182,40 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
   const int wst = (wlim + C::SROWS - 1) / C::SROWS;
   const int wmin = rw < Tn ? rw / s : 0;
 
-  // S^T of stage kk for both 16-key tiles; each K fragment feeds NQ products.
-  auto scores = [&](int kk, f32x4 (&sc)[2][C::NQ]) {
+  // K^T fragments of stage kk (row c of each tile, this lane group's chunk
+  // of every k-step), and S^T of one tile from them: each fragment feeds NQ
+  // products.
+  auto read_k = [&](int kk, bf16x8 (&kf)[2][C::KS]) {
     const char *sb = smem + (kk % nst) * C::STAGE_B;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int qi = 0; qi < C::NQ; ++qi) sc[t][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < C::KS; ++ks)
+        kf[t][ks] = *(const bf16x8 *)(sb + t * C::TILE_B + tile_off(c, ks * 64 + g * 16));
+  };
+  auto mma_tile = [&](const bf16x8 (&kf)[C::KS], f32x4 (&sc)[C::NQ]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const char *tile = sb + t * C::TILE_B;
+    for (int qi = 0; qi < C::NQ; ++qi) sc[qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, ks * 64 + g * 16));
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int qi = 0; qi < C::NQ; ++qi) sc[t][qi] = mma_k32(af, q[qi][ks], sc[t][qi]);
-      }
-    }
+      for (int qi = 0; qi < C::NQ; ++qi) sc[qi] = mma_k32(kf[ks], q[qi][ks], sc[qi]);
   };
 
   // Software pipeline: the scores of stage k+1 are computed while the
-  // softmax of stage k runs, so that each wave has matrix products to issue
-  // between its dependent vector operations.
+  // softmax of stage k runs -- tile 0's products beside the row maxima,
+  // tile 1's beside the exponentials -- so that each wave has matrix
+  // products to issue between its dependent vector operations.
   f32x4 scur[2][C::NQ];
   if (nstage > 0) {
     wait_stages<C::LPW>(last);           // stage 0
     bar();
-    if (wst > 0) scores(0, scur);
+    if (wst > 0) {
+      bf16x8 kf[2][C::KS];
+      read_k(0, kf);
+      mma_tile(kf[0], scur[0]);
+      mma_tile(kf[1], scur[1]);
+    }
   }
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
   for (int k = 0; k < nstage; ++k) {
@@ -217,11 +233,15 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
     const char *sb = smem + (k % nst) * C::STAGE_B;
     const int kb = k * C::SROWS;
 
-    // V^T fragments of stage k: lane (g, c) addresses row 4g + c/4, channels
-    // 16 mb + 4 (c%4)..+3; the transposing read hands it channel 16 mb + c of
-    // keys 4g..4g+3 (tile 0: low half, tile 1: high half).  The eight reads
-    // go out in one asm statement (ds_read_tr8): the builtin form would make
-    // the compiler wait for every direct-to-LDS load in flight first.
+    // K^T of stage k+1 (past the last stage the slot holds stale data whose
+    // products go unused), then V^T of stage k: lane (g, c) addresses row
+    // 4g + c/4, channels 16 mb + 4 (c%4)..+3; the transposing read hands it
+    // channel 16 mb + c of keys 4g..4g+3 (tile 0: low half, tile 1: high
+    // half).  The eight transposing reads go out in one asm statement that
+    // waits for all of this wave's LDS reads (ds_read_tr8): the builtin form
+    // would make the compiler wait for every direct-to-LDS load in flight.
+    bf16x8 kf[2][C::KS];
+    read_k(k + 1, kf);
     bf16x8 vf[C::MB];
     {
       uint32_t ad[8];
@@ -238,10 +258,6 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
         vf[mb] = __builtin_shufflevector(vv[2 * mb], vv[2 * mb + 1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
-    const bool nxt = k + 1 < wst;
-    f32x4 snext[2][C::NQ];
-    if (nxt) scores(k + 1, snext);
-
     // Online softmax of stage k per row (lane holds keys 4g..4g+3 of each
     // tile), in log2 units; the reference maximum moves only by steps > 2^8.
     // Keys a row cannot see become -inf (only on stages that reach past the
@@ -255,6 +271,8 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
           for (int e = 0; e < 4; ++e)
             if (!(kb + 16 * t + 4 * g + e < lim[qi])) scur[t][qi][e] = kNegInfH;
     }
+    f32x4 snext[2][C::NQ];
+    mma_tile(kf[0], snext[0]);
     bool up_any = false;
     float mnew[C::NQ];
 #pragma unroll
@@ -266,6 +284,11 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
       mnew[qi] = up ? mx : m[qi];
       up_any |= up;
     }
+#pragma unroll
+    for (int i = 0; i < C::KS * C::NQ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+    }
     if (__builtin_amdgcn_ballot_w64(up_any)) {
 #pragma unroll
       for (int qi = 0; qi < C::NQ; ++qi) {
@@ -276,6 +299,7 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
         m[qi] = mnew[qi];
       }
     }
+    mma_tile(kf[1], snext[1]);
     bf16x8 pf[C::NQ];
 #pragma unroll
     for (int qi = 0; qi < C::NQ; ++qi) {
@@ -290,6 +314,11 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
         l[qi] = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pf[qi][e], pf[qi][e + 1]}, ones, l[qi],
                                                 false);
     }
+#pragma unroll
+    for (int i = 0; i < C::KS * C::NQ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    }
 
     // O^T += V^T P^T; each V^T fragment feeds NQ products.
 #pragma unroll
@@ -297,12 +326,10 @@ __global__ __launch_bounds__(256, 2) void heads_attn_kernel(HeadsArgs a) {
 #pragma unroll
       for (int qi = 0; qi < C::NQ; ++qi) o[qi][mb] = mma_k32(vf[mb], pf[qi], o[qi][mb]);
 
-    if (nxt) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int qi = 0; qi < C::NQ; ++qi) scur[t][qi] = snext[t][qi];
-    }
+      for (int qi = 0; qi < C::NQ; ++qi) scur[t][qi] = snext[t][qi];
   }
 
   // O = O^T / l, row (b, m), columns h*DH + channel.
@@ -340,7 +367,7 @@ hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const
   if (!(sl2 >= FLT_MIN)) sl2 = FLT_MIN;
   HeadsArgs args{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
                  (bf16 *)O, B, T, H, s, tiles, nst, sl2};
-  return launch_timed((const void *)heads_attn_kernel, dim3(tiles * B * H), dim3(256), lds,
+  return launch_timed((const void *)heads_attn_kernel, dim3(tiles * B * H), dim3(64 * C::NW), lds,
                       stream, &args, ev0, ev1);
 }
 
