@@ -315,6 +315,93 @@ def mha_unabsorbed(X, QR, KR, Cp, W_Q, W_K, W_V, W_O, s, scale):
     return Y
 
 
+def prefill_unabsorbed(X, QR, KR, W, s, scale):
+    """Parallel forward in the per-head form: the gate and group sums of the
+    strided prefill, then ``mha_unabsorbed``.  W holds the hyper-network
+    (W_dkv, W_hc, b_hc, P) and the per-head maps W_Q [H, d, d_h],
+    W_K, W_V [H, r, d_h], W_O [H, d_h, d].  Returns dict(Y, Cp)."""
+    _, U = gated_latents(X, W, s)
+    Cp = intermediate_states(U, s)
+    Y = mha_unabsorbed(X, QR, KR, Cp, W["W_Q"], W["W_K"], W["W_V"], W["W_O"], s, scale)
+    return dict(Y=Y, Cp=Cp)
+
+
+# ---------------------------------------------------------------------------
+# backward of the per-head parallel form (the gradients that training under
+# the stride-aware mask needs: [Notes] stride-aware causal mask, the parallel
+# training it enables; [Fig2] (c)), by the chain rule through the forward
+# steps above, last step first
+# ---------------------------------------------------------------------------
+
+
+def prefill_unabsorbed_backward(X, QR, KR, W, s, scale, dY):
+    """Gradients of <dY, Y> for Y = prefill_unabsorbed(X, QR, KR, W, s, scale).
+
+    Returns dict with dX [T, d], dQR [T, H, d_hR], dKR [T, d_hR], and the
+    weight gradients dW_dkv [r, d], dW_hc [r, r], db_hc [r], dP [rows, r]
+    (rows of the position-branch table P = Linear(pe_j)), dW_Q [H, d, d_h],
+    dW_K, dW_V [H, r, d_h], dW_O [H, d_h, d]."""
+    T = X.shape[0]
+    H = W["W_Q"].shape[0]
+    C, U = gated_latents(X, W, s)
+    Cp = intermediate_states(U, s)
+    Mk = mask_matrix(T, s)
+    g = {k: np.zeros_like(W[k]) for k in ("W_dkv", "W_hc", "b_hc", "P", "W_Q", "W_K", "W_V",
+                                           "W_O")}
+    dX = np.zeros_like(X)
+    dQR = np.zeros_like(QR)
+    dKR = np.zeros_like(KR)
+    dCp = np.zeros_like(Cp)
+    # attention, head by head: Y = sum_h softmax(Z_h) V_h W_O^(h)
+    for h in range(H):
+        Q = X @ W["W_Q"][h]
+        K = Cp @ W["W_K"][h]
+        V = Cp @ W["W_V"][h]
+        Z = np.where(Mk, (Q @ K.T + QR[:, h, :] @ KR.T) * scale, -np.inf)
+        Pm = softmax_rows(Z)
+        O = Pm @ V
+        g["W_O"][h] = O.T @ dY
+        dO = dY @ W["W_O"][h].T
+        dPm = dO @ V.T
+        dV = Pm.T @ dO
+        # softmax rows: dZ = P * (dP - <dP, P>_row); then the logit scale
+        dZ = Pm * (dPm - np.sum(dPm * Pm, axis=1, keepdims=True)) * scale
+        dQ = dZ @ K
+        dK = dZ.T @ Q
+        dQR[:, h, :] = dZ @ KR
+        dKR += dZ.T @ QR[:, h, :]
+        g["W_Q"][h] = X.T @ dQ
+        dX += dQ @ W["W_Q"][h].T
+        g["W_K"][h] = Cp.T @ dK
+        g["W_V"][h] = Cp.T @ dV
+        dCp += dK @ W["W_K"][h].T + dV @ W["W_V"][h].T
+    # group sums: C'_i = sum of U over the frames of i's group up to i, so
+    # dU_i = sum of dC' over the frames of i's group from i on
+    dU = np.empty_like(dCp)
+    for i in range(T - 1, -1, -1):
+        if i % s == s - 1 or i == T - 1:
+            dU[i] = dCp[i]
+        else:
+            dU[i] = dCp[i] + dU[i + 1]
+    # gate, frame by frame: a = W_hc c + b_hc, w = Sigmoid(a * P_j), u = w * c
+    for i in range(T):
+        j = slot_of(i, s)
+        c = C[i]
+        a = W["W_hc"] @ c + W["b_hc"]
+        w = sigmoid(a * W["P"][j])
+        dw = dU[i] * c
+        dgate = dw * w * (1.0 - w)
+        da = dgate * W["P"][j]
+        g["P"][j] += dgate * a
+        g["b_hc"] += da
+        g["W_hc"] += np.outer(da, c)
+        dc = dU[i] * w + W["W_hc"].T @ da
+        g["W_dkv"] += np.outer(dc, X[i])
+        dX[i] += W["W_dkv"].T @ dc
+    return dict(dX=dX, dQR=dQR, dKR=dKR, dW_dkv=g["W_dkv"], dW_hc=g["W_hc"], db_hc=g["b_hc"],
+                dP=g["P"], dW_Q=g["W_Q"], dW_K=g["W_K"], dW_V=g["W_V"], dW_O=g["W_O"])
+
+
 # ---------------------------------------------------------------------------
 # reference forms used only to pin the ones above
 # ---------------------------------------------------------------------------

@@ -322,6 +322,41 @@ def pin_unabsorbed_matches_sdpa():
         assert relerr(ref, Y) < 1e-12, (s, T, relerr(ref, Y))
 
 
+def pin_backward_matches_finite_differences():
+    """Every gradient of the per-head parallel form against central finite
+    differences of the (separately pinned) forward: for a random direction V
+    of each input and weight, <grad, V> equals (L(+eps V) - L(-eps V)) / 2eps
+    with L = <dY, Y>, in fp64.  Partial last groups (T mod s != 0) and s = 1
+    included."""
+    rng = np.random.default_rng(1301)
+    for s, T in ((3, 10), (2, 9), (1, 6)):
+        dims = Dims(d=16, H=2, d_h=4, r=8, d_hR=4, s=s)
+        W = synth.make_weights(dims, 1300 + s, "f64", pe_rows=om.n_slots(T, s) + 1)
+        W = om.with_position_table(W, W["pe"].shape[0])
+        seq = synth.make_sequence(dims, W, 1, T, 1310 + s, "f64")
+        inp = dict(X=seq["X"][0], QR=seq["QR"][0], KR=seq["KR"][0])
+        dY = rng.normal(size=(T, dims.d))
+        gr = om.prefill_unabsorbed_backward(inp["X"], inp["QR"], inp["KR"], W, s, dims.scale, dY)
+
+        def loss(i, w):
+            return float(np.sum(om.prefill_unabsorbed(i["X"], i["QR"], i["KR"], w, s,
+                                                      dims.scale)["Y"] * dY))
+        eps = 1e-5
+        for name, key in (("dX", "X"), ("dQR", "QR"), ("dKR", "KR")):
+            V = rng.normal(size=inp[key].shape)
+            fd = (loss({**inp, key: inp[key] + eps * V}, W)
+                  - loss({**inp, key: inp[key] - eps * V}, W)) / (2 * eps)
+            an = float(np.sum(gr[name] * V))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (s, name, fd, an)
+        for name, key in (("dW_dkv", "W_dkv"), ("dW_hc", "W_hc"), ("db_hc", "b_hc"), ("dP", "P"),
+                          ("dW_Q", "W_Q"), ("dW_K", "W_K"), ("dW_V", "W_V"), ("dW_O", "W_O")):
+            V = rng.normal(size=W[key].shape)
+            fd = (loss(inp, {**W, key: W[key] + eps * V})
+                  - loss(inp, {**W, key: W[key] - eps * V})) / (2 * eps)
+            an = float(np.sum(gr[name] * V))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (s, name, fd, an)
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
@@ -473,4 +508,5 @@ ALL_PINS = [
     pin_s1_is_causal_mla, pin_any_s_matches_sdpa, pin_half_gate_group_mean, pin_large_s_limit,
     pin_uniform_softmax, pin_first_step, pin_predownsampling_differs,
     pin_chunked_append_equals_prefill, pin_chunk_continues_live_slot, pin_unabsorbed_matches_sdpa,
+    pin_backward_matches_finite_differences,
 ]

@@ -157,6 +157,41 @@ def _mut_unabsorbed_causal_mask(mp):
     mp.setattr(om, "mha_unabsorbed", mha)
 
 
+def _edit_backward(mp, old, new):
+    """Replace one expression in a copy of the oracle's backward."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(om.prefill_unabsorbed_backward))
+    assert old in src, old
+    ns = dict(vars(om))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    mp.setattr(om, "prefill_unabsorbed_backward", ns["prefill_unabsorbed_backward"])
+
+
+def _mut_bwd_no_softmax_correction(mp):
+    _edit_backward(mp, "(dPm - np.sum(dPm * Pm, axis=1, keepdims=True))", "dPm")
+
+
+def _mut_bwd_scan_not_accumulated(mp):
+    _edit_backward(mp, "dU[i] = dCp[i] + dU[i + 1]", "dU[i] = dCp[i]")
+
+
+def _mut_bwd_no_sigmoid_derivative(mp):
+    _edit_backward(mp, "dgate = dw * w * (1.0 - w)", "dgate = dw * w")
+
+
+def _mut_bwd_transposed_whc(mp):
+    _edit_backward(mp, 'W["W_hc"].T @ da', 'W["W_hc"] @ da')
+
+
+def _mut_bwd_rope_keys_one_head(mp):
+    _edit_backward(mp, "dKR += dZ.T @ QR[:, h, :]", "dKR = dZ.T @ QR[:, h, :]")
+
+
+def _mut_bwd_missing_scale(mp):
+    _edit_backward(mp, "keepdims=True)) * scale", "keepdims=True))")
+
+
 MUTANTS = [
     _mut_group_final_zero, _mut_drop_rope, _mut_transpose_whc, _mut_position_by_frame,
     _mut_additive_gate, _mut_no_reset, _mut_rope_key_first_frame, _mut_plain_prefix_sum,
@@ -164,6 +199,8 @@ MUTANTS = [
     _mut_scale_with_rope_width, _mut_sigmoid_sign, _mut_decode_excludes_newest,
     _mut_chunk_opens_fresh, _mut_chunk_relative_positions, _mut_chunk_state_before_merge,
     _mut_unabsorbed_values_from_keys, _mut_unabsorbed_causal_mask,
+    _mut_bwd_no_softmax_correction, _mut_bwd_scan_not_accumulated, _mut_bwd_no_sigmoid_derivative,
+    _mut_bwd_transposed_whc, _mut_bwd_rope_keys_one_head, _mut_bwd_missing_scale,
 ]
 
 
