@@ -225,6 +225,40 @@ mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed
                                     void *Cprime_out, void *workspace, size_t ws_bytes,
                                     void *stream);
 
+/* Gradients of the per-head form's weights (device pointers, FP32,
+ * overwritten by mtla_prefill_unabsorbed_backward), in the layouts of the
+ * weights themselves. */
+typedef struct {
+  float *dW_dkv;     /* [r, d] */
+  float *dW_hc;      /* [r, r]  the content-branch weight W_hc (the pages' parameter) */
+  float *db_hc;      /* [r] */
+  float *dgate_pos;  /* [gate_pos_rows, r] the position-branch table Linear(pe_j) */
+  float *dW_Q;       /* [H*d_h, d] */
+  float *dW_K;       /* [H*d_h, r] */
+  float *dW_V;       /* [H*d_h, r] */
+  float *dW_O;       /* [d, H*d_h] */
+} mtla_unabsorbed_grads;
+
+/* Backward of mtla_prefill_unabsorbed ([Notes] stride-aware causal mask: the
+ * parallel form is what training runs; [Fig2] (c)): for the loss gradient
+ * dY [B, T, d], the gradients of <dY, Y> with respect to the inputs --
+ * dX [B, T, d], dQR [B, T, H, d_hR], dKR [B, T, d_hR] (storage dtype) -- and
+ * to every weight (FP32, `grads`): through the output map, the masked
+ * softmax (scores recomputed), the key, value and query maps, the group sums
+ * (a reverse scan inside each group) and the sigmoid gate.  The gate's
+ * content branch is differentiated in the pages' form, Linear(c) = W_hc c +
+ * b_hc, so W_hc [r, r] (storage dtype) is passed besides the folded W_gate
+ * the forward uses; the position branch is differentiated as its table.
+ * The forward is recomputed inside.  Supported: bf16 storage, d_h = 64,
+ * d_hR = 32.  Workspace: mtla_workspace_bytes(op=5, B, T). */
+mtla_status mtla_prefill_unabsorbed_backward(const mtla_dims *dims,
+                                             const mtla_unabsorbed_weights *w, const void *W_hc,
+                                             const void *X, const void *QR, const void *KR,
+                                             int32_t B, int32_t T, const void *dY, void *dX,
+                                             void *dQR, void *dKR,
+                                             const mtla_unabsorbed_grads *grads, void *workspace,
+                                             size_t ws_bytes, void *stream);
+
 /* Profiling variants of mtla_decode_step, mtla_prefill_strided and
  * mtla_prefill_unabsorbed: the same
  * computation, and in addition the attention kernel (the split-K decode
@@ -252,8 +286,8 @@ mtla_status mtla_prefill_unabsorbed_timed(const mtla_dims *dims, const mtla_unab
 
 /* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
  * T_or_max_pos = max_pos), 2 (prefill, with T_or_max_pos = T), 3 (chunked
- * merge-append, with T_or_max_pos = L) or 4 (per-head prefill, with
- * T_or_max_pos = T).  Returns 0 for invalid arguments.
+ * merge-append, with T_or_max_pos = L), 4 (per-head prefill, with
+ * T_or_max_pos = T) or 5 (its backward, with T_or_max_pos = T).  Returns 0 for invalid arguments.
  * Pure host function. */
 size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos);
 

@@ -18,12 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtla.so"
 
 MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = range(5)
 MTLA_F32, MTLA_BF16 = 0, 1
-OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK, OP_UNABSORBED = 0, 1, 2, 3, 4
+OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK, OP_UNABSORBED, OP_BACKWARD = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
             "mtla_append_chunk", "mtla_decode_step", "mtla_prefill_strided",
             "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_prefill_unabsorbed",
-            "mtla_prefill_unabsorbed_timed", "mtla_workspace_bytes",
+            "mtla_prefill_unabsorbed_timed", "mtla_prefill_unabsorbed_backward",
+            "mtla_workspace_bytes",
             "mtla_status_string", "mtla_last_error_detail")
 
 
@@ -49,6 +50,12 @@ class UnabsorbedWeights(ctypes.Structure):
     _fields_ = [("W_dkv", c_void_p), ("W_gate", c_void_p), ("b_hc", c_void_p),
                 ("gate_pos", c_void_p), ("gate_pos_rows", c_int32), ("W_Q", c_void_p),
                 ("W_K", c_void_p), ("W_V", c_void_p), ("W_O", c_void_p)]
+
+
+class UnabsorbedGrads(ctypes.Structure):
+    _fields_ = [("dW_dkv", c_void_p), ("dW_hc", c_void_p), ("db_hc", c_void_p),
+                ("dgate_pos", c_void_p), ("dW_Q", c_void_p), ("dW_K", c_void_p),
+                ("dW_V", c_void_p), ("dW_O", c_void_p)]
 
 
 class Cache(ctypes.Structure):
@@ -86,12 +93,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             c_void_p, c_int32, c_int32, c_void_p, P(Cache),
                                             c_void_p, c_void_p, c_size_t, c_void_p]
     lib.mtla_prefill_unabsorbed_timed.argtypes = lib.mtla_prefill_unabsorbed.argtypes + [c_void_p]
+    lib.mtla_prefill_unabsorbed_backward.argtypes = [
+        P(Dims), P(UnabsorbedWeights), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+        c_void_p, c_void_p, c_void_p, c_void_p, P(UnabsorbedGrads), c_void_p, c_size_t, c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
     for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
               "mtla_append_chunk", "mtla_decode_step",
               "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed",
-              "mtla_prefill_unabsorbed", "mtla_prefill_unabsorbed_timed"):
+              "mtla_prefill_unabsorbed", "mtla_prefill_unabsorbed_timed",
+              "mtla_prefill_unabsorbed_backward"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
     lib.mtla_workspace_bytes.restype = c_size_t
@@ -279,6 +290,31 @@ def mtla_prefill_unabsorbed(dims: Dims, w: UnabsorbedWeights, X, QR, KR, Y=None,
     else:
         _check(lib.mtla_prefill_unabsorbed_timed(*args, _events(events)))
     return Y
+
+
+GRAD_NAMES = ("dW_dkv", "dW_hc", "db_hc", "dgate_pos", "dW_Q", "dW_K", "dW_V", "dW_O")
+
+
+def mtla_prefill_unabsorbed_backward(dims: Dims, w: UnabsorbedWeights, W_hc, X, QR, KR, dY,
+                                     grads: dict, dX=None, dQR=None, dKR=None, ws=None):
+    """Gradients of <dY, Y> for the per-head forward: returns (dX, dQR, dKR);
+    the FP32 weight gradients go into the tensors of ``grads`` (keys
+    GRAD_NAMES, preallocated by the caller in the weights' layouts)."""
+    B, T = X.shape[0], X.shape[1]
+    if dX is None:
+        dX = torch.empty_like(X)
+    if dQR is None:
+        dQR = torch.empty_like(QR)
+    if dKR is None:
+        dKR = torch.empty_like(KR)
+    if ws is None:
+        ws = workspace(dims, OP_BACKWARD, B, T, X.device)
+    g = UnabsorbedGrads(*[_ptr(grads[k]) for k in GRAD_NAMES])
+    _check(load_library().mtla_prefill_unabsorbed_backward(
+        ctypes.byref(dims), ctypes.byref(w), _ptr(W_hc), _ptr(X), _ptr(QR), _ptr(KR), B, T,
+        _ptr(dY), _ptr(dX), _ptr(dQR), _ptr(dKR), ctypes.byref(g), _ptr(ws), ws.numel(),
+        _stream()))
+    return dX, dQR, dKR
 
 
 def n_slots(T: int, s: int) -> int:

@@ -393,6 +393,17 @@ template <typename T> struct EpiStore {
   __device__ void operator()(int m, int n, float v) const { out[(size_t)m * ldc + n] = from_f32<T>(v); }
 };
 
+// fp32 output, stored or added to what is there.
+struct EpiAccF32 {
+  float *out;
+  int ldc;
+  int add;
+  __device__ void operator()(int m, int n, float v) const {
+    float *p = out + (size_t)m * ldc + n;
+    *p = add ? *p + v : v;
+  }
+};
+
 struct EpiBiasF32 {
   float *out;
   const void *bias;
@@ -599,6 +610,14 @@ hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1,
                           stream);
   return run_gemm<float>((const float *)A, lda, bs, M, N, K, EpiStore<float>{(float *)out, ldc},
                          stream);
+}
+
+hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, int ldb, int M, int N,
+                           int K, float *out, int ldc, bool add, hipStream_t stream) {
+  BSeg bs{Bm, Bm, Bm, N, N, ldb};
+  const EpiAccF32 epi{out, ldc, add ? 1 : 0};
+  if (dtype == 1) return run_gemm<bf16>((const bf16 *)A, lda, bs, M, N, K, epi, stream);
+  return run_gemm<float>((const float *)A, lda, bs, M, N, K, epi, stream);
 }
 
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,

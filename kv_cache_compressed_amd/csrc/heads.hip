@@ -51,6 +51,7 @@ struct HeadsArgs {
   const bf16 *KV;   // [B*T, 2*H*DH]: K_h at column h*DH, V_h at (H + h)*DH
   const bf16 *KR;   // [B*T, DR]
   bf16 *O;          // [B*T, H*DH]
+  float *lse;       // [B*T, H] or null: log2 of each row's softmax sum, in scaled log2 units
   int B, T, H, s, tiles, nst;
   float sl2;        // scale * log2(e)
 };
@@ -336,6 +337,9 @@ __global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kern
 #pragma unroll
   for (int qi = 0; qi < C::NQ; ++qi) {
     const float lt = sum_g(l[qi]);
+    // p = exp2(z * sl2 - lse) recovers a row's softmax weights from its scores.
+    if (a.lse && g == 0 && rw + 16 * qi + c < Tn)
+      a.lse[((size_t)b * Tn + rw + 16 * qi + c) * H + h] = m[qi] + __log2f(lt);
     const int fr = rw + 16 * qi + c;
     if (fr < Tn) {
       const float inv = 1.0f / lt;
@@ -354,7 +358,7 @@ bool heads_attention_supported(int dtype, int H, int d_h, int dR) {
 
 hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const void *q,
                                   const void *QR, const void *KV, const void *KR, void *O,
-                                  hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                                  float *lse, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using C = HdCfg;
   const int tiles = (T + C::ROWS - 1) / C::ROWS;
   const int nst = C::NST;
@@ -366,7 +370,7 @@ hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const
   float sl2 = scale * kLog2e;
   if (!(sl2 >= FLT_MIN)) sl2 = FLT_MIN;
   HeadsArgs args{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
-                 (bf16 *)O, B, T, H, s, tiles, nst, sl2};
+                 (bf16 *)O, lse, B, T, H, s, tiles, nst, sl2};
   return launch_timed((const void *)heads_attn_kernel, dim3(tiles * B * H), dim3(64 * C::NW), lds,
                       stream, &args, ev0, ev1);
 }

@@ -22,6 +22,10 @@ hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1,
                               int N1, int ldb, int M, int N, int K, void *out, int ldc,
                               hipStream_t stream);
 
+// out[M, N] (fp32, row stride ldc) = A[M, K] B[N, K]^T, or += when add.
+hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, int ldb, int M, int N,
+                           int K, float *out, int ldc, bool add, hipStream_t stream);
+
 // table[rows, r] (fp32) = pe[rows, d_pe] W_hp[r, d_pe]^T + b_hp.
 hipError_t launch_pos_table(int dtype, const void *pe, int rows, int d_pe, const void *W_hp,
                             const void *b_hp, int r, float *table, hipStream_t stream);
@@ -122,10 +126,47 @@ bool prefill_attention_supported(int dtype, int H, int r, int dR);
 // Per-head (unabsorbed) stride-aware masked attention, bf16, d_h = 64,
 // dR = 32: O [B*T, H*64] from q [B*T, H*64], QR [B*T, H, dR], KV
 // [B*T, 2*H*64] (K_h at column 64 h, V_h at 64 (H + h)) and KR [B*T, dR].
+// lse (nullable) [B*T, H] fp32 receives each row's log2 softmax sum in the
+// kernel's scaled log2 units (weights p = exp2(z * scale * log2(e) - lse)).
 hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const void *q,
                                   const void *QR, const void *KV, const void *KR, void *O,
-                                  hipStream_t stream, hipEvent_t ev0 = nullptr,
+                                  float *lse, hipStream_t stream, hipEvent_t ev0 = nullptr,
                                   hipEvent_t ev1 = nullptr);
 bool heads_attention_supported(int dtype, int H, int d_h, int dR);
+
+// ---- backward of the per-head parallel form (bf16, d_h = 64, dR = 32) ----
+
+bool attn_bwd_supported(int dtype, int H, int d_h, int dR);
+// Attention backward over the forward's q, QR, KV, KR, its lse and
+// D = rowsum(dO * O): key-role gradients of the compact keys into dKVc
+// [B*nS, 2*H*64] and dKRc [B*nS, H, dR] (fp32 scratch), then every frame's
+// total dK | dV into dKV [B*T, 2*H*64] (bf16) and per-head dK^R into dKRh
+// [B*T, H, dR] (fp32), and dQ [B*T, H*64], dQR [B*T, H, dR] (bf16).
+hipError_t launch_attn_bwd(int B, int T, int H, int s, float scale, const void *q, const void *QR,
+                           const void *KV, const void *KR, const void *dO, const float *lse,
+                           const float *D, float *dKVc, float *dKRc, void *dKV, float *dKRh,
+                           void *dQ, void *dQR, hipStream_t stream);
+// D[i] = sum over 64 channels of dO[i, :] * O[i, :], i < MH (rows of 64).
+hipError_t launch_rowdot(const void *dO, const void *O, int MH, float *D, hipStream_t stream);
+// dKR [M, dR] (bf16) = sum over heads of dKRh [M, H, dR].
+hipError_t launch_head_sum(const float *dKRh, int M, int H, void *dKR, hipStream_t stream);
+// Reverse group scan and gate backward from dC' [B*T, R] (fp32) and the
+// forward's cg: da (fp32 and bf16), dc's direct term (fp32), c (bf16), and
+// dPtab [rows, R] += the position-branch gradient.
+hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b_hc,
+                                const float *table, int B, int T, int R, int s, float *da32,
+                                void *dab, float *dc32, void *cb, float *dPtab,
+                                hipStream_t stream);
+// out[N] += column sums of x [M, N] (fp32).
+hipError_t launch_colsum(const float *x, int M, int N, float *out, hipStream_t stream);
+hipError_t launch_f32_to_bf16(const float *x, size_t n, void *y, hipStream_t stream);
+hipError_t launch_zero_f32(float *p, size_t n, hipStream_t stream);
+// out[C, R] (row stride ldo) = in[R, C]^T (bf16, row stride ldi).
+hipError_t launch_transpose(const void *in, int R, int C, int ldi, void *out, int ldo,
+                            hipStream_t stream);
+// out[N1, N2] (fp32, row stride ldo) += A[M, N1]^T B[M, N2] (bf16), split
+// over M with atomic adds: the caller zeroes out.
+hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
+                          float *out, int ldo, hipStream_t stream);
 
 }  // namespace mtla

@@ -164,6 +164,46 @@ HeadsWs heads_ws(const mtla_dims *d, int B, int T) {
   return w;
 }
 
+// Workspace of the backward of the per-head form: the forward's buffers, the
+// transposed weights, and the backward's intermediate gradients.
+struct BwdWs {
+  HeadsWs f;
+  size_t O_, lse, WOt, WKVt, Whct, Wdkvt, WQt, dO, D, dKVc, dKRc, dKV, dKRh, dQ, dCp, da32, dab,
+      dc32, cb, dcb, dX32, total;
+};
+
+BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
+  BwdWs w;
+  w.f = heads_ws(d, B, T);
+  const size_t e = esize(d), r = d->r, HD = (size_t)d->H * d->d_h, M = (size_t)B * T;
+  const size_t nS = (T + d->s - 1) / d->s, dd = d->d, H = d->H, dR = d->d_hR;
+  size_t off = w.f.total;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  w.O_ = w.f.O;
+  w.lse = take(M * H * 4);
+  w.WOt = take(HD * dd * e);
+  w.WKVt = take(r * 2 * HD * e);
+  w.Whct = take(r * r * e);
+  w.Wdkvt = take(dd * r * e);
+  w.WQt = take(dd * HD * e);
+  w.dO = take(M * HD * e);
+  w.D = take(M * H * 4);
+  w.dKVc = take((size_t)B * nS * 2 * HD * 4);
+  w.dKRc = take((size_t)B * nS * H * dR * 4);
+  w.dKV = take(M * 2 * HD * e);
+  w.dKRh = take(M * H * dR * 4);
+  w.dQ = take(M * HD * e);
+  w.dCp = take(M * r * 4);
+  w.da32 = take(M * r * 4);
+  w.dab = take(M * r * e);
+  w.dc32 = take(M * r * 4);
+  w.cb = take(M * r * e);
+  w.dcb = take(M * r * e);
+  w.dX32 = take(M * dd * 4);
+  w.total = off;
+  return w;
+}
+
 // Workspace of a chunked merge-append of L frames: cg [B*L, 2r] fp32.
 size_t chunk_ws(const mtla_dims *d, int B, int L) {
   return align_up((size_t)B * L * 2 * d->r * 4);
@@ -217,6 +257,10 @@ size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_
   if (op == 4) {
     if (T_or_max_pos < 1) return 0;
     return heads_ws(dims, B, T_or_max_pos).total;
+  }
+  if (op == 5) {
+    if (T_or_max_pos < 1) return 0;
+    return bwd_ws(dims, B, T_or_max_pos).total;
   }
   return 0;
 }
@@ -467,17 +511,146 @@ mtla_status prefill_unabsorbed_impl(const mtla_dims *dims, const mtla_unabsorbed
   LAUNCH(mtla::launch_gemm_store2(dims->dtype, Cp, dims->r, w->W_K, w->W_V, HD, dims->r, M, 2 * HD,
                                   dims->r, KV, 2 * HD, s),
          "per-head key and value projection");
-  LAUNCH(mtla::launch_heads_attention(B, T, dims->H, dims->s, eff_scale(dims), q, QR, KV, KR, O, s,
-                                      ev0(events), ev1(events)),
+  LAUNCH(mtla::launch_heads_attention(B, T, dims->H, dims->s, eff_scale(dims), q, QR, KV, KR, O,
+                                      nullptr, s, ev0(events), ev1(events)),
          "per-head strided attention");
   LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HD, w->W_O, dims->d, Y, nullptr, nullptr, s),
          "output projection");
   return ok();
 }
 
+mtla_status prefill_unabsorbed_backward_impl(
+    const mtla_dims *dims, const mtla_unabsorbed_weights *w, const void *W_hc, const void *X,
+    const void *QR, const void *KR, int32_t B, int32_t T, const void *dY, void *dX, void *dQR,
+    void *dKR, const mtla_unabsorbed_grads *gr, void *workspace, size_t ws_bytes, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if (!w) return fail(MTLA_ERR_ARG, "weights is null");
+  if (!gr) return fail(MTLA_ERR_ARG, "grads is null");
+  CHECK_PTR(w->W_dkv);
+  CHECK_PTR(w->W_gate);
+  CHECK_PTR(w->b_hc);
+  CHECK_PTR(w->gate_pos);
+  if (w->gate_pos_rows <= 0) return fail(MTLA_ERR_ARG, "gate_pos_rows=%d", w->gate_pos_rows);
+  CHECK_PTR(w->W_Q);
+  CHECK_PTR(w->W_K);
+  CHECK_PTR(w->W_V);
+  CHECK_PTR(w->W_O);
+  CHECK_PTR(W_hc);
+  CHECK_PTR(X);
+  CHECK_PTR(QR);
+  CHECK_PTR(KR);
+  CHECK_PTR(dY);
+  CHECK_PTR(dX);
+  CHECK_PTR(dQR);
+  CHECK_PTR(dKR);
+  CHECK_PTR(gr->dW_dkv);
+  CHECK_PTR(gr->dW_hc);
+  CHECK_PTR(gr->db_hc);
+  CHECK_PTR(gr->dgate_pos);
+  CHECK_PTR(gr->dW_Q);
+  CHECK_PTR(gr->dW_K);
+  CHECK_PTR(gr->dW_V);
+  CHECK_PTR(gr->dW_O);
+  CHECK_PTR(workspace);
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (T < 1) return fail(MTLA_ERR_ARG, "T=%d < 1", T);
+  if ((int64_t)B * T * dims->H * dims->d_h > 0x7fffffffLL / 4 ||
+      (int64_t)B * T * dims->d > 0x7fffffffLL / 4)
+    return fail(MTLA_ERR_UNSUPPORTED, "B*T too large");
+  if (!mtla::attn_bwd_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR))
+    return fail(MTLA_ERR_UNSUPPORTED, "backward needs bf16 storage, d_h = 64, d_hR = 32");
+  if ((T - 1) / dims->s >= w->gate_pos_rows)
+    return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
+  const BwdWs ws = bwd_ws(dims, B, T);
+  if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)workspace;
+  auto P = [&](size_t off) { return (void *)(base + off); };
+  auto F = [&](size_t off) { return (float *)(base + off); };
+  const int M = B * T, HD = dims->H * dims->d_h, r = dims->r, d = dims->d, H = dims->H;
+  const int dt = dims->dtype;
+  const float scale = eff_scale(dims);
+  void *Cp = P(ws.f.Cp), *q = P(ws.f.q), *KV = P(ws.f.KV), *O = P(ws.f.O);
+  float *cg = F(ws.f.cg), *lse = F(ws.lse);
+  // forward, keeping what the backward reads
+  LAUNCH(mtla::launch_proj(dt, X, M, d, w->W_dkv, w->W_gate, r, w->W_Q, HD, cg, q, nullptr, 0, s),
+         "forward projection");
+  LAUNCH(mtla::launch_group_scan(dt, cg, w->b_hc, w->gate_pos, KR, B, T, r, dims->d_hR, dims->s, Cp,
+                                 P(ws.f.keys), ws.f.keys_stride, nullptr, 0, s),
+         "forward group scan");
+  LAUNCH(mtla::launch_gemm_store2(dt, Cp, r, w->W_K, w->W_V, HD, r, M, 2 * HD, r, KV, 2 * HD, s),
+         "forward key and value projection");
+  LAUNCH(mtla::launch_heads_attention(B, T, H, dims->s, scale, q, QR, KV, KR, O, lse, s),
+         "forward attention");
+  // transposed weights for the products against them
+  LAUNCH(mtla::launch_transpose(w->W_O, d, HD, HD, P(ws.WOt), d, s), "transpose W_O");
+  LAUNCH(mtla::launch_transpose(w->W_K, HD, r, r, P(ws.WKVt), 2 * HD, s), "transpose W_K");
+  LAUNCH(mtla::launch_transpose(w->W_V, HD, r, r, (char *)P(ws.WKVt) + (size_t)HD * 2, 2 * HD, s),
+         "transpose W_V");
+  LAUNCH(mtla::launch_transpose(W_hc, r, r, r, P(ws.Whct), r, s), "transpose W_hc");
+  LAUNCH(mtla::launch_transpose(w->W_dkv, r, d, d, P(ws.Wdkvt), r, s), "transpose W_dkv");
+  LAUNCH(mtla::launch_transpose(w->W_Q, HD, d, d, P(ws.WQt), HD, s), "transpose W_Q");
+  // output map
+  LAUNCH(mtla::launch_gemm_store(dt, dY, d, P(ws.WOt), d, M, HD, d, P(ws.dO), HD, s), "dO");
+  LAUNCH(mtla::launch_rowdot(P(ws.dO), O, M * H, F(ws.D), s), "rowsum dO * O");
+  // attention
+  LAUNCH(mtla::launch_attn_bwd(B, T, H, dims->s, scale, q, QR, KV, KR, P(ws.dO), lse, F(ws.D),
+                               F(ws.dKVc), F(ws.dKRc), P(ws.dKV), F(ws.dKRh), P(ws.dQ), dQR, s),
+         "attention backward");
+  LAUNCH(mtla::launch_head_sum(F(ws.dKRh), M, H, dKR, s), "dK^R over heads");
+  // key and value maps
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dKV), 2 * HD, P(ws.WKVt), 2 * HD, M, r, 2 * HD, F(ws.dCp), r,
+                               false, s),
+         "dC'");
+  // group sums and gate
+  LAUNCH(mtla::launch_zero_f32(gr->dgate_pos, (size_t)w->gate_pos_rows * r, s), "zero dP");
+  LAUNCH(mtla::launch_zero_f32(gr->db_hc, r, s), "zero db");
+  LAUNCH(mtla::launch_scan_gate_bwd(F(ws.dCp), cg, w->b_hc, w->gate_pos, B, T, r, dims->s,
+                                    F(ws.da32), P(ws.dab), F(ws.dc32), P(ws.cb), gr->dgate_pos, s),
+         "group scan and gate backward");
+  LAUNCH(mtla::launch_colsum(F(ws.da32), M, r, gr->db_hc, s), "db");
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), r, true, s),
+         "dc");
+  LAUNCH(mtla::launch_f32_to_bf16(F(ws.dc32), (size_t)M * r, P(ws.dcb), s), "dc to bf16");
+  // inputs
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), d, false, s),
+         "dX from the latent map");
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, true, s),
+         "dX from the query map");
+  LAUNCH(mtla::launch_f32_to_bf16(F(ws.dX32), (size_t)M * d, dX, s), "dX to bf16");
+  // weight gradients
+  LAUNCH(mtla::launch_zero_f32(gr->dW_O, (size_t)d * HD, s), "zero dW_O");
+  LAUNCH(mtla::launch_zero_f32(gr->dW_Q, (size_t)HD * d, s), "zero dW_Q");
+  LAUNCH(mtla::launch_zero_f32(gr->dW_K, (size_t)HD * r, s), "zero dW_K");
+  LAUNCH(mtla::launch_zero_f32(gr->dW_V, (size_t)HD * r, s), "zero dW_V");
+  LAUNCH(mtla::launch_zero_f32(gr->dW_hc, (size_t)r * r, s), "zero dW_hc");
+  LAUNCH(mtla::launch_zero_f32(gr->dW_dkv, (size_t)r * d, s), "zero dW_dkv");
+  LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, s), "dW_O");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, s), "dW_Q");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, s), "dW_K");
+  LAUNCH(mtla::launch_tn_gemm((char *)P(ws.dKV) + (size_t)HD * 2, 2 * HD, Cp, r, M, HD, r, gr->dW_V,
+                              r, s),
+         "dW_V");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, s), "dW_hc");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, s), "dW_dkv");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+mtla_status mtla_prefill_unabsorbed_backward(const mtla_dims *dims,
+                                             const mtla_unabsorbed_weights *w, const void *W_hc,
+                                             const void *X, const void *QR, const void *KR,
+                                             int32_t B, int32_t T, const void *dY, void *dX,
+                                             void *dQR, void *dKR,
+                                             const mtla_unabsorbed_grads *grads, void *workspace,
+                                             size_t ws_bytes, void *stream) {
+  return prefill_unabsorbed_backward_impl(dims, w, W_hc, X, QR, KR, B, T, dY, dX, dQR, dKR, grads,
+                                          workspace, ws_bytes, stream);
+}
 
 mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
                                     const void *X, const void *QR, const void *KR, int32_t B,

@@ -96,3 +96,19 @@ class MTLALayer:
         return L.mtla_prefill_unabsorbed(self.dims, self.wu, X, QR, KR, Y, c, Cprime,
                                          self.workspace(L.OP_UNABSORBED, X.shape[0], X.shape[1]),
                                          events)
+
+    def backward_unabsorbed(self, X, QR, KR, dY):
+        """Gradients of <dY, Y> for prefill_unabsorbed: (dX, dQR, dKR, grads)
+        with grads a dict of FP32 weight gradients in the weights' layouts."""
+        if self.wu is None:
+            raise ValueError("the layer was built without the per-head maps W_Qh, W_Kh, W_Vh, W_Oh")
+        d = self.dims
+        HD = d.H * d.d_h
+        shapes = dict(dW_dkv=(d.r, d.d), dW_hc=(d.r, d.r), db_hc=(d.r,),
+                      dgate_pos=tuple(self.gate_pos.shape), dW_Q=(HD, d.d), dW_K=(HD, d.r),
+                      dW_V=(HD, d.r), dW_O=(d.d, HD))
+        grads = {k: torch.empty(v, dtype=torch.float32, device=X.device) for k, v in shapes.items()}
+        dX, dQR, dKR = L.mtla_prefill_unabsorbed_backward(
+            d, self.wu, self.t["W_hc"], X, QR, KR, dY, grads,
+            ws=self.workspace(L.OP_BACKWARD, X.shape[0], X.shape[1]))
+        return dX, dQR, dKR, grads

@@ -1,0 +1,89 @@
+"""GPU parity of mtla_prefill_unabsorbed_backward (the backward of the
+per-head parallel form) against the oracle's chain-rule backward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.mtla as om
+import synth
+from synth import Dims
+from gpu_util import TOL, dev, host, needs_gpu, relerr, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(dims, seed, pe_rows):
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    w = synth.make_weights(dims, seed, "bf16", pe_rows=pe_rows)
+    W = om.with_position_table(w, pe_rows)
+    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    return w, W, L
+
+
+def _oracle_abi(gr, dims):
+    """Oracle gradients in the library's layouts."""
+    H, d, dh, r = dims.H, dims.d, dims.d_h, dims.r
+    return dict(dW_dkv=gr["dW_dkv"], dW_hc=gr["dW_hc"], db_hc=gr["db_hc"], dgate_pos=gr["dP"],
+                dW_Q=np.transpose(gr["dW_Q"], (0, 2, 1)).reshape(H * dh, d),
+                dW_K=np.transpose(gr["dW_K"], (0, 2, 1)).reshape(H * dh, r),
+                dW_V=np.transpose(gr["dW_V"], (0, 2, 1)).reshape(H * dh, r),
+                dW_O=np.transpose(gr["dW_O"], (2, 0, 1)).reshape(d, H * dh))
+
+
+def _check(dims, B, T, seed, T0=None, rows=None):
+    """Backward at [B, T]; dY is nonzero only on sequences `rows` and frames
+    < T0 (defaults: all), so the oracle runs on those prefixes only (frames
+    before T0 do not depend on later ones) and the rest must be exact zeros."""
+    T0 = T if T0 is None else T0
+    rows = list(range(B)) if rows is None else rows
+    ms = om.n_slots(T, dims.s) + 1
+    w, W, L = _layer(dims, seed, ms)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, "bf16")
+    rng = np.random.default_rng(seed + 2)
+    dY = np.zeros((B, T, dims.d))
+    for b in rows:
+        dY[b, :T0] = synth.round_to(rng.normal(size=(T0, dims.d)), "bf16")
+    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
+    dX, dQR, dKR, grads = L.backward_unabsorbed(X, QR, KR, dev(dY, "bf16"))
+    torch.cuda.synchronize()
+    gX, gQR, gKR = host(dX), host(dQR), host(dKR)
+    ref_w = None
+    worst = 0.0
+    for b in rows:
+        x, qr, kr = seq["X"][b, :T0], seq["QR"][b, :T0], seq["KR"][b, :T0]
+        gr = om.prefill_unabsorbed_backward(x, qr, kr, W, dims.s, dims.scale, dY[b, :T0])
+        for name, got in (("dX", gX[b, :T0]), ("dQR", gQR[b, :T0]), ("dKR", gKR[b, :T0])):
+            e = relerr(got, gr[name])
+            worst = max(worst, e)
+            assert e < TOL["bf16"], (b, name, e)
+        ab = _oracle_abi(gr, dims)
+        ref_w = ab if ref_w is None else {k: ref_w[k] + ab[k] for k in ref_w}
+    # frames and sequences without a loss gradient get exactly zero
+    assert not np.any(gX[:, T0:]) and not np.any(gQR[:, T0:]) and not np.any(gKR[:, T0:])
+    for b in set(range(B)) - set(rows):
+        assert not np.any(gX[b]) and not np.any(gQR[b]) and not np.any(gKR[b])
+    for k, ref in ref_w.items():
+        e = relerr(host(grads[k]), ref)
+        worst = max(worst, e)
+        assert e < TOL["bf16"], (k, e)
+    say(f"  worst relerr {worst:.3g}")
+
+
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 8, 1), (2, 130, 8, 2), (3, 257, 4, 1),
+                                       (1, 64, 2, 2), (4, 300, 8, 1), (80, 100, 2, 1),
+                                       (5, 96, 3, 2), (2, 513, 8, 1)])
+def test_backward_matches_oracle(s, T, H, B):
+    needs_gpu()
+    dims = Dims(d=512, H=H, d_h=64, r=256, d_hR=32, s=s)
+    say("backward per-head", s, T, H, B)
+    _check(dims, B, T, 9500 + 7 * s + T + H)
+
+
+def test_backward_full_size_prefix():
+    """The benchmark's backward launch (B=16, T=4096, s=2) with the loss on
+    the first 320 frames of two sequences: those gradients against the
+    oracle, everything else exactly zero."""
+    needs_gpu()
+    name, dims, ex = synth.config(4)
+    say("backward full size", name)
+    _check(dims, ex["B"], ex["T"], 9600, T0=320, rows=[0, ex["B"] - 1])
