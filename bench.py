@@ -28,7 +28,8 @@ second pass.
 Also reported (same line): the ragged and LLM-scale decode workloads, the
 strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
 of the whole forward, in the absorbed form and in the per-head form), the
-chunked merge-append (frames/s), and the CPU oracle timed on the host cores on a bounded
+backward of the per-head form, the chunked merge-append (frames/s), and the
+CPU oracle timed on the host cores on a bounded
 sample of the headline workload.
 
 All inputs are seeded synthetic tensors (no datasets or trained weights).
@@ -372,6 +373,39 @@ def run_prefill_unabsorbed(steps: int = 10, warmup: int = 3) -> dict:
                 tokens_per_s=M / (fwd_ms * 1e-3))
 
 
+def run_backward(steps: int = 5, warmup: int = 2) -> dict:
+    """Backward of the per-head form on the prefill workload: one step is one
+    mtla_prefill_unabsorbed_backward call (the forward recomputed inside,
+    then every input and weight gradient) for a seeded loss gradient dY."""
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    ms = -(-T // dims.s)
+    w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
+    layer = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    X, QR, KR = dev(seq["X"]), dev(seq["QR"]), dev(seq["KR"])
+    del seq
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.seed_for(4) + 3)
+    dY = torch.randn(B, T, dims.d, generator=gen, device="cuda").to(torch.bfloat16)
+    run = lambda i: layer.backward_unabsorbed(X, QR, KR, dY)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    step_ms = _timed_loop(run, steps) / steps
+    _, pairs = prefill_flops(B, T, dims.H, dims.r, dims.d_hR, dims.s)
+    dh, dR, H, M = dims.d_h, dims.d_hR, dims.H, B * T
+    # attention backward, each product once: S, dP, dV, dK, dK^R, dQ, dQ^R
+    attn_flops = B * H * pairs * (2 * (dh + dR) + 2 * dh + 2 * dh + 2 * dh + 2 * dR + 2 * dh + 2 * dR)
+    return dict(name=name + "_backward", B=B, T=T, dims=dims.asdict(), steps=steps,
+                step_ms=step_ms, attn_bwd_flops=attn_flops,
+                tokens_per_s=M / (step_ms * 1e-3))
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The oracle (numpy, fp32) on the headline decode workload: full-batch
     decode steps repeated until `seconds` of wall time have passed."""
@@ -415,7 +449,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
                                        "llm_decode_b128_ctx32768", "prefill_b16_t4096",
-                                       "append_chunk_b32_l512", "prefill_b16_t4096_per_head"],
+                                       "append_chunk_b32_l512", "prefill_b16_t4096_per_head",
+                                       "prefill_b16_t4096_backward"],
                     help="time one workload alone and print its record (for profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise pass reading and writing MIB MiB each "
@@ -433,6 +468,9 @@ def main():
 
     if args.calib_copy:
         calib_copy(args.calib_copy)
+    if args.only == "prefill_b16_t4096_backward":
+        print(json.dumps(run_backward(args.steps, args.warmup)), flush=True)
+        return
     if args.only == "prefill_b16_t4096_per_head":
         print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup)), flush=True)
         return
@@ -474,6 +512,9 @@ def main():
         u["attn_mfma_frac"] = u["attn_tflops"] / BF16_PEAK_TFLOPS
         log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
             f"({u['attn_mfma_frac']:.1%}), forward {u['forward_ms']:.3f} ms")
+        log("prefill_b16_t4096_backward ...")
+        bw = extra["prefill_b16_t4096_backward"] = run_backward()
+        log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
         log("append_chunk_b32_l512 ...")
         a = extra["append_chunk_b32_l512"] = run_append()
         log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")

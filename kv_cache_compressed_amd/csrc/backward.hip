@@ -543,20 +543,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
 }
 
-// D[row, h] = sum over the head's channels of dO * O (one thread per (row, h)).
+// D[row, h] = sum over the head's channels of dO * O: eight consecutive
+// lanes share a 64-channel row, 16 bytes each (coalesced), and add their
+// partial sums across the eight lanes.
 __global__ __launch_bounds__(256) void rowdot_kernel(const bf16 *dO, const bf16 *O, int MH,
                                                      float *D) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= MH) return;
-  const bf16 *x = dO + (size_t)i * DH, *y = O + (size_t)i * DH;
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t i = t >> 3;
+  const int part = (int)(t & 7);
   float acc = 0.0f;
-#pragma unroll
-  for (int k = 0; k < DH; k += 8) {
-    const bf16x8 u = *(const bf16x8 *)(x + k), v = *(const bf16x8 *)(y + k);
+  if (i < (size_t)MH) {
+    const bf16x8 u = *(const bf16x8 *)(dO + i * DH + 8 * part);
+    const bf16x8 v = *(const bf16x8 *)(O + i * DH + 8 * part);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)u[e] * (float)v[e];
   }
-  D[i] = acc;
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (i < (size_t)MH && part == 0) D[i] = acc;
 }
 
 // dKR[row, ch] = sum_h dKRh[row, h, ch] (the RoPE key is shared by the heads).
@@ -603,15 +608,20 @@ __global__ __launch_bounds__(256) void scan_gate_bwd_kernel(const float *dCp, co
   atomicAdd(dPtab + (size_t)j * R + ch, dPacc);
 }
 
-// out[ch] += column sums of x [M, N] (fp32), each workgroup a block of rows.
+// out[ch] += column sums of x [M, N] (fp32), each workgroup a block of rows
+// (eight independent partial sums per thread keep eight loads in flight).
 __global__ __launch_bounds__(256) void colsum_kernel(const float *x, int M, int N, int rows,
                                                      float *out) {
   const int ch = blockIdx.x * 256 + threadIdx.x;
   if (ch >= N) return;
   const int r0 = blockIdx.y * rows, r1 = min(M, r0 + rows);
-  float acc = 0.0f;
-  for (int r = r0; r < r1; ++r) acc += x[(size_t)r * N + ch];
-  atomicAdd(out + ch, acc);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int r = r0;
+  for (; r + 8 <= r1; r += 8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[(size_t)(r + e) * N + ch];
+  for (; r < r1; ++r) acc[0] += x[(size_t)r * N + ch];
+  atomicAdd(out + ch, ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *x, size_t n, bf16 *y) {
@@ -751,7 +761,8 @@ hipError_t launch_attn_bwd(int B, int T, int H, int s, float scale, const void *
 }
 
 hipError_t launch_rowdot(const void *dO, const void *O, int MH, float *D, hipStream_t stream) {
-  hipLaunchKernelGGL(rowdot_kernel, dim3((MH + 255) / 256), dim3(256), 0, stream,
+  hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)(((size_t)MH * 8 + 255) / 256)), dim3(256), 0,
+                     stream,
                      (const bf16 *)dO, (const bf16 *)O, MH, D);
   return hipGetLastError();
 }
@@ -774,7 +785,7 @@ hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b
 }
 
 hipError_t launch_colsum(const float *x, int M, int N, float *out, hipStream_t stream) {
-  const int rows = 256;
+  const int rows = 64;
   dim3 grid((N + 255) / 256, (M + rows - 1) / rows);
   hipLaunchKernelGGL(colsum_kernel, grid, dim3(256), 0, stream, x, M, N, rows, out);
   return hipGetLastError();
