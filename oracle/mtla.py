@@ -403,6 +403,39 @@ def prefill_unabsorbed_backward(X, QR, KR, W, s, scale, dY):
 
 
 # ---------------------------------------------------------------------------
+# decoupled RoPE inputs ([Notes] decoupled RoPE with temporal compression: the
+# RoPE-carrying query and key parts Q^R, K^R).  The pages do not spell out
+# the rotary form; the reading taken is the standard one: adjacent pairs
+# (2k, 2k+1) of a width-w vector turn by pos * base^(-2k/w); Q^R per head from
+# W_QR^(h) x, K^R shared by the heads from W_KR x.
+# ---------------------------------------------------------------------------
+
+
+def rope_rotate(v, pos, base=10000.0):
+    """Rotate the adjacent pairs of the last axis of v [..., w] by the
+    angles pos * base^(-2k/w), k = 0 .. w/2-1; ``pos`` broadcasts against
+    v's leading axes."""
+    w = v.shape[-1]
+    theta = base ** (-2.0 * np.arange(w // 2) / w)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    cs, sn = np.cos(ang), np.sin(ang)
+    out = np.empty_like(v)
+    out[..., 0::2] = v[..., 0::2] * cs - v[..., 1::2] * sn
+    out[..., 1::2] = v[..., 0::2] * sn + v[..., 1::2] * cs
+    return out
+
+
+def rope_inputs(X, W_QR, W_KR, positions, base=10000.0):
+    """Q^R [T, H, d_hR] and K^R [T, d_hR] of frames X [T, d] at absolute
+    positions [T]: W_QR [H, d_hR, d] ([out, in] per head), W_KR [d_hR, d]."""
+    H, dR, d = W_QR.shape
+    q = (X @ W_QR.reshape(H * dR, d).T).reshape(X.shape[0], H, dR)
+    k = X @ W_KR.T
+    pos = np.asarray(positions, dtype=np.float64)
+    return rope_rotate(q, pos[:, None], base), rope_rotate(k, pos, base)
+
+
+# ---------------------------------------------------------------------------
 # reference forms used only to pin the ones above
 # ---------------------------------------------------------------------------
 

@@ -357,6 +357,37 @@ def pin_backward_matches_finite_differences():
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (s, name, fd, an)
 
 
+def pin_rope_closed_form():
+    """Rotary pairs by hand: width 4, base 16 -- pair 0 turns by pos, pair 1
+    by pos / 4; unit vectors land on (cos, sin) and (-sin, cos); position 0
+    is the identity; lengths of pairs are kept."""
+    for p in (0.0, 1.0, 3.0, 1000.0):
+        v = np.array([1.0, 0.0, 0.0, 1.0])
+        got = om.rope_rotate(v, p, base=16.0)
+        a0, a1 = p, p / 4.0
+        ref = np.array([math.cos(a0), math.sin(a0), -math.sin(a1), math.cos(a1)])
+        assert np.max(np.abs(got - ref)) < 1e-12, (p, got, ref)
+    rng = np.random.default_rng(1401)
+    v = rng.normal(size=(5, 32))
+    r = om.rope_rotate(v, np.arange(5) * 7.0)
+    assert np.array_equal(om.rope_rotate(v, 0.0), v)
+    n0 = v[:, 0::2] ** 2 + v[:, 1::2] ** 2
+    n1 = r[:, 0::2] ** 2 + r[:, 1::2] ** 2
+    assert np.max(np.abs(n0 - n1)) < 1e-12
+
+
+def pin_rope_relative_position():
+    """The rotary score depends on the offset only: <R_m q, R_n k> =
+    <R_(m-n) q, k> for any positions (rotations compose)."""
+    rng = np.random.default_rng(1402)
+    for w in (2, 8, 32):
+        q, k = rng.normal(size=w), rng.normal(size=w)
+        for m, n in ((5, 3), (0, 9), (4096, 4000), (12, 12)):
+            lhs = om.rope_rotate(q, m) @ om.rope_rotate(k, n)
+            rhs = om.rope_rotate(q, m - n) @ k
+            assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(lhs)), (w, m, n, lhs, rhs)
+
+
 # ---------------------------------------------------------------------------
 # closed forms
 # ---------------------------------------------------------------------------
@@ -508,5 +539,5 @@ ALL_PINS = [
     pin_s1_is_causal_mla, pin_any_s_matches_sdpa, pin_half_gate_group_mean, pin_large_s_limit,
     pin_uniform_softmax, pin_first_step, pin_predownsampling_differs,
     pin_chunked_append_equals_prefill, pin_chunk_continues_live_slot, pin_unabsorbed_matches_sdpa,
-    pin_backward_matches_finite_differences,
+    pin_backward_matches_finite_differences, pin_rope_closed_form, pin_rope_relative_position,
 ]

@@ -192,6 +192,35 @@ def _mut_bwd_missing_scale(mp):
     _edit_backward(mp, "keepdims=True)) * scale", "keepdims=True))")
 
 
+def _edit_rope(mp, old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(om.rope_rotate))
+    assert old in src, old
+    ns = dict(vars(om))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    mp.setattr(om, "rope_rotate", ns["rope_rotate"])
+
+
+def _mut_rope_sign(mp):
+    _edit_rope(mp, "v[..., 0::2] * cs - v[..., 1::2] * sn", "v[..., 0::2] * cs + v[..., 1::2] * sn")
+
+
+def _mut_rope_exponent(mp):
+    _edit_rope(mp, "base ** (-2.0 * np.arange(w // 2) / w)", "base ** (-1.0 * np.arange(w // 2) / w)")
+
+
+def _mut_rope_half_split(mp):
+    def rot(v, pos, base=10000.0):
+        w = v.shape[-1]
+        theta = base ** (-2.0 * np.arange(w // 2) / w)
+        ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+        a, b = v[..., : w // 2], v[..., w // 2:]
+        return np.concatenate([a * np.cos(ang) - b * np.sin(ang),
+                               a * np.sin(ang) + b * np.cos(ang)], axis=-1)
+    mp.setattr(om, "rope_rotate", rot)
+
+
 MUTANTS = [
     _mut_group_final_zero, _mut_drop_rope, _mut_transpose_whc, _mut_position_by_frame,
     _mut_additive_gate, _mut_no_reset, _mut_rope_key_first_frame, _mut_plain_prefix_sum,
@@ -201,6 +230,7 @@ MUTANTS = [
     _mut_unabsorbed_values_from_keys, _mut_unabsorbed_causal_mask,
     _mut_bwd_no_softmax_correction, _mut_bwd_scan_not_accumulated, _mut_bwd_no_sigmoid_derivative,
     _mut_bwd_transposed_whc, _mut_bwd_rope_keys_one_head, _mut_bwd_missing_scale,
+    _mut_rope_sign, _mut_rope_exponent, _mut_rope_half_split,
 ]
 
 
