@@ -28,8 +28,9 @@ second pass.
 Also reported (same line): the ragged and LLM-scale decode workloads, the
 strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
 of the whole forward, in the absorbed form and in the per-head form), the
-backward of the per-head form, the chunked merge-append (frames/s), and the
-CPU oracle timed on the host cores on a bounded
+backward of the per-head form, the chunked merge-append (frames/s), the
+library's decoupled-RoPE inputs, the headline decode at s = 1 (the MLA
+reduction: twice the slots, for the speed and memory ratio), and the CPU oracle timed on the host cores on a bounded
 sample of the headline workload.
 
 All inputs are seeded synthetic tensors (no datasets or trained weights).
@@ -139,11 +140,14 @@ def calib_copy(mib: int):
     torch.cuda.empty_cache()
 
 
-def _decode_setup(cfg: int, seed_pos=None):
+def _decode_setup(cfg: int, seed_pos=None, stride=None):
     import torch
     import synth
     from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
     name, dims, ex = synth.config(cfg)
+    if stride is not None:
+        dims = synth.Dims(**{**dims.asdict(), "s": stride})
+        name = f"{name}_s{stride}"
     B = ex["B"]
     if "ctx" in ex:
         pos = np.full(B, ex["ctx"] - 1, dtype=np.int32)
@@ -206,10 +210,12 @@ def _timed_loop(fn, n):
     raise RuntimeError("could not keep the GPU busy while enqueueing the timed steps")
 
 
-def run_decode(cfg: int, steps: int, warmup: int) -> dict:
-    """Time `steps` decode steps; returns step and attention-kernel times."""
+def run_decode(cfg: int, steps: int, warmup: int, stride=None) -> dict:
+    """Time `steps` decode steps; returns step and attention-kernel times.
+    `stride` overrides the workload's s (s = 1 is the MLA reduction: one
+    slot per frame)."""
     import torch
-    S = _decode_setup(cfg)
+    S = _decode_setup(cfg, stride=stride)
     layer, caches, (x, qr, kr, pos), Y = S["layer"], S["caches"], S["inputs"], S["Y"]
     n_rep, max_pos = len(caches), S["max_pos"]
     hip = HipEvents()
@@ -406,6 +412,37 @@ def run_backward(steps: int = 5, warmup: int = 2) -> dict:
                 tokens_per_s=M / (step_ms * 1e-3))
 
 
+def run_rope(steps: int = 20, warmup: int = 3) -> dict:
+    """Decoupled-RoPE inputs of the prefill workload's 65,536 frames
+    (mtla_rope_inputs: one product pass and the rotation)."""
+    import torch
+    import synth
+    from kv_cache_compressed_amd import MTLA_BF16, make_dims, mtla_rope_inputs, workspace, OP_ROPE
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=8)
+    d = make_dims(dims.d, dims.H, dims.d_h, dims.r, dims.d_hR, dims.s, MTLA_BF16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(synth.seed_for(4) + 5)
+    X = torch.randn(B, T, dims.d, generator=gen, device="cuda").to(torch.bfloat16)
+    W_QR, W_KR = dev(w["W_QR"].reshape(-1, dims.d)), dev(w["W_KR"])
+    pos = torch.arange(T, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+    QR = torch.empty(B, T, dims.H, dims.d_hR, dtype=torch.bfloat16, device="cuda")
+    KR = torch.empty(B, T, dims.d_hR, dtype=torch.bfloat16, device="cuda")
+    ws = workspace(d, OP_ROPE, B * T, 1)
+    run = lambda i: mtla_rope_inputs(d, W_QR, W_KR, X, pos, 10000.0, QR, KR, ws)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    step_ms = _timed_loop(run, steps) / steps
+    M = B * T
+    N = (dims.H + 1) * dims.d_hR
+    return dict(name=name + "_rope_inputs", B=B, T=T, step_ms=step_ms,
+                frames_per_s=M / (step_ms * 1e-3),
+                io_bytes=M * (dims.d + N) * 2 + M * 4, flops=2 * M * dims.d * N)
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The oracle (numpy, fp32) on the headline decode workload: full-batch
     decode steps repeated until `seconds` of wall time have passed."""
@@ -450,7 +487,8 @@ def main():
     ap.add_argument("--only", choices=["decode_b32_ctx2048", "ragged_decode_b64_s4",
                                        "llm_decode_b128_ctx32768", "prefill_b16_t4096",
                                        "append_chunk_b32_l512", "prefill_b16_t4096_per_head",
-                                       "prefill_b16_t4096_backward"],
+                                       "prefill_b16_t4096_backward", "rope_inputs_b16_t4096",
+                                       "decode_b32_ctx2048_s1"],
                     help="time one workload alone and print its record (for profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise pass reading and writing MIB MiB each "
@@ -468,6 +506,12 @@ def main():
 
     if args.calib_copy:
         calib_copy(args.calib_copy)
+    if args.only == "rope_inputs_b16_t4096":
+        print(json.dumps(run_rope(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "decode_b32_ctx2048_s1":
+        print(json.dumps(run_decode(2, args.steps, args.warmup, stride=1)), flush=True)
+        return
     if args.only == "prefill_b16_t4096_backward":
         print(json.dumps(run_backward(args.steps, args.warmup)), flush=True)
         return
@@ -515,6 +559,15 @@ def main():
         log("prefill_b16_t4096_backward ...")
         bw = extra["prefill_b16_t4096_backward"] = run_backward()
         log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
+        log("decode_b32_ctx2048_s1 (the MLA reduction, one slot per frame) ...")
+        m1 = extra["decode_b32_ctx2048_s1"] = run_decode(2, 50, 10, stride=1)
+        m1["cache_bytes_vs_s2"] = m1["cache_bytes"] / head["cache_bytes"]
+        m1["step_time_vs_s2"] = m1["step_ms"] / head["step_ms"]
+        log(f"  s=1: step {m1['step_ms']*1e3:.2f} us, cache {m1['cache_bytes']/1e6:.1f} MB "
+            f"({m1['cache_bytes_vs_s2']:.2f}x s=2), step time {m1['step_time_vs_s2']:.2f}x s=2")
+        log("rope_inputs_b16_t4096 ...")
+        ro = extra["rope_inputs_b16_t4096"] = run_rope()
+        log(f"  rotary inputs: {ro['step_ms']*1e3:.1f} us for {ro['B'] * ro['T']} frames")
         log("append_chunk_b32_l512 ...")
         a = extra["append_chunk_b32_l512"] = run_append()
         log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")

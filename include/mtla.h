@@ -115,6 +115,20 @@ mtla_status mtla_gate_pos_table(const mtla_dims *dims, const void *pe, int32_t r
 mtla_status mtla_gate_content_map(const mtla_dims *dims, const void *W_hc, const void *W_dkv,
                                   void *W_gate, void *stream);
 
+/* Decoupled-RoPE inputs ([Notes] decoupled RoPE with temporal compression:
+ * the RoPE-carrying parts of the queries and keys), for M frames X [M, d] at
+ * absolute positions pos [M] (device int32, >= 0):
+ *   QR[m, h] = R(pos[m]) W_QR[h] x_m   (W_QR [H*d_hR, d]: rows of head h)
+ *   KR[m]    = R(pos[m]) W_KR x_m      (W_KR [d_hR, d]; one key for all heads)
+ * where R(p) turns the adjacent pairs (2k, 2k+1) of a d_hR-wide vector by
+ * p * base^(-2k/d_hR) (the standard rotary form, base typically 10000; the
+ * pages do not spell the form out).  QR [M, H, d_hR], KR [M, d_hR] in the
+ * storage dtype: the inputs every other entry point takes already rotated.
+ * Angles are reduced in fp64.  Workspace: mtla_workspace_bytes(op=6, M, 1). */
+mtla_status mtla_rope_inputs(const mtla_dims *dims, const void *W_QR, const void *W_KR,
+                             const void *X, const int32_t *pos, int32_t M, float base, void *QR,
+                             void *KR, void *workspace, size_t ws_bytes, void *stream);
+
 /* Merge-append ([Notes] temporal merging; [Fig2] (a)): for every sequence b
  * with frame position t = pos[b] and j = floor(t/s):
  *   c = W_dkv x_t;  w = Sigmoid((W_gate x_t + b_hc) * gate_pos[j]);  u = w * c
@@ -287,7 +301,8 @@ mtla_status mtla_prefill_unabsorbed_timed(const mtla_dims *dims, const mtla_unab
 /* Workspace size in bytes for op 0 (merge-append), 1 (decode step, with
  * T_or_max_pos = max_pos), 2 (prefill, with T_or_max_pos = T), 3 (chunked
  * merge-append, with T_or_max_pos = L), 4 (per-head prefill, with
- * T_or_max_pos = T) or 5 (its backward, with T_or_max_pos = T).  Returns 0 for invalid arguments.
+ * T_or_max_pos = T), 5 (its backward, with T_or_max_pos = T) or 6 (rotary
+ * inputs of B * T_or_max_pos frames).  Returns 0 for invalid arguments.
  * Pure host function. */
 size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_t T_or_max_pos);
 

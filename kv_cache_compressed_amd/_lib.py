@@ -18,13 +18,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtla.so"
 
 MTLA_OK, MTLA_ERR_ARG, MTLA_ERR_CAPACITY, MTLA_ERR_UNSUPPORTED, MTLA_ERR_HIP = range(5)
 MTLA_F32, MTLA_BF16 = 0, 1
-OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK, OP_UNABSORBED, OP_BACKWARD = 0, 1, 2, 3, 4, 5
+OP_MERGE, OP_DECODE, OP_PREFILL, OP_CHUNK, OP_UNABSORBED, OP_BACKWARD, OP_ROPE = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
             "mtla_append_chunk", "mtla_decode_step", "mtla_prefill_strided",
             "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_prefill_unabsorbed",
             "mtla_prefill_unabsorbed_timed", "mtla_prefill_unabsorbed_backward",
-            "mtla_workspace_bytes",
+            "mtla_rope_inputs", "mtla_workspace_bytes",
             "mtla_status_string", "mtla_last_error_detail")
 
 
@@ -96,13 +96,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtla_prefill_unabsorbed_backward.argtypes = [
         P(Dims), P(UnabsorbedWeights), c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
         c_void_p, c_void_p, c_void_p, c_void_p, P(UnabsorbedGrads), c_void_p, c_size_t, c_void_p]
+    lib.mtla_rope_inputs.argtypes = [P(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                     c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
     for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
               "mtla_append_chunk", "mtla_decode_step",
               "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed",
               "mtla_prefill_unabsorbed", "mtla_prefill_unabsorbed_timed",
-              "mtla_prefill_unabsorbed_backward"):
+              "mtla_prefill_unabsorbed_backward", "mtla_rope_inputs"):
         getattr(lib, f).restype = c_int32
     lib.mtla_workspace_bytes.argtypes = [P(Dims), c_int32, c_int32, c_int32]
     lib.mtla_workspace_bytes.restype = c_size_t
@@ -290,6 +292,26 @@ def mtla_prefill_unabsorbed(dims: Dims, w: UnabsorbedWeights, X, QR, KR, Y=None,
     else:
         _check(lib.mtla_prefill_unabsorbed_timed(*args, _events(events)))
     return Y
+
+
+def mtla_rope_inputs(dims: Dims, W_QR, W_KR, X, pos, base: float = 10000.0, QR=None, KR=None,
+                     ws=None):
+    """Rotary query and key parts of the frames X [..., d] at positions pos
+    (same leading shape, int32): returns (QR [..., H, d_hR], KR [..., d_hR])."""
+    lead = tuple(X.shape[:-1])
+    M = 1
+    for n in lead:
+        M *= int(n)
+    if QR is None:
+        QR = torch.empty(*lead, dims.H, dims.d_hR, dtype=X.dtype, device=X.device)
+    if KR is None:
+        KR = torch.empty(*lead, dims.d_hR, dtype=X.dtype, device=X.device)
+    if ws is None:
+        ws = workspace(dims, OP_ROPE, M, 1, X.device)
+    _check(load_library().mtla_rope_inputs(ctypes.byref(dims), _ptr(W_QR), _ptr(W_KR), _ptr(X),
+                                           _ptr(pos), M, float(base), _ptr(QR), _ptr(KR),
+                                           _ptr(ws), ws.numel(), _stream()))
+    return QR, KR
 
 
 GRAD_NAMES = ("dW_dkv", "dW_hc", "db_hc", "dgate_pos", "dW_Q", "dW_K", "dW_V", "dW_O")

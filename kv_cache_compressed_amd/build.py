@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmtla.so")
-SOURCES = ["gemm.hip", "decode.hip", "attention.hip", "append.hip", "heads.hip", "backward.hip", "mtla_api.hip"]
+SOURCES = ["gemm.hip", "decode.hip", "attention.hip", "append.hip", "heads.hip", "backward.hip", "rope.hip", "mtla_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

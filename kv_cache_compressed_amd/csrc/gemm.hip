@@ -620,6 +620,15 @@ hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, in
   return run_gemm<float>((const float *)A, lda, bs, M, N, K, epi, stream);
 }
 
+hipError_t launch_gemm_f32_2(int dtype, const void *A, int lda, const void *B1, const void *B2,
+                             int N1, int ldb, int M, int N, int K, float *out, int ldc,
+                             hipStream_t stream) {
+  BSeg bs{B1, B2, B2, N1, N, ldb};
+  const EpiAccF32 epi{out, ldc, 0};
+  if (dtype == 1) return run_gemm<bf16>((const bf16 *)A, lda, bs, M, N, K, epi, stream);
+  return run_gemm<float>((const float *)A, lda, bs, M, N, K, epi, stream);
+}
+
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
                            float *part, int *counters, hipStream_t stream) {
   if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);

@@ -26,6 +26,18 @@ hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1,
 hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, int ldb, int M, int N,
                            int K, float *out, int ldc, bool add, hipStream_t stream);
 
+// out[M, N] (fp32) = A[M, K] [B1; B2]^T (columns < N1 from B1's rows).
+hipError_t launch_gemm_f32_2(int dtype, const void *A, int lda, const void *B1, const void *B2,
+                             int N1, int ldb, int M, int N, int K, float *out, int ldc,
+                             hipStream_t stream);
+
+// Decoupled-RoPE inputs: G [M, HR + DR] (fp32 scratch) = X [M, d] [W_QR; W_KR]^T,
+// then QR [M, HR] and KR [M, DR] (storage type) = G's adjacent pairs turned
+// by pos[m] * base^(-2k/DR) (k: the pair's index within its DR-wide vector).
+hipError_t launch_rope_inputs(int dtype, const void *X, int M, int d, const void *W_QR, int HR,
+                              const void *W_KR, int DR, const int32_t *pos, float base, float *G,
+                              void *QR, void *KR, hipStream_t stream);
+
 // table[rows, r] (fp32) = pe[rows, d_pe] W_hp[r, d_pe]^T + b_hp.
 hipError_t launch_pos_table(int dtype, const void *pe, int rows, int d_pe, const void *W_hp,
                             const void *b_hp, int r, float *table, hipStream_t stream);

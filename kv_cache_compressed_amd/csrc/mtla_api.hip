@@ -204,6 +204,11 @@ BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
   return w;
 }
 
+// Workspace of the rotary inputs of M frames: [M, (H + 1) d_hR] fp32.
+size_t rope_ws(const mtla_dims *d, int M) {
+  return align_up((size_t)M * (d->H + 1) * d->d_hR * 4);
+}
+
 // Workspace of a chunked merge-append of L frames: cg [B*L, 2r] fp32.
 size_t chunk_ws(const mtla_dims *d, int B, int L) {
   return align_up((size_t)B * L * 2 * d->r * 4);
@@ -258,6 +263,7 @@ size_t mtla_workspace_bytes(const mtla_dims *dims, int32_t op, int32_t B, int32_
     if (T_or_max_pos < 1) return 0;
     return heads_ws(dims, B, T_or_max_pos).total;
   }
+  if (op == 6) return rope_ws(dims, B * T_or_max_pos);
   if (op == 5) {
     if (T_or_max_pos < 1) return 0;
     return bwd_ws(dims, B, T_or_max_pos).total;
@@ -292,6 +298,32 @@ mtla_status mtla_gate_content_map(const mtla_dims *dims, const void *W_hc, const
   LAUNCH(mtla::launch_gate_map(dims->dtype, W_hc, W_dkv, dims->r, dims->d, W_gate,
                                (hipStream_t)stream),
          "gate content map");
+  return ok();
+}
+
+mtla_status mtla_rope_inputs(const mtla_dims *dims, const void *W_QR, const void *W_KR,
+                             const void *X, const int32_t *pos, int32_t M, float base, void *QR,
+                             void *KR, void *workspace, size_t ws_bytes, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  CHECK_PTR(W_QR);
+  CHECK_PTR(W_KR);
+  CHECK_PTR(X);
+  CHECK_PTR(pos);
+  CHECK_PTR(QR);
+  CHECK_PTR(KR);
+  CHECK_PTR(workspace);
+  if (M < 1) return fail(MTLA_ERR_ARG, "M=%d < 1", M);
+  if (!(base > 1.0f) || isinf(base)) return fail(MTLA_ERR_ARG, "base must be finite and > 1");
+  if (dims->d_hR % 2 != 0) return fail(MTLA_ERR_ARG, "d_hR=%d is odd", dims->d_hR);
+  const int N = dims->H * dims->d_hR + dims->d_hR;
+  if ((int64_t)M * N > 0x7fffffffLL) return fail(MTLA_ERR_UNSUPPORTED, "M too large");
+  const size_t need = rope_ws(dims, M);
+  if (ws_bytes < need) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, need);
+  LAUNCH(mtla::launch_rope_inputs(dims->dtype, X, M, dims->d, W_QR, dims->H * dims->d_hR, W_KR,
+                                  dims->d_hR, pos, base, (float *)workspace, QR, KR,
+                                  (hipStream_t)stream),
+         "rotary inputs");
   return ok();
 }
 

@@ -215,3 +215,15 @@ def test_append_chunk_workspace():
     d = _dims()
     assert K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 16) >= 4 * 16 * 2 * 256 * 4
     assert K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 16) < K.mtla_workspace_bytes(d, L.OP_CHUNK, 4, 17)
+
+
+def test_rope_inputs_reject_before_launch():
+    lib = K.load_library()
+    d = _dims()
+    args = lambda base, ws_bytes=1 << 20, M=4: (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, M,
+                                                 ctypes.c_float(base), FAKE, FAKE, FAKE,
+                                                 ws_bytes, None)
+    assert lib.mtla_rope_inputs(*args(1.0)) == L.MTLA_ERR_ARG
+    assert lib.mtla_rope_inputs(*args(10000.0, M=0)) == L.MTLA_ERR_ARG
+    assert lib.mtla_rope_inputs(*args(10000.0, ws_bytes=16)) == L.MTLA_ERR_ARG
+    assert K.mtla_workspace_bytes(d, L.OP_ROPE, 4, 1) >= 4 * 9 * 32 * 4
