@@ -488,6 +488,14 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   // Ring: about 4 stages of 36 KB, or more of smaller stages (at most 8).
   int nst = (int)(144 * 1024 / stage);
   if (nst > 8) nst = 8;
+  if (nst < 2) {
+    // A one-slot ring cannot refill a slot that the same stage still reads:
+    // give each split a single stage instead (more splits, same bytes).
+    nst = 1;
+    chunk = srows;
+    p.chunk = (int)chunk;
+    p.splits = (int)((nmax + chunk - 1) / chunk);
+  }
   if (nst > chunk / srows) nst = (int)(chunk / srows);
   if (nst < 1) nst = 1;
   p.nst = nst;

@@ -141,6 +141,23 @@ def test_decode_wide_latent_fp32():
     _decode_case(dims, [0, 3, 300], "f32", 7200)
 
 
+@pytest.mark.parametrize("H,r,dR,storage,s", [
+    (8, 256, 32, "bf16", 1),     # 64-row stages, 9 loads per wave: register-staged stream
+    (32, 256, 32, "bf16", 1),    # 32-row stages, 5 loads per wave, 8-slot ring
+    (48, 256, 32, "bf16", 1),    # 16-row stages, padding load blocks
+    (4, 512, 64, "f32", 2),      # 147 KB stages: one-slot ring, one stage per split
+])
+def test_decode_long_splits(H, r, dR, storage, s):
+    """Contexts long enough that each split streams many stages (beyond the
+    LDS ring: the later ones pass through registers), with ragged ends."""
+    needs_gpu()
+    dims = Dims(d=256, H=H, d_h=max(r // 4, 64), r=r, d_hR=dR, s=s)
+    rng = np.random.default_rng(7400 + H)
+    pos = rng.integers(8000 * s, 16000 * s, size=8)
+    say("decode long splits", H, r, storage, s)
+    _decode_case(dims, pos, storage, 7400 + H, check=[0, 3, 7])
+
+
 def test_decode_is_deterministic():
     needs_gpu()
     _, dims, ex = synth.config(2)
