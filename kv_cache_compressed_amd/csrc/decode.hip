@@ -282,6 +282,44 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     bar();
 
     // O^T += C^T P^T for this wave's channel quarter, every pair of the stage.
+    if constexpr (sizeof(T) == 2 && C::TPS % 2 == 0) {
+      // bf16: two 16-slot tiles form one 32-deep contraction (the full-rate
+      // 16x16x32 product).  k index 8g+e stands for slot 4g+e of the first
+      // tile (e < 4) and of the second (e >= 4), in both operands: C^T from
+      // one transposing read of each tile, P^T from the two tiles' P blocks.
+#pragma unroll
+      for (int tl = 0; tl < C::TPS; tl += 2) {
+        // A pair wholly past the split contributes nothing (a partly past
+        // second tile has P = 0 and zeroed rows).
+        if (row0 + tl * 16 >= end) continue;
+        const char *t0 = sb + tl * C::TILE_B;
+        bf16x8 pp[NHB];
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          const bf16x4 p0 = *(const bf16x4 *)(pbuf + ((tl * NHB + hb) * 64 + lane) * 8);
+          const bf16x4 p1 = *(const bf16x4 *)(pbuf + (((tl + 1) * NHB + hb) * 64 + lane) * 8);
+          pp[hb] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int q0 = 0; q0 < C::MQ; q0 += 4) {
+          uint32_t ad[8];
+          bf16x4 v[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ch0 = 16 * (wave * C::MQ + q0 + j);
+            ad[2 * j] = lds_addr(t0 + tile_off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
+            ad[2 * j + 1] = ad[2 * j] + C::TILE_B;
+          }
+          ds_read_tr8(v, ad);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 vv = __builtin_shufflevector(v[2 * j], v[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) o[hb][q0 + j] = mma_k32(vv, pp[hb], o[hb][q0 + j]);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int tl = 0; tl < C::TPS; ++tl) {
       if (row0 + tl * 16 >= end) continue;
@@ -311,6 +349,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb) o[hb][q0 + j] = mma_k16(vv[j], pp[hb], o[hb][q0 + j]);
       }
+    }
     }
   }
 
