@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmtla.so")
-SOURCES = ["gemm.hip", "decode.hip", "attention.hip", "append.hip", "heads.hip", "backward.hip", "rope.hip", "mtla_api.hip"]
+SOURCES = ["gemm.hip", "gemm_big.hip", "decode.hip", "attention.hip", "append.hip", "heads.hip", "backward.hip", "rope.hip", "mtla_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
@@ -33,8 +33,26 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Sources whose accumulators should live in AGPRs (a wave holding 256
+# accumulator registers at one wave per SIMD): built without the VGPR form.
+AGPR_SOURCES = {"gemm_big.hip"}
+
+
+def _flags(src: str):
+    if src not in AGPR_SOURCES:
+        return FLAGS
+    out, i = [], 0
+    while i < len(FLAGS):
+        if FLAGS[i] == "-mllvm" and FLAGS[i + 1].startswith("-amdgpu-mfma-vgpr-form"):
+            i += 2
+            continue
+        out.append(FLAGS[i])
+        i += 1
+    return out
+
+
 def _compile(src: str, obj: str, verbose: bool):
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

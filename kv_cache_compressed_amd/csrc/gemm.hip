@@ -3,7 +3,8 @@
 // notes, method section: overall framework, hyper-network temporal merging,
 // the Y formula of decoupled RoPE).
 //
-// Two kernels:
+// Two kernels here, and gemm_big_kernel (gemm_big.hip) for large bf16
+// products:
 //  * gemm_nt_kernel, for many rows (the parallel form): a workgroup of 4
 //    waves owns a BM x BN output tile; K advances 32 at a time through two
 //    LDS buffers with register prefetch (one barrier per step); LDS rows are
@@ -20,7 +21,10 @@
 // rest from B3), so that one pass over X yields the latent c = X W_dkv^T, the
 // gate pre-activation X W_gate^T and the absorbed queries q~ = X A^T.
 
+#include <type_traits>
+
 #include "common.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace mtla {
@@ -29,16 +33,6 @@ namespace {
 
 constexpr int BK = 32;
 
-struct BSeg {
-  const void *B1, *B2, *B3;
-  int N1, N2;
-  int ldb;
-  template <typename T> __device__ __forceinline__ const T *row(int n) const {
-    if (n < N1) return (const T *)B1 + (size_t)n * ldb;
-    if (n < N2) return (const T *)B2 + (size_t)(n - N1) * ldb;
-    return (const T *)B3 + (size_t)(n - N2) * ldb;
-  }
-};
 
 // K split over blockIdx.z: split z covers k in [z kchunk, (z+1) kchunk).
 // With more than one split the fp32 partial tiles go to `part` (coherent
@@ -385,48 +379,6 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a, Epi epi)
   if (tid == 0) __hip_atomic_store(&a.counters[strip], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- epilogues ---------------------------------------------------------------
-
-template <typename T> struct EpiStore {
-  T *out;
-  int ldc;
-  __device__ void operator()(int m, int n, float v) const { out[(size_t)m * ldc + n] = from_f32<T>(v); }
-};
-
-// fp32 output, stored or added to what is there.
-struct EpiAccF32 {
-  float *out;
-  int ldc;
-  int add;
-  __device__ void operator()(int m, int n, float v) const {
-    float *p = out + (size_t)m * ldc + n;
-    *p = add ? *p + v : v;
-  }
-};
-
-struct EpiBiasF32 {
-  float *out;
-  const void *bias;
-  int is_bf16;
-  int ldc;
-  __device__ void operator()(int m, int n, float v) const {
-    float b = is_bf16 ? to_f32(((const bf16 *)bias)[n]) : ((const float *)bias)[n];
-    out[(size_t)m * ldc + n] = v + b;
-  }
-};
-
-// Columns [0, 2r): latent c and gate pre-activation, fp32 into cg [M, 2r];
-// columns [2r, 2r + HR): absorbed queries into qt [M, HR] (storage type).
-template <typename T> struct EpiProj {
-  float *cg;
-  T *qt;
-  int r2, HR;
-  __device__ void operator()(int m, int n, float v) const {
-    if (n < r2) cg[(size_t)m * r2 + n] = v;
-    else qt[(size_t)m * HR + (n - r2)] = from_f32<T>(v);
-  }
-};
-
 // W_gate[i, k] = sum_j W_hc[i, j] W_dkv[j, k], accumulated in fp32.
 template <typename T>
 __global__ __launch_bounds__(256) void gate_map_kernel(const T *W_hc, const T *W_dkv, int r, int d,
@@ -444,6 +396,10 @@ template <typename T, class Epi>
 hipError_t run_gemm(const T *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
                     hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  // Stored outputs of large bf16 products take the 256 x 256 tile; fp32
+  // read-modify-write epilogues stay here (they outweigh its gain).
+  if constexpr (sizeof(T) == 2 && (std::is_same_v<Epi, EpiStore<bf16>> || std::is_same_v<Epi, EpiProj<bf16>>))
+    if (gemm_big_supported(M, N, K)) return launch_gemm_big(A, lda, bs, M, N, K, epi, stream);
   if (M <= 128 || sizeof(T) == 4) {
     // fp32 tiles of 128 x 128 would need more than 64 KB of static LDS.
     dim3 grid((N + 63) / 64, (M + 127) / 128);

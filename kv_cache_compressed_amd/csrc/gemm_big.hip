@@ -1,0 +1,170 @@
+// Large bf16 NT products C = A B^T on gfx950 MFMA (the projections of the
+// parallel form: many thousands of rows), with the fused epilogues of
+// gemm_common.h.
+//
+// A workgroup of 4 waves owns a 256 x 256 output tile, one workgroup per
+// compute unit, and each wave a 128 x 128 quarter: 64 accumulator tiles of
+// 16 x 16 (256 registers, held in AGPRs -- this file is built without the
+// flag that keeps accumulators in ordinary VGPRs).  Each 16-byte operand
+// fragment read from LDS then feeds 8 products (32 flops per LDS byte per
+// operand), against 4 in a 64 x 64 wave tile, which left the older kernel
+// bound by LDS bandwidth.
+//
+// K advances 32 at a time through a ring of 4 LDS stages (32 KB each: the
+// 256 A rows and 256 B rows of the step, as 16-row tiles in the swizzled
+// layout of common.h) filled by direct global->LDS loads.  Stage k+1's
+// fragments are read into the second register set while the products of
+// stage k run, so the products never wait on LDS; one barrier per stage.
+
+#include "common.h"
+#include "gemm_common.h"
+
+namespace mtla {
+
+namespace {
+
+constexpr int GB_TILE = 1024;                    // 16 rows x 64 bytes
+constexpr int GB_ROWT = 256 / 16;                // 16-row tiles of A (and of B) per stage
+constexpr int GB_STAGE = 2 * GB_ROWT * GB_TILE;  // 32 KB
+constexpr int GB_NST = 4;
+constexpr int GB_LPW = 2 * GB_ROWT / 4;          // loads per wave per stage
+constexpr int GB_LDS = GB_NST * GB_STAGE;
+
+typedef bf16x8 GbFrag[8];
+
+template <class Epi>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict__ A, int lda,
+                                                          BSeg bs, int M, int N, int K, Epi epi) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Workgroups go round-robin to the 8 XCDs; when the tile count allows,
+  // XCD x takes a contiguous run of tiles in row-major order, so the column
+  // tiles sharing an A row block run together on one L2.
+  int tm = blockIdx.y, tn = blockIdx.x;
+  {
+    const int nT = gridDim.x * gridDim.y;
+    if (nT % 8 == 0) {
+      const int id = blockIdx.y * gridDim.x + blockIdx.x;
+      const int t = (id % 8) * (nT / 8) + id / 8;
+      tm = t / gridDim.x;
+      tn = t % gridDim.x;
+    }
+  }
+  const int m0 = tm * 256, n0 = tn * 256;
+
+  // This wave's loads of a stage: block blk = wave + 4 i is A row tile blk
+  // (blk < 16) or B row tile blk - 16; lane l copies row l/4 of the tile.
+  // Rows past M or N read the last row (valid memory; never stored).
+  const char *rp[GB_LPW];
+#pragma unroll
+  for (int i = 0; i < GB_LPW; ++i) {
+    const int blk = wave + 4 * i;
+    if (blk < GB_ROWT) {
+      const int row = min(m0 + 16 * blk + (lane >> 2), M - 1);
+      rp[i] = (const char *)(A + (size_t)row * lda);
+    } else {
+      const int row = min(n0 + 16 * (blk - GB_ROWT) + (lane >> 2), N - 1);
+      rp[i] = (const char *)bs.row<bf16>(row);
+    }
+  }
+  auto issue = [&](int kt) {
+    char *sb = smem + (kt % GB_NST) * GB_STAGE;
+#pragma unroll
+    for (int i = 0; i < GB_LPW; ++i) dma_block(rp[i] + kt * 64, 0, sb + (wave + 4 * i) * GB_TILE);
+  };
+  // Fragments of stage kt: A row tiles 8 wm + i, B row tiles 8 wn + j; lane
+  // (g, c) holds row c, k 8 g .. 8 g + 7 of the stage.
+  auto frags = [&](int kt, GbFrag &fa, GbFrag &fb) {
+    const char *sb = smem + (kt % GB_NST) * GB_STAGE + tile_off(c, g * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa[i] = *(const bf16x8 *)(sb + (8 * wm + i) * GB_TILE);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8 *)(sb + (GB_ROWT + 8 * wn + j) * GB_TILE);
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int KT = K / 32;
+  const int pro = min(GB_NST, KT);
+  for (int kt = 0; kt < pro; ++kt) issue(kt);
+  int last = pro - 1;
+  // Stages 0 and 1 resident before the first barrier.
+  wait_stages<GB_LPW>(last - min(1, KT - 1));
+  bar();
+  GbFrag fa0, fb0, fa1, fb1;
+  frags(0, fa0, fb0);
+
+  // Iteration kt: refill the slot of stage kt (its fragments were read in
+  // iteration kt-1, before the last barrier) with stage kt + NST; read stage
+  // kt+1's fragments (resident and visible since that barrier); the 64
+  // products of stage kt; stage kt+2 resident, then the barrier.
+  auto iter = [&](int kt, GbFrag &fa, GbFrag &fb, GbFrag &na, GbFrag &nb) {
+    if (kt + GB_NST < KT) {
+      issue(kt + GB_NST);
+      last = kt + GB_NST;
+    }
+    if (kt + 1 < KT) frags(kt + 1, na, nb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mma_k32(fa[i], fb[j], acc[i][j]);
+    if (kt + 2 < KT) wait_stages<GB_LPW>(last - (kt + 2));
+    // Stage kt+1's fragments are in registers before its slot can be refilled.
+    wait_lgkm0();
+    bar();
+  };
+  // KT is even (K is a multiple of 64): the two register sets alternate.
+  for (int kt = 0; kt < KT; kt += 2) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    iter(kt + 1, fa1, fb1, fa0, fb0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + 128 * wn + 16 * j + c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 128 * wm + 16 * i + 4 * g + e;
+        if (m < M && n < N) epi(m, n, acc[i][j][e]);
+      }
+    }
+}
+
+}  // namespace
+
+bool gemm_big_supported(int M, int N, int K) {
+  // Enough 256 x 256 tiles to fill the compute units, and K long enough
+  // (1024: 32 stages) that a tile's loop outweighs its epilogue, which with
+  // one workgroup per compute unit overlaps nothing (at K = 512 the input
+  // projection of the parallel form measured 371 us against 311 us for
+  // gemm_nt_kernel; at K = 2048 the output projection 172 against 206 us).
+  return M >= 2048 && N >= 256 && K >= 1024 && K % 64 == 0 &&
+         (size_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
+}
+
+template <class Epi>
+hipError_t launch_gemm_big(const bf16 *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
+                           hipStream_t stream) {
+  allow_lds<gemm_big_kernel<Epi>>();
+  dim3 grid((N + 255) / 256, (M + 255) / 256);
+  hipLaunchKernelGGL(gemm_big_kernel<Epi>, grid, dim3(256), GB_LDS, stream, A, lda, bs, M, N, K,
+                     epi);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gemm_big<EpiStore<bf16>>(const bf16 *, int, const BSeg &, int, int, int,
+                                                    EpiStore<bf16>, hipStream_t);
+template hipError_t launch_gemm_big<EpiProj<bf16>>(const bf16 *, int, const BSeg &, int, int, int,
+                                                   EpiProj<bf16>, hipStream_t);
+
+}  // namespace mtla

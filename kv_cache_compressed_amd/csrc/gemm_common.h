@@ -1,0 +1,70 @@
+// Shared by the dense-product sources: B as up to three row segments, the
+// fused epilogues, and the large-tile bf16 product of gemm_big.hip.
+#pragma once
+
+#include "common.h"
+
+namespace mtla {
+
+struct BSeg {
+  const void *B1, *B2, *B3;
+  int N1, N2;
+  int ldb;
+  template <typename T> __device__ __forceinline__ const T *row(int n) const {
+    if (n < N1) return (const T *)B1 + (size_t)n * ldb;
+    if (n < N2) return (const T *)B2 + (size_t)(n - N1) * ldb;
+    return (const T *)B3 + (size_t)(n - N2) * ldb;
+  }
+};
+
+// ---- epilogues: called per output element (m, n) with its fp32 value ----
+
+template <typename T> struct EpiStore {
+  T *out;
+  int ldc;
+  __device__ void operator()(int m, int n, float v) const { out[(size_t)m * ldc + n] = from_f32<T>(v); }
+};
+
+// fp32 output, stored or added to what is there.
+struct EpiAccF32 {
+  float *out;
+  int ldc;
+  int add;
+  __device__ void operator()(int m, int n, float v) const {
+    float *p = out + (size_t)m * ldc + n;
+    *p = add ? *p + v : v;
+  }
+};
+
+struct EpiBiasF32 {
+  float *out;
+  const void *bias;
+  int is_bf16;
+  int ldc;
+  __device__ void operator()(int m, int n, float v) const {
+    float b = is_bf16 ? to_f32(((const bf16 *)bias)[n]) : ((const float *)bias)[n];
+    out[(size_t)m * ldc + n] = v + b;
+  }
+};
+
+// Columns [0, 2r): latent c and gate pre-activation, fp32 into cg [M, 2r];
+// columns [2r, 2r + HR): absorbed queries into qt [M, HR] (storage type).
+template <typename T> struct EpiProj {
+  float *cg;
+  T *qt;
+  int r2, HR;
+  __device__ void operator()(int m, int n, float v) const {
+    if (n < r2) cg[(size_t)m * r2 + n] = v;
+    else qt[(size_t)m * HR + (n - r2)] = from_f32<T>(v);
+  }
+};
+
+// Large bf16 products (gemm_big.hip): C = A B^T with M, N large and K a
+// multiple of 64 (at least 1024); one workgroup of 4 waves per compute unit
+// owns a 256 x 256 tile.  Instantiated for EpiStore<bf16> and EpiProj<bf16>.
+bool gemm_big_supported(int M, int N, int K);
+template <class Epi>
+hipError_t launch_gemm_big(const bf16 *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
+                           hipStream_t stream);
+
+}  // namespace mtla

@@ -136,3 +136,35 @@ def test_prefill_then_decode_resumes():
         e = relerr(got, ref["Y"][T0:])
         say(f"  b={b} resumed relerr {e:.3g}")
         assert e < TOL["bf16"]
+
+
+def test_large_tile_product_ragged_edges():
+    """The output projection of a long batch takes the 256 x 256-tile product
+    (K = H r = 2048): here with 32,769 rows (the last row tile holds one row)
+    and d = 320 columns (the second column tile holds 64), checked on sampled
+    rows that include the last one, all columns."""
+    needs_gpu()
+    dims = Dims(d=320, H=8, d_h=64, r=256, d_hR=32, s=2)
+    B, T = 9, 3641
+    assert B * T == 32769
+    ms = om.n_slots(T, dims.s)
+    w, W, L = layer(dims, 4100, "bf16", pe_rows=ms)
+    seq = synth.make_sequence(dims, w, B, T, 4101, "bf16")
+    say("prefill ragged large-tile product", B, T, dims.d)
+    Y = L.prefill(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16"))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4102)
+    for b in (0, 4, B - 1):
+        X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
+        _, U = om.gated_latents(X, W, dims.s)
+        Cpr = om.intermediate_states(U, dims.s)
+        rows = sorted(set([0, 1, 255, 256, T - 2, T - 1] + list(rng.integers(0, T, size=16))))
+        Yg = host(Y[b, rows])
+        Yr = []
+        for m in rows:
+            vis = [n for n in range(m + 1) if om.visible(m, n, dims.s)]
+            o = om.attend_cache(W["A"] @ X[m], QR[m], Cpr[vis], KR[vis], dims.scale)
+            Yr.append(om.output_projection(o, W["Bvo"]))
+        e = relerr(Yg, np.stack(Yr))
+        say(f"  b={b} sampled-row relerr {e:.3g}")
+        assert e < TOL["bf16"]
