@@ -19,6 +19,10 @@
 #include "common.h"
 #include "gemm_common.h"
 
+#ifndef MTLA_GEMM_BIG_MIN_K
+#define MTLA_GEMM_BIG_MIN_K 1024
+#endif
+
 namespace mtla {
 
 namespace {
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mma_k32(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < 8; ++j) acc[i][j] = mma_k32(fb[j], fa[i], acc[i][j]);
     if (kt + 2 < KT) wait_stages<GB_LPW>(last - (kt + 2));
     // Stage kt+1's fragments are in registers before its slot can be refilled.
     wait_lgkm0();
@@ -127,15 +131,22 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
     iter(kt + 1, fa1, fb1, fa0, fb0);
   }
 
+  // The products are C^T tiles (B rows as the A operand): lane (g, c) holds
+  // row m = ... + c and the four consecutive columns n = ... + 4 g .. + 3,
+  // stored together.
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int n = n0 + 128 * wn + 16 * j + c;
+      const int m = m0 + 128 * wm + 16 * i + c;
+      const int n = n0 + 128 * wn + 16 * j + 4 * g;
+      if (m >= M) continue;
+      if (n + 3 < N) {
+        epi.four(m, n, acc[i][j]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 128 * wm + 16 * i + 4 * g + e;
-        if (m < M && n < N) epi(m, n, acc[i][j][e]);
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) epi(m, n + e, acc[i][j][e]);
       }
     }
 }
@@ -148,7 +159,7 @@ bool gemm_big_supported(int M, int N, int K) {
   // one workgroup per compute unit overlaps nothing (at K = 512 the input
   // projection of the parallel form measured 371 us against 311 us for
   // gemm_nt_kernel; at K = 2048 the output projection 172 against 206 us).
-  return M >= 2048 && N >= 256 && K >= 1024 && K % 64 == 0 &&
+  return M >= 2048 && N >= 256 && K >= MTLA_GEMM_BIG_MIN_K && K % 64 == 0 &&
          (size_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
 }
 

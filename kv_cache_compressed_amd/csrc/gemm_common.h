@@ -23,6 +23,9 @@ template <typename T> struct EpiStore {
   T *out;
   int ldc;
   __device__ void operator()(int m, int n, float v) const { out[(size_t)m * ldc + n] = from_f32<T>(v); }
+  // Columns n .. n+3 of row m (n + 3 < N, n a multiple of 4).
+  __device__ void four(int m, int n, f32x4 v) const { store4f(out + (size_t)m * ldc + n, v); }
+  bool four_aligned() const { return ldc % 4 == 0; }
 };
 
 // fp32 output, stored or added to what is there.
@@ -57,11 +60,19 @@ template <typename T> struct EpiProj {
     if (n < r2) cg[(size_t)m * r2 + n] = v;
     else qt[(size_t)m * HR + (n - r2)] = from_f32<T>(v);
   }
+  // Columns n .. n+3 of row m (n + 3 < N; r2 is a multiple of 4, so the four
+  // lie on one side of it).
+  __device__ void four(int m, int n, f32x4 v) const {
+    if (n < r2) *(f32x4 *)(cg + (size_t)m * r2 + n) = v;
+    else store4f(qt + (size_t)m * HR + (n - r2), v);
+  }
+  bool four_aligned() const { return r2 % 4 == 0 && HR % 4 == 0; }
 };
 
 // Large bf16 products (gemm_big.hip): C = A B^T with M, N large and K a
-// multiple of 64 (at least 1024); one workgroup of 4 waves per compute unit
-// owns a 256 x 256 tile.  Instantiated for EpiStore<bf16> and EpiProj<bf16>.
+// multiple of 64; one workgroup of 4 waves per compute unit owns a 256 x 256
+// tile, stored four columns at a time (epi.four, rows aligned to 4 values:
+// epi.four_aligned()).  Instantiated for EpiStore<bf16> and EpiProj<bf16>.
 bool gemm_big_supported(int M, int N, int K);
 template <class Epi>
 hipError_t launch_gemm_big(const bf16 *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
