@@ -168,3 +168,37 @@ def test_large_tile_product_ragged_edges():
         e = relerr(Yg, np.stack(Yr))
         say(f"  b={b} sampled-row relerr {e:.3g}")
         assert e < TOL["bf16"]
+
+
+def test_large_tile_input_projection():
+    """d = 1024 puts the input projection (latent, gate pre-activation and
+    absorbed queries: N = 2r + H r = 2560 columns, K = d) on the 256 x 256-tile
+    product too, with 6,600 rows (the last row tile partly filled): the
+    intermediate states in full, outputs on sampled rows."""
+    needs_gpu()
+    dims = Dims(d=1024, H=8, d_h=64, r=256, d_hR=32, s=2)
+    B, T = 2, 3300
+    ms = om.n_slots(T, dims.s)
+    w, W, L = layer(dims, 4200, "bf16", pe_rows=ms)
+    seq = synth.make_sequence(dims, w, B, T, 4201, "bf16")
+    say("prefill large-tile input projection", B, T, dims.d)
+    Cp = torch.empty(B, T, dims.r, dtype=torch.bfloat16, device="cuda")
+    Y = L.prefill(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16"), Cprime=Cp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4202)
+    for b in range(B):
+        X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
+        _, U = om.gated_latents(X, W, dims.s)
+        Cpr = om.intermediate_states(U, dims.s)
+        ec = relerr(host(Cp[b]), Cpr)
+        rows = sorted(set([0, 1, 255, 256, T - 2, T - 1] + list(rng.integers(0, T, size=16))))
+        Yg = host(Y[b, rows])
+        Yr = []
+        for m in rows:
+            vis = [n for n in range(m + 1) if om.visible(m, n, dims.s)]
+            o = om.attend_cache(W["A"] @ X[m], QR[m], Cpr[vis], KR[vis], dims.scale)
+            Yr.append(om.output_projection(o, W["Bvo"]))
+        e = relerr(Yg, np.stack(Yr))
+        say(f"  b={b} C' relerr {ec:.3g}  sampled-row relerr {e:.3g}")
+        assert ec < TOL["bf16"]
+        assert e < TOL["bf16"]
