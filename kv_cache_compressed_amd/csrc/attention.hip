@@ -52,28 +52,32 @@ __global__ __launch_bounds__(256) void group_scan_kernel(const float *cg, const 
                                                          int T_len, int R, int DR, int s, int nS,
                                                          T *Cp, T *keys, int64_t kstride, T *cache,
                                                          int64_t cstride) {
+  // One thread per (slot j, four consecutive channels): 16-byte fp32 loads of
+  // c and g, 4-value stores (R, DR and every row stride are multiples of 4).
   const int b = blockIdx.y;
-  const int RK = R + DR;
+  const int RK = R + DR, Q = RK / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)nS * RK) return;
-  const int j = (int)(idx / RK), ch = (int)(idx % RK);
+  if (idx >= (int64_t)nS * Q) return;
+  const int j = (int)(idx / Q), ch = 4 * (int)(idx % Q);
   const int i0 = j * s, i1 = min(i0 + s, T_len) - 1;
-  T v;
+  f32x4 v;
   if (ch < R) {
-    const float bb = to_f32(b_hc[ch]), pj = table[(size_t)j * R + ch];
-    float acc = 0.0f;
+    const f32x4 bb = load4f(b_hc + ch), pj = *(const f32x4 *)(table + (size_t)j * R + ch);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int i = i0; i <= i1; ++i) {
       const size_t row = (size_t)b * T_len + i;
       const float *r = cg + row * 2 * R;
-      acc += sigmoidf((r[R + ch] + bb) * pj) * r[ch];
-      Cp[row * R + ch] = from_f32<T>(acc);
+      const f32x4 c = *(const f32x4 *)(r + ch), g = *(const f32x4 *)(r + R + ch);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += sigmoidf((g[e] + bb[e]) * pj[e]) * c[e];
+      store4f(Cp + row * R + ch, acc);
     }
-    v = from_f32<T>(acc);
+    v = acc;
   } else {
-    v = KR[((size_t)b * T_len + i1) * DR + (ch - R)];
+    v = load4f(KR + ((size_t)b * T_len + i1) * DR + (ch - R));
   }
-  keys[(size_t)b * kstride + (size_t)j * RK + ch] = v;
-  if (cache) cache[(size_t)b * cstride + (size_t)j * RK + ch] = v;
+  store4f(keys + (size_t)b * kstride + (size_t)j * RK + ch, v);
+  if (cache) store4f(cache + (size_t)b * cstride + (size_t)j * RK + ch, v);
 }
 
 struct PrefillArgs {
@@ -733,7 +737,7 @@ hipError_t launch_group_scan(int dtype, const float *cg, const void *b_hc, const
                              void *keys, int64_t keys_stride, void *cache, int64_t cache_stride,
                              hipStream_t stream) {
   const int nS = (T + s - 1) / s;
-  const int64_t work = (int64_t)nS * (r + dR);
+  const int64_t work = (int64_t)nS * ((r + dR) / 4);
   dim3 grid((unsigned)((work + 255) / 256), B);
   if (dtype == 1)
     hipLaunchKernelGGL(group_scan_kernel<bf16>, grid, dim3(256), 0, stream, cg, (const bf16 *)b_hc,
