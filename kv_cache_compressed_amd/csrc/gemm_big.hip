@@ -20,7 +20,7 @@
 #include "gemm_common.h"
 
 #ifndef MTLA_GEMM_BIG_MIN_K
-#define MTLA_GEMM_BIG_MIN_K 1024
+#define MTLA_GEMM_BIG_MIN_K 512
 #endif
 
 namespace mtla {
@@ -105,6 +105,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
   bar();
   GbFrag fa0, fb0, fa1, fb1;
   frags(0, fa0, fb0);
+  // Nothing from LDS may be in flight at the loop head: the compiler merges
+  // the loop entry with the back edge there, and reads still pending from
+  // the entry made it wait for every LDS read, including the next stage's,
+  // before the products of each even stage.
+  wait_lgkm0();
 
   // Iteration kt: refill the slot of stage kt (its fragments were read in
   // iteration kt-1, before the last barrier) with stage kt + NST; read stage
@@ -155,10 +160,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
 
 bool gemm_big_supported(int M, int N, int K) {
   // Enough 256 x 256 tiles to fill the compute units, and K long enough
-  // (1024: 32 stages) that a tile's loop outweighs its epilogue, which with
-  // one workgroup per compute unit overlaps nothing (at K = 512 the input
-  // projection of the parallel form measured 371 us against 311 us for
-  // gemm_nt_kernel; at K = 2048 the output projection 172 against 206 us).
+  // (512: 16 stages) that a tile's loop outweighs its epilogue, which with
+  // one workgroup per compute unit overlaps nothing.  At K = 512 the input
+  // projection of the parallel form (65,536 rows, 2,560 columns) takes
+  // 13-30 us less than in gemm_nt_kernel; at K = 2048 the output projection
+  // 172 against 206 us.
   return M >= 2048 && N >= 256 && K >= MTLA_GEMM_BIG_MIN_K && K % 64 == 0 &&
          (size_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
 }
