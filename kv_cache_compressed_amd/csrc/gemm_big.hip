@@ -116,15 +116,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
   // kt+1's fragments (resident and visible since that barrier); the 64
   // products of stage kt; stage kt+2 resident, then the barrier.
   auto iter = [&](int kt, GbFrag &fa, GbFrag &fb, GbFrag &na, GbFrag &nb) {
-    if (kt + GB_NST < KT) {
-      issue(kt + GB_NST);
-      last = kt + GB_NST;
-    }
+    const bool refill = kt + GB_NST < KT;
+    if (refill) last = kt + GB_NST;
     if (kt + 1 < KT) frags(kt + 1, na, nb);
+    // The refill's 8 loads go one per row of 8 products, so that a wave (the
+    // only one on its SIMD) never holds the matrix core idle behind a burst
+    // of load issues.
+    char *rs = smem + (kt % GB_NST) * GB_STAGE;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      if (refill) dma_block(rp[i] + (kt + GB_NST) * 64, 0, rs + (wave + 4 * i) * GB_TILE);
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = mma_k32(fb[j], fa[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (kt + 2 < KT) wait_stages<GB_LPW>(last - (kt + 2));
     // Stage kt+1's fragments are in registers before its slot can be refilled.
     wait_lgkm0();
