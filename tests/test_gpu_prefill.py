@@ -171,10 +171,11 @@ def test_large_tile_product_ragged_edges():
 
 
 def test_large_tile_input_projection():
-    """d = 1024 puts the input projection (latent, gate pre-activation and
-    absorbed queries: N = 2r + H r = 2560 columns, K = d) on the 256 x 256-tile
-    product too, with 6,600 rows (the last row tile partly filled): the
-    intermediate states in full, outputs on sampled rows."""
+    """The input projection (latent, gate pre-activation and absorbed
+    queries: N = 2r + H r = 2560 columns, K = d) on the 256 x 256-tile product
+    at d = 1024, a K twice the one the other prefill tests use, with 6,600 rows
+    (the last row tile partly filled): the intermediate states in full, outputs
+    on sampled rows."""
     needs_gpu()
     dims = Dims(d=1024, H=8, d_h=64, r=256, d_hR=32, s=2)
     B, T = 2, 3300
