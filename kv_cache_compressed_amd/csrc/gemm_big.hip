@@ -142,23 +142,36 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
   }
 
   // The products are C^T tiles (B rows as the A operand): lane (g, c) holds
-  // row m = ... + c and the four consecutive columns n = ... + 4 g .. + 3,
-  // stored together.
+  // row 16 i + c and the four consecutive columns 16 j + 4 g .. + 3 of the
+  // wave's quarter.  Stored like that, each store instruction would write
+  // 32-byte pieces of 16 rows.  Instead each wave passes its rows through
+  // its own LDS block (the ring is free after the last barrier), 16 at a
+  // time: written in the product layout, read back so that 32 lanes cover
+  // one row's 128 columns, and stored as whole row runs.  Rows are padded to
+  // 528 bytes so that the 16 rows of a write fall in distinct banks.  A
+  // wave's LDS accesses complete in order, so no barrier is needed.
+  constexpr int SROW = 528;
+  char *stg = smem + wave * 16 * SROW;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int m = m0 + 128 * wm + 16 * i + c;
-      const int n = n0 + 128 * wn + 16 * j + 4 * g;
+    for (int j = 0; j < 8; ++j) *(f32x4 *)(stg + c * SROW + (16 * j + 4 * g) * 4) = acc[i][j];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 2 * k + (lane >> 5), cc = 4 * (lane & 31);
+      const f32x4 v = *(const f32x4 *)(stg + rr * SROW + cc * 4);
+      const int m = m0 + 128 * wm + 16 * i + rr;
+      const int n = n0 + 128 * wn + cc;
       if (m >= M) continue;
       if (n + 3 < N) {
-        epi.four(m, n, acc[i][j]);
+        epi.four(m, n, v);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < N) epi(m, n + e, acc[i][j][e]);
+          if (n + e < N) epi(m, n + e, v[e]);
       }
     }
+  }
 }
 
 }  // namespace
