@@ -139,7 +139,11 @@ mtla_status mtla_rope_inputs(const mtla_dims *dims, const void *W_QR, const void
  * X_t [B, d], KR_t [B, d_hR] (already rotated), pos [B] int32 device array.
  * max_pos: host-side upper bound of every pos[b] (the caller's contract);
  * floor(max_pos/s) must be < cache->max_slots and < gate_pos_rows
- * (else MTLA_ERR_CAPACITY).  Workspace: mtla_workspace_bytes(op=0). */
+ * (else MTLA_ERR_CAPACITY).  The device checks the contract as well: a
+ * sequence whose pos[b] lies outside [0, max_pos] is dropped (nothing of it
+ * is read or written), and the int32 status word at byte 0 of the workspace
+ * holds, once the call has completed, the number of dropped sequences (each
+ * call clears it first).  Workspace: mtla_workspace_bytes(op=0). */
 mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                               const void *X_t, const void *KR_t, const int32_t *pos, int32_t B,
                               int32_t max_pos, void *workspace, size_t ws_bytes, void *stream);
@@ -178,8 +182,14 @@ mtla_status mtla_append_chunk(const mtla_dims *dims, const mtla_weights *w, cons
  *   z_j  = (q~_h . c^_j + QR_t[b, h] . k^R_j) * scale,  j = 0 .. floor(pos[b]/s)
  *   o_h  = sum_j softmax(z)_j c^_j        (the newest slot may be temporary)
  *   Y[b] = sum_h Bvo[:, h, :] o_h
- * QR_t [B, H, d_hR] already rotated; Y [B, d].  Workspace:
- * mtla_workspace_bytes(op=1). */
+ * QR_t [B, H, d_hR] already rotated; Y [B, d].  Positions follow
+ * mtla_merge_append's contract and device check: a sequence whose pos[b] lies
+ * outside [0, max_pos] is dropped -- no cache row of it is read or written,
+ * Y[b] = 0 -- and counted in the int32 status word at byte 0 of the
+ * workspace.  The slot work is balanced over the workgroups from the actual
+ * positions (up to 256 sequences).  Results do not depend on the workspace's
+ * prior contents, and two calls on the same inputs give identical bits.
+ * Workspace: mtla_workspace_bytes(op=1). */
 mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const mtla_cache *cache,
                              const void *X_t, const void *QR_t, const void *KR_t, const int32_t *pos,
                              int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,

@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     make_unabsorbed_weights, make_weights, mtla_append_chunk, mtla_decode_step,
     mtla_gate_content_map, mtla_gate_pos_table, mtla_merge_append, mtla_prefill_strided,
     mtla_prefill_unabsorbed, mtla_prefill_unabsorbed_backward, mtla_rope_inputs,
-    mtla_status_string, mtla_workspace_bytes, workspace)
+    mtla_status_string, mtla_workspace_bytes, workspace, dropped_frames)
 from .layer import MTLALayer  # noqa: F401

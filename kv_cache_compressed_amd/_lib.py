@@ -180,6 +180,14 @@ def workspace(dims: Dims, op: int, B: int, T_or_max_pos: int, device="cuda") -> 
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def dropped_frames(ws: torch.Tensor) -> int:
+    """The status word of a merge-append or decode-step workspace: the number
+    of sequences whose position lay outside [0, max_pos] in the last call on
+    it (their frames were not merged).  Reading it synchronises with the
+    device."""
+    return int(ws[:4].view(torch.int32).item())
+
+
 def mtla_gate_pos_table(dims: Dims, pe, W_hp, b_hp, table=None):
     rows, d_pe = pe.shape
     if table is None:

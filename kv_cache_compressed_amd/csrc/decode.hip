@@ -8,13 +8,22 @@
 // decoupled RoPE with temporal compression (the Y formula).
 // [Fig2] = "Multi-head Temporal Latent Attention" (sciencestack.ai), Fig. 2 (a).
 //
-// Attention kernel, one workgroup (4 waves) per (sequence b, split of `chunk`
+// Attention kernel: one workgroup (4 waves) per (sequence b, split of its
 // slots).  All heads of a sequence read the same compressed rows (one latent
 // cache shared by every head), so each row is fetched from HBM once:
-//  * The split's rows stream into a ring of LDS stages by direct
-//    global->LDS loads (global_load_lds_dwordx4, no register staging), up to
-//    `nst` stages in flight.  A stage is TPS 16-row tiles, TPS = 4 / NHB for
-//    NHB blocks of 16 heads.
+//  * Work list.  Every workgroup derives the same balanced assignment from
+//    the positions: a sequence of m_b stages (SROWS slots each) gets
+//    ceil(m_b / c) splits of at most c stages, c the smallest value (from
+//    ceil(sum m_b / G) up) for which all splits fit the G workgroups of the
+//    grid, so ragged batches stream equal slot counts per workgroup.  Above
+//    256 sequences the splits are uniform, sized from max_pos.
+//  * Streaming.  The split's rows stream HBM -> LDS by direct loads
+//    (global_load_lds_dwordx4, non-temporal) into a ring of up to `nst`
+//    stages.  Each 1 KB load covers 8 rows x one whole 128-byte line (rows of
+//    576 bytes are paired into 1152-byte super-rows), with a per-row XOR
+//    permutation of the 16-byte chunks that keeps the MFMA operand reads
+//    below conflict free.  A stage is TPS 16-row tiles, TPS = 4 / NHB for NHB
+//    blocks of 16 heads.
 //  * Scores: wave w takes one (tile, head block) pair of the stage and
 //    computes S^T (16 keys x 16 heads) = K . Q^T on the K=32 MFMA, K (latent
 //    ++ RoPE key, r + d_hR wide) from LDS as the A operand, Q^T from
@@ -25,10 +34,9 @@
 //    almost every stage.  P = 2^(z - m) goes to LDS in bf16 (fp32 storage:
 //    fp32).
 //  * Values: wave w accumulates O^T for its quarter of the r latent channels,
-//    all heads, all tiles of the stage: O^T += C^T . P^T on the K=16 MFMA,
-//    C^T read from the row-major tile with ds_read_tr16_b64 (its A layout)
-//    and P^T from LDS (the score layout is the B layout).  O needs no
-//    cross-wave reduction at the end.
+//    all heads, all tiles of the stage: O^T += C^T . P^T, C^T read from the
+//    tile with ds_read_b64_tr_b16 (its A layout) and P^T from LDS (the score
+//    layout is the B layout).  O needs no cross-wave reduction at the end.
 //  * The split that owns the newest slot j = floor(t/s) first merges the new
 //    frame: u = Sigmoid((g + b_hc) * Linear(pe_j)) * c, slot j = u (t mod s
 //    == 0) or slot j + u, RoPE key j = K^R_t, written to the cache and into
@@ -37,6 +45,10 @@
 //    last split of a sequence to finish (atomic counter) merges them by
 //    log-sum-exp in split order (deterministic results).  A sequence that
 //    fits one split is normalised and written directly.
+//  * Positions.  A sequence whose pos[b] lies outside [0, max_pos] (the
+//    caller's bound, which the host checked against the cache and the gate
+//    table) is dropped: nothing is merged or read, its output row is zero,
+//    and the status word counts it.
 
 #include <math.h>
 
@@ -50,6 +62,46 @@ namespace {
 constexpr float kNegInf = -INFINITY;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// LDS layout of one 16-row tile of streamed cache rows (RB bytes each): RB/64
+// blocks of 1 KB, each filled by one direct load of 8 rows x one 128-byte
+// line.  Rows whose length is a multiple of 128 bytes: block 2q + h holds
+// line q of rows 8h..8h+7 (row i of the block at 128 i).  576-byte rows: rows
+// 2k and 2k+1 form a 1152-byte super-row k, and block q holds line q of the
+// 8 super-rows.  The 16-byte chunks of the 128-byte run of block row i are
+// permuted by XOR with i, which keeps both the score operand reads (16 rows x
+// 16 bytes per k-step) and the transposing reads (4 rows x 32 bytes per 16
+// lanes) free of bank conflicts; the choice was measured with the LDS
+// bank-conflict counter against other permutations, several of which
+// conflict two-way.
+template <int RB> struct DecLayout {
+  static constexpr bool PAIRED = (RB % 128) != 0;
+  static_assert(!PAIRED || RB == 576, "rows must be 576 bytes or a multiple of 128");
+  // Byte offset within the tile of byte b of row R (0 <= R < 16).
+  __device__ static int off(int R, int b) {
+    if constexpr (!PAIRED) {
+      return ((b >> 7) << 11) + ((R >> 3) << 10) + ((R & 7) << 7) +
+             ((((b >> 4) & 7) ^ (R & 7)) << 4) + (b & 15);
+    } else {
+      const int sb = (R & 1) * 576 + b, k = R >> 1;
+      return ((sb >> 7) << 10) + (k << 7) + ((((sb >> 4) & 7) ^ k) << 4) + (sb & 15);
+    }
+  }
+  // The row and byte that lane `lane` copies for block `blk` of a tile (its
+  // 16 bytes land at byte 16 lane of the block).
+  __device__ static void src(int blk, int lane, int &R, int &b) {
+    const int i = lane >> 3, v = lane & 7;
+    if constexpr (!PAIRED) {
+      R = ((blk & 1) << 3) + i;
+      b = ((blk >> 1) << 7) + ((v ^ i) << 4);
+    } else {
+      const int sb = (blk << 7) + ((v ^ i) << 4);
+      const int hi = sb >= 576;
+      R = 2 * i + hi;
+      b = sb - (hi ? 576 : 0);
+    }
+  }
+};
 
 template <typename T, int R, int DR, int NHB> struct DecCfg {
   static constexpr int RK = R + DR, ES = (int)sizeof(T), RB = RK * ES, NSEG = RB / 64;
@@ -68,6 +120,30 @@ template <typename T, int R, int DR, int NHB> struct DecCfg {
   static_assert(NHB * TPS == 4, "one (tile, head block) pair per wave");
 };
 
+// Score operand (row `row`, k-step ks, lane group g) and fp32 value operand
+// from a tile in the decode layout; the same lane mapping as s_frag and
+// v_frag_f32.
+template <typename T, class Lay>
+__device__ __forceinline__ typename Frag<T>::type dec_frag(const char *tile, int row, int ks, int g) {
+  if constexpr (sizeof(T) == 2) {
+    return *(const bf16x8 *)(tile + Lay::off(row, ks * 64 + g * 16));
+  } else {
+    const f32x4 x = *(const f32x4 *)(tile + Lay::off(row, ks * 128 + g * 32));
+    const f32x4 y = *(const f32x4 *)(tile + Lay::off(row, ks * 128 + g * 32 + 16));
+    return (f32x8){x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  }
+}
+template <class Lay>
+__device__ __forceinline__ f32x4 dec_vfrag_f32(const char *tile, int ch0, int g, int j) {
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = *(const float *)(tile + Lay::off(4 * g + e, (ch0 + j) * 4));
+  return v;
+}
+
+// Cache policy of the stream's loads: non-temporal (each row is read once).
+constexpr int kStreamPolicy = 2;
+
 struct DecodeArgs {
   const int32_t *pos;
   char *cache;
@@ -78,32 +154,173 @@ struct DecodeArgs {
   const float *cg;     // [B, 2R]: latent c then gate pre-activation g
   const void *b_hc;    // [R]
   const float *gate_pos;
-  float *part_o;       // [B, splits, H, R]
-  float *part_ml;      // [B, splits, H, 2]
+  float *part_o;       // [nparts, H, R]
+  float *part_ml;      // [nparts, H, 2]
   int *counters;       // [B], zero on entry (zero again on exit)
+  int *status;         // count of dropped sequences (cleared before the kernel)
   void *o;             // [B, H, R]
-  int H, s, chunk, splits, nst;
+  int B, H, s, chunk, splits, nst, nparts, max_pos, flat;
   float sl2;
 };
+
+// Wave-wide integer scans and reductions on DPP row shifts and lane reads
+// (VALU only: no LDS round trips in the kernel's prologue).
+__device__ __forceinline__ int dpp_shr(int v, int n) {
+  switch (n) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  }
+}
+// Inclusive scan over the 64 lanes; *total receives the sum of all lanes.
+__device__ __forceinline__ int wave_incl_scan(int v, int *total) {
+  v += dpp_shr(v, 1);
+  v += dpp_shr(v, 2);
+  v += dpp_shr(v, 4);
+  v += dpp_shr(v, 8);   // inclusive within each row of 16 lanes
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  const int row = (threadIdx.x & 63) >> 4;
+  v += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  *total = r0 + r1 + r2 + r3;
+  return v;
+}
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, dpp_shr(v, 1));
+  v = max(v, dpp_shr(v, 2));
+  v = max(v, dpp_shr(v, 4));
+  v = max(v, dpp_shr(v, 8));
+  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Balanced work list (every wave of every workgroup computes the same one):
+// sequence b has m_b = ceil(n_b / SROWS) stages (n_b slots; 0 when dropped)
+// and takes max(1, ceil(m_b / c)) splits of at most c stages.  c is the
+// smallest value from ceil(sum m_b / G) up (eight tries, then max m_b, which
+// always fits because G >= B) for which the splits fit the G workgroups.
+// Lane l owns sequences [l P, l P + P).  Returns the sequence of workgroup w
+// (-1 when w has no work) with its split index, split count, first partial
+// index and c.
+template <int SROWS>
+__device__ void flat_assign(const DecodeArgs &a, int w, int &b, int &split, int &ns, int &pbase,
+                            int &cst) {
+  constexpr int PMAX = 4;
+  const int lane = threadIdx.x & 63;
+  const int P = (a.B + 63) / 64;
+  int m[PMAX];
+  int msum = 0, mmax = 0;
+#pragma unroll
+  for (int i = 0; i < PMAX; ++i) {
+    m[i] = 0;
+    const int bb = lane * P + i;
+    if (i < P && bb < a.B) {
+      const int t = a.pos[bb];
+      const bool valid = t >= 0 && t <= a.max_pos;
+      m[i] = valid ? (t / a.s + SROWS) / SROWS : 0;   // ceil((floor(t/s) + 1) / SROWS)
+    }
+    msum += m[i];
+    mmax = max(mmax, m[i]);
+  }
+  int M;
+  (void)wave_incl_scan(msum, &M);
+  mmax = wave_max_nonneg(mmax);
+  const int G = (int)gridDim.x;
+  auto splits_of = [&](int c) {
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < PMAX; ++i)
+      if (i < P && lane * P + i < a.B) v += m[i] > 0 ? (m[i] + c - 1) / c : 1;
+    return v;
+  };
+  int c = max(1, (M + G - 1) / G);
+  int tries = 0, mine, total;
+  for (;;) {
+    mine = splits_of(c);
+    (void)wave_incl_scan(mine, &total);
+    if (total <= G) break;
+    if (++tries >= 8) {
+      c = max(1, mmax);
+      mine = splits_of(c);
+      break;
+    }
+    ++c;
+  }
+  // Exclusive prefix of the split counts over the lanes, then the owner.
+  int pre = wave_incl_scan(mine, &total) - mine;
+  int fb = -1, fs = 0, fn = 0, fp = 0;
+#pragma unroll
+  for (int i = 0; i < PMAX; ++i) {
+    const int bb = lane * P + i;
+    if (i < P && bb < a.B) {
+      const int k = m[i] > 0 ? (m[i] + c - 1) / c : 1;
+      if (w >= pre && w < pre + k) {
+        fb = bb;
+        fs = w - pre;
+        fn = k;
+        fp = pre;
+      }
+      pre += k;
+    }
+  }
+  // At most one lane found w: its values reach every lane.
+  const unsigned long long hit = __ballot(fb >= 0);
+  if (hit == 0ull) {
+    b = -1;
+    split = ns = pbase = 0;
+  } else {
+    const int src = __ffsll((long long)hit) - 1;
+    b = __builtin_amdgcn_readlane(fb, src);
+    split = __builtin_amdgcn_readlane(fs, src);
+    ns = __builtin_amdgcn_readlane(fn, src);
+    pbase = __builtin_amdgcn_readlane(fp, src);
+  }
+  cst = c;
+}
 
 template <typename T, int R, int DR, int NHB>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   using C = DecCfg<T, R, DR, NHB>;
+  using Lay = DecLayout<C::RB>;
   typedef typename Frag4<T>::type P4;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int b = blockIdx.y, split = blockIdx.x;
-  const int t = a.pos[b], s = a.s, jn = t / s, n = jn + 1;
-  const int start = split * a.chunk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int b, split, ns, pbase, start, end;
+  if (a.flat) {
+    int cst;
+    flat_assign<C::SROWS>(a, (int)blockIdx.x, b, split, ns, pbase, cst);
+    if (b < 0) return;
+    start = split * cst * C::SROWS;
+    end = start + cst * C::SROWS;   // clipped to n below
+  } else {
+    b = blockIdx.y;
+    split = blockIdx.x;
+    pbase = b * a.splits;
+    start = split * a.chunk;
+    end = start + a.chunk;
+    ns = -1;   // from n below
+  }
+  const int t = a.pos[b], s = a.s;
+  const bool valid = t >= 0 && t <= a.max_pos;
+  const int H = a.H;
+  if (!valid) {
+    // Dropped frame: only the sequence's first split acts.
+    if (split != 0) return;
+    if (tid == 0) atomicAdd(a.status, 1);
+    for (int i = tid; i < H * R; i += 256) ((T *)a.o)[(size_t)b * H * R + i] = from_f32<T>(0.0f);
+    return;
+  }
+  const int jn = t / s, n = jn + 1;
+  if (ns < 0) ns = (n + a.chunk - 1) / a.chunk;
   if (start >= n) return;
-  const int end = min(n, start + a.chunk);
-  const int ns = (n + a.chunk - 1) / a.chunk;
+  end = min(n, end);
   const bool owner = end == n;
   const int nstage = (end - start + C::SROWS - 1) / C::SROWS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int st_tile = wave % C::TPS, st_hb = wave / C::TPS;   // score pair of this wave
-  const int H = a.H, shead = st_hb * 16 + c;
+  const int shead = st_hb * 16 + c;
   char *seq = a.cache + (size_t)b * a.bstride_bytes;
   char *dummy = smem + a.nst * C::STAGE_B;
   float *smax = (float *)(dummy + 1024);                       // [TPS][HW]
@@ -153,9 +370,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     for (int i = 0; i < C::LPW; ++i) {
       const int blk = wave + 4 * i;
       const bool real = (C::NBLK % 4 == 0) || blk < C::NBLK;
-      const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
-      const int slot = min(row0 + tl * 16 + (lane >> 2), end - 1);
-      dma_block(seq + (size_t)slot * C::RB, qq, real ? sb + tl * C::TILE_B + qq * 1024 : dummy);
+      const int tl = real ? blk / C::NSEG : 0, bq = real ? blk % C::NSEG : 0;
+      int rr, bb;
+      Lay::src(bq, lane, rr, bb);
+      const int slot = min(row0 + tl * 16 + rr, end - 1);
+      __builtin_amdgcn_global_load_lds((const void *)(seq + (size_t)slot * C::RB + bb),
+                                       (lds_void *)(real ? sb + tl * C::TILE_B + bq * 1024 : dummy),
+                                       16, 0, kStreamPolicy);
     }
   };
   const int pro = min(a.nst, nstage);
@@ -175,15 +396,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   }
   float lp = 0.0f;
 
-  for (int k = 0; k < nstage; ++k) {
+  // Software pipeline over the stages: an iteration computes the scores of
+  // stage k+1 beside the P.V of stage k (independent work), then the max
+  // exchange and softmax of stage k+1 (after P.V(k), so a moved reference max
+  // rescales O with stage k already in it).  Stage k's ring slot stays in use
+  // until P.V(k), so the slot refilled after stage k+1 lands is stage k-1's.
+  auto land = [&](int k) {
     // Stage k has landed once at most lastst - k stages issued after it are
     // still in flight (this wave's loads complete in issue order).
     wait_stages<C::LPW>(lastst - k);
     bar();
-    // Every wave is past stage k-1 here: its ring slot can be refilled.
-    if (k >= 1 && k - 1 + a.nst < nstage) {
-      issue(k - 1 + a.nst);
-      lastst = k - 1 + a.nst;
+    // Every wave is past the P.V of stage k-2 here: its slot can be refilled.
+    if (k >= 2 && k - 2 + a.nst < nstage) {
+      issue(k - 2 + a.nst);
+      lastst = k - 2 + a.nst;
     }
     char *sb = smem + (k % a.nst) * C::STAGE_B;
     const int row0 = start + k * C::SROWS;
@@ -193,7 +419,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       const int nz = row0 + C::SROWS - end;
       for (int idx = tid; idx < nz * (C::RB / 16); idx += 256) {
         const int r = end - row0 + idx / (C::RB / 16), ch = idx % (C::RB / 16);
-        *(u32x4 *)(sb + (r >> 4) * C::TILE_B + tile_off(r & 15, ch * 16)) = (u32x4){0u, 0u, 0u, 0u};
+        *(u32x4 *)(sb + (r >> 4) * C::TILE_B + Lay::off(r & 15, ch * 16)) = (u32x4){0u, 0u, 0u, 0u};
       }
       if (owner) {
         // Merge the new frame into the newest slot ([Notes] hyper-network
@@ -206,7 +432,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
         for (int i = 0; i < C::NU; ++i) {
           const int ch = tid + 256 * i;
           if (ch < R) {
-            T *lpnt = (T *)(trow + tile_off(rr & 15, ch * C::ES));
+            T *lpnt = (T *)(trow + Lay::off(rr & 15, ch * C::ES));
             const float u = sigmoidf((mg[i] + to_f32(mb[i])) * mp[i]) * mc[i];
             const T v = from_f32<T>(open ? u : to_f32(*lpnt) + u);
             *lpnt = v;
@@ -215,7 +441,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
         }
         if (tid < DR) {
           const T v = mkr;
-          *(T *)(trow + tile_off(rr & 15, (R + tid) * C::ES)) = v;
+          *(T *)(trow + Lay::off(rr & 15, (R + tid) * C::ES)) = v;
           grow[R + tid] = v;
         }
       }
@@ -223,27 +449,35 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
       bar();
     }
 
+  };
+  auto stage_scores = [&](int k, float (&z)[4]) {
+    char *sb = smem + (k % a.nst) * C::STAGE_B;
+    const int row0 = start + k * C::SROWS;
     // Scores of this wave's (tile, head block) pair.
     const char *stile = sb + st_tile * C::TILE_B;
     const int kb = row0 + st_tile * 16;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks + 1 < C::KS; ks += 2) {
-      s0 = mma_k32(s_frag<T>(stile, c, ks, g), q[ks], s0);
-      s1 = mma_k32(s_frag<T>(stile, c, ks + 1, g), q[ks + 1], s1);
+      s0 = mma_k32(dec_frag<T, Lay>(stile, c, ks, g), q[ks], s0);
+      s1 = mma_k32(dec_frag<T, Lay>(stile, c, ks + 1, g), q[ks + 1], s1);
     }
-    if constexpr (C::KS % 2) s0 = mma_k32(s_frag<T>(stile, c, C::KS - 1, g), q[C::KS - 1], s0);
-    float z[4], mx = kNegInf;
+    if constexpr (C::KS % 2) s0 = mma_k32(dec_frag<T, Lay>(stile, c, C::KS - 1, g), q[C::KS - 1], s0);
+    float mx = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       z[e] = (kb + 4 * g + e < end) ? (s0[e] + s1[e]) * a.sl2 : kNegInf;
       mx = fmaxf(mx, z[e]);
     }
+  };
+  // Max exchange and softmax of a stage's scores: rescales O when a head's
+  // reference max moves, writes P to LDS.
+  auto stage_softmax = [&](float (&z)[4]) {
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mx = max_g(mx);   // -inf only for a tile wholly past the split
     if (g == 0) smax[st_tile * C::HW + shead] = mx;
     wait_lgkm0();
     bar();
-
     // Reference max per head, identical in every wave; rescale when it moves.
     float mnew[NHB];
     bool up_any = false;
@@ -280,7 +514,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     *(P4 *)(pbuf + ((st_tile * NHB + st_hb) * 64 + lane) * 4 * C::ES) = pf;
     wait_lgkm0();
     bar();
-
+  };
+  auto stage_pv = [&](int k) {
+    char *sb = smem + (k % a.nst) * C::STAGE_B;
+    const int row0 = start + k * C::SROWS;
     // O^T += C^T P^T for this wave's channel quarter, every pair of the stage.
     if constexpr (sizeof(T) == 2 && C::TPS % 2 == 0) {
       // bf16: two 16-slot tiles form one 32-deep contraction (the full-rate
@@ -307,7 +544,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int ch0 = 16 * (wave * C::MQ + q0 + j);
-            ad[2 * j] = lds_addr(t0 + tile_off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
+            ad[2 * j] = lds_addr(t0 + Lay::off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
             ad[2 * j + 1] = ad[2 * j] + C::TILE_B;
           }
           ds_read_tr8(v, ad);
@@ -337,12 +574,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int ch0 = 16 * (wave * C::MQ + q0 + (j < QN ? j : 0));
-            ad[j] = lds_addr(tile + tile_off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
+            ad[j] = lds_addr(tile + Lay::off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
           }
           ds_read_tr8(vv, ad);
         } else {
 #pragma unroll
-          for (int j = 0; j < QN; ++j) vv[j] = v_frag_f32(tile, 16 * (wave * C::MQ + q0 + j), g, c);
+          for (int j = 0; j < QN; ++j) vv[j] = dec_vfrag_f32<Lay>(tile, 16 * (wave * C::MQ + q0 + j), g, c);
         }
 #pragma unroll
         for (int j = 0; j < QN; ++j)
@@ -350,6 +587,22 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
           for (int hb = 0; hb < NHB; ++hb) o[hb][q0 + j] = mma_k16(vv[j], pp[hb], o[hb][q0 + j]);
       }
     }
+    }
+  };
+
+  float zc[4];
+  land(0);
+  stage_scores(0, zc);
+  stage_softmax(zc);
+  for (int k = 0; k < nstage; ++k) {
+    if (k + 1 < nstage) {
+      land(k + 1);
+      float zn[4];
+      stage_scores(k + 1, zn);
+      stage_pv(k);
+      stage_softmax(zn);
+    } else {
+      stage_pv(k);
     }
   }
 
@@ -360,11 +613,11 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   if (g == 0) smax[st_tile * C::HW + shead] = lt;
   wait_lgkm0();
   bar();
-  const size_t pbase = ((size_t)b * a.splits + split) * H;
+  const size_t pidx = ((size_t)pbase + split) * H;
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(a.part_o, (uint32_t)((size_t)gridDim.y * a.splits * H * R * 4));
+      make_rsrc(a.part_o, (uint32_t)((size_t)a.nparts * H * R * 4));
   const __amdgpu_buffer_rsrc_t rml =
-      make_rsrc(a.part_ml, (uint32_t)((size_t)gridDim.y * a.splits * H * 8));
+      make_rsrc(a.part_ml, (uint32_t)((size_t)a.nparts * H * 8));
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     const int head = hb * 16 + c;
@@ -381,12 +634,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[hb][qb][e] * inv);
       } else {
-        st_coh4(ro, (uint32_t)(((pbase + head) * R + ch) * 4), o[hb][qb]);
+        st_coh4(ro, (uint32_t)(((pidx + head) * R + ch) * 4), o[hb][qb]);
       }
     }
     if (ns > 1 && wave == 0 && g == 0) {
-      st_coh1(rml, (uint32_t)((pbase + head) * 8), m[hb]);
-      st_coh1(rml, (uint32_t)((pbase + head) * 8 + 4), L);
+      st_coh1(rml, (uint32_t)((pidx + head) * 8), m[hb]);
+      st_coh1(rml, (uint32_t)((pidx + head) * 8 + 4), L);
     }
   }
   if (ns == 1) return;
@@ -403,7 +656,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   constexpr int QC = R / 4;   // 4-channel chunks per head
   constexpr int UB = 2, SB = 8;
   const int nch = H * QC;
-  const size_t base = (size_t)b * a.splits * H;
+  const size_t base = (size_t)pbase * H;
   for (int c0 = tid; c0 < nch; c0 += UB * 256) {
     float M[UB], L[UB];
     f32x4 acc[UB];
@@ -463,13 +716,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   if (tid == 0) __hip_atomic_store(&a.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stand-alone merge-append: one workgroup per sequence.
+// Stand-alone merge-append: one workgroup per sequence.  A position outside
+// [0, max_pos] drops the frame (counted in *status).
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t *pos, int s, int R, int DR,
-                                                    const float *cg, const T *b_hc,
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t *pos, int max_pos, int s, int R,
+                                                    int DR, const float *cg, const T *b_hc,
                                                     const float *gate_pos, const T *KR,
-                                                    char *cache, int64_t bstride_bytes) {
-  const int b = blockIdx.x, t = pos[b], j = t / s;
+                                                    char *cache, int64_t bstride_bytes,
+                                                    int *status) {
+  const int b = blockIdx.x, t = pos[b];
+  if (t < 0 || t > max_pos) {
+    if (threadIdx.x == 0) atomicAdd(status, 1);
+    return;
+  }
+  const int j = t / s;
   const bool open = (t % s) == 0;
   T *row = (T *)(cache + (size_t)b * bstride_bytes) + (size_t)j * (R + DR);
   for (int ch = threadIdx.x; ch < R; ch += blockDim.x) {
@@ -487,8 +747,8 @@ hipError_t decode_attn_t(const DecodePlan &p, int B, DecodeArgs args, hipStream_
                          hipEvent_t ev0, hipEvent_t ev1) {
   auto kern = decode_attn_kernel<T, R, DR, NHB>;
   allow_lds<decode_attn_kernel<T, R, DR, NHB>>();
-  return launch_timed((const void *)kern, dim3(p.splits, B), dim3(256), p.lds, stream, &args,
-                      ev0, ev1);
+  const dim3 grid = p.flat ? dim3(p.grid) : dim3(p.splits, B);
+  return launch_timed((const void *)kern, grid, dim3(256), p.lds, stream, &args, ev0, ev1);
 }
 
 template <typename T, int R, int DR>
@@ -516,26 +776,45 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   const size_t extra =
       1024 + (size_t)tps * 16 * p.nhb * 4 + (size_t)tps * p.nhb * 64 * 4 * esz + 16;
   const int64_t nmax = max_pos / s + 1;
-  const int64_t total = (int64_t)B * nmax;
-  int64_t chunk = (total + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS;
-  chunk = ((chunk + srows - 1) / srows) * srows;
-  const int64_t cap = ((nmax + srows - 1) / srows) * srows;
-  if (chunk > cap) chunk = cap;
+  const int64_t mstages = (nmax + srows - 1) / srows;   // stages of the longest sequence
   p.block = srows;
-  p.chunk = (int)chunk;
-  p.splits = (int)((nmax + chunk - 1) / chunk);
   // Ring: about 4 stages of 36 KB, or more of smaller stages (at most 8).
   int nst = (int)(144 * 1024 / stage);
   if (nst > 8) nst = 8;
-  if (nst < 2) {
-    // A one-slot ring cannot refill a slot that the same stage still reads:
-    // give each split a single stage instead (more splits, same bytes).
-    nst = 1;
-    chunk = srows;
+  // Balanced work list on the device for up to 256 sequences (four per lane
+  // of the kernel's tables), when a split may hold more than one stage.
+  p.flat = (B <= 256 && nst >= 2) ? 1 : 0;
+  if (p.flat) {
+    int64_t G = B <= MTLA_DECODE_TARGET_WGS / 2
+                    ? MTLA_DECODE_TARGET_WGS
+                    : ((2 * (int64_t)B + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS) *
+                          MTLA_DECODE_TARGET_WGS;
+    if (G > (int64_t)B * mstages) G = (int64_t)B * mstages;   // never more splits than stages
+    if (G < B) G = B;
+    p.grid = (int)G;
+    p.nparts = (int)G;
+    p.chunk = 0;
+    p.splits = 0;
+    if (nst > mstages) nst = (int)mstages;
+  } else {
+    const int64_t total = (int64_t)B * nmax;
+    int64_t chunk = (total + MTLA_DECODE_TARGET_WGS - 1) / MTLA_DECODE_TARGET_WGS;
+    chunk = ((chunk + srows - 1) / srows) * srows;
+    const int64_t cap = mstages * srows;
+    if (chunk > cap) chunk = cap;
+    if (nst < 2) {
+      // A one-slot ring cannot refill a slot that the same stage still reads:
+      // give each split a single stage instead (more splits, same bytes).
+      nst = 1;
+      chunk = srows;
+    }
+    if (nst > chunk / srows) nst = (int)(chunk / srows);
     p.chunk = (int)chunk;
     p.splits = (int)((nmax + chunk - 1) / chunk);
+    p.grid = 0;
+    if ((int64_t)B * p.splits > 0x7fffffffLL) return false;
+    p.nparts = B * p.splits;
   }
-  if (nst > chunk / srows) nst = (int)(chunk / srows);
   if (nst < 1) nst = 1;
   p.nst = nst;
   p.lds = nst * stage + extra;
@@ -545,17 +824,38 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
 }
 
 hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
-                                   int s, float scale, const int32_t *pos, void *cache,
+                                   int s, float scale, const int32_t *pos, int max_pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
                                    const float *gate_pos, float *part_o, float *part_ml,
-                                   int *counters, void *o, hipStream_t stream, hipEvent_t ev0,
-                                   hipEvent_t ev1) {
+                                   int *counters, int *status, void *o, hipStream_t stream,
+                                   hipEvent_t ev0, hipEvent_t ev1) {
   const int esz = dtype == 1 ? 2 : 4;
-  DecodeArgs args{pos,      (char *)cache, batch_stride * esz, qt,         QR,
-                  KR_t,     cg,            b_hc,               gate_pos,   part_o,
-                  part_ml,  counters,      o,                  H,          s,
-                  plan.chunk, plan.splits, plan.nst,           scale * kLog2e};
+  DecodeArgs args;
+  args.pos = pos;
+  args.cache = (char *)cache;
+  args.bstride_bytes = batch_stride * esz;
+  args.qt = qt;
+  args.QR = QR;
+  args.KR = KR_t;
+  args.cg = cg;
+  args.b_hc = b_hc;
+  args.gate_pos = gate_pos;
+  args.part_o = part_o;
+  args.part_ml = part_ml;
+  args.counters = counters;
+  args.status = status;
+  args.o = o;
+  args.B = B;
+  args.H = H;
+  args.s = s;
+  args.chunk = plan.chunk;
+  args.splits = plan.splits;
+  args.nst = plan.nst;
+  args.nparts = plan.nparts;
+  args.max_pos = max_pos;
+  args.flat = plan.flat;
+  args.sl2 = scale * kLog2e;
   if (dtype == 1) {
     if (r == 256) return decode_attn_h<bf16, 256, 32>(plan, B, args, stream, ev0, ev1);
     return decode_attn_h<bf16, 512, 64>(plan, B, args, stream, ev0, ev1);
@@ -564,18 +864,18 @@ hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int
   return decode_attn_h<float, 512, 64>(plan, B, args, stream, ev0, ev1);
 }
 
-hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,
-                        const void *b_hc, const float *gate_pos, const void *KR_t, void *cache,
-                        int64_t batch_stride, hipStream_t stream) {
+hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, int max_pos,
+                        const float *cg, const void *b_hc, const float *gate_pos, const void *KR_t,
+                        void *cache, int64_t batch_stride, int *status, hipStream_t stream) {
   const int esz = dtype == 1 ? 2 : 4;
   if (dtype == 1)
-    hipLaunchKernelGGL(merge_kernel<bf16>, dim3(B), dim3(256), 0, stream, pos, s, r, dR, cg,
-                       (const bf16 *)b_hc, gate_pos, (const bf16 *)KR_t, (char *)cache,
-                       batch_stride * esz);
+    hipLaunchKernelGGL(merge_kernel<bf16>, dim3(B), dim3(256), 0, stream, pos, max_pos, s, r, dR,
+                       cg, (const bf16 *)b_hc, gate_pos, (const bf16 *)KR_t, (char *)cache,
+                       batch_stride * esz, status);
   else
-    hipLaunchKernelGGL(merge_kernel<float>, dim3(B), dim3(256), 0, stream, pos, s, r, dR, cg,
-                       (const float *)b_hc, gate_pos, (const float *)KR_t, (char *)cache,
-                       batch_stride * esz);
+    hipLaunchKernelGGL(merge_kernel<float>, dim3(B), dim3(256), 0, stream, pos, max_pos, s, r, dR,
+                       cg, (const float *)b_hc, gate_pos, (const float *)KR_t, (char *)cache,
+                       batch_stride * esz, status);
   return hipGetLastError();
 }
 

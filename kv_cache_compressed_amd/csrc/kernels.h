@@ -71,8 +71,11 @@ int out_proj_strips(int M, int N);
 struct DecodePlan {
   int nhb;      // head blocks of 16
   int block;    // slots per LDS stage
-  int chunk;    // slots per split (workgroup)
-  int splits;   // splits per sequence (grid x)
+  int flat;     // 1: balanced work list derived on the device from the positions
+  int grid;     // workgroups (flat)
+  int chunk;    // slots per split (uniform splits, flat == 0)
+  int splits;   // splits per sequence (uniform: grid x, with grid y = B)
+  int nparts;   // split partials the workspace holds
   int nst;      // LDS ring stages
   size_t lds;   // dynamic LDS bytes
 };
@@ -84,21 +87,23 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
 // Merge of frame pos[b] into slot floor(pos[b]/s) of every sequence (from
 // cg = (c, gate pre-activation) and the tables), then attention over slots
 // 0..floor(pos[b]/s) into o [B, H, r] (storage type).  qt [B, H, r], QR
-// [B, H, dR], KR_t [B, dR]; split partials part_o [B, splits, H, r] and
-// part_ml [B, splits, H, 2] fp32; counters [B], zero on entry (zero again on
-// exit).
+// [B, H, dR], KR_t [B, dR]; split partials part_o [plan.nparts, H, r] and
+// part_ml [plan.nparts, H, 2] fp32; counters [B], zero on entry (zero again
+// on exit).  A sequence with pos[b] outside [0, max_pos] is dropped (no
+// merge, o row zero) and counted in *status (cleared by the caller).
 hipError_t launch_decode_attention(int dtype, const DecodePlan &plan, int B, int H, int r, int dR,
-                                   int s, float scale, const int32_t *pos, void *cache,
+                                   int s, float scale, const int32_t *pos, int max_pos, void *cache,
                                    int64_t batch_stride, const void *qt, const void *QR,
                                    const void *KR_t, const float *cg, const void *b_hc,
                                    const float *gate_pos, float *part_o, float *part_ml,
-                                   int *counters, void *o, hipStream_t stream,
+                                   int *counters, int *status, void *o, hipStream_t stream,
                                    hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
-// Merge alone (no attention), one workgroup per sequence.
-hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, const float *cg,
-                        const void *b_hc, const float *gate_pos, const void *KR_t, void *cache,
-                        int64_t batch_stride, hipStream_t stream);
+// Merge alone (no attention), one workgroup per sequence; positions outside
+// [0, max_pos] are dropped and counted in *status.
+hipError_t launch_merge(int dtype, int B, int r, int dR, int s, const int32_t *pos, int max_pos,
+                        const float *cg, const void *b_hc, const float *gate_pos, const void *KR_t,
+                        void *cache, int64_t batch_stride, int *status, hipStream_t stream);
 
 // Chunked merge-append: sequence b folds frames pos0[b] .. pos0[b] + n_b - 1
 // (n_b = lens[b] clamped to [0, L], or L when lens is null) into its cache in

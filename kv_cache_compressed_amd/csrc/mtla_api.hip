@@ -97,26 +97,30 @@ mtla_status launched(hipError_t e, const char *what) {
   } while (0)
 
 struct DecodeWs {
-  size_t cg, qt, part_o, part_ml, o, ypart, counters, total;
-  int ncount;
+  size_t status, cg, qt, part_o, part_ml, o, ypart, counters, total;
+  int ncount;   // ints cleared at the start of a call: the status word and the counters
 };
 
-// Workspace of one decoding step (plan != nullptr) or of a merge-append.
+// Workspace of one decoding step (plan != nullptr) or of a merge-append.  The
+// int32 status word (dropped frames of the last call) sits at byte 0 and the
+// split counters right after it, so one clear covers both.
 DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
   DecodeWs w;
   const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r;
+  const int nctr = plan ? B + mtla::out_proj_strips(B, d->d) : 0;
   size_t off = 0;
+  w.status = off;
+  w.counters = off + 4;
+  w.ncount = 1 + nctr;
+  off += align_up((size_t)w.ncount * 4);
   w.cg = off; off += align_up(B * 2 * r * 4);
-  w.qt = w.part_o = w.part_ml = w.o = w.ypart = w.counters = 0;
-  w.ncount = 0;
+  w.qt = w.part_o = w.part_ml = w.o = w.ypart = 0;
   if (plan) {
-    w.ncount = B + mtla::out_proj_strips(B, d->d);
     w.qt = off;       off += align_up(B * HR * e);
-    w.part_o = off;   off += align_up((size_t)B * plan->splits * HR * 4);
-    w.part_ml = off;  off += align_up((size_t)B * plan->splits * d->H * 2 * 4);
+    w.part_o = off;   off += align_up((size_t)plan->nparts * HR * 4);
+    w.part_ml = off;  off += align_up((size_t)plan->nparts * d->H * 2 * 4);
     w.o = off;        off += align_up(B * HR * e);
     w.ypart = off;    off += align_up(mtla::out_proj_part_bytes((int)e, B, d->d, (int)HR));
-    w.counters = off; off += align_up((size_t)w.ncount * 4);
   }
   w.total = off;
   return w;
@@ -343,11 +347,13 @@ mtla_status mtla_merge_append(const mtla_dims *dims, const mtla_weights *w, cons
   if (ws_bytes < ws.total) return fail(MTLA_ERR_ARG, "workspace %zu < %zu bytes", ws_bytes, ws.total);
   hipStream_t s = (hipStream_t)stream;
   float *cg = (float *)((char *)workspace + ws.cg);
+  int *status = (int *)((char *)workspace + ws.status);
   LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, nullptr, 0,
-                           cg, nullptr, nullptr, 0, s),
+                           cg, nullptr, status, ws.ncount, s),
          "latent and gate projection");
-  LAUNCH(mtla::launch_merge(dims->dtype, B, dims->r, dims->d_hR, dims->s, pos, cg, w->b_hc,
-                            w->gate_pos, KR_t, cache->slots, cache->batch_stride, s),
+  LAUNCH(mtla::launch_merge(dims->dtype, B, dims->r, dims->d_hR, dims->s, pos, max_pos, cg,
+                            w->b_hc, w->gate_pos, KR_t, cache->slots, cache->batch_stride, status,
+                            s),
          "merge");
   return ok();
 }
@@ -420,15 +426,16 @@ mtla_status decode_step_impl(const mtla_dims *dims, const mtla_weights *w, const
   void *qt = base + ws.qt, *o = base + ws.o;
   float *part_o = (float *)(base + ws.part_o), *part_ml = (float *)(base + ws.part_ml);
   float *ypart = (float *)(base + ws.ypart);
-  int *counters = (int *)(base + ws.counters);
+  int *status = (int *)(base + ws.status), *counters = (int *)(base + ws.counters);
   const int HR = dims->H * dims->r;
   LAUNCH(mtla::launch_proj(dims->dtype, X_t, B, dims->d, w->W_dkv, w->W_gate, dims->r, w->A, HR, cg,
-                           qt, counters, ws.ncount, s),
+                           qt, status, ws.ncount, s),
          "latent, gate and query projection");
   LAUNCH(mtla::launch_decode_attention(dims->dtype, plan, B, dims->H, dims->r, dims->d_hR, dims->s,
-                                       eff_scale(dims), pos, cache->slots, cache->batch_stride, qt,
-                                       QR_t, KR_t, cg, w->b_hc, w->gate_pos, part_o, part_ml,
-                                       counters, o, s, ev0(events), ev1(events)),
+                                       eff_scale(dims), pos, max_pos, cache->slots,
+                                       cache->batch_stride, qt, QR_t, KR_t, cg, w->b_hc,
+                                       w->gate_pos, part_o, part_ml, counters, status, o, s,
+                                       ev0(events), ev1(events)),
          "merge and decode attention");
   LAUNCH(mtla::launch_out_proj(dims->dtype, o, B, HR, w->Bvo, dims->d, Y, ypart, counters + B, s),
          "output projection");

@@ -39,6 +39,7 @@ class MTLALayer:
             self.wu = L.make_unabsorbed_weights(W_dkv, self.W_gate, b_hc, self.gate_pos, W_Qh,
                                                 W_Kh, W_Vh, W_Oh)
         self._ws = {}
+        self._retired = []
 
     @classmethod
     def from_arrays(cls, dims, arrays: dict, dtype=L.MTLA_BF16, device="cuda", scale=0.0):
@@ -59,12 +60,22 @@ class MTLALayer:
         return torch.full((B, max_slots, self.row), fill, dtype=self.dtype, device="cuda")
 
     def workspace(self, op: int, B: int, n: int) -> torch.Tensor:
+        """The layer's workspace for entry point ``op``, grown when a call
+        needs more.  A buffer that a larger one replaces is kept alive for the
+        layer's lifetime: a graph captured earlier may still write to it."""
         need = L.mtla_workspace_bytes(self.dims, op, B, n)
         ws = self._ws.get(op)
         if ws is None or ws.numel() < need:
+            if ws is not None:
+                self._retired.append(ws)
             ws = L.workspace(self.dims, op, B, n)
             self._ws[op] = ws
         return ws
+
+    def dropped_frames(self, op: int = L.OP_DECODE) -> int:
+        """Sequences whose frame the last merge-append (op OP_MERGE) or decode
+        step (OP_DECODE) dropped for a position outside [0, max_pos]."""
+        return L.dropped_frames(self._ws[op])
 
     def merge_append(self, cache: torch.Tensor, X_t, KR_t, pos, max_pos: int):
         L.mtla_merge_append(self.dims, self.w, L.make_cache(cache), X_t, KR_t, pos, max_pos,

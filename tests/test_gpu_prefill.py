@@ -72,9 +72,10 @@ def test_bf16_wide_latent():
 
 
 def test_full_size_prefill_sampled():
-    """The benchmark's prefill launch (B=16, T=4096, s=2), checked on sampled
-    sequences and rows: intermediate states and cache in full, outputs on
-    sampled rows computed one by one from the oracle's visible sets."""
+    """The benchmark's prefill launch (B=16, T=4096, s=2): intermediate states
+    and cache in full on three sequences, outputs on their sampled rows
+    computed one by one from the oracle's visible sets, and every output row
+    of one sequence against the oracle's dense masked form."""
     needs_gpu()
     name, dims, ex = synth.config(4)
     B, T = ex["B"], ex["T"]
@@ -110,6 +111,13 @@ def test_full_size_prefill_sampled():
         e = relerr(Yg, np.stack(Yr))
         say(f"  b={b} sampled-row relerr {e:.3g}")
         assert e < TOL["bf16"]
+    # One whole sequence, every row and head, against the oracle's dense
+    # masked form (fp64).
+    b = 9
+    ref = om.prefill(seq["X"][b], seq["QR"][b], seq["KR"][b], W, dims.s, dims.scale)
+    e = relerr(host(Y[b]), ref["Y"])
+    say(f"  b={b} all {T} rows relerr {e:.3g}")
+    assert e < TOL["bf16"]
 
 
 def test_prefill_then_decode_resumes():
