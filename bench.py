@@ -2,12 +2,13 @@
 """Benchmark of the MTLA hot path on one MI355X.
 
 Headline (the JSON line's `value`): decode tokens/s of one MTLA layer on the
-speech-decoder-shaped step (B=32, d=512, H=8, d_h=64, r=256, d_hR=32, s=2,
-2048 frames of context = 1024 compressed slots, bf16 cache, fp32
-accumulation).  One step is one full mtla_decode_step: latent and absorbed
-query projection, hyper-network gate with the in-place merge into slot
-floor(t/s), split-K attention over the compressed cache, combine and the
-absorbed output projection.  tokens/s = B / step time.
+LLM-scale step (B=128, d=4096, H=32, d_h=128, r=512, d_hR=64, s=2, 32768
+frames of context = 16384 compressed slots per sequence, bf16 cache, fp32
+accumulation), the largest decode workload.  One step is one full
+mtla_decode_step: latent and absorbed query projection, hyper-network gate
+with the in-place merge into slot floor(t/s), split-K attention over the
+compressed cache, combine and the absorbed output projection.  tokens/s = B /
+step time.
 
 The timed region is `--steps` consecutive decode steps enqueued while the GPU
 is held by a spin kernel, so that they then execute back to back: host launch
@@ -15,23 +16,26 @@ latency stays out of the GPU timeline, as it would under graph replay.  A
 second pass of the same steps launches the attention kernel with a pair of HIP
 events that the runtime stamps with that kernel's own start and end
 (hipExtLaunchKernel through the library's timed entry point); its step time
-is reported beside the first pass's.  Every step
-reads a different replica of the cache, the replicas together exceeding
-1 GiB, so the cache is streamed from HBM and not from the 256 MB Infinity
-Cache.
+is reported beside the first pass's.  Caches smaller than 1 GiB are
+replicated and each step reads a different replica, so the cache is streamed
+from HBM and not from the 256 MB Infinity Cache (the LLM-scale cache is
+2.4 GB and needs none).
 
 `roofline` is that of the split-K attention kernel: algorithmic bytes (the
 compressed cache rows the step must read, sum_b (floor(t_b/s)+1) *
 (r + d_hR) * 2 B) over its average duration, from the HIP event pairs of the
-second pass.
+second pass; `traffic` is the HBM bytes per launch from the committed counter
+summary under profiles/ while the kernel's sources are unchanged.
 
-Also reported (same line): the ragged and LLM-scale decode workloads, the
-strided prefill (TFLOP/s of the attention kernel on visible pairs only, and
-of the whole forward, in the absorbed form and in the per-head form), the
-backward of the per-head form, the chunked merge-append (frames/s), the
-library's decoupled-RoPE inputs, the headline decode at s = 1 (the MLA
-reduction: twice the slots, for the speed and memory ratio), and the CPU oracle timed on the host cores on a bounded
-sample of the headline workload.
+Also reported (same line): the speech-decoder and ragged decode workloads
+(each with its roofline), the strided prefill (TFLOP/s of the attention kernel
+on visible pairs only, and of the whole forward, in the absorbed form and in
+the per-head form), the backward of the per-head form, the chunked
+merge-append (frames/s), the library's decoupled-RoPE inputs, the speech
+decode at s = 1 (the MLA reduction: twice the slots, for the speed and memory
+ratio), and the CPU oracle timed on the host cores beside each decode workload
+and the prefill, on bounded samples (`cpu_baseline` for the headline,
+`cpu_baseline` entries inside the other records).
 
 All inputs are seeded synthetic tensors (no datasets or trained weights).
 """
@@ -443,39 +447,97 @@ def run_rope(steps: int = 20, warmup: int = 3) -> dict:
                 io_bytes=M * (dims.d + N) * 2 + M * 4, flops=2 * M * dims.d * N)
 
 
-def cpu_baseline(seconds: float) -> dict:
-    """The oracle (numpy, fp32) on the headline decode workload: full-batch
-    decode steps repeated until `seconds` of wall time have passed."""
+def _blas_info():
+    from threadpoolctl import threadpool_info
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    return int(threads), (blas[0].get("internal_api") if blas else "none")
+
+
+def _decode_positions(cfg: int, ex: dict, B: int) -> np.ndarray:
+    """The positions _decode_setup uses for workload cfg (same seed)."""
+    import synth
+    if "ctx" in ex:
+        return np.full(B, ex["ctx"] - 1, dtype=np.int32)
+    rng = np.random.default_rng(synth.seed_for(cfg))
+    return (rng.integers(ex["ctx_lo"], ex["ctx_hi"] + 1, size=B) - 1).astype(np.int32)
+
+
+def cpu_baseline(cfg: int, seconds: float, max_seqs: int) -> dict:
+    """The oracle (numpy, fp32, untuned) on a bounded sample of decode
+    workload `cfg`: its first `max_seqs` sequences (at their own positions),
+    each given a seeded cache of its length, stepped one after another with
+    oracle.decode_step until `seconds` of wall time have passed.  tokens/s =
+    sequence steps done / time (every sequence of a step costs the same at
+    equal lengths; at ragged lengths the sample is the workload's first
+    sequences)."""
     import synth
     import oracle.mtla as om
-    from threadpoolctl import threadpool_info
-    name, dims, ex = synth.config(2)
-    B, t = ex["B"], ex["ctx"] - 1
-    ms = t // dims.s + 1
-    w = synth.make_weights(dims, synth.seed_for(2), "bf16", pe_rows=ms)
+    name, dims, ex = synth.config(cfg)
+    B = ex["B"]
+    pos = _decode_positions(cfg, ex, B)[:max_seqs]
+    n = len(pos)
+    ms = int(pos.max()) // dims.s + 1
+    w = synth.make_weights(dims, synth.seed_for(cfg), "bf16", pe_rows=ms)
     W = om.with_position_table(w, ms)
     W = {k: np.asarray(v, dtype=np.float32) for k, v in W.items()}
-    rng = np.random.default_rng(synth.seed_for(2))
-    lat = rng.normal(0, 0.7, size=(B, ms, dims.r)).astype(np.float32)
-    rk = rng.normal(0, 1.0, size=(B, ms, dims.d_hR)).astype(np.float32)
-    step = synth.make_step(dims, w, np.full(B, t), seed=synth.seed_for(2) + 2)
+    rng = np.random.default_rng(synth.seed_for(cfg))
+    lat = [rng.normal(0, 0.7, size=(int(t) // dims.s + 1, dims.r)).astype(np.float32) for t in pos]
+    rk = [rng.normal(0, 1.0, size=(int(t) // dims.s + 1, dims.d_hR)).astype(np.float32) for t in pos]
+    step = synth.make_step(dims, w, pos, seed=synth.seed_for(cfg) + 2)
     x, qr, kr = (np.asarray(step[k], dtype=np.float32) for k in ("x", "QR", "KR"))
-    n_tok, t0 = 0, time.perf_counter()
-    batches = 0
+    n_tok, rounds = 0, 0
+    t0 = time.perf_counter()
     while True:
-        for b in range(B):
-            om.decode_step(lat[b], rk[b], t, x[b], qr[b], kr[b], W, dims.s, np.float32(dims.scale))
+        for b in range(n):
+            om.decode_step(lat[b], rk[b], int(pos[b]), x[b], qr[b], kr[b], W, dims.s,
+                           np.float32(dims.scale))
             n_tok += 1
-        batches += 1
+        rounds += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-    threads = max([i.get("num_threads", 1) for i in blas] or [1])
-    return dict(value=n_tok / el, unit="tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{batches} full-batch decode steps of {name} (B={B}, {ms} slots), "
-                       f"numpy fp32, {el:.1f} s; host cores visible: {len(os.sched_getaffinity(0))}; "
-                       f"BLAS: {blas[0].get('internal_api') if blas else 'none'}")
+    threads, blas = _blas_info()
+    return dict(value=round(n_tok / el, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{rounds} rounds of decode steps over {n} of the {B} sequences of {name} "
+                       f"({int(pos.min()) // dims.s + 1}-{ms} slots each), numpy fp32, {el:.1f} s; "
+                       f"host cores visible: {len(os.sched_getaffinity(0))}; BLAS: {blas}")
+
+
+def cpu_prefill_baseline() -> dict:
+    """The oracle (numpy, fp32) on the prefill workload: sequence 0 alone
+    (1/16 of the batch: sequences are independent), one oracle.prefill call;
+    the full-batch figure is that time x 16."""
+    import synth
+    import oracle.mtla as om
+    name, dims, ex = synth.config(4)
+    B, T = ex["B"], ex["T"]
+    ms = -(-T // dims.s)
+    w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
+    W = om.with_position_table(w, ms)
+    W = {k: np.asarray(v, dtype=np.float32) for k, v in W.items()}
+    seq = synth.make_sequence(dims, w, 1, T, synth.seed_for(4) + 1, "bf16")
+    X, QR, KR = (np.asarray(seq[k][0], dtype=np.float32) for k in ("X", "QR", "KR"))
+    t0 = time.perf_counter()
+    om.prefill(X, QR, KR, W, dims.s, np.float32(dims.scale))
+    el = time.perf_counter() - t0
+    threads, blas = _blas_info()
+    return dict(value=round(T / el, 2), unit="frames/s", cores=threads, kind="oracle",
+                full_batch_s=round(el * B, 2),
+                sample=f"sequence 0 of {name} ({T} frames), one oracle.prefill call, numpy fp32, "
+                       f"{el:.1f} s (x{B} for the batch); host cores visible: "
+                       f"{len(os.sched_getaffinity(0))}; BLAS: {blas}")
+
+
+def roofline(rec: dict, workload: str) -> dict:
+    """Roofline block of the attention kernel of a decode record."""
+    tr = measured_traffic(workload, "decode_attn_kernel")
+    traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None
+    return {"bound": "hbm", "kernel": "decode_attn_kernel",
+            "achieved": round(rec["attn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(rec["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_launch": rec["cache_bytes"],
+            "avg_kernel_us": round(rec["attn_ms"] * 1e3, 3)}
 
 
 def main():
@@ -526,60 +588,62 @@ def main():
                "llm_decode_b128_ctx32768": 5, "prefill_b16_t4096": 4}[args.only]
         rec = run_prefill(args.steps, args.warmup) if cfg == 4 else \
             run_decode(cfg, args.steps, args.warmup)
+        if cfg != 4:
+            rec["roofline"] = roofline(rec, args.only)
         print(json.dumps(rec), flush=True)
         return
-    log("decode_b32_ctx2048 ...")
-    head = run_decode(2, args.steps, args.warmup)
-    log(f"  step {head['step_ms']*1e3:.2f} us, attention {head['attn_ms']*1e3:.2f} us, "
+    log("llm_decode_b128_ctx32768 ...")
+    head = run_decode(5, args.steps, args.warmup)
+    log(f"  step {head['step_ms']*1e3:.1f} us, attention {head['attn_ms']*1e3:.1f} us, "
         f"{head['attn_gbs']:.0f} GB/s, {head['tokens_per_s']:.0f} tok/s")
     extra = {}
-    cpu = None
-    if True:
-        log("ragged_decode_b64_s4 ...")
-        extra["ragged_decode_b64_s4"] = run_decode(3, 20, 5)
-        log("llm_decode_b128_ctx32768 ...")
-        extra["llm_decode_b128_ctx32768"] = run_decode(5, 10, 3)
-        torch.cuda.empty_cache()
-        log("prefill_b16_t4096 ...")
-        extra["prefill_b16_t4096"] = run_prefill()
-        for k in ("ragged_decode_b64_s4", "llm_decode_b128_ctx32768"):
-            e = extra[k]
-            e["attn_hbm_frac"] = e["attn_gbs"] / HBM_PEAK_GBS
-            log(f"  {k}: attention {e['attn_ms']*1e3:.1f} us {e['attn_gbs']:.0f} GB/s "
-                f"({e['attn_hbm_frac']:.1%}), {e['tokens_per_s']:.0f} tok/s")
-        p = extra["prefill_b16_t4096"]
-        p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
-        log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
-            f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
-        log("prefill_b16_t4096_per_head ...")
-        u = extra["prefill_b16_t4096_per_head"] = run_prefill_unabsorbed()
-        u["attn_mfma_frac"] = u["attn_tflops"] / BF16_PEAK_TFLOPS
-        log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
-            f"({u['attn_mfma_frac']:.1%}), forward {u['forward_ms']:.3f} ms")
-        log("prefill_b16_t4096_backward ...")
-        bw = extra["prefill_b16_t4096_backward"] = run_backward()
-        log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
-        log("decode_b32_ctx2048_s1 (the MLA reduction, one slot per frame) ...")
-        m1 = extra["decode_b32_ctx2048_s1"] = run_decode(2, 50, 10, stride=1)
-        m1["cache_bytes_vs_s2"] = m1["cache_bytes"] / head["cache_bytes"]
-        m1["step_time_vs_s2"] = m1["step_ms"] / head["step_ms"]
-        log(f"  s=1: step {m1['step_ms']*1e3:.2f} us, cache {m1['cache_bytes']/1e6:.1f} MB "
-            f"({m1['cache_bytes_vs_s2']:.2f}x s=2), step time {m1['step_time_vs_s2']:.2f}x s=2")
-        log("rope_inputs_b16_t4096 ...")
-        ro = extra["rope_inputs_b16_t4096"] = run_rope()
-        log(f"  rotary inputs: {ro['step_ms']*1e3:.1f} us for {ro['B'] * ro['T']} frames")
-        log("append_chunk_b32_l512 ...")
-        a = extra["append_chunk_b32_l512"] = run_append()
-        log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")
-        log("cpu baseline ...")
-        cpu = cpu_baseline(args.cpu_seconds)
-        cpu["value"] = round(cpu["value"], 2)
-    tr = measured_traffic("decode_b32_ctx2048", "decode_attn_kernel")
-    traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None
+    log("decode_b32_ctx2048 ...")
+    c2 = extra["decode_b32_ctx2048"] = run_decode(2, 50, 10)
+    log("ragged_decode_b64_s4 ...")
+    c3 = extra["ragged_decode_b64_s4"] = run_decode(3, 50, 10)
+    for k, rec in (("decode_b32_ctx2048", c2), ("ragged_decode_b64_s4", c3)):
+        rec["roofline"] = roofline(rec, k)
+        log(f"  {k}: step {rec['step_ms']*1e3:.2f} us, attention {rec['attn_ms']*1e3:.2f} us "
+            f"{rec['attn_gbs']:.0f} GB/s ({rec['roofline']['frac']:.1%}), "
+            f"{rec['tokens_per_s']:.0f} tok/s")
+    torch.cuda.empty_cache()
+    log("prefill_b16_t4096 ...")
+    p = extra["prefill_b16_t4096"] = run_prefill()
+    p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
     ptr = measured_traffic("prefill_b16_t4096", "prefill_ws_kernel")
     if ptr:
-        extra["prefill_b16_t4096"]["attn_hbm_traffic_bytes"] = round(
-            ptr["fetch_bytes_per_launch"] + ptr["write_bytes_per_launch"])
+        p["attn_hbm_traffic_bytes"] = round(ptr["fetch_bytes_per_launch"] + ptr["write_bytes_per_launch"])
+    log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
+        f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
+    log("prefill_b16_t4096_per_head ...")
+    u = extra["prefill_b16_t4096_per_head"] = run_prefill_unabsorbed()
+    u["attn_mfma_frac"] = u["attn_tflops"] / BF16_PEAK_TFLOPS
+    log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
+        f"({u['attn_mfma_frac']:.1%}), forward {u['forward_ms']:.3f} ms")
+    log("prefill_b16_t4096_backward ...")
+    bw = extra["prefill_b16_t4096_backward"] = run_backward()
+    log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
+    log("decode_b32_ctx2048_s1 (the MLA reduction, one slot per frame) ...")
+    m1 = extra["decode_b32_ctx2048_s1"] = run_decode(2, 50, 10, stride=1)
+    m1["cache_bytes_vs_s2"] = m1["cache_bytes"] / c2["cache_bytes"]
+    m1["step_time_vs_s2"] = m1["step_ms"] / c2["step_ms"]
+    log(f"  s=1: step {m1['step_ms']*1e3:.2f} us, cache {m1['cache_bytes']/1e6:.1f} MB "
+        f"({m1['cache_bytes_vs_s2']:.2f}x s=2), step time {m1['step_time_vs_s2']:.2f}x s=2")
+    log("rope_inputs_b16_t4096 ...")
+    ro = extra["rope_inputs_b16_t4096"] = run_rope()
+    log(f"  rotary inputs: {ro['step_ms']*1e3:.1f} us for {ro['B'] * ro['T']} frames")
+    log("append_chunk_b32_l512 ...")
+    a = extra["append_chunk_b32_l512"] = run_append()
+    log(f"  append: {a['step_ms']*1e3:.1f} us per chunk, {a['frames_per_s']:.3g} frames/s")
+    log("cpu baselines (the oracle on bounded samples) ...")
+    cpu = cpu_baseline(5, args.cpu_seconds, 8)
+    log(f"  llm decode: {cpu['value']:.1f} tok/s ({cpu['sample']})")
+    c2["cpu_baseline"] = cpu_baseline(2, args.cpu_seconds / 2, 32)
+    c3["cpu_baseline"] = cpu_baseline(3, args.cpu_seconds / 2, 16)
+    p["cpu_baseline"] = cpu_prefill_baseline()
+    log(f"  speech decode {c2['cpu_baseline']['value']:.0f} tok/s, ragged "
+        f"{c3['cpu_baseline']['value']:.0f} tok/s, prefill {p['cpu_baseline']['value']:.0f} frames/s")
+    _, dims5, ex5 = __import__("synth").config(5)
     out = {
         "metric": METRIC,
         "value": round(head["tokens_per_s"], 1),
@@ -593,14 +657,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random inputs and random-init weights of the workload's shapes)",
-        "config": {"workload": "decode_b32_ctx2048", "B": 32, "d": 512, "H": 8, "d_h": 64,
-                   "r": 256, "d_hR": 32, "s": 2, "context_frames": 2048, "slots": 1024,
-                   "cache_replicas": head["replicas"]},
-        "roofline": {"bound": "hbm", "kernel": "decode_attn_kernel",
-                     "achieved": round(head["attn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": head["cache_bytes"],
-                     "avg_kernel_us": round(head["attn_ms"] * 1e3, 3)},
+        "config": {"workload": "llm_decode_b128_ctx32768", "B": ex5["B"], "d": dims5.d,
+                   "H": dims5.H, "d_h": dims5.d_h, "r": dims5.r, "d_hR": dims5.d_hR,
+                   "s": dims5.s, "context_frames": ex5["ctx"],
+                   "slots": ex5["ctx"] // dims5.s, "cache_replicas": head["replicas"]},
+        "roofline": roofline(head, "llm_decode_b128_ctx32768"),
         "cpu_baseline": cpu,
         "extra": extra,
     }
