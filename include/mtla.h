@@ -195,6 +195,25 @@ mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const
                              int32_t B, int32_t max_pos, void *Y, void *workspace, size_t ws_bytes,
                              void *stream);
 
+/* mtla_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as mtla_decode_step minus the workspace: the
+ * step runs in a device scratch array of 64 MiB that the library holds per
+ * GPU for the life of the process (the LLM-scale step, B = 128, H = 32,
+ * r = 512, 16384 slots, needs 40.6 MiB).  A shape whose workspace
+ * (mtla_workspace_bytes(op=1)) exceeds it returns MTLA_ERR_CAPACITY and
+ * launches nothing.  `stream` must belong to the current device.  Nothing is
+ * allocated or freed: the scratch's device address is looked up once per
+ * device (hipGetSymbolAddress).  Every call on a GPU shares that GPU's
+ * scratch, which keeps the last call's contents (each call clears what must
+ * start at zero itself): calls that may overlap on one GPU -- different
+ * streams, or host threads -- race; keep them on one stream.  The dropped-
+ * frame status word is not readable through this entry point. */
+mtla_status mtla_decode_step_noalloc(const mtla_dims *dims, const mtla_weights *w,
+                                     const mtla_cache *cache, const void *X_t, const void *QR_t,
+                                     const void *KR_t, const int32_t *pos, int32_t B,
+                                     int32_t max_pos, void *Y, void *stream);
+
 /* Parallel (prefill / training-forward) form under the stride-aware causal
  * mask ([Notes] stride-aware causal mask and decoupled RoPE; [Fig2] (c)), for
  * frames 0..T-1 of B sequences:

@@ -24,7 +24,7 @@ EXPORTED = ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
             "mtla_append_chunk", "mtla_decode_step", "mtla_prefill_strided",
             "mtla_decode_step_timed", "mtla_prefill_strided_timed", "mtla_prefill_unabsorbed",
             "mtla_prefill_unabsorbed_timed", "mtla_prefill_unabsorbed_backward",
-            "mtla_rope_inputs", "mtla_workspace_bytes",
+            "mtla_rope_inputs", "mtla_workspace_bytes", "mtla_decode_step_noalloc",
             "mtla_status_string", "mtla_last_error_detail")
 
 
@@ -99,9 +99,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mtla_rope_inputs.argtypes = [P(Dims), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                      c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.mtla_decode_step_timed.argtypes = lib.mtla_decode_step.argtypes + [c_void_p]
+    lib.mtla_decode_step_noalloc.argtypes = [P(Dims), P(Weights), P(Cache), c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                             c_void_p]
     lib.mtla_prefill_strided_timed.argtypes = lib.mtla_prefill_strided.argtypes + [c_void_p]
     for f in ("mtla_gate_pos_table", "mtla_gate_content_map", "mtla_merge_append",
-              "mtla_append_chunk", "mtla_decode_step",
+              "mtla_append_chunk", "mtla_decode_step", "mtla_decode_step_noalloc",
               "mtla_prefill_strided", "mtla_decode_step_timed", "mtla_prefill_strided_timed",
               "mtla_prefill_unabsorbed", "mtla_prefill_unabsorbed_timed",
               "mtla_prefill_unabsorbed_backward", "mtla_rope_inputs"):
@@ -259,6 +262,19 @@ def mtla_decode_step(dims: Dims, w: Weights, cache: Cache, X_t, QR_t, KR_t, pos,
         _check(lib.mtla_decode_step(*args))
     else:
         _check(lib.mtla_decode_step_timed(*args, _events(events)))
+    return Y
+
+
+def mtla_decode_step_noalloc(dims: Dims, w: Weights, cache: Cache, X_t, QR_t, KR_t, pos,
+                             max_pos: int, Y=None):
+    """mtla_decode_step without a workspace: the library's per-GPU scratch is
+    used (``Y`` must be given when nothing may be allocated)."""
+    B = X_t.shape[0]
+    if Y is None:
+        Y = torch.empty(B, dims.d, dtype=X_t.dtype, device=X_t.device)
+    _check(load_library().mtla_decode_step_noalloc(
+        ctypes.byref(dims), ctypes.byref(w), ctypes.byref(cache), _ptr(X_t), _ptr(QR_t),
+        _ptr(KR_t), _ptr(pos), B, int(max_pos), _ptr(Y), _stream()))
     return Y
 
 

@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/mtla.h"
 #include "kernels.h"
 
@@ -229,6 +231,36 @@ mtla_status check_positions(const mtla_dims *d, const mtla_weights *w, const mtl
   if (jmax >= w->gate_pos_rows)
     return fail(MTLA_ERR_CAPACITY, "slot %d (max_pos %d) >= gate_pos_rows %d", jmax, max_pos,
                 w->gate_pos_rows);
+  return MTLA_OK;
+}
+
+}  // namespace
+
+// Device scratch of mtla_decode_step_noalloc: a file-scope array, so that the
+// entry point allocates nothing.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code the array's name is only a
+// stand-in: its device address (per device) comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// once per device.
+mtla_status scratch_for(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MTLA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(MTLA_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return MTLA_OK;
 }
 
@@ -717,6 +749,32 @@ mtla_status mtla_decode_step(const mtla_dims *dims, const mtla_weights *w, const
                              void *stream) {
   return decode_step_impl(dims, w, cache, X_t, QR_t, KR_t, pos, B, max_pos, Y, workspace, ws_bytes,
                           stream, nullptr);
+}
+
+mtla_status mtla_decode_step_noalloc(const mtla_dims *dims, const mtla_weights *w,
+                                     const mtla_cache *cache, const void *X_t, const void *QR_t,
+                                     const void *KR_t, const int32_t *pos, int32_t B,
+                                     int32_t max_pos, void *Y, void *stream) {
+  mtla_status st;
+  if ((st = check_dims(dims)) != MTLA_OK) return st;
+  if (B < 1 || B > 65535) return fail(MTLA_ERR_ARG, "B=%d outside [1, 65535]", B);
+  if (max_pos < 0) return fail(MTLA_ERR_ARG, "max_pos=%d < 0", max_pos);
+  const size_t need = mtla_workspace_bytes(dims, 1, B, max_pos);
+  if (need == 0) return fail(MTLA_ERR_UNSUPPORTED, "no decode plan for this shape");
+  if (need > kNoAllocScratchBytes)
+    return fail(MTLA_ERR_CAPACITY, "decode step needs %zu bytes of scratch > %zu", need,
+                kNoAllocScratchBytes);
+  int dev = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MTLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+  if (e != hipSuccess) return fail(MTLA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  if (sdev != dev)
+    return fail(MTLA_ERR_ARG, "stream belongs to device %d, current device is %d", sdev, dev);
+  void *ws = nullptr;
+  if ((st = scratch_for(dev, &ws)) != MTLA_OK) return st;
+  return decode_step_impl(dims, w, cache, X_t, QR_t, KR_t, pos, B, max_pos, Y, ws,
+                          kNoAllocScratchBytes, stream, nullptr);
 }
 
 mtla_status mtla_decode_step_timed(const mtla_dims *dims, const mtla_weights *w,

@@ -92,6 +92,11 @@ class MTLALayer:
                                   max_pos, Y, self.workspace(L.OP_DECODE, X_t.shape[0], max_pos),
                                   events)
 
+    def decode_step_noalloc(self, cache: torch.Tensor, X_t, QR_t, KR_t, pos, max_pos: int, Y):
+        """decode_step on the library's per-GPU scratch (no workspace)."""
+        return L.mtla_decode_step_noalloc(self.dims, self.w, L.make_cache(cache), X_t, QR_t, KR_t,
+                                          pos, max_pos, Y)
+
     def prefill(self, X, QR, KR, Y=None, cache: torch.Tensor | None = None, Cprime=None,
                 events=None):
         c = L.make_cache(cache) if cache is not None else None
