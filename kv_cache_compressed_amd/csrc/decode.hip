@@ -279,21 +279,21 @@ __device__ void flat_assign(const DecodeArgs &a, int w, int &b, int &split, int 
   cst = c;
 }
 
-template <typename T, int R, int DR, int NHB>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
-  using C = DecCfg<T, R, DR, NHB>;
-  using Lay = DecLayout<C::RB>;
-  typedef typename Frag4<T>::type P4;
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int b, split, ns, pbase, start, end;
+// The slot range [start, end) of sequence b that this workgroup attends,
+// from the balanced work list or the uniform splits, with the sequence's
+// split count ns and first partial index pbase; t = pos[b].  Returns false
+// when the workgroup has nothing to attend -- no split of its own, or a
+// dropped frame (a position outside [0, max_pos]), whose output row the
+// sequence's first split then writes as zeros and counts.
+template <typename T, int R, int SROWS>
+__device__ bool decode_work(const DecodeArgs &a, int &b, int &split, int &ns, int &pbase,
+                            int &start, int &end, int &t) {
   if (a.flat) {
     int cst;
-    flat_assign<C::SROWS>(a, (int)blockIdx.x, b, split, ns, pbase, cst);
-    if (b < 0) return;
-    start = split * cst * C::SROWS;
-    end = start + cst * C::SROWS;   // clipped to n below
+    flat_assign<SROWS>(a, (int)blockIdx.x, b, split, ns, pbase, cst);
+    if (b < 0) return false;
+    start = split * cst * SROWS;
+    end = start + cst * SROWS;   // clipped to n below
   } else {
     b = blockIdx.y;
     split = blockIdx.x;
@@ -302,20 +302,105 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
     end = start + a.chunk;
     ns = -1;   // from n below
   }
-  const int t = a.pos[b], s = a.s;
-  const bool valid = t >= 0 && t <= a.max_pos;
-  const int H = a.H;
-  if (!valid) {
-    // Dropped frame: only the sequence's first split acts.
-    if (split != 0) return;
-    if (tid == 0) atomicAdd(a.status, 1);
-    for (int i = tid; i < H * R; i += 256) ((T *)a.o)[(size_t)b * H * R + i] = from_f32<T>(0.0f);
-    return;
+  t = a.pos[b];
+  if (t < 0 || t > a.max_pos) {
+    if (split != 0) return false;
+    if (threadIdx.x == 0) atomicAdd(a.status, 1);
+    for (int i = threadIdx.x; i < a.H * R; i += blockDim.x)
+      ((T *)a.o)[(size_t)b * a.H * R + i] = from_f32<T>(0.0f);
+    return false;
   }
-  const int jn = t / s, n = jn + 1;
+  const int n = t / a.s + 1;
   if (ns < 0) ns = (n + a.chunk - 1) / a.chunk;
-  if (start >= n) return;
+  if (start >= n) return false;
   end = min(n, end);
+  return true;
+}
+
+// The last split of a sequence to finish merges all of its partials (log-sum-
+// exp in split order: deterministic).  A thread takes two 4-channel chunks at
+// a time and loads up to eight splits' partials of both in one batch, so a
+// merge of up to eight splits waits for one round trip.
+template <typename T, int R>
+__device__ void merge_partials(const DecodeArgs &a, int b, int ns, int pbase,
+                               __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml) {
+  constexpr int QC = R / 4;   // 4-channel chunks per head
+  constexpr int UB = 2, SB = 8;
+  const int H = a.H, nthr = blockDim.x;
+  const int nch = H * QC;
+  const size_t base = (size_t)pbase * H;
+  for (int c0 = threadIdx.x; c0 < nch; c0 += UB * nthr) {
+    float M[UB], L[UB];
+    f32x4 acc[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      M[u] = kNegInf;
+      L[u] = 0.0f;
+      acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int k0 = 0; k0 < ns; k0 += SB) {
+      float pm[UB][SB], pl[UB][SB];
+      f32x4 po[UB][SB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int ci = min(c0 + nthr * u, nch - 1), h = ci / QC, ch = (ci % QC) * 4;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          pm[u][j] = kNegInf;
+          pl[u][j] = 0.0f;
+          po[u][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          if (k0 + j < ns) {
+            const size_t i = base + (size_t)(k0 + j) * H + h;
+            pm[u][j] = ld_coh1(rml, (uint32_t)(i * 8));
+            pl[u][j] = ld_coh1(rml, (uint32_t)(i * 8 + 4));
+            po[u][j] = ld_coh4(ro, (uint32_t)((i * R + ch) * 4));
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        float Mn = M[u];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) Mn = fmaxf(Mn, pm[u][j]);
+        const float sc = __builtin_amdgcn_exp2f(M[u] - Mn);
+        L[u] *= sc;
+        acc[u] *= sc;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const float w = (k0 + j < ns) ? __builtin_amdgcn_exp2f(pm[u][j] - Mn) : 0.0f;
+          L[u] += w * pl[u][j];
+          acc[u] += w * po[u][j];
+        }
+        M[u] = Mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int ci = c0 + nthr * u;
+      if (ci >= nch) continue;
+      const int h = ci / QC, ch = (ci % QC) * 4;
+      T *dst = (T *)a.o + ((size_t)b * H + h) * R + ch;
+      const float inv = 1.0f / L[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[u][e] * inv);
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int R, int DR, int NHB>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
+  using C = DecCfg<T, R, DR, NHB>;
+  using Lay = DecLayout<C::RB>;
+  typedef typename Frag4<T>::type P4;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int b, split, ns, pbase, start, end, t;
+  if (!decode_work<T, R, C::SROWS>(a, b, split, ns, pbase, start, end, t)) return;
+  const int s = a.s, H = a.H;
+  const int jn = t / s, n = jn + 1;
   const bool owner = end == n;
   const int nstage = (end - start + C::SROWS - 1) / C::SROWS;
   const int g = lane >> 4, c = lane & 15;
@@ -644,76 +729,383 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a) {
   }
   if (ns == 1) return;
 
-  // The last split of this sequence to finish merges all of them (log-sum-
-  // exp in split order: deterministic).  A thread takes two 4-channel chunks
-  // at a time and loads up to eight splits' partials of both in one batch,
-  // so a merge of up to eight splits waits for one round trip.
+  // The last split of this sequence to finish merges all of them.
   int *last = (int *)(pbuf + C::P_B);
   __syncthreads();   // this workgroup's partial stores have completed
   if (tid == 0) *last = ctr_add(&a.counters[b], 1) == ns - 1;
   __syncthreads();
   if (!*last) return;
-  constexpr int QC = R / 4;   // 4-channel chunks per head
-  constexpr int UB = 2, SB = 8;
-  const int nch = H * QC;
-  const size_t base = (size_t)pbase * H;
-  for (int c0 = tid; c0 < nch; c0 += UB * 256) {
-    float M[UB], L[UB];
-    f32x4 acc[UB];
+  merge_partials<T, R>(a, b, ns, pbase, ro, rml);
+}
+
+// Nine score operand fragments of a tile (row lane % 16, k-steps ks0 ..
+// ks0 + 8), read in one batch: k-step ks sits at (ks odd ? o : e) +
+// (ks >> 1) * stride bytes in the decode tile layout (stride 2048 for rows of
+// a multiple of 128 bytes, 1024 for paired 576-byte rows).  Each asm block
+// waits for its own reads.
+__device__ __forceinline__ void read_frags_l1_lo(bf16x8 (&f)[9], uint32_t e, uint32_t o) {
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:0\n\t"
+      "ds_read_b128 %1, %10 offset:0\n\t"
+      "ds_read_b128 %2, %9 offset:2048\n\t"
+      "ds_read_b128 %3, %10 offset:2048\n\t"
+      "ds_read_b128 %4, %9 offset:4096\n\t"
+      "ds_read_b128 %5, %10 offset:4096\n\t"
+      "ds_read_b128 %6, %9 offset:6144\n\t"
+      "ds_read_b128 %7, %10 offset:6144\n\t"
+      "ds_read_b128 %8, %9 offset:8192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7]), "=&v"(f[8])
+      : "v"(e), "v"(o)
+      : "memory");
+}
+__device__ __forceinline__ void read_frags_l1_hi(bf16x8 (&f)[9], uint32_t e, uint32_t o) {
+  asm volatile(
+      "ds_read_b128 %0, %10 offset:8192\n\t"
+      "ds_read_b128 %1, %9 offset:10240\n\t"
+      "ds_read_b128 %2, %10 offset:10240\n\t"
+      "ds_read_b128 %3, %9 offset:12288\n\t"
+      "ds_read_b128 %4, %10 offset:12288\n\t"
+      "ds_read_b128 %5, %9 offset:14336\n\t"
+      "ds_read_b128 %6, %10 offset:14336\n\t"
+      "ds_read_b128 %7, %9 offset:16384\n\t"
+      "ds_read_b128 %8, %10 offset:16384\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7]), "=&v"(f[8])
+      : "v"(e), "v"(o)
+      : "memory");
+}
+__device__ __forceinline__ void read_frags_l2(bf16x8 (&f)[9], uint32_t e, uint32_t o) {
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:0\n\t"
+      "ds_read_b128 %1, %10 offset:0\n\t"
+      "ds_read_b128 %2, %9 offset:1024\n\t"
+      "ds_read_b128 %3, %10 offset:1024\n\t"
+      "ds_read_b128 %4, %9 offset:2048\n\t"
+      "ds_read_b128 %5, %10 offset:2048\n\t"
+      "ds_read_b128 %6, %9 offset:3072\n\t"
+      "ds_read_b128 %7, %10 offset:3072\n\t"
+      "ds_read_b128 %8, %9 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7]), "=&v"(f[8])
+      : "v"(e), "v"(o)
+      : "memory");
+}
+
+// Warp-specialised form of the attention kernel (bf16, an even number of
+// 16-row tiles per stage: up to 32 heads).  Eight waves, two per SIMD:
+//  * score waves 0-3 stream the stages and compute the scores of stage k
+//    (wave w: one (tile, head block) pair), writing the scaled scores and the
+//    pair's per-head maxima to LDS;
+//  * value waves 4-7 run the softmax of stage k (reference max per head,
+//    lazily moved; O rescaled when it moves; P kept in registers in the
+//    layout of the P.V operand, which is the layout of the score products)
+//    and accumulate O^T += C^T P^T of stage k for their quarter of the latent
+//    channels, while the score waves compute stage k+1.
+// A score wave and a value wave share each SIMD, so one's products and
+// waits overlap the other's.  One barrier per stage: once it is passed,
+// stage k has landed, the scores of stage k-1 are written (scores and maxima
+// are double-buffered by stage parity), and the P.V of stage k-2 is done, so
+// its ring slot can be refilled.
+template <int R, int DR, int NHB>
+__global__ __launch_bounds__(512) void decode_ws_kernel(DecodeArgs a) {
+  using T = bf16;
+  using C = DecCfg<T, R, DR, NHB>;
+  using Lay = DecLayout<C::RB>;
+  static_assert(C::TPS % 2 == 0, "pairs of 16-row tiles per stage");
+  static_assert(C::KS == 18 || C::KS == 9, "batched score reads for r + d_hR = 576 or 288");
+  constexpr int HW = C::HW;
+  constexpr int NPAIR = C::TPS / 2;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int b, split, ns, pbase, start, end, t;
+  if (!decode_work<T, R, C::SROWS>(a, b, split, ns, pbase, start, end, t)) return;
+  const int s = a.s, H = a.H;
+  const int jn = t / s, n = jn + 1;
+  const bool owner = end == n;
+  const int nstage = (end - start + C::SROWS - 1) / C::SROWS;
+  const bool scorer = wave < 4;
+  const int w4 = wave & 3, stid = tid & 255;
+  const int g = lane >> 4, c = lane & 15;
+  char *seq = a.cache + (size_t)b * a.bstride_bytes;
+  char *dummy = smem + a.nst * C::STAGE_B;
+  float *smax = (float *)(dummy + 1024);                  // [2][TPS][HW] maxima of the pairs
+  f32x4 *zbuf = (f32x4 *)((char *)smax + 2 * C::SMAX_B);  // [2][TPS][NHB][64] scaled scores
+  int *last = (int *)(zbuf + 2 * C::TPS * NHB * 64);      // last-split flag
+  constexpr int ZB = C::TPS * NHB * 64;                   // scores per buffer
+
+  auto issue = [&](int sidx) {
+    char *sb = smem + (sidx % a.nst) * C::STAGE_B;
+    const int row0 = start + sidx * C::SROWS;
 #pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      M[u] = kNegInf;
-      L[u] = 0.0f;
-      acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < C::LPW; ++i) {
+      const int blk = w4 + 4 * i;
+      const bool real = (C::NBLK % 4 == 0) || blk < C::NBLK;
+      const int tl = real ? blk / C::NSEG : 0, bq = real ? blk % C::NSEG : 0;
+      int rr, bb;
+      Lay::src(bq, lane, rr, bb);
+      const int slot = min(row0 + tl * 16 + rr, end - 1);
+      __builtin_amdgcn_global_load_lds((const void *)(seq + (size_t)slot * C::RB + bb),
+                                       (lds_void *)(real ? sb + tl * C::TILE_B + bq * 1024 : dummy),
+                                       16, 0, kStreamPolicy);
     }
-    for (int k0 = 0; k0 < ns; k0 += SB) {
-      float pm[UB][SB], pl[UB][SB];
-      f32x4 po[UB][SB];
+  };
+
+  const size_t pidx = ((size_t)pbase + split) * H;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o, (uint32_t)((size_t)a.nparts * H * R * 4));
+  const __amdgpu_buffer_rsrc_t rml = make_rsrc(a.part_ml, (uint32_t)((size_t)a.nparts * H * 8));
+
+  // The two roles run separate loops with the same barriers in the same
+  // order (so each role's registers are live only in its own loop).
+  if (scorer) {
+    const int st_tile = w4 % C::TPS, st_hb = w4 / C::TPS;   // this wave's score pair
+    const int shead = st_hb * 16 + c;
+    // Queries, and (owner) the merge inputs, fetched before the stream so
+    // that later waits for them never wait for the stream.
+    bf16x8 q[C::KS];
 #pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int ci = min(c0 + 256 * u, nch - 1), h = ci / QC, ch = (ci % QC) * 4;
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int k = 32 * ks + 8 * g;
+      if (shead < H) {
+        if (k < R) load8(q[ks], (const T *)a.qt + ((size_t)b * H + shead) * R + k);
+        else load8(q[ks], (const T *)a.QR + ((size_t)b * H + shead) * DR + (k - R));
+      } else {
+        q[ks] = zero_frag<T>();
+      }
+    }
+    float mc[C::NU], mg[C::NU], mp[C::NU];
+    T mb[C::NU], mkr = from_f32<T>(0.0f);
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          pm[u][j] = kNegInf;
-          pl[u][j] = 0.0f;
-          po[u][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-          if (k0 + j < ns) {
-            const size_t i = base + (size_t)(k0 + j) * H + h;
-            pm[u][j] = ld_coh1(rml, (uint32_t)(i * 8));
-            pl[u][j] = ld_coh1(rml, (uint32_t)(i * 8 + 4));
-            po[u][j] = ld_coh4(ro, (uint32_t)((i * R + ch) * 4));
+    for (int i = 0; i < C::NU; ++i) {
+      mc[i] = mg[i] = mp[i] = 0.0f;
+      mb[i] = from_f32<T>(0.0f);
+    }
+    if (owner) {
+#pragma unroll
+      for (int i = 0; i < C::NU; ++i) {
+        const int ch = stid + 256 * i;
+        if (ch < R) {
+          mc[i] = a.cg[(size_t)b * 2 * R + ch];
+          mg[i] = a.cg[(size_t)b * 2 * R + R + ch];
+          mb[i] = ((const T *)a.b_hc)[ch];
+          mp[i] = a.gate_pos[(size_t)jn * R + ch];
+        }
+      }
+      if (stid < DR) mkr = ((const T *)a.KR)[(size_t)b * DR + stid];
+    }
+    asm volatile("" ::: "memory");
+    const int pro = min(a.nst, nstage);
+    for (int k = 0; k < pro; ++k) issue(k);
+    int lastst = pro - 1;   // newest stage issued so far
+
+    for (int k = 0; k <= nstage; ++k) {
+      if (k < nstage) wait_stages<C::LPW>(lastst - k);
+      wait_lgkm0();
+      bar();   // stage k landed; scores k-1 written; P.V(k-2) done, its slot free
+      if (k >= 2 && k - 2 + a.nst < nstage) {
+        issue(k - 2 + a.nst);
+        lastst = k - 2 + a.nst;
+      }
+      if (k == nstage - 1) {
+        // Last stage: rows past the split read as zeros (their weight is
+        // exactly 0, but the P.V product must not meet stale non-finite LDS
+        // contents), and the owner merges the new frame into the newest slot
+        // ([Notes] hyper-network temporal merging; [Fig2] (a)), in the cache
+        // and in its LDS copy.
+        char *sb = smem + (k % a.nst) * C::STAGE_B;
+        const int row0 = start + k * C::SROWS;
+        const int nz = row0 + C::SROWS - end;
+        for (int idx = stid; idx < nz * (C::RB / 16); idx += 256) {
+          const int r = end - row0 + idx / (C::RB / 16), ch = idx % (C::RB / 16);
+          *(u32x4 *)(sb + (r >> 4) * C::TILE_B + Lay::off(r & 15, ch * 16)) = (u32x4){0u, 0u, 0u, 0u};
+        }
+        if (owner) {
+          const int rr = jn - row0;
+          char *trow = sb + (rr >> 4) * C::TILE_B;
+          T *grow = (T *)(seq + (size_t)jn * C::RB);
+          const bool open = (t % s) == 0;
+#pragma unroll
+          for (int i = 0; i < C::NU; ++i) {
+            const int ch = stid + 256 * i;
+            if (ch < R) {
+              T *lpnt = (T *)(trow + Lay::off(rr & 15, ch * 2));
+              const float u = sigmoidf((mg[i] + to_f32(mb[i])) * mp[i]) * mc[i];
+              const T v = from_f32<T>(open ? u : to_f32(*lpnt) + u);
+              *lpnt = v;
+              grow[ch] = v;
+            }
+          }
+          if (stid < DR) {
+            *(T *)(trow + Lay::off(rr & 15, (R + stid) * 2)) = mkr;
+            grow[R + stid] = mkr;
+          }
+        }
+        wait_lgkm0();
+        bar();
+      }
+      if (k < nstage) {
+        // Scores of this wave's (tile, head block) pair.
+        const char *stile = smem + (k % a.nst) * C::STAGE_B + st_tile * C::TILE_B;
+        const int kb = start + k * C::SROWS + st_tile * 16;
+        const uint32_t fe = lds_addr(stile + Lay::off(c, 16 * g));
+        const uint32_t fo = lds_addr(stile + Lay::off(c, 64 + 16 * g));
+        f32x4 sa[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        {
+          bf16x8 kf[9];
+          if constexpr (C::KS == 18) read_frags_l1_lo(kf, fe, fo);
+          else read_frags_l2(kf, fe, fo);
+#pragma unroll
+          for (int i = 0; i < 9; ++i) sa[i & 3] = mma_k32(kf[i], q[i], sa[i & 3]);
+        }
+        if constexpr (C::KS == 18) {
+          bf16x8 kf[9];
+          read_frags_l1_hi(kf, fe, fo);
+#pragma unroll
+          for (int i = 0; i < 9; ++i) sa[(9 + i) & 3] = mma_k32(kf[i], q[9 + i], sa[(9 + i) & 3]);
+        }
+        f32x4 z;
+        float mx = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          z[e] = (kb + 4 * g + e < end) ? ((sa[0][e] + sa[1][e]) + (sa[2][e] + sa[3][e])) * a.sl2
+                                        : kNegInf;
+          mx = fmaxf(mx, z[e]);
+        }
+        mx = max_g(mx);   // -inf only for a tile wholly past the split
+        if (g == 0) smax[(k & 1) * (C::TPS * HW) + st_tile * HW + shead] = mx;
+        zbuf[(k & 1) * ZB + (st_tile * NHB + st_hb) * 64 + lane] = z;
+      }
+    }
+  } else {
+    // o[hb][qb]: O^T of channels 16 (w4 * MQ + qb) + 4g + e, head hb * 16 +
+    // c.  m[hb]: reference max of that head (the same in every value wave);
+    // lp[hb]: this lane's partial sum of its P.  pp: P of the stage awaiting
+    // its P.V, per head block and tile pair, in the operand layout (k index
+    // 8g + e: slot 4g + e of the pair's first tile for e < 4, of its second
+    // for e >= 4).
+    f32x4 o[NHB][C::MQ];
+    float m[NHB], lp[NHB];
+    bf16x8 pp[NHB][NPAIR];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      m[hb] = kNegInf;
+      lp[hb] = 0.0f;
+#pragma unroll
+      for (int qb = 0; qb < C::MQ; ++qb) o[hb][qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int k = 0; k <= nstage; ++k) {
+      wait_lgkm0();
+      bar();   // stage k landed; scores k-1 written
+      if (k == nstage - 1) bar();   // the score waves' last-stage fix-ups
+      if (k == 0) continue;
+      const int kk = k - 1;   // the stage this iteration finishes
+      {
+        // Softmax of stage kk: move the reference max of a head when a score
+        // exceeds it by more than 2^8 (rescaling O, which holds the stages
+        // before kk), then P = 2^(z - m) in the operand layout.
+        const float *sm_k = smax + (kk & 1) * (C::TPS * HW);
+        const f32x4 *zb = zbuf + (kk & 1) * ZB;
+        float mnew[NHB];
+        bool up_any = false;
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          float sm = kNegInf;
+#pragma unroll
+          for (int tl = 0; tl < C::TPS; ++tl) sm = fmaxf(sm, sm_k[tl * HW + hb * 16 + c]);
+          const bool up = sm > m[hb] + 8.0f;
+          mnew[hb] = up ? sm : m[hb];
+          up_any |= up;
+        }
+        if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            const float alpha = __builtin_amdgcn_exp2f(m[hb] - mnew[hb]);
+#pragma unroll
+            for (int qb = 0; qb < C::MQ; ++qb) o[hb][qb] *= alpha;
+            lp[hb] *= alpha;
+            m[hb] = mnew[hb];
+          }
+        }
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+          for (int pair = 0; pair < NPAIR; ++pair) {
+            const f32x4 z0 = zb[((2 * pair) * NHB + hb) * 64 + lane];
+            const f32x4 z1 = zb[((2 * pair + 1) * NHB + hb) * 64 + lane];
+            bf16x8 pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(z0[e] - m[hb]);
+              const float p1 = __builtin_amdgcn_exp2f(z1[e] - m[hb]);
+              lp[hb] += p0 + p1;
+              pv[e] = from_f32<T>(p0);
+              pv[4 + e] = from_f32<T>(p1);
+            }
+            pp[hb][pair] = pv;
           }
         }
       }
+      // O^T += C^T P^T of stage kk, this wave's channel quarter.
+      const char *sb = smem + (kk % a.nst) * C::STAGE_B;
+      const int row0 = start + kk * C::SROWS;
 #pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        float Mn = M[u];
+      for (int pair = 0; pair < NPAIR; ++pair) {
+        const int tl = 2 * pair;
+        if (row0 + tl * 16 >= end) continue;   // a pair wholly past the split
+        const char *t0 = sb + tl * C::TILE_B;
 #pragma unroll
-        for (int j = 0; j < SB; ++j) Mn = fmaxf(Mn, pm[u][j]);
-        const float sc = __builtin_amdgcn_exp2f(M[u] - Mn);
-        L[u] *= sc;
-        acc[u] *= sc;
+        for (int q0 = 0; q0 < C::MQ; q0 += 4) {
+          uint32_t ad[8];
+          bf16x4 v[8];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const float w = (k0 + j < ns) ? __builtin_amdgcn_exp2f(pm[u][j] - Mn) : 0.0f;
-          L[u] += w * pl[u][j];
-          acc[u] += w * po[u][j];
+          for (int j = 0; j < 4; ++j) {
+            const int ch0 = 16 * (w4 * C::MQ + q0 + j);
+            ad[2 * j] = lds_addr(t0 + Lay::off(4 * g + (c >> 2), (ch0 + 4 * (c & 3)) * 2));
+            ad[2 * j + 1] = ad[2 * j] + C::TILE_B;
+          }
+          ds_read_tr8(v, ad);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8 vv = __builtin_shufflevector(v[2 * j], v[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) o[hb][q0 + j] = mma_k32(vv, pp[hb][pair], o[hb][q0 + j]);
+          }
         }
-        M[u] = Mn;
       }
     }
+    // Row sums over the lane groups, then this split's result.
 #pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int ci = c0 + 256 * u;
-      if (ci >= nch) continue;
-      const int h = ci / QC, ch = (ci % QC) * 4;
-      T *dst = (T *)a.o + ((size_t)b * H + h) * R + ch;
-      const float inv = 1.0f / L[u];
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int head = hb * 16 + c;
+      const float L = sum_g(lp[hb]);
+      if (head >= H) continue;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(acc[u][e] * inv);
+      for (int qb = 0; qb < C::MQ; ++qb) {
+        const int ch = 16 * (w4 * C::MQ + qb) + 4 * g;
+        if (ns == 1) {
+          T *dst = (T *)a.o + ((size_t)b * H + head) * R + ch;
+          const float inv = 1.0f / L;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(o[hb][qb][e] * inv);
+        } else {
+          st_coh4(ro, (uint32_t)(((pidx + head) * R + ch) * 4), o[hb][qb]);
+        }
+      }
+      if (ns > 1 && w4 == 0 && g == 0) {
+        st_coh1(rml, (uint32_t)((pidx + head) * 8), m[hb]);
+        st_coh1(rml, (uint32_t)((pidx + head) * 8 + 4), L);
+      }
     }
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (ns == 1) return;
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (tid == 0) *last = ctr_add(&a.counters[b], 1) == ns - 1;
+  __syncthreads();
+  if (!*last) return;
+  merge_partials<T, R>(a, b, ns, pbase, ro, rml);
 }
 
 // Stand-alone merge-append: one workgroup per sequence.  A position outside
@@ -745,9 +1137,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t *pos, int max_
 template <typename T, int R, int DR, int NHB>
 hipError_t decode_attn_t(const DecodePlan &p, int B, DecodeArgs args, hipStream_t stream,
                          hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 grid = p.flat ? dim3(p.grid) : dim3(p.splits, B);
+  if constexpr (sizeof(T) == 2 && NHB <= 2) {
+    if (p.ws) {
+      auto kern = decode_ws_kernel<R, DR, NHB>;
+      allow_lds<decode_ws_kernel<R, DR, NHB>>();
+      return launch_timed((const void *)kern, grid, dim3(512), p.lds, stream, &args, ev0, ev1);
+    }
+  }
   auto kern = decode_attn_kernel<T, R, DR, NHB>;
   allow_lds<decode_attn_kernel<T, R, DR, NHB>>();
-  const dim3 grid = p.flat ? dim3(p.grid) : dim3(p.splits, B);
   return launch_timed((const void *)kern, grid, dim3(256), p.lds, stream, &args, ev0, ev1);
 }
 
@@ -773,17 +1172,22 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
   p.nhb = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
   const int tps = 4 / p.nhb, srows = 16 * tps;
   const size_t stage = (size_t)srows * (r + dR) * esz;
-  const size_t extra =
-      1024 + (size_t)tps * 16 * p.nhb * 4 + (size_t)tps * p.nhb * 64 * 4 * esz + 16;
+  // Warp-specialised kernel: bf16 with pairs of 16-row tiles per stage.
+  p.ws = (dtype == 1 && p.nhb <= 2) ? 1 : 0;
+  const size_t hw = (size_t)16 * p.nhb;
+  const size_t extra = p.ws ? 1024 + 2 * (size_t)tps * hw * 4 + 2 * (size_t)tps * p.nhb * 64 * 16 + 16
+                            : 1024 + (size_t)tps * hw * 4 + (size_t)tps * p.nhb * 64 * 4 * esz + 16;
   const int64_t nmax = max_pos / s + 1;
   const int64_t mstages = (nmax + srows - 1) / srows;   // stages of the longest sequence
   p.block = srows;
   // Ring: about 4 stages of 36 KB, or more of smaller stages (at most 8).
   int nst = (int)(144 * 1024 / stage);
   if (nst > 8) nst = 8;
+  // The kernels refill a stage's slot two stages after its scores (once its
+  // P.V is done), so a split of several stages needs a ring of at least three.
   // Balanced work list on the device for up to 256 sequences (four per lane
   // of the kernel's tables), when a split may hold more than one stage.
-  p.flat = (B <= 256 && nst >= 2) ? 1 : 0;
+  p.flat = (B <= 256 && nst >= 3) ? 1 : 0;
   if (p.flat) {
     int64_t G = B <= MTLA_DECODE_TARGET_WGS / 2
                     ? MTLA_DECODE_TARGET_WGS
@@ -802,9 +1206,10 @@ bool decode_plan(int dtype, int H, int r, int dR, int s, int B, int max_pos, Dec
     chunk = ((chunk + srows - 1) / srows) * srows;
     const int64_t cap = mstages * srows;
     if (chunk > cap) chunk = cap;
-    if (nst < 2) {
-      // A one-slot ring cannot refill a slot that the same stage still reads:
-      // give each split a single stage instead (more splits, same bytes).
+    if (nst < 3) {
+      // A ring of fewer than three slots cannot refill the slot two stages
+      // back while the newest one is read: give each split a single stage
+      // instead (more splits, same bytes).
       nst = 1;
       chunk = srows;
     }

@@ -72,6 +72,7 @@ struct DecodePlan {
   int nhb;      // head blocks of 16
   int block;    // slots per LDS stage
   int flat;     // 1: balanced work list derived on the device from the positions
+  int ws;       // 1: warp-specialised kernel (512 threads)
   int grid;     // workgroups (flat)
   int chunk;    // slots per split (uniform splits, flat == 0)
   int splits;   // splits per sequence (uniform: grid x, with grid y = B)

@@ -146,6 +146,7 @@ def test_decode_wide_latent_fp32():
     (32, 256, 32, "bf16", 1),    # 32-row stages, 5 loads per wave, 8-slot ring
     (48, 256, 32, "bf16", 1),    # 16-row stages, padding load blocks
     (4, 512, 64, "f32", 2),      # 147 KB stages: one-slot ring, one stage per split
+    (8, 256, 32, "f32", 2),      # 72 KB stages: a two-slot ring cannot refill, one stage per split
 ])
 def test_decode_long_splits(H, r, dR, storage, s):
     """Contexts long enough that each split streams many stages (beyond the
