@@ -56,7 +56,7 @@ CSRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc")
 # Sources that define each timed kernel: a counter summary under profiles/
 # applies only while these files are unchanged.
 KERNEL_SOURCES = {
-    "decode_attn_kernel": ("decode.hip", "common.h", "kernels.h"),
+    "decode_ws_kernel": ("decode.hip", "common.h", "kernels.h"),
     "prefill_ws_kernel": ("attention.hip", "common.h", "kernels.h"),
 }
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
@@ -531,9 +531,9 @@ def cpu_prefill_baseline() -> dict:
 
 def roofline(rec: dict, workload: str) -> dict:
     """Roofline block of the attention kernel of a decode record."""
-    tr = measured_traffic(workload, "decode_attn_kernel")
+    tr = measured_traffic(workload, "decode_ws_kernel")
     traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None
-    return {"bound": "hbm", "kernel": "decode_attn_kernel",
+    return {"bound": "hbm", "kernel": "decode_ws_kernel",
             "achieved": round(rec["attn_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(rec["attn_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
             "bytes_per_launch": rec["cache_bytes"],
