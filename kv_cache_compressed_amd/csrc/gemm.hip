@@ -513,6 +513,14 @@ hipError_t proj_t(const void *X, int M, int d, const void *W_dkv, const void *W_
   if (M <= 64)
     return run_skinny<T>((const T *)X, d, bs, M, N, d, 1, nullptr, nullptr, zero, nzero, epi,
                          stream);
+  if constexpr (sizeof(T) == 2) {
+    // 65..128 rows: the weight-streaming product (no K split for this shape
+    // when the columns fill the compute units; it clears `zero` itself).
+    StreamPlan sp;
+    if (stream_gemm_plan(2, M, N, d, &sp) && sp.splits == 1)
+      return launch_stream_gemm((const bf16 *)X, d, bs, M, N, d, sp, nullptr, nullptr, zero, nzero,
+                                epi, stream);
+  }
   if (zero && nzero > 0) {
     hipLaunchKernelGGL(zero_kernel, dim3((nzero + 255) / 256), dim3(256), 0, stream, zero, nzero);
     const hipError_t e = hipGetLastError();
@@ -528,8 +536,17 @@ int out_proj_strips(int M, int N) {
   return M <= 64 ? (N + 15) / 16 : (N + 31) / 32;
 }
 
+int out_proj_counters(int esz, int M, int N, int K) {
+  StreamPlan sp;
+  int n = out_proj_strips(M, N);
+  if (stream_gemm_plan(esz, M, N, K, &sp) && sp.tiles > n) n = sp.tiles;
+  return n;
+}
+
 size_t out_proj_part_bytes(int esz, int M, int N, int K) {
   if (M > 128) return 0;
+  StreamPlan sp;
+  if (stream_gemm_plan(esz, M, N, K, &sp)) return stream_gemm_part_bytes(sp);
   const int mpad = M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
   if (M > 64) {
     const TiledSplit t = tiled_splitk_plan(esz, N, K);
@@ -590,6 +607,10 @@ hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *B
                            float *part, int *counters, hipStream_t stream) {
   if (M > 128) return launch_gemm_store(dtype, O, K, Bvo, K, M, N, K, Y, N, stream);
   BSeg bs{Bvo, Bvo, Bvo, N, N, K};
+  StreamPlan sp;
+  if (dtype == 1 && stream_gemm_plan(2, M, N, K, &sp) && (sp.splits == 1 || (part && counters)))
+    return launch_stream_gemm((const bf16 *)O, K, bs, M, N, K, sp, part, counters, nullptr, 0,
+                              EpiStore<bf16>{(bf16 *)Y, N}, stream);
   if (M > 64 && part && counters) {
     // 65..128 rows: the tiled product (fragments reused across each wave's
     // block of tiles) with K split, instead of narrow strips that each read

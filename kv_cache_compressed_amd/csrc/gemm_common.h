@@ -74,6 +74,23 @@ template <typename T> struct EpiProj {
 // tile, stored four columns at a time (epi.four, rows aligned to 4 values:
 // epi.four_aligned()).  Instantiated for EpiStore<bf16> and EpiProj<bf16>.
 bool gemm_big_supported(int M, int N, int K);
+
+// Weight-streaming bf16 product for 65..128 rows (gemm_stream.hip): C = X W^T
+// with K a multiple of 64.  The plan fixes the work split: `tiles` column
+// tiles of `ng` 16-column groups (at most), each split `splits` ways over K
+// (`kst` 64-wide k-stages per split) with an LDS ring of `nst` stages.  With
+// splits > 1, `part` holds stream_gemm_part_bytes of fp32 partials and
+// `counters` `tiles` ints that are zero on entry (and again on exit).
+// `zero`: ints cleared by the kernel before anything else (may be null).
+struct StreamPlan {
+  int ng, tiles, gbase, grem, splits, kst, nst;
+};
+bool stream_gemm_plan(int esz, int M, int N, int K, StreamPlan *p);
+size_t stream_gemm_part_bytes(const StreamPlan &p);
+template <class Epi>
+hipError_t launch_stream_gemm(const bf16 *X, int ldx, const BSeg &bs, int M, int N, int K,
+                              const StreamPlan &p, float *part, int *counters, int *zero,
+                              int nzero, Epi epi, hipStream_t stream);
 template <class Epi>
 hipError_t launch_gemm_big(const bf16 *A, int lda, const BSeg &bs, int M, int N, int K, Epi epi,
                            hipStream_t stream);

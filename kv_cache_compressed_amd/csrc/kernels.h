@@ -56,15 +56,19 @@ hipError_t launch_proj(int dtype, const void *X, int M, int d, const void *W_dkv
 
 // Y [M, N] = O [M, K] Bvo [N, K]^T.  For M <= 128 with `part` and `counters`
 // given, K is split over workgroups with fp32 partials in `part`
-// (out_proj_part_bytes) and counters (at most out_proj_strips of them), zero
-// on entry and zero again on exit: up to 64 rows as narrow column strips
-// (out_proj_splits splits), 65..128 rows as 128-row tiles.
+// (out_proj_part_bytes) and counters (at most out_proj_counters of them),
+// zero on entry and zero again on exit: up to 64 rows as narrow column strips
+// (out_proj_splits splits); 65..128 rows in bf16 with K a multiple of 64 by
+// the weight-streaming product (stream_gemm_plan), otherwise as 128-row
+// tiles.
 hipError_t launch_out_proj(int dtype, const void *O, int M, int K, const void *Bvo, int N, void *Y,
                            float *part, int *counters, hipStream_t stream);
 int out_proj_splits(int M, int N, int K);
 // Bytes of fp32 partials launch_out_proj needs in `part` (esz: storage bytes).
 size_t out_proj_part_bytes(int esz, int M, int N, int K);
 int out_proj_strips(int M, int N);
+// Counters launch_out_proj may use (esz: storage bytes).
+int out_proj_counters(int esz, int M, int N, int K);
 
 // ---- incremental decoding ---------------------------------------------------
 

@@ -109,7 +109,7 @@ struct DecodeWs {
 DecodeWs decode_ws(const mtla_dims *d, int B, const mtla::DecodePlan *plan) {
   DecodeWs w;
   const size_t e = esize(d), r = d->r, HR = (size_t)d->H * d->r;
-  const int nctr = plan ? B + mtla::out_proj_strips(B, d->d) : 0;
+  const int nctr = plan ? B + mtla::out_proj_counters((int)e, B, d->d, (int)HR) : 0;
   size_t off = 0;
   w.status = off;
   w.counters = off + 4;

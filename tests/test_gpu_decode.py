@@ -134,6 +134,25 @@ def test_decode_batch_between_64_and_128(storage):
     _decode_case(dims, pos, storage, 7350, check=[0, 1, 50, 99])
 
 
+@pytest.mark.parametrize("B,d,H,r,dR", [
+    (128, 1024, 32, 512, 64),   # input: 1088 column groups, 4 or 5 per workgroup, 16 stages
+                                # through a 15-slot ring; output: 16 tiles x 8 splits (XCD-placed)
+    (65, 1024, 32, 512, 64),    # 65 rows: the last wave's rows mostly padding
+    (97, 224, 8, 256, 32),      # output: 14 groups in 4 tiles of 3 or 4, 8 splits
+    (80, 5120, 4, 256, 32),     # output: 80 tiles x 3 splits, the last one shorter
+])
+def test_decode_weight_streaming_projections(B, d, H, r, dR):
+    """65..128 sequences in bf16: the projections stream the weights (the
+    workgroup's columns through an LDS ring, its rows of X in registers);
+    every branch of the work split against the oracle."""
+    needs_gpu()
+    dims = Dims(d=d, H=H, d_h=64, r=r, d_hR=dR, s=2)
+    rng = np.random.default_rng(7600 + B + d)
+    pos = rng.integers(0, 600, size=B)
+    say("decode weight streaming", B, d, H, r)
+    _decode_case(dims, pos, "bf16", 7600 + B, check=[0, 1, B // 2, B - 1])
+
+
 def test_decode_wide_latent_fp32():
     needs_gpu()
     dims = Dims(d=256, H=4, d_h=128, r=512, d_hR=64, s=2)
