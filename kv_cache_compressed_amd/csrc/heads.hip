@@ -63,23 +63,34 @@ struct HeadsArgs {
 #define MTLA_HEADS_NST 5
 #endif
 
-struct HdCfg {
-  static constexpr int DH = 64, DR = 32, QK = DH + DR;   // 96 score channels
-  static constexpr int RB = (QK + DH) * 2;                // LDS key row K | K^R | V: 320 B
+// Head widths (DH, DR): (64, 32) and, at the LLM-scale model dims
+// (r = 4 d_h = 512), (128, 64).  NQ 16-row query tiles per wave, NST ring
+// stages, OCC workgroups per CU (the register and LDS budget: at d_h = 128 a
+// wave holds two row tiles so that queries, accumulators and both tiles'
+// K^T fragments stay within the 256 registers of two waves per SIMD).
+template <int DH_, int DR_, int NQ_, int NST_, int OCC_> struct HdCfg {
+  static constexpr int DH = DH_, DR = DR_, QK = DH + DR;  // score channels
+  static constexpr int RB = (QK + DH) * 2;                // LDS key row K | K^R | V
   static constexpr int NSEG = RB / 64;                    // 64-byte blocks per row
+  static constexpr int KSEG = DH * 2 / 64, RSEG = DR * 2 / 64;   // blocks of K, of K^R
   static constexpr int VOFF = QK * 2;                     // byte offset of V in a key row
-  static constexpr int KS = QK / 32, MB = DH / 16;        // 3 k-steps, 4 channel blocks
+  static constexpr int KS = QK / 32, MB = DH / 16;        // k-steps, channel blocks
   static constexpr int NW = MTLA_HEADS_WAVES;            // waves per workgroup
-  static constexpr int NQ = 4, ROWS_W = 16 * NQ, ROWS = NW * ROWS_W;
+  static constexpr int NQ = NQ_, ROWS_W = 16 * NQ, ROWS = NW * ROWS_W;
   static constexpr int SROWS = 32, TILE_B = 16 * RB, STAGE_B = 2 * TILE_B;
   static constexpr int NBLK = 2 * NSEG, LPW = (NBLK + NW - 1) / NW;
-  static constexpr int NST = MTLA_HEADS_NST;   // ring stages (>= 3: slots k, k+1 and the refill)
+  static constexpr int NST = NST_;   // ring stages (>= 3: slots k, k+1 and the refill)
+  static constexpr int OCC = OCC_;
   static_assert(NST >= 3, "the pipeline reads two stages while a third is refilled");
-  static_assert(NSEG == 5 && VOFF == 192, "block map of the key rows");
+  static_assert(QK % 32 == 0 && DH % 32 == 0 && DR % 32 == 0, "whole 64-byte blocks");
+  static_assert(MB % 4 == 0, "transposing reads issued eight at a time");
+  static_assert(OCC * (NST * STAGE_B + 1024) <= 160 * 1024, "LDS per CU");
 };
+using HdCfg64 = HdCfg<64, 32, 4, MTLA_HEADS_NST, 2>;
+using HdCfg128 = HdCfg<128, 64, 2, 3, 2>;
 
-__global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kernel(HeadsArgs a) {
-  using C = HdCfg;
+template <class C>
+__global__ __launch_bounds__(64 * C::NW, C::OCC) void heads_attn_kernel(HeadsArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,9 +177,9 @@ __global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kern
       const int key = min(row0 + tl * 16 + (lane >> 2), kmax - 1);
       const size_t fr = (size_t)b * Tn + (size_t)s * key + (s - 1);
       const char *seg;
-      if (qq < 2) seg = (const char *)(a.KV + fr * kvw + h * C::DH) + qq * 64;
-      else if (qq == 2) seg = (const char *)(a.KR + fr * C::DR);
-      else seg = (const char *)(a.KV + fr * kvw + (size_t)(H + h) * C::DH) + (qq - 3) * 64;
+      if (qq < C::KSEG) seg = (const char *)(a.KV + fr * kvw + h * C::DH) + qq * 64;
+      else if (qq < C::KSEG + C::RSEG) seg = (const char *)(a.KR + fr * C::DR) + (qq - C::KSEG) * 64;
+      else seg = (const char *)(a.KV + fr * kvw + (size_t)(H + h) * C::DH) + (qq - C::KSEG - C::RSEG) * 64;
       __builtin_amdgcn_global_load_lds((const void *)(seg + u * 16),
                                        (lds_void *)(real ? sb + tl * C::TILE_B + qq * 1024 : dummy),
                                        16, 0, 0);
@@ -244,19 +255,20 @@ __global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kern
     bf16x8 kf[2][C::KS];
     read_k(k + 1, kf);
     bf16x8 vf[C::MB];
-    {
+#pragma unroll
+    for (int m0 = 0; m0 < C::MB; m0 += 4) {
       uint32_t ad[8];
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        const char *p0 = sb + tile_off(4 * g + (c >> 2), C::VOFF + (16 * mb + 4 * (c & 3)) * 2);
+      for (int mb = 0; mb < 4; ++mb) {
+        const char *p0 = sb + tile_off(4 * g + (c >> 2), C::VOFF + (16 * (m0 + mb) + 4 * (c & 3)) * 2);
         ad[2 * mb] = lds_addr(p0);
         ad[2 * mb + 1] = lds_addr(p0 + C::TILE_B);
       }
       bf16x4 vv[8];
       ds_read_tr8(vv, ad);
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        vf[mb] = __builtin_shufflevector(vv[2 * mb], vv[2 * mb + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int mb = 0; mb < 4; ++mb)
+        vf[m0 + mb] = __builtin_shufflevector(vv[2 * mb], vv[2 * mb + 1], 0, 1, 2, 3, 4, 5, 6, 7);
     }
 
     // Online softmax of stage k per row (lane holds keys 4g..4g+3 of each
@@ -353,26 +365,35 @@ __global__ __launch_bounds__(64 * HdCfg::NW, 8 / HdCfg::NW) void heads_attn_kern
 }  // namespace
 
 bool heads_attention_supported(int dtype, int H, int d_h, int dR) {
-  return dtype == 1 && d_h == HdCfg::DH && dR == HdCfg::DR && H >= 1 && H <= 64;
+  return dtype == 1 && ((d_h == 64 && dR == 32) || (d_h == 128 && dR == 64)) && H >= 1 && H <= 64;
 }
 
-hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const void *q,
+namespace {
+template <class C>
+hipError_t heads_t(int B, int T, int H, int s, float sl2, const void *q, const void *QR,
+                   const void *KV, const void *KR, void *O, float *lse, hipStream_t stream,
+                   hipEvent_t ev0, hipEvent_t ev1) {
+  const int tiles = (T + C::ROWS - 1) / C::ROWS;
+  const size_t lds = (size_t)C::NST * C::STAGE_B + 1024;
+  allow_lds<heads_attn_kernel<C>>();
+  HeadsArgs args{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
+                 (bf16 *)O, lse, B, T, H, s, tiles, C::NST, sl2};
+  return launch_timed((const void *)heads_attn_kernel<C>, dim3(tiles * B * H), dim3(64 * C::NW),
+                      lds, stream, &args, ev0, ev1);
+}
+}  // namespace
+
+hipError_t launch_heads_attention(int B, int T, int H, int d_h, int s, float scale, const void *q,
                                   const void *QR, const void *KV, const void *KR, void *O,
                                   float *lse, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-  using C = HdCfg;
-  const int tiles = (T + C::ROWS - 1) / C::ROWS;
-  const int nst = C::NST;
-  const size_t lds = (size_t)nst * C::STAGE_B + 1024;
-  allow_lds<heads_attn_kernel>();
   // Masked scores are -inf before the fused scale-and-subtract, which needs
   // a positive scale (0 * -inf is NaN): a scale that underflows to zero is
   // raised to the smallest normal value.
   float sl2 = scale * kLog2e;
   if (!(sl2 >= FLT_MIN)) sl2 = FLT_MIN;
-  HeadsArgs args{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
-                 (bf16 *)O, lse, B, T, H, s, tiles, nst, sl2};
-  return launch_timed((const void *)heads_attn_kernel, dim3(tiles * B * H), dim3(64 * C::NW), lds,
-                      stream, &args, ev0, ev1);
+  if (d_h == 128)
+    return heads_t<HdCfg128>(B, T, H, s, sl2, q, QR, KV, KR, O, lse, stream, ev0, ev1);
+  return heads_t<HdCfg64>(B, T, H, s, sl2, q, QR, KV, KR, O, lse, stream, ev0, ev1);
 }
 
 }  // namespace mtla

@@ -145,12 +145,13 @@ hipError_t launch_prefill_attention(int dtype, int B, int T, int H, int r, int d
 
 bool prefill_attention_supported(int dtype, int H, int r, int dR);
 
-// Per-head (unabsorbed) stride-aware masked attention, bf16, d_h = 64,
-// dR = 32: O [B*T, H*64] from q [B*T, H*64], QR [B*T, H, dR], KV
-// [B*T, 2*H*64] (K_h at column 64 h, V_h at 64 (H + h)) and KR [B*T, dR].
-// lse (nullable) [B*T, H] fp32 receives each row's log2 softmax sum in the
-// kernel's scaled log2 units (weights p = exp2(z * scale * log2(e) - lse)).
-hipError_t launch_heads_attention(int B, int T, int H, int s, float scale, const void *q,
+// Per-head (unabsorbed) stride-aware masked attention, bf16, (d_h, dR) =
+// (64, 32) or (128, 64): O [B*T, H*d_h] from q [B*T, H*d_h], QR [B*T, H, dR],
+// KV [B*T, 2*H*d_h] (K_h at column d_h h, V_h at d_h (H + h)) and KR
+// [B*T, dR].  lse (nullable) [B*T, H] fp32 receives each row's log2 softmax
+// sum in the kernel's scaled log2 units (weights p = exp2(z * scale *
+// log2(e) - lse)).
+hipError_t launch_heads_attention(int B, int T, int H, int d_h, int s, float scale, const void *q,
                                   const void *QR, const void *KV, const void *KR, void *O,
                                   float *lse, hipStream_t stream, hipEvent_t ev0 = nullptr,
                                   hipEvent_t ev1 = nullptr);

@@ -56,6 +56,19 @@ def test_unabsorbed_matches_oracle(s, T, H, B):
     _case(dims, B, T, 9000 + 13 * s + T + H)
 
 
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 4, 1), (2, 300, 4, 2), (3, 257, 8, 1), (1, 64, 2, 2),
+                                       (4, 513, 4, 1), (80, 100, 2, 1), (5, 96, 3, 2),
+                                       (2, 1024, 8, 1)])
+def test_unabsorbed_llm_head_width(s, T, H, B):
+    """The per-head form at the LLM-scale head widths (d_h = 128, d_hR = 64,
+    r = 4 d_h = 512): 640-byte key rows, two 16-row query tiles per wave,
+    128 query frames per workgroup."""
+    needs_gpu()
+    dims = Dims(d=512, H=H, d_h=128, r=512, d_hR=64, s=s)
+    say("prefill per-head d_h=128", s, T, H, B)
+    _case(dims, B, T, 9400 + 13 * s + T + H)
+
+
 def test_unabsorbed_full_size_sampled():
     """The benchmark's per-head launch (B=16, T=4096, s=2), checked on
     sampled rows of two sequences against the oracle's per-head attention of
