@@ -292,8 +292,9 @@ typedef struct {
  * content branch is differentiated in the pages' form, Linear(c) = W_hc c +
  * b_hc, so W_hc [r, r] (storage dtype) is passed besides the folded W_gate
  * the forward uses; the position branch is differentiated as its table.
- * The forward is recomputed inside.  Supported: bf16 storage, d_h = 64,
- * d_hR = 32.  Workspace: mtla_workspace_bytes(op=5, B, T). */
+ * The forward is recomputed inside.  Supported: bf16 storage with
+ * (d_h, d_hR) = (64, 32) or (128, 64).  Workspace:
+ * mtla_workspace_bytes(op=5, B, T). */
 mtla_status mtla_prefill_unabsorbed_backward(const mtla_dims *dims,
                                              const mtla_unabsorbed_weights *w, const void *W_hc,
                                              const void *X, const void *QR, const void *KR,

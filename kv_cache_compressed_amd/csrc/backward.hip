@@ -37,14 +37,30 @@ namespace mtla {
 namespace {
 
 constexpr float kNegInfB = -INFINITY;
-constexpr int DH = 64, DR = 32, QK = DH + DR;
-// LDS row of a streamed frame, in the 16-row swizzled tile layout: 160 bf16
-// (320 B, five 64-byte blocks).  Key rows: K_h | K^R | V_h.  Query rows:
-// Q_h | Q^R_h | dO_h.  Byte offsets of the parts:
-constexpr int RB = 320, NSEG = 5, OFF_B = 128, OFF_C = 192;
-constexpr int TILE_B = 16 * RB, STAGE_B = 2 * TILE_B, SROWS = 32;
-constexpr int NBLK = 2 * NSEG, LPW = (NBLK + 3) / 4;
-constexpr int NST = 4;
+
+// Head widths and tiling of the attention backward: (DH, DR) = (64, 32) with
+// two 16-row tiles (32 keys, or 32 query frames) per wave and two workgroups
+// per CU, or (128, 64) with one tile per wave and one workgroup per CU (the
+// accumulators of twice the width then fit without spills).
+// Streamed rows hold, in the 16-row swizzled tile layout, K_h | K^R | V_h
+// (key rows) or Q_h | Q^R_h | dO_h (query rows): 2 DH + DR bf16.
+template <int DH_, int DR_, int NT_, int NST_, int OCC_> struct BwCfg {
+  static constexpr int DH = DH_, DR = DR_, QK = DH + DR;
+  static constexpr int RB = (2 * DH + DR) * 2, NSEG = RB / 64;
+  static constexpr int KSEG = DH * 2 / 64, RSEG = DR * 2 / 64;   // 64-byte blocks of K, of K^R
+  static constexpr int OFF_C = QK * 2;                           // byte offset of V_h / dO_h
+  static constexpr int KS = QK / 32, VS = DH / 32;               // k-steps of the scores, of dP
+  static constexpr int MB = DH / 16, RBK = DR / 16;              // 16-channel blocks
+  static constexpr int NT = NT_, WROWS = 16 * NT, GROWS = 4 * WROWS;
+  static constexpr int TILE_B = 16 * RB, STAGE_B = 2 * TILE_B, SROWS = 32;
+  static constexpr int NBLK = 2 * NSEG, LPW = (NBLK + 3) / 4;
+  static constexpr int NST = NST_, OCC = OCC_;
+  static_assert(QK % 32 == 0 && DH % 32 == 0 && DR % 32 == 0, "whole 64-byte blocks");
+  static_assert(MB % 4 == 0 && (RBK % 4 == 0 || RBK == 2), "transposing reads eight at a time");
+  static_assert(OCC * (NST * STAGE_B + 1024) <= 160 * 1024, "LDS per CU");
+};
+using Bw64 = BwCfg<64, 32, 2, 4, 2>;
+using Bw128 = BwCfg<128, 64, 1, 4, 1>;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_b4;
 
@@ -57,6 +73,39 @@ __device__ __forceinline__ uint32_t tr_addr(const char *sb, int ch0, int g, int 
 
 __device__ __forceinline__ bf16x8 join(const bf16x4 &lo, const bf16x4 &hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// fr[i] = the transposed fragment of channels ch0 + 16 i .. + 15 (i < N), in
+// batches of eight transposing reads.
+template <class C, int N>
+__device__ __forceinline__ void read_tr(const char *sb, int ch0, int g, int c, bf16x8 (&fr)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i0 = 0; i0 < N; i0 += 4) {
+      uint32_t ad[8];
+      bf16x4 v[8];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        ad[2 * mb] = tr_addr(sb, ch0 + 16 * (i0 + mb), g, c);
+        ad[2 * mb + 1] = ad[2 * mb] + C::TILE_B;
+      }
+      ds_read_tr8(v, ad);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) fr[i0 + mb] = join(v[2 * mb], v[2 * mb + 1]);
+    }
+  } else {
+    static_assert(N == 2, "two blocks, each read twice to fill the batch");
+    uint32_t ad[8];
+    bf16x4 v[8];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      ad[2 * mb] = tr_addr(sb, ch0 + 16 * (mb & 1), g, c);
+      ad[2 * mb + 1] = ad[2 * mb] + C::TILE_B;
+    }
+    ds_read_tr8(v, ad);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) fr[mb] = join(v[2 * mb], v[2 * mb + 1]);
+  }
 }
 
 // One direct global->LDS load of 16 bytes per lane into block dst (lane l
@@ -85,17 +134,19 @@ struct AttnBwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Key-stationary pass: a workgroup owns 128 compact keys of one (sequence,
-// head) -- 32 per wave, with K^T and V^T fragments in registers -- and
-// streams the query frames that can see them (frame m sees key j iff
-// j < floor(m/s)) through an LDS ring of 32-frame stages (Q | Q^R | dO).
-// Per stage a wave computes S and dP for its 32 keys (the query tile from
-// LDS as the A operand), P and dS on the VALU, and accumulates
-// dV^T += dO^T P, dK^T += Q^T dS, dK^R^T += Q^R^T dS with the transposed
-// query-side tiles from transposing reads.  Results are the key-role
-// gradients of each compact key, written to dKVc / dKRc.
+// Key-stationary pass: a workgroup owns 4 * 16 NT compact keys of one
+// (sequence, head) -- 16 NT per wave, with K^T and V^T fragments in
+// registers -- and streams the query frames that can see them (frame m sees
+// key j iff j < floor(m/s)) through an LDS ring of 32-frame stages
+// (Q | Q^R | dO).  Per stage a wave computes S and dP for its keys (the
+// query tile from LDS as the A operand), P and dS on the VALU, and
+// accumulates dV^T += dO^T P, dK^T += Q^T dS, dK^R^T += Q^R^T dS with the
+// transposed query-side tiles from transposing reads.  Results are the
+// key-role gradients of each compact key, written to dKVc / dKRc.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+template <class C>
+__global__ __launch_bounds__(256, C::OCC) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int DH = C::DH, DR = C::DR, NT = C::NT, SROWS = C::SROWS, NST = C::NST;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,32 +169,34 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   }
   const int b = bh / H, h = bh % H;
   const size_t kvw = (size_t)2 * H * DH;
-  const int kb0 = kblk * 128;                 // first key of the workgroup
-  const int kw0 = kb0 + 32 * wave;            // first key of this wave
+  const int kb0 = kblk * C::GROWS;            // first key of the workgroup
+  const int kw0 = kb0 + C::WROWS * wave;      // first key of this wave
   if (kb0 >= a.nK) return;                    // whole workgroup: uniform
 
   // K^T / V^T fragments (B operands): lane (g, c) holds key kw0 + 16 nk + c,
   // channels 32 ks + 8 g .. + 7.
-  bf16x8 kf[2][3], vf[2][2];
+  bf16x8 kf[NT][C::KS], vf[NT][C::VS];
 #pragma unroll
-  for (int nk = 0; nk < 2; ++nk) {
+  for (int nk = 0; nk < NT; ++nk) {
     const int j = min(kw0 + 16 * nk + c, a.nK - 1);
     const size_t fr = (size_t)b * Tn + (size_t)s * j + (s - 1);
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
       const int k = 32 * ks + 8 * g;
       if (k < DH) load8(kf[nk][ks], a.KV + fr * kvw + h * DH + k);
       else load8(kf[nk][ks], a.KR + fr * DR + (k - DH));
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) load8(vf[nk][ks], a.KV + fr * kvw + (size_t)(H + h) * DH + 32 * ks + 8 * g);
+    for (int ks = 0; ks < C::VS; ++ks)
+      load8(vf[nk][ks], a.KV + fr * kvw + (size_t)(H + h) * DH + 32 * ks + 8 * g);
   }
-  f32x4 dv[2][4], dk[2][4], dkr[2][2];
+  f32x4 dv[NT][C::MB], dk[NT][C::MB], dkr[NT][C::RBK];
 #pragma unroll
-  for (int nk = 0; nk < 2; ++nk) {
+  for (int nk = 0; nk < NT; ++nk) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) dv[nk][mb] = dk[nk][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    dkr[nk][0] = dkr[nk][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < C::MB; ++mb) dv[nk][mb] = dk[nk][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < C::RBK; ++mb) dkr[nk][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   asm volatile("" ::: "memory");
 
@@ -151,23 +204,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int q0 = (s * (kb0 + 1)) / SROWS * SROWS;
   const int nstage = q0 < Tn ? (Tn - q0 + SROWS - 1) / SROWS : 0;
   const int wfirst = s * (kw0 + 1);           // first frame that sees a key of this wave
-  char *dummy = smem + NST * STAGE_B;
+  char *dummy = smem + NST * C::STAGE_B;
   const int u = (lane & 3) ^ swz(lane >> 2);
   auto issue = [&](int sidx) {
-    char *sb = smem + (sidx % NST) * STAGE_B;
+    char *sb = smem + (sidx % NST) * C::STAGE_B;
     const int f0 = q0 + sidx * SROWS;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
+    for (int i = 0; i < C::LPW; ++i) {
       const int blk = wave + 4 * i;
-      const bool real = blk < NBLK;
-      const int tl = real ? blk / NSEG : 0, qq = real ? blk % NSEG : 0;
+      const bool real = blk < C::NBLK;
+      const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
       const int f = min(f0 + tl * 16 + (lane >> 2), Tn - 1);
       const size_t row = (size_t)b * Tn + f;
       const char *seg;
-      if (qq < 2) seg = (const char *)(a.q + row * H * DH + h * DH) + qq * 64;
-      else if (qq == 2) seg = (const char *)(a.QR + (row * H + h) * DR);
-      else seg = (const char *)(a.dO + row * H * DH + h * DH) + (qq - 3) * 64;
-      dma_seg(seg, real ? sb + tl * TILE_B + qq * 1024 : dummy, u);
+      if (qq < C::KSEG) seg = (const char *)(a.q + row * H * DH + h * DH) + qq * 64;
+      else if (qq < C::KSEG + C::RSEG) seg = (const char *)(a.QR + (row * H + h) * DR) + (qq - C::KSEG) * 64;
+      else seg = (const char *)(a.dO + row * H * DH + h * DH) + (qq - C::KSEG - C::RSEG) * 64;
+      dma_seg(seg, real ? sb + tl * C::TILE_B + qq * 1024 : dummy, u);
     }
   };
   const int pro = min(NST, nstage);
@@ -175,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   int last = pro - 1;
 
   for (int k = 0; k < nstage; ++k) {
-    wait_stages<LPW>(last - k);
+    wait_stages<C::LPW>(last - k);
     bar();
     if (k >= 1 && k - 1 + NST < nstage) {
       issue(k - 1 + NST);
@@ -183,31 +236,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     }
     const int fs = q0 + k * SROWS;            // first frame of the stage
     if (fs + SROWS <= wfirst) continue;       // no frame here sees this wave's keys
-    const char *sb = smem + (k % NST) * STAGE_B;
+    const char *sb = smem + (k % NST) * C::STAGE_B;
 
     // S[q, key] and dP[q, key] for both 16-frame tiles: lane (g, c) holds key
     // column c, frames 4g..4g+3 of the tile.
-    f32x4 sc[2][2], dp[2][2];
+    f32x4 sc[2][NT], dp[2][NT];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const char *tile = sb + t * TILE_B;
+      const char *tile = sb + t * C::TILE_B;
 #pragma unroll
-      for (int nk = 0; nk < 2; ++nk) sc[t][nk] = dp[t][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int nk = 0; nk < NT; ++nk) sc[t][nk] = dp[t][nk] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
+      for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, ks * 64 + g * 16));
 #pragma unroll
-        for (int nk = 0; nk < 2; ++nk) sc[t][nk] = mma_k32(af, kf[nk][ks], sc[t][nk]);
+        for (int nk = 0; nk < NT; ++nk) sc[t][nk] = mma_k32(af, kf[nk][ks], sc[t][nk]);
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, OFF_C + ks * 64 + g * 16));
+      for (int ks = 0; ks < C::VS; ++ks) {
+        const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, C::OFF_C + ks * 64 + g * 16));
 #pragma unroll
-        for (int nk = 0; nk < 2; ++nk) dp[t][nk] = mma_k32(af, vf[nk][ks], dp[t][nk]);
+        for (int nk = 0; nk < NT; ++nk) dp[t][nk] = mma_k32(af, vf[nk][ks], dp[t][nk]);
       }
     }
     // P and dS; frame f sees key j iff j < floor(f/s) (and f < T).
-    bf16x8 pp[2], ds[2];
+    bf16x8 pp[NT], ds[NT];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -218,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         const float L = a.lse[ri], Dv = a.Dr[ri];
         const int lim = f < Tn ? f / s : 0;
 #pragma unroll
-        for (int nk = 0; nk < 2; ++nk) {
+        for (int nk = 0; nk < NT; ++nk) {
           const int j = kw0 + 16 * nk + c;
           const float p = j < lim ? __builtin_amdgcn_exp2f(sc[t][nk][e] * a.sl2 - L) : 0.0f;
           pp[nk][4 * t + e] = (bf16)p;
@@ -226,71 +279,57 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
         }
       }
     }
-    // Transposed query-side tiles: Q^T (channels 0..63), Q^R^T (64..95),
-    // dO^T (96..159), low half frames of tile 0, high half of tile 1.
-    bf16x8 qT[4], qrT[2], doT[4];
+    // Transposed query-side tiles (frames of tile 0 in the low half, tile 1
+    // in the high half), one part at a time: dO^T (channels QK ..), then
+    // Q^T (0 ..), then Q^R^T (DH ..).
     {
-      uint32_t ad[8];
-      bf16x4 v[8];
+      bf16x8 doT[C::MB];
+      read_tr<C>(sb, C::QK, g, c, doT);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        ad[2 * mb] = tr_addr(sb, 16 * mb, g, c);
-        ad[2 * mb + 1] = ad[2 * mb] + TILE_B;
-      }
-      ds_read_tr8(v, ad);
+      for (int nk = 0; nk < NT; ++nk)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) qT[mb] = join(v[2 * mb], v[2 * mb + 1]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        ad[2 * mb] = tr_addr(sb, 96 + 16 * mb, g, c);
-        ad[2 * mb + 1] = ad[2 * mb] + TILE_B;
-      }
-      ds_read_tr8(v, ad);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) doT[mb] = join(v[2 * mb], v[2 * mb + 1]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        ad[2 * mb] = tr_addr(sb, 64 + 16 * (mb & 1), g, c);
-        ad[2 * mb + 1] = ad[2 * mb] + TILE_B;
-      }
-      ds_read_tr8(v, ad);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) qrT[mb] = join(v[2 * mb], v[2 * mb + 1]);
+        for (int mb = 0; mb < C::MB; ++mb) dv[nk][mb] = mma_k32(doT[mb], pp[nk], dv[nk][mb]);
     }
-    // dV^T += dO^T P,  dK^T += Q^T dS,  dK^R^T += Q^R^T dS.
+    {
+      bf16x8 qT[C::MB];
+      read_tr<C>(sb, 0, g, c, qT);
 #pragma unroll
-    for (int nk = 0; nk < 2; ++nk) {
+      for (int nk = 0; nk < NT; ++nk)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) dv[nk][mb] = mma_k32(doT[mb], pp[nk], dv[nk][mb]);
+        for (int mb = 0; mb < C::MB; ++mb) dk[nk][mb] = mma_k32(qT[mb], ds[nk], dk[nk][mb]);
+    }
+    {
+      bf16x8 qrT[C::RBK];
+      read_tr<C>(sb, DH, g, c, qrT);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) dk[nk][mb] = mma_k32(qT[mb], ds[nk], dk[nk][mb]);
+      for (int nk = 0; nk < NT; ++nk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) dkr[nk][mb] = mma_k32(qrT[mb], ds[nk], dkr[nk][mb]);
+        for (int mb = 0; mb < C::RBK; ++mb) dkr[nk][mb] = mma_k32(qrT[mb], ds[nk], dkr[nk][mb]);
     }
   }
 
   // Key-role gradients of compact key (b, j): lane holds key column c,
   // channels 16 mb + 4g .. + 3.
 #pragma unroll
-  for (int nk = 0; nk < 2; ++nk) {
+  for (int nk = 0; nk < NT; ++nk) {
     const int j = kw0 + 16 * nk + c;
     if (j < a.nK) {
       float *row = a.dKVc + ((size_t)b * a.nS + j) * kvw;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < C::MB; ++mb) {
         *(f32x4 *)(row + h * DH + 16 * mb + 4 * g) = dk[nk][mb];
         *(f32x4 *)(row + (size_t)(H + h) * DH + 16 * mb + 4 * g) = dv[nk][mb];
       }
       float *rr = a.dKRc + (((size_t)b * a.nS + j) * H + h) * DR;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) *(f32x4 *)(rr + 16 * mb + 4 * g) = dkr[nk][mb];
+      for (int mb = 0; mb < C::RBK; ++mb) *(f32x4 *)(rr + 16 * mb + 4 * g) = dkr[nk][mb];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Query-stationary pass: a workgroup owns 128 query frames of one (sequence,
-// head), 32 per wave (two 16-row tiles) with Q, Q^R and dO fragments in
+// Query-stationary pass: a workgroup owns 4 * 16 NT query frames of one
+// (sequence, head), 16 NT per wave with Q, Q^R and dO fragments in
 // registers; the compact keys stream through the forward's LDS ring
 // (K | K^R | V).  Per stage: S^T and dP^T (key tile from LDS as the A
 // operand), P and dS, then dQ^T += K^T dS^T and dQ^R^T += K^R^T dS^T with the
@@ -299,7 +338,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 // dS_mm Q^R_m) are added to the key-role gradients of the frame (if it is a
 // compact key) and written out as the frame's total dK, dV and dK^R.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+template <class C>
+__global__ __launch_bounds__(256, C::OCC) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int DH = C::DH, DR = C::DR, NT = C::NT, SROWS = C::SROWS, NST = C::NST;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -320,14 +361,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
   const int b = bh / H, h = bh % H;
   const size_t kvw = (size_t)2 * H * DH;
-  const int rw = qtile * 128 + wave * 32;     // first frame of this wave
+  const int rw = qtile * C::GROWS + wave * C::WROWS;   // first frame of this wave
 
-  bf16x8 qf[2][3], dof[2][2];
-  f32x4 dq[2][4], dqr[2][2];
-  float L[2], Dv[2];
-  int lim[2];
+  bf16x8 qf[NT][C::KS], dof[NT][C::VS];
+  f32x4 dq[NT][C::MB], dqr[NT][C::RBK];
+  float L[NT], Dv[NT];
+  int lim[NT];
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < NT; ++qi) {
     const int fr = rw + 16 * qi + c;
     const bool ok = fr < Tn;
     const int mf = ok ? fr : 0;
@@ -337,9 +378,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     L[qi] = a.lse[ri];
     Dv[qi] = a.Dr[ri];
     float sdot = 0.0f, pdot = 0.0f;
-    bf16x8 kd[3], vd[2];
+    bf16x8 kd[C::KS], vd[C::VS];
 #pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
       const int k = 32 * ks + 8 * g;
       if (k < DH) {
         load8(qf[qi][ks], a.q + row * H * DH + h * DH + k);
@@ -352,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
       for (int e = 0; e < 8; ++e) sdot += (float)qf[qi][ks][e] * (float)kd[ks][e];
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < C::VS; ++ks) {
       load8(dof[qi][ks], a.dO + row * H * DH + h * DH + 32 * ks + 8 * g);
       load8(vd[ks], a.KV + row * kvw + (size_t)(H + h) * DH + 32 * ks + 8 * g);
 #pragma unroll
@@ -364,10 +405,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     // dQ and dQ^R start from the own column's dS K_m and dS K^R_m (O^T
     // layout: lane holds frame c, channels 16 mb + 4 g .. + 3).
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb)
       dq[qi][mb] = load4f(a.KV + row * kvw + h * DH + 16 * mb + 4 * g) * dss;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) dqr[qi][mb] = load4f(a.KR + row * DR + 16 * mb + 4 * g) * dss;
+    for (int mb = 0; mb < C::RBK; ++mb)
+      dqr[qi][mb] = load4f(a.KR + row * DR + 16 * mb + 4 * g) * dss;
     if (ok) {
       // Total dK, dV, dK^R of frame fr: the own column's terms plus the
       // key-role gradients when fr is a compact key (group-final with a
@@ -377,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
       const float *kc = a.dKVc + ((size_t)b * a.nS + j) * kvw;
       const float *krc = a.dKRc + (((size_t)b * a.nS + j) * H + h) * DR;
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
+      for (int ks = 0; ks < C::KS; ++ks) {
         const int k = 32 * ks + 8 * g;
         float v8[8];
 #pragma unroll
@@ -404,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < C::VS; ++ks) {
         const int k = 32 * ks + 8 * g;
         float v8[8];
 #pragma unroll
@@ -424,30 +466,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
   asm volatile("" ::: "memory");
 
-  const int wlast = min(rw + 32, Tn) - 1;
+  const int wlast = min(rw + C::WROWS, Tn) - 1;
   const int wlim = wlast >= rw ? wlast / s : 0;
-  const int glast = min(qtile * 128 + 128, Tn) - 1;
+  const int glast = min(qtile * C::GROWS + C::GROWS, Tn) - 1;
   const int kmax = glast / s;
   const int nstage = (kmax + SROWS - 1) / SROWS;
   const int wst = (wlim + SROWS - 1) / SROWS;
   const int wmin = rw < Tn ? rw / s : 0;
-  char *dummy = smem + NST * STAGE_B;
+  char *dummy = smem + NST * C::STAGE_B;
   const int u = (lane & 3) ^ swz(lane >> 2);
   auto issue = [&](int sidx) {
-    char *sb = smem + (sidx % NST) * STAGE_B;
+    char *sb = smem + (sidx % NST) * C::STAGE_B;
     const int row0 = sidx * SROWS;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
+    for (int i = 0; i < C::LPW; ++i) {
       const int blk = wave + 4 * i;
-      const bool real = blk < NBLK;
-      const int tl = real ? blk / NSEG : 0, qq = real ? blk % NSEG : 0;
+      const bool real = blk < C::NBLK;
+      const int tl = real ? blk / C::NSEG : 0, qq = real ? blk % C::NSEG : 0;
       const int key = min(row0 + tl * 16 + (lane >> 2), kmax - 1);
       const size_t fr = (size_t)b * Tn + (size_t)s * key + (s - 1);
       const char *seg;
-      if (qq < 2) seg = (const char *)(a.KV + fr * kvw + h * DH) + qq * 64;
-      else if (qq == 2) seg = (const char *)(a.KR + fr * DR);
-      else seg = (const char *)(a.KV + fr * kvw + (size_t)(H + h) * DH) + (qq - 3) * 64;
-      dma_seg(seg, real ? sb + tl * TILE_B + qq * 1024 : dummy, u);
+      if (qq < C::KSEG) seg = (const char *)(a.KV + fr * kvw + h * DH) + qq * 64;
+      else if (qq < C::KSEG + C::RSEG) seg = (const char *)(a.KR + fr * DR) + (qq - C::KSEG) * 64;
+      else seg = (const char *)(a.KV + fr * kvw + (size_t)(H + h) * DH) + (qq - C::KSEG - C::RSEG) * 64;
+      dma_seg(seg, real ? sb + tl * C::TILE_B + qq * 1024 : dummy, u);
     }
   };
   const int pro = min(NST, nstage);
@@ -455,62 +497,44 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   int last = pro - 1;
 
   for (int k = 0; k < nstage; ++k) {
-    wait_stages<LPW>(last - k);
+    wait_stages<C::LPW>(last - k);
     bar();
     if (k >= 1 && k - 1 + NST < nstage) {
       issue(k - 1 + NST);
       last = k - 1 + NST;
     }
     if (k >= wst) continue;
-    const char *sb = smem + (k % NST) * STAGE_B;
+    const char *sb = smem + (k % NST) * C::STAGE_B;
     const int kb = k * SROWS;
-    // Transposed key tiles: K^T (channels 0..63) and K^R^T (64..95).
-    bf16x8 kT[4], krT[2];
-    {
-      uint32_t ad[8];
-      bf16x4 v[8];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        ad[2 * mb] = tr_addr(sb, 16 * mb, g, c);
-        ad[2 * mb + 1] = ad[2 * mb] + TILE_B;
-      }
-      ds_read_tr8(v, ad);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) kT[mb] = join(v[2 * mb], v[2 * mb + 1]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        ad[2 * mb] = tr_addr(sb, 64 + 16 * (mb & 1), g, c);
-        ad[2 * mb + 1] = ad[2 * mb] + TILE_B;
-      }
-      ds_read_tr8(v, ad);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) krT[mb] = join(v[2 * mb], v[2 * mb + 1]);
-    }
+    // Transposed key tiles: K^T (channels 0 ..) and K^R^T (DH ..).
+    bf16x8 kT[C::MB], krT[C::RBK];
+    read_tr<C>(sb, 0, g, c, kT);
+    read_tr<C>(sb, DH, g, c, krT);
     // S^T[key, q] and dP^T[key, q]: lane (g, c) holds frame column c, keys
     // 4g..4g+3 of the tile.
-    f32x4 sc[2][2], dp[2][2];
+    f32x4 sc[2][NT], dp[2][NT];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const char *tile = sb + t * TILE_B;
+      const char *tile = sb + t * C::TILE_B;
 #pragma unroll
-      for (int qi = 0; qi < 2; ++qi) sc[t][qi] = dp[t][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int qi = 0; qi < NT; ++qi) sc[t][qi] = dp[t][qi] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
+      for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, ks * 64 + g * 16));
 #pragma unroll
-        for (int qi = 0; qi < 2; ++qi) sc[t][qi] = mma_k32(af, qf[qi][ks], sc[t][qi]);
+        for (int qi = 0; qi < NT; ++qi) sc[t][qi] = mma_k32(af, qf[qi][ks], sc[t][qi]);
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, OFF_C + ks * 64 + g * 16));
+      for (int ks = 0; ks < C::VS; ++ks) {
+        const bf16x8 af = *(const bf16x8 *)(tile + tile_off(c, C::OFF_C + ks * 64 + g * 16));
 #pragma unroll
-        for (int qi = 0; qi < 2; ++qi) dp[t][qi] = mma_k32(af, dof[qi][ks], dp[t][qi]);
+        for (int qi = 0; qi < NT; ++qi) dp[t][qi] = mma_k32(af, dof[qi][ks], dp[t][qi]);
       }
     }
     const bool full = kb + SROWS <= wmin;
-    bf16x8 ds[2];
+    bf16x8 ds[NT];
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi)
+    for (int qi = 0; qi < NT; ++qi)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -520,37 +544,38 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnBwdArgs a) {
           ds[qi][4 * t + e] = (bf16)(p * (dp[t][qi][e] - Dv[qi]) * a.scale);
         }
 #pragma unroll
-    for (int qi = 0; qi < 2; ++qi) {
+    for (int qi = 0; qi < NT; ++qi) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) dq[qi][mb] = mma_k32(kT[mb], ds[qi], dq[qi][mb]);
+      for (int mb = 0; mb < C::MB; ++mb) dq[qi][mb] = mma_k32(kT[mb], ds[qi], dq[qi][mb]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) dqr[qi][mb] = mma_k32(krT[mb], ds[qi], dqr[qi][mb]);
+      for (int mb = 0; mb < C::RBK; ++mb) dqr[qi][mb] = mma_k32(krT[mb], ds[qi], dqr[qi][mb]);
     }
   }
 
 #pragma unroll
-  for (int qi = 0; qi < 2; ++qi) {
+  for (int qi = 0; qi < NT; ++qi) {
     const int fr = rw + 16 * qi + c;
     if (fr < Tn) {
       const size_t row = (size_t)b * Tn + fr;
       bf16 *dst = a.dQ + row * H * DH + h * DH + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) store4f(dst + 16 * mb, dq[qi][mb]);
+      for (int mb = 0; mb < C::MB; ++mb) store4f(dst + 16 * mb, dq[qi][mb]);
       bf16 *dr = a.dQR + (row * H + h) * DR + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) store4f(dr + 16 * mb, dqr[qi][mb]);
+      for (int mb = 0; mb < C::RBK; ++mb) store4f(dr + 16 * mb, dqr[qi][mb]);
     }
   }
 }
 
-// D[row, h] = sum over the head's channels of dO * O: eight consecutive
-// lanes share a 64-channel row, 16 bytes each (coalesced), and add their
-// partial sums across the eight lanes.
+// D[row, h] = sum over the head's DH channels of dO * O: DH / 8 consecutive
+// lanes (8 or 16) share a row, 16 bytes each (coalesced), and add their
+// partial sums across those lanes.
 __global__ __launch_bounds__(256) void rowdot_kernel(const bf16 *dO, const bf16 *O, int MH,
-                                                     float *D) {
+                                                     int DH, float *D) {
+  const int lpr = DH / 8;   // lanes per row: a power of two dividing the wave
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t i = t >> 3;
-  const int part = (int)(t & 7);
+  const size_t i = t / lpr;
+  const int part = (int)(t % lpr);
   float acc = 0.0f;
   if (i < (size_t)MH) {
     const bf16x8 u = *(const bf16x8 *)(dO + i * DH + 8 * part);
@@ -558,14 +583,12 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const bf16 *dO, const bf16 
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)u[e] * (float)v[e];
   }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
+  for (int m = 1; m < lpr; m <<= 1) acc += __shfl_xor(acc, m);
   if (i < (size_t)MH && part == 0) D[i] = acc;
 }
 
 // dKR[row, ch] = sum_h dKRh[row, h, ch] (the RoPE key is shared by the heads).
-__global__ __launch_bounds__(256) void head_sum_kernel(const float *dKRh, int M, int H,
+__global__ __launch_bounds__(256) void head_sum_kernel(const float *dKRh, int M, int H, int DR,
                                                        bf16 *dKR) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= M * DR) return;
@@ -734,42 +757,57 @@ __global__ __launch_bounds__(256) void tn_gemm_kernel(const bf16 *A, int lda, co
 }  // namespace
 
 bool attn_bwd_supported(int dtype, int H, int d_h, int dR) {
-  return dtype == 1 && d_h == DH && dR == DR && H >= 1 && H <= 64;
+  return dtype == 1 && ((d_h == 64 && dR == 32) || (d_h == 128 && dR == 64)) && H >= 1 && H <= 64;
 }
 
-hipError_t launch_attn_bwd(int B, int T, int H, int s, float scale, const void *q, const void *QR,
-                           const void *KV, const void *KR, const void *dO, const float *lse,
-                           const float *D, float *dKVc, float *dKRc, void *dKV, float *dKRh,
-                           void *dQ, void *dQR, hipStream_t stream) {
+namespace {
+template <class C>
+hipError_t attn_bwd_t(int B, int T, int H, int s, float scale, const void *q, const void *QR,
+                      const void *KV, const void *KR, const void *dO, const float *lse,
+                      const float *D, float *dKVc, float *dKRc, void *dKV, float *dKRh, void *dQ,
+                      void *dQR, hipStream_t stream) {
   const int nS = (T + s - 1) / s, nK = (T - 1) / s;
   float sl2 = scale * kLog2e;
   if (!(sl2 >= FLT_MIN)) sl2 = FLT_MIN;
   AttnBwdArgs a{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
                 (const bf16 *)dO, lse, D, dKVc, dKRc, (bf16 *)dKV, dKRh, (bf16 *)dQ,
-                (bf16 *)dQR, B, T, H, s, nS, nK, (T + 127) / 128, sl2, scale};
-  const size_t lds = (size_t)NST * STAGE_B + 1024;
-  allow_lds<attn_bwd_dkdv_kernel>();
-  allow_lds<attn_bwd_dq_kernel>();
-  const int kblocks = (nK + 127) / 128;
+                (bf16 *)dQR, B, T, H, s, nS, nK, (T + C::GROWS - 1) / C::GROWS, sl2, scale};
+  const size_t lds = (size_t)C::NST * C::STAGE_B + 1024;
+  allow_lds<attn_bwd_dkdv_kernel<C>>();
+  allow_lds<attn_bwd_dq_kernel<C>>();
+  const int kblocks = (nK + C::GROWS - 1) / C::GROWS;
   if (kblocks > 0) {
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3(kblocks * B * H), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3(kblocks * B * H), dim3(256), lds, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(a.tiles * B * H), dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3(a.tiles * B * H), dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_bwd(int B, int T, int H, int d_h, int s, float scale, const void *q,
+                           const void *QR, const void *KV, const void *KR, const void *dO,
+                           const float *lse, const float *D, float *dKVc, float *dKRc, void *dKV,
+                           float *dKRh, void *dQ, void *dQR, hipStream_t stream) {
+  if (d_h == 128)
+    return attn_bwd_t<Bw128>(B, T, H, s, scale, q, QR, KV, KR, dO, lse, D, dKVc, dKRc, dKV, dKRh,
+                             dQ, dQR, stream);
+  return attn_bwd_t<Bw64>(B, T, H, s, scale, q, QR, KV, KR, dO, lse, D, dKVc, dKRc, dKV, dKRh, dQ,
+                          dQR, stream);
+}
+
+hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *D,
+                         hipStream_t stream) {
+  const size_t lanes = (size_t)MH * (d_h / 8);
+  hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream,
+                     (const bf16 *)dO, (const bf16 *)O, MH, d_h, D);
   return hipGetLastError();
 }
 
-hipError_t launch_rowdot(const void *dO, const void *O, int MH, float *D, hipStream_t stream) {
-  hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)(((size_t)MH * 8 + 255) / 256)), dim3(256), 0,
-                     stream,
-                     (const bf16 *)dO, (const bf16 *)O, MH, D);
-  return hipGetLastError();
-}
-
-hipError_t launch_head_sum(const float *dKRh, int M, int H, void *dKR, hipStream_t stream) {
-  hipLaunchKernelGGL(head_sum_kernel, dim3((M * DR + 255) / 256), dim3(256), 0, stream, dKRh, M, H,
-                     (bf16 *)dKR);
+hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, hipStream_t stream) {
+  hipLaunchKernelGGL(head_sum_kernel, dim3((M * dR + 255) / 256), dim3(256), 0, stream, dKRh, M, H,
+                     dR, (bf16 *)dKR);
   return hipGetLastError();
 }
 

@@ -157,22 +157,23 @@ hipError_t launch_heads_attention(int B, int T, int H, int d_h, int s, float sca
                                   hipEvent_t ev1 = nullptr);
 bool heads_attention_supported(int dtype, int H, int d_h, int dR);
 
-// ---- backward of the per-head parallel form (bf16, d_h = 64, dR = 32) ----
+// ---- backward of the per-head parallel form (bf16, (d_h, dR) = (64, 32) or (128, 64)) ----
 
 bool attn_bwd_supported(int dtype, int H, int d_h, int dR);
 // Attention backward over the forward's q, QR, KV, KR, its lse and
 // D = rowsum(dO * O): key-role gradients of the compact keys into dKVc
-// [B*nS, 2*H*64] and dKRc [B*nS, H, dR] (fp32 scratch), then every frame's
-// total dK | dV into dKV [B*T, 2*H*64] (bf16) and per-head dK^R into dKRh
-// [B*T, H, dR] (fp32), and dQ [B*T, H*64], dQR [B*T, H, dR] (bf16).
-hipError_t launch_attn_bwd(int B, int T, int H, int s, float scale, const void *q, const void *QR,
-                           const void *KV, const void *KR, const void *dO, const float *lse,
-                           const float *D, float *dKVc, float *dKRc, void *dKV, float *dKRh,
-                           void *dQ, void *dQR, hipStream_t stream);
-// D[i] = sum over 64 channels of dO[i, :] * O[i, :], i < MH (rows of 64).
-hipError_t launch_rowdot(const void *dO, const void *O, int MH, float *D, hipStream_t stream);
+// [B*nS, 2*H*d_h] and dKRc [B*nS, H, dR] (fp32 scratch), then every frame's
+// total dK | dV into dKV [B*T, 2*H*d_h] (bf16) and per-head dK^R into dKRh
+// [B*T, H, dR] (fp32), and dQ [B*T, H*d_h], dQR [B*T, H, dR] (bf16).
+hipError_t launch_attn_bwd(int B, int T, int H, int d_h, int s, float scale, const void *q,
+                           const void *QR, const void *KV, const void *KR, const void *dO,
+                           const float *lse, const float *D, float *dKVc, float *dKRc, void *dKV,
+                           float *dKRh, void *dQ, void *dQR, hipStream_t stream);
+// D[i] = sum over d_h channels of dO[i, :] * O[i, :], i < MH (rows of d_h).
+hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *D,
+                         hipStream_t stream);
 // dKR [M, dR] (bf16) = sum over heads of dKRh [M, H, dR].
-hipError_t launch_head_sum(const float *dKRh, int M, int H, void *dKR, hipStream_t stream);
+hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, hipStream_t stream);
 // Reverse group scan and gate backward from dC' [B*T, R] (fp32) and the
 // forward's cg: da (fp32 and bf16), dc's direct term (fp32), c (bf16), and
 // dPtab [rows, R] += the position-branch gradient.

@@ -630,7 +630,7 @@ mtla_status prefill_unabsorbed_backward_impl(
       (int64_t)B * T * dims->d > 0x7fffffffLL / 4)
     return fail(MTLA_ERR_UNSUPPORTED, "B*T too large");
   if (!mtla::attn_bwd_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR))
-    return fail(MTLA_ERR_UNSUPPORTED, "backward needs bf16 storage, d_h = 64, d_hR = 32");
+    return fail(MTLA_ERR_UNSUPPORTED, "backward needs bf16 storage and (d_h, d_hR) = (64, 32) or (128, 64)");
   if ((T - 1) / dims->s >= w->gate_pos_rows)
     return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
   const BwdWs ws = bwd_ws(dims, B, T);
@@ -664,12 +664,12 @@ mtla_status prefill_unabsorbed_backward_impl(
   LAUNCH(mtla::launch_transpose(w->W_Q, HD, d, d, P(ws.WQt), HD, s), "transpose W_Q");
   // output map
   LAUNCH(mtla::launch_gemm_store(dt, dY, d, P(ws.WOt), d, M, HD, d, P(ws.dO), HD, s), "dO");
-  LAUNCH(mtla::launch_rowdot(P(ws.dO), O, M * H, F(ws.D), s), "rowsum dO * O");
+  LAUNCH(mtla::launch_rowdot(P(ws.dO), O, M * H, dims->d_h, F(ws.D), s), "rowsum dO * O");
   // attention
-  LAUNCH(mtla::launch_attn_bwd(B, T, H, dims->s, scale, q, QR, KV, KR, P(ws.dO), lse, F(ws.D),
+  LAUNCH(mtla::launch_attn_bwd(B, T, H, dims->d_h, dims->s, scale, q, QR, KV, KR, P(ws.dO), lse, F(ws.D),
                                F(ws.dKVc), F(ws.dKRc), P(ws.dKV), F(ws.dKRh), P(ws.dQ), dQR, s),
          "attention backward");
-  LAUNCH(mtla::launch_head_sum(F(ws.dKRh), M, H, dKR, s), "dK^R over heads");
+  LAUNCH(mtla::launch_head_sum(F(ws.dKRh), M, H, dims->d_hR, dKR, s), "dK^R over heads");
   // key and value maps
   LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dKV), 2 * HD, P(ws.WKVt), 2 * HD, M, r, 2 * HD, F(ws.dCp), r,
                                false, s),

@@ -79,6 +79,18 @@ def test_backward_matches_oracle(s, T, H, B):
     _check(dims, B, T, 9500 + 7 * s + T + H)
 
 
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 4, 1), (2, 130, 4, 2), (3, 257, 4, 1),
+                                       (1, 64, 2, 2), (4, 300, 4, 1), (80, 100, 2, 1),
+                                       (5, 96, 3, 2)])
+def test_backward_llm_head_width(s, T, H, B):
+    """The backward at the LLM-scale head widths (d_h = 128, d_hR = 64,
+    r = 512): one 16-row tile per wave in both attention passes."""
+    needs_gpu()
+    dims = Dims(d=512, H=H, d_h=128, r=512, d_hR=64, s=s)
+    say("backward per-head d_h=128", s, T, H, B)
+    _check(dims, B, T, 9600 + 7 * s + T + H)
+
+
 def test_backward_full_size_prefix():
     """The benchmark's backward launch (B=16, T=4096, s=2) with the loss on
     the first 320 frames of two sequences: those gradients against the
