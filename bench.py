@@ -53,11 +53,12 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc")
-# Sources that define each timed kernel: a counter summary under profiles/
-# applies only while these files are unchanged.
+# Sources that define each timed kernel (its device code and launch plan):
+# a counter summary under profiles/ applies only while these files are
+# unchanged.
 KERNEL_SOURCES = {
-    "decode_ws_kernel": ("decode.hip", "common.h", "kernels.h"),
-    "prefill_ws_kernel": ("attention.hip", "common.h", "kernels.h"),
+    "decode_ws_kernel": ("decode.hip", "common.h"),
+    "prefill_ws_kernel": ("attention.hip", "common.h"),
 }
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "decode tokens/s + achieved HBM GB/s (compressed cache); prefill TFLOP/s, 1 GPU"
