@@ -295,11 +295,9 @@ typedef struct {
  * The forward is recomputed inside.  Supported: bf16 storage with
  * (d_h, d_hR) = (64, 32) or (128, 64).  Workspace:
  * mtla_workspace_bytes(op=5, B, T).
- * Reproducibility: dX, dQR and dKR are computed without atomics and repeat
- * bit for bit; the weight gradients, db_hc and dgate_pos are sums over
- * frames (and sequences) accumulated with fp32 atomic adds across
- * workgroups, so their last bits may differ from call to call (the order
- * of the additions is not fixed). */
+ * Reproducibility: every output repeats bit for bit from call to call --
+ * the sums over frames and sequences behind the weight gradients, db_hc and
+ * dgate_pos add their per-workgroup partials in a fixed order. */
 mtla_status mtla_prefill_unabsorbed_backward(const mtla_dims *dims,
                                              const mtla_unabsorbed_weights *w, const void *W_hc,
                                              const void *X, const void *QR, const void *KR,

@@ -24,7 +24,9 @@
 // the forward -- one stationary in the queries (dQ, dQ^R, and every frame's
 // own column), one stationary in the compact keys (dK, dV, dK^R of the
 // group-final frames) -- the reverse group scan with the gate backward, a
-// split-M product A^T B for the weight gradients, and small helpers.
+// split-M product A^T B for the weight gradients, and small helpers.  Every
+// reduction across workgroups adds its partials in a fixed order (the last
+// workgroup to finish sums them), so the gradients repeat bit for bit.
 
 #include <float.h>
 #include <math.h>
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(256) void scan_gate_bwd_kernel(const float *dCp, co
                                                             const bf16 *b_hc, const float *table,
                                                             int T, int R, int s, int nS,
                                                             float *da32, bf16 *dab, float *dc32,
-                                                            bf16 *cb, float *dPtab) {
+                                                            bf16 *cb, float *dPpart) {
   const int b = blockIdx.y;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= nS * R) return;
@@ -628,23 +630,63 @@ __global__ __launch_bounds__(256) void scan_gate_bwd_kernel(const float *dCp, co
     dc32[row * R + ch] = dU * w;
     cb[row * R + ch] = (bf16)cv;
   }
-  atomicAdd(dPtab + (size_t)j * R + ch, dPacc);
+  dPpart[((size_t)b * nS + j) * R + ch] = dPacc;   // summed over b in order by sum_b_kernel
+}
+
+// out[j, ch] = sum over b = 0..B-1, in that order, of part[b, j, ch] for
+// j < nS; rows nS..rows-1 of out are zero.
+__global__ __launch_bounds__(256) void sum_b_kernel(const float *part, int B, int nS, int R,
+                                                    int rows, float *out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * R) return;
+  const size_t j = i / R;
+  float acc = 0.0f;
+  if (j < (size_t)nS)
+    for (int b = 0; b < B; ++b) acc += part[(size_t)b * nS * R + i];
+  out[i] = acc;
 }
 
 // out[ch] += column sums of x [M, N] (fp32), each workgroup a block of rows
 // (eight independent partial sums per thread keep eight loads in flight).
+// out[ch] = sum over the M rows of x[., ch]: workgroup (column block, row
+// chunk) sums its chunk, stores the partial (XCD-coherent), and the last
+// chunk of a column block to finish adds the chunks' partials in chunk
+// order (deterministic).  part: [chunks, N]; ctr: one int per column block,
+// zero on entry and again on exit.
 __global__ __launch_bounds__(256) void colsum_kernel(const float *x, int M, int N, int rows,
-                                                     float *out) {
+                                                     float *part, int *ctr, float *out) {
   const int ch = blockIdx.x * 256 + threadIdx.x;
-  if (ch >= N) return;
-  const int r0 = blockIdx.y * rows, r1 = min(M, r0 + rows);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int r = r0;
-  for (; r + 8 <= r1; r += 8)
+  const int chunks = gridDim.y;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)chunks * N * 4));
+  if (ch < N) {
+    const int r0 = blockIdx.y * rows, r1 = min(M, r0 + rows);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int r = r0;
+    for (; r + 8 <= r1; r += 8)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += x[(size_t)(r + e) * N + ch];
-  for (; r < r1; ++r) acc[0] += x[(size_t)r * N + ch];
-  atomicAdd(out + ch, ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+      for (int e = 0; e < 8; ++e) acc[e] += x[(size_t)(r + e) * N + ch];
+    for (; r < r1; ++r) acc[0] += x[(size_t)r * N + ch];
+    st_coh1(rp, (uint32_t)(((size_t)blockIdx.y * N + ch) * 4),
+            ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+  }
+  __shared__ int last;
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (threadIdx.x == 0) last = ctr_add(&ctr[blockIdx.x], 1) == chunks - 1;
+  __syncthreads();
+  if (!last) return;
+  if (ch < N) {
+    float v = 0.0f;
+    for (int c0 = 0; c0 < chunks; c0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = ld_coh1(rp, (uint32_t)(((size_t)min(c0 + u, chunks - 1) * N + ch) * 4));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < chunks) v += pv[u];
+    }
+    out[ch] = v;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&ctr[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *x, size_t n, bf16 *y) {
@@ -678,15 +720,18 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *in, int R, i
   }
 }
 
-// out[N1, N2] += A[M, N1]^T B[M, N2] over the rows of this split (fp32,
-// added atomically: the caller zeroes `out`).  Workgroup tile 64 x 64, each
+// out[N1, N2] = A[M, N1]^T B[M, N2] (fp32).  M may be split over
+// workgroups (blockIdx.z): the splits' partial tiles then meet in the last
+// split of each tile to finish, which adds them in split order and stores
+// the result (part: tn_gemm_part_bytes; ctr: one int per tile, zero on
+// entry and again on exit).  Workgroup tile 64 x 64, each
 // wave 32 x 32 (2 x 2 MFMA tiles); per step 32 rows of A and B are staged in
 // LDS as two 16-row tiles each, and both operands come from transposing
 // reads (lane (g, c): column c of rows 4g..4g+3 of each tile -- the same
 // row order for A and B, so the products pair the right rows).
 __global__ __launch_bounds__(256) void tn_gemm_kernel(const bf16 *A, int lda, const bf16 *Bm,
                                                       int ldb, int M, int N1, int N2, int mchunk,
-                                                      float *out, int ldo) {
+                                                      float *out, int ldo, float *part, int *ctr) {
   __shared__ __attribute__((aligned(1024))) char lds[2][2 * 2048];   // [A|B][2 tiles x 2 blocks]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -741,17 +786,52 @@ __global__ __launch_bounds__(256) void tn_gemm_kernel(const bf16 *A, int lda, co
       for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma_k32(fa[i], fb[jj], acc[i][jj]);
   }
   // acc[i][jj]: lane (g, c) holds column n2 = .. + c, rows n1 = .. + 4g + e.
+  auto store = [&](int i, int jj, f32x4 v) {
+    const int n2 = n2_0 + 32 * wx + 16 * jj + c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n1 = n1_0 + 32 * wy + 16 * i + 4 * g + e;
+      if (n1 < N1 && n2 < N2) out[(size_t)n1 * ldo + n2] = v[e];
+    }
+  };
+  const int splits = gridDim.z;
+  if (splits == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) store(i, jj, acc[i][jj]);
+    return;
+  }
+  // Split over M: fp32 partial tiles in fragment order (XCD-coherent
+  // stores); the last split of the tile to finish adds them in split order.
+  const int tiles = gridDim.x * gridDim.y, tile = blockIdx.y * gridDim.x + blockIdx.x;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)splits * tiles * 16384));
+  auto poff = [&](int sp, int f) {
+    return (uint32_t)(((((size_t)sp * tiles + tile) * 4 + wave) * 4 + f) * 64 + lane) * 16;
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int n2 = n2_0 + 32 * wx + 16 * jj + c;
+    for (int jj = 0; jj < 2; ++jj) st_coh4(rp, poff(blockIdx.z, 2 * i + jj), acc[i][jj]);
+  __shared__ int last;
+  __syncthreads();   // this workgroup's partial stores have completed
+  if (tid == 0) last = ctr_add(&ctr[tile], 1) == splits - 1;
+  __syncthreads();
+  if (!last) return;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n1 = n1_0 + 32 * wy + 16 * i + 4 * g + e;
-        if (n1 < N1 && n2 < N2) atomicAdd(out + (size_t)n1 * ldo + n2, acc[i][jj][e]);
-      }
+  for (int f = 0; f < 4; ++f) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      f32x4 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = ld_coh4(rp, poff(min(s0 + u, splits - 1), f));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) v += pv[u];
     }
+    store(f >> 1, f & 1, v);
+  }
+  if (tid == 0) __hip_atomic_store(&ctr[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -813,19 +893,31 @@ hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, h
 
 hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b_hc,
                                 const float *table, int B, int T, int R, int s, float *da32,
-                                void *dab, float *dc32, void *cb, float *dPtab,
-                                hipStream_t stream) {
+                                void *dab, float *dc32, void *cb, float *dPpart, int rows,
+                                float *dPtab, hipStream_t stream) {
   const int nS = (T + s - 1) / s;
   dim3 grid((unsigned)(((int64_t)nS * R + 255) / 256), B);
   hipLaunchKernelGGL(scan_gate_bwd_kernel, grid, dim3(256), 0, stream, dCp, cg, (const bf16 *)b_hc,
-                     table, T, R, s, nS, da32, (bf16 *)dab, dc32, (bf16 *)cb, dPtab);
+                     table, T, R, s, nS, da32, (bf16 *)dab, dc32, (bf16 *)cb, dPpart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sum_b_kernel, dim3((unsigned)(((size_t)rows * R + 255) / 256)), dim3(256), 0,
+                     stream, dPpart, B, nS, R, rows, dPtab);
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float *x, int M, int N, float *out, hipStream_t stream) {
-  const int rows = 64;
+namespace {
+int colsum_chunks(int M) { return M < 64 ? (M > 0 ? M : 1) : 64; }
+}  // namespace
+
+size_t colsum_part_bytes(int M, int N) { return (size_t)colsum_chunks(M) * N * 4; }
+int colsum_counters(int N) { return (N + 255) / 256; }
+
+hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, float *out,
+                         hipStream_t stream) {
+  const int chunks = colsum_chunks(M), rows = (M + chunks - 1) / chunks;
   dim3 grid((N + 255) / 256, (M + rows - 1) / rows);
-  hipLaunchKernelGGL(colsum_kernel, grid, dim3(256), 0, stream, x, M, N, rows, out);
+  hipLaunchKernelGGL(colsum_kernel, grid, dim3(256), 0, stream, x, M, N, rows, part, ctr, out);
   return hipGetLastError();
 }
 
@@ -833,6 +925,10 @@ hipError_t launch_f32_to_bf16(const float *x, size_t n, void *y, hipStream_t str
   hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream,
                      x, n, (bf16 *)y);
   return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int *p, size_t n, hipStream_t stream) {
+  return launch_zero_f32((float *)p, n, stream);   // all-zero bits either way
 }
 
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t stream) {
@@ -850,18 +946,36 @@ hipError_t launch_transpose(const void *in, int R, int C, int ldi, void *out, in
   return hipGetLastError();
 }
 
-hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
-                          float *out, int ldo, hipStream_t stream) {
-  const int tiles = ((N1 + 63) / 64) * ((N2 + 63) / 64);
-  int splits = (1024 + tiles - 1) / tiles;                 // about 1024 workgroups
-  const int maxs = (M + 255) / 256;                         // at least 8 steps each
+namespace {
+struct TnPlan {
+  int tiles, splits, mchunk;
+};
+TnPlan tn_plan(int M, int N1, int N2) {
+  TnPlan p;
+  p.tiles = ((N1 + 63) / 64) * ((N2 + 63) / 64);
+  int splits = (1024 + p.tiles - 1) / p.tiles;   // about 1024 workgroups
+  const int maxs = (M + 255) / 256;              // at least 8 steps each
   if (splits > maxs) splits = maxs;
+  if (splits > 32) splits = 32;                  // a short in-order sum of the partials
   if (splits < 1) splits = 1;
-  const int mchunk = ((M + splits - 1) / splits + 31) / 32 * 32;
-  splits = (M + mchunk - 1) / mchunk;
-  dim3 grid((N2 + 63) / 64, (N1 + 63) / 64, splits);
+  p.mchunk = ((M + splits - 1) / splits + 31) / 32 * 32;
+  p.splits = (M + p.mchunk - 1) / p.mchunk;
+  return p;
+}
+}  // namespace
+
+size_t tn_gemm_part_bytes(int M, int N1, int N2) {
+  const TnPlan p = tn_plan(M, N1, N2);
+  return p.splits > 1 ? (size_t)p.splits * p.tiles * 16384 : 0;
+}
+int tn_gemm_counters(int N1, int N2) { return ((N1 + 63) / 64) * ((N2 + 63) / 64); }
+
+hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
+                          float *out, int ldo, float *part, int *ctr, hipStream_t stream) {
+  const TnPlan p = tn_plan(M, N1, N2);
+  dim3 grid((N2 + 63) / 64, (N1 + 63) / 64, p.splits);
   hipLaunchKernelGGL(tn_gemm_kernel, grid, dim3(256), 0, stream, (const bf16 *)A, lda,
-                     (const bf16 *)Bm, ldb, M, N1, N2, mchunk, out, ldo);
+                     (const bf16 *)Bm, ldb, M, N1, N2, p.mchunk, out, ldo, part, ctr);
   return hipGetLastError();
 }
 

@@ -175,22 +175,33 @@ hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *
 // dKR [M, dR] (bf16) = sum over heads of dKRh [M, H, dR].
 hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, hipStream_t stream);
 // Reverse group scan and gate backward from dC' [B*T, R] (fp32) and the
-// forward's cg: da (fp32 and bf16), dc's direct term (fp32), c (bf16), and
-// dPtab [rows, R] += the position-branch gradient.
+// forward's cg: da (fp32 and bf16), dc's direct term (fp32), c (bf16).
+// dPpart [B, ceil(T/s), R] receives each sequence's position-branch
+// gradient, and dPtab [rows, R] = their sum over the sequences in order
+// (rows past ceil(T/s) are zero).
 hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b_hc,
                                 const float *table, int B, int T, int R, int s, float *da32,
-                                void *dab, float *dc32, void *cb, float *dPtab,
-                                hipStream_t stream);
-// out[N] += column sums of x [M, N] (fp32).
-hipError_t launch_colsum(const float *x, int M, int N, float *out, hipStream_t stream);
+                                void *dab, float *dc32, void *cb, float *dPpart, int rows,
+                                float *dPtab, hipStream_t stream);
+// out[N] = column sums of x [M, N] (fp32), partial sums over row chunks
+// added in chunk order: part holds colsum_part_bytes, ctr colsum_counters
+// ints (zero on entry, zero again on exit).
+hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, float *out,
+                         hipStream_t stream);
+size_t colsum_part_bytes(int M, int N);
+int colsum_counters(int N);
 hipError_t launch_f32_to_bf16(const float *x, size_t n, void *y, hipStream_t stream);
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t stream);
+hipError_t launch_zero_i32(int *p, size_t n, hipStream_t stream);
 // out[C, R] (row stride ldo) = in[R, C]^T (bf16, row stride ldi).
 hipError_t launch_transpose(const void *in, int R, int C, int ldi, void *out, int ldo,
                             hipStream_t stream);
-// out[N1, N2] (fp32, row stride ldo) += A[M, N1]^T B[M, N2] (bf16), split
-// over M with atomic adds: the caller zeroes out.
+// out[N1, N2] (fp32, row stride ldo) = A[M, N1]^T B[M, N2] (bf16), split
+// over M; the splits' partials are added in split order.
 hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
-                          float *out, int ldo, hipStream_t stream);
+                          float *out, int ldo, float *part, int *ctr, hipStream_t stream);
+// Partials (bytes) and counters launch_tn_gemm needs for this shape.
+size_t tn_gemm_part_bytes(int M, int N1, int N2);
+int tn_gemm_counters(int N1, int N2);
 
 }  // namespace mtla

@@ -175,7 +175,8 @@ HeadsWs heads_ws(const mtla_dims *d, int B, int T) {
 struct BwdWs {
   HeadsWs f;
   size_t O_, lse, WOt, WKVt, Whct, Wdkvt, WQt, dO, D, dKVc, dKRc, dKV, dKRh, dQ, dCp, da32, dab,
-      dc32, cb, dcb, dX32, total;
+      dc32, cb, dcb, dX32, dPpart, red_part, red_ctr, total;
+  int nctr;   // ints at red_ctr: counters of the ordered reductions (zero between uses)
 };
 
 BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
@@ -206,6 +207,25 @@ BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
   w.cb = take(M * r * e);
   w.dcb = take(M * r * e);
   w.dX32 = take(M * dd * 4);
+  w.dPpart = take((size_t)B * nS * r * 4);
+  // Partials of the ordered reductions (weight-gradient products and the
+  // bias column sums run one after another and share one buffer).
+  const int Mi = (int)M, HDi = (int)HD, ri = (int)r, di = (int)dd;
+  const size_t tp[6] = {mtla::tn_gemm_part_bytes(Mi, di, HDi), mtla::tn_gemm_part_bytes(Mi, HDi, di),
+                        mtla::tn_gemm_part_bytes(Mi, HDi, ri), mtla::tn_gemm_part_bytes(Mi, HDi, ri),
+                        mtla::tn_gemm_part_bytes(Mi, ri, ri), mtla::tn_gemm_part_bytes(Mi, ri, di)};
+  const int tc[6] = {mtla::tn_gemm_counters(di, HDi), mtla::tn_gemm_counters(HDi, di),
+                     mtla::tn_gemm_counters(HDi, ri), mtla::tn_gemm_counters(HDi, ri),
+                     mtla::tn_gemm_counters(ri, ri), mtla::tn_gemm_counters(ri, di)};
+  size_t pmax = mtla::colsum_part_bytes(Mi, ri);
+  int cmax = mtla::colsum_counters(ri);
+  for (int i = 0; i < 6; ++i) {
+    if (tp[i] > pmax) pmax = tp[i];
+    if (tc[i] > cmax) cmax = tc[i];
+  }
+  w.red_part = take(pmax);
+  w.nctr = cmax;
+  w.red_ctr = take((size_t)cmax * 4);
   w.total = off;
   return w;
 }
@@ -675,12 +695,14 @@ mtla_status prefill_unabsorbed_backward_impl(
                                false, s),
          "dC'");
   // group sums and gate
-  LAUNCH(mtla::launch_zero_f32(gr->dgate_pos, (size_t)w->gate_pos_rows * r, s), "zero dP");
-  LAUNCH(mtla::launch_zero_f32(gr->db_hc, r, s), "zero db");
+  int *rctr = (int *)P(ws.red_ctr);
+  float *rpart = F(ws.red_part);
+  LAUNCH(mtla::launch_zero_i32(rctr, ws.nctr, s), "clear the reduction counters");
   LAUNCH(mtla::launch_scan_gate_bwd(F(ws.dCp), cg, w->b_hc, w->gate_pos, B, T, r, dims->s,
-                                    F(ws.da32), P(ws.dab), F(ws.dc32), P(ws.cb), gr->dgate_pos, s),
+                                    F(ws.da32), P(ws.dab), F(ws.dc32), P(ws.cb), F(ws.dPpart),
+                                    w->gate_pos_rows, gr->dgate_pos, s),
          "group scan and gate backward");
-  LAUNCH(mtla::launch_colsum(F(ws.da32), M, r, gr->db_hc, s), "db");
+  LAUNCH(mtla::launch_colsum(F(ws.da32), M, r, rpart, rctr, gr->db_hc, s), "db");
   LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), r, true, s),
          "dc");
   LAUNCH(mtla::launch_f32_to_bf16(F(ws.dc32), (size_t)M * r, P(ws.dcb), s), "dc to bf16");
@@ -690,21 +712,18 @@ mtla_status prefill_unabsorbed_backward_impl(
   LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, true, s),
          "dX from the query map");
   LAUNCH(mtla::launch_f32_to_bf16(F(ws.dX32), (size_t)M * d, dX, s), "dX to bf16");
-  // weight gradients
-  LAUNCH(mtla::launch_zero_f32(gr->dW_O, (size_t)d * HD, s), "zero dW_O");
-  LAUNCH(mtla::launch_zero_f32(gr->dW_Q, (size_t)HD * d, s), "zero dW_Q");
-  LAUNCH(mtla::launch_zero_f32(gr->dW_K, (size_t)HD * r, s), "zero dW_K");
-  LAUNCH(mtla::launch_zero_f32(gr->dW_V, (size_t)HD * r, s), "zero dW_V");
-  LAUNCH(mtla::launch_zero_f32(gr->dW_hc, (size_t)r * r, s), "zero dW_hc");
-  LAUNCH(mtla::launch_zero_f32(gr->dW_dkv, (size_t)r * d, s), "zero dW_dkv");
-  LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, s), "dW_O");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, s), "dW_Q");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, s), "dW_K");
+  // weight gradients (each product's partials added in split order)
+  LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, rpart, rctr, s), "dW_O");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, rpart, rctr, s), "dW_Q");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, rpart, rctr, s),
+         "dW_K");
   LAUNCH(mtla::launch_tn_gemm((char *)P(ws.dKV) + (size_t)HD * 2, 2 * HD, Cp, r, M, HD, r, gr->dW_V,
-                              r, s),
+                              r, rpart, rctr, s),
          "dW_V");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, s), "dW_hc");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, s), "dW_dkv");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, rpart, rctr, s),
+         "dW_hc");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, rpart, rctr, s),
+         "dW_dkv");
   return ok();
 }
 

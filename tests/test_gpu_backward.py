@@ -99,3 +99,30 @@ def test_backward_full_size_prefix():
     name, dims, ex = synth.config(4)
     say("backward full size", name)
     _check(dims, ex["B"], ex["T"], 9600, T0=320, rows=[0, ex["B"] - 1])
+
+
+@pytest.mark.parametrize("d_h,r,dR", [(64, 256, 32), (128, 512, 64)])
+def test_backward_is_deterministic(d_h, r, dR):
+    """Two calls on the same inputs give the same bits in every output:
+    the input gradients and every reduction across workgroups (weight
+    gradients, bias and position-table gradients) add their partials in a
+    fixed order."""
+    needs_gpu()
+    dims = Dims(d=512, H=4, d_h=d_h, r=r, d_hR=dR, s=3)
+    B, T = 2, 700
+    ms = om.n_slots(T, dims.s) + 1
+    w, W, L = _layer(dims, 9700 + d_h, ms)
+    seq = synth.make_sequence(dims, w, B, T, 9701, "bf16")
+    rng = np.random.default_rng(9702)
+    dY = dev(synth.round_to(rng.normal(size=(B, T, dims.d)), "bf16"), "bf16")
+    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
+    outs = []
+    for _ in range(2):
+        dX, dQR, dKR, grads = L.backward_unabsorbed(X, QR, KR, dY)
+        outs.append([dX.clone(), dQR.clone(), dKR.clone()] + [grads[k].clone() for k in sorted(grads)])
+    torch.cuda.synchronize()
+    say("backward determinism", d_h)
+    names = ["dX", "dQR", "dKR"] + sorted(grads)
+    for n, a, b in zip(names, outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), n
