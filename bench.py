@@ -30,7 +30,8 @@ summary under profiles/ while the kernel's sources are unchanged.
 Also reported (same line): the speech-decoder and ragged decode workloads
 (each with its roofline), the strided prefill (TFLOP/s of the attention kernel
 on visible pairs only, and of the whole forward, in the absorbed form and in
-the per-head form), the backward of the per-head form, the chunked
+the per-head form), the backward of the per-head form (also both at the
+LLM-scale head widths d_h = 128, d_hR = 64, r = 512), the chunked
 merge-append (frames/s), the library's decoupled-RoPE inputs, the speech
 decode at s = 1 (the MLA reduction: twice the slots, for the speed and memory
 ratio), and the CPU oracle timed on the host cores beside each decode workload
@@ -340,14 +341,25 @@ def run_append(steps: int = 20, warmup: int = 3) -> dict:
                 proj_flops=proj_flops, proj_tflops=proj_flops / (step_ms * 1e-3) / 1e12)
 
 
-def run_prefill_unabsorbed(steps: int = 10, warmup: int = 3) -> dict:
+def _prefill_workload(wide: bool):
+    """(name, dims, B, T) of the prefill workload, or with wide=True the same
+    frames per sequence at the LLM-scale head widths (d_h = 128, d_hR = 64,
+    r = 4 d_h = 512; d = 1024, 8 heads, 8 sequences)."""
+    import synth
+    name, dims, ex = synth.config(4)
+    if not wide:
+        return name, dims, ex["B"], ex["T"]
+    from synth import Dims
+    return "prefill_b8_t4096_dh128", Dims(d=1024, H=8, d_h=128, r=512, d_hR=64, s=2), 8, ex["T"]
+
+
+def run_prefill_unabsorbed(steps: int = 10, warmup: int = 3, wide: bool = False) -> dict:
     """The same prefill workload in the per-head form (mtla_prefill_unabsorbed):
     attention at head width over explicit per-head keys and values."""
     import torch
     import synth
     from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
-    name, dims, ex = synth.config(4)
-    B, T = ex["B"], ex["T"]
+    name, dims, B, T = _prefill_workload(wide)
     ms = -(-T // dims.s)
     w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
     layer = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
@@ -384,15 +396,14 @@ def run_prefill_unabsorbed(steps: int = 10, warmup: int = 3) -> dict:
                 tokens_per_s=M / (fwd_ms * 1e-3))
 
 
-def run_backward(steps: int = 5, warmup: int = 2) -> dict:
+def run_backward(steps: int = 5, warmup: int = 2, wide: bool = False) -> dict:
     """Backward of the per-head form on the prefill workload: one step is one
     mtla_prefill_unabsorbed_backward call (the forward recomputed inside,
     then every input and weight gradient) for a seeded loss gradient dY."""
     import torch
     import synth
     from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
-    name, dims, ex = synth.config(4)
-    B, T = ex["B"], ex["T"]
+    name, dims, B, T = _prefill_workload(wide)
     ms = -(-T // dims.s)
     w = synth.make_weights(dims, synth.seed_for(4), "bf16", pe_rows=ms)
     layer = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
@@ -551,6 +562,8 @@ def main():
                                        "llm_decode_b128_ctx32768", "prefill_b16_t4096",
                                        "append_chunk_b32_l512", "prefill_b16_t4096_per_head",
                                        "prefill_b16_t4096_backward", "rope_inputs_b16_t4096",
+                                       "prefill_b8_t4096_dh128_per_head",
+                                       "prefill_b8_t4096_dh128_backward",
                                        "decode_b32_ctx2048_s1"],
                     help="time one workload alone and print its record (for profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -580,6 +593,12 @@ def main():
         return
     if args.only == "prefill_b16_t4096_per_head":
         print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "prefill_b8_t4096_dh128_per_head":
+        print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup, wide=True)), flush=True)
+        return
+    if args.only == "prefill_b8_t4096_dh128_backward":
+        print(json.dumps(run_backward(args.steps, args.warmup, wide=True)), flush=True)
         return
     if args.only == "append_chunk_b32_l512":
         print(json.dumps(run_append(args.steps, args.warmup)), flush=True)
@@ -624,6 +643,13 @@ def main():
     log("prefill_b16_t4096_backward ...")
     bw = extra["prefill_b16_t4096_backward"] = run_backward()
     log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
+    torch.cuda.empty_cache()
+    log("prefill_b8_t4096_dh128 (per-head form and backward at d_h = 128) ...")
+    uw = extra["prefill_b8_t4096_dh128_per_head"] = run_prefill_unabsorbed(wide=True)
+    uw["attn_mfma_frac"] = uw["attn_tflops"] / BF16_PEAK_TFLOPS
+    bww = extra["prefill_b8_t4096_dh128_backward"] = run_backward(wide=True)
+    log(f"  d_h=128 per-head: attention {uw['attn_ms']:.3f} ms {uw['attn_tflops']:.0f} TFLOP/s "
+        f"({uw['attn_mfma_frac']:.1%}), forward {uw['forward_ms']:.3f} ms; backward {bww['step_ms']:.3f} ms")
     log("decode_b32_ctx2048_s1 (the MLA reduction, one slot per frame) ...")
     m1 = extra["decode_b32_ctx2048_s1"] = run_decode(2, 50, 10, stride=1)
     m1["cache_bytes_vs_s2"] = m1["cache_bytes"] / c2["cache_bytes"]
