@@ -30,6 +30,8 @@
 // (deterministic; its eight waves share the tile's fragments, all loads of a
 // round in flight together) before the epilogue.
 
+#include <atomic>
+
 #include "common.h"
 #include "gemm_common.h"
 
@@ -251,13 +253,23 @@ __global__ __launch_bounds__(512) void stream_gemm_kernel(StreamArgs a, Epi epi)
   if (tid == 0) __hip_atomic_store(&a.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compute units of the current device, looked up once per device (the plan
+// is made on every call; races only ever store the same value).
 int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
     (void)hipGetLastError();
     return 256;
   }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cus[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
