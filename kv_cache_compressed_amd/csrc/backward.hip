@@ -41,9 +41,10 @@ namespace {
 constexpr float kNegInfB = -INFINITY;
 
 // Head widths and tiling of the attention backward: (DH, DR) = (64, 32) with
-// two 16-row tiles (32 keys, or 32 query frames) per wave and two workgroups
-// per CU, or (128, 64) with one tile per wave and one workgroup per CU (the
-// accumulators of twice the width then fit without spills).
+// two 16-row tiles (32 keys, or 32 query frames) per wave, or (128, 64) with
+// one (the accumulators of twice the width then fit the 256 registers of two
+// waves per SIMD, with four spilled in the key pass: two workgroups per CU
+// measured 3.86 ms per backward call against 4.59 ms for one without spills).
 // Streamed rows hold, in the 16-row swizzled tile layout, K_h | K^R | V_h
 // (key rows) or Q_h | Q^R_h | dO_h (query rows): 2 DH + DR bf16.
 template <int DH_, int DR_, int NT_, int NST_, int OCC_> struct BwCfg {
@@ -62,7 +63,7 @@ template <int DH_, int DR_, int NT_, int NST_, int OCC_> struct BwCfg {
   static_assert(OCC * (NST * STAGE_B + 1024) <= 160 * 1024, "LDS per CU");
 };
 using Bw64 = BwCfg<64, 32, 2, 4, 2>;
-using Bw128 = BwCfg<128, 64, 1, 4, 1>;
+using Bw128 = BwCfg<128, 64, 1, 3, 2>;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_b4;
 
