@@ -348,6 +348,10 @@ struct WsCfg {
   static constexpr int F_B = 16;                 // rescale flags of the 4 score waves
   static constexpr int EXTRA = 2 * P_B + 3 * A_B + 2 * F_B + 1024;
   static constexpr int MAX_NST = 6;
+  // Before stage 0's P is written, the two P slots hold the rows [C'_f | K^R_f]
+  // of the workgroup's frames (RB bytes each), copied in 1 KB loads: at most
+  // SELF_FR frames (every H >= 5; fewer heads read them per lane instead).
+  static constexpr int SELF_FR = (2 * P_B / 1024) * (1024 / 16) / (RB / 16);
   static_assert(KS == NSEG, "a K^T fragment row spans one 1 KB block per k-step");
 };
 
@@ -388,6 +392,11 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
   float *lbuf = abase + 2 * (C::A_B / 4);          // row sums
   float *fbase = lbuf + C::A_B / 4;                // rescale flags, two slots
   char *dummy = (char *)(fbase + 2 * (C::F_B / 4));
+  // Frames of the workgroup's rows: the self terms and the value waves'
+  // starting O^T come from their rows, each copied once into LDS when they fit.
+  const int f0 = (qtile * C::ROWS) / H, nfr = glast / H - f0 + 1;
+  const bool self_lds = nfr <= C::SELF_FR;
+  const char *selfb = pbase;
 
   if (wave < 4) {
     // ---------------- score wave ----------------
@@ -412,38 +421,60 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
     for (int k = 0; k < pro; ++k) issue(k);
 
     bf16x8 q[C::NQ][C::KS];
-    float m[C::NQ], l[C::NQ];
-    int lim[C::NQ];
+    float m[C::NQ], l[C::NQ], dot[C::NQ];
+    int lim[C::NQ], fl[C::NQ];
 #pragma unroll
     for (int qi = 0; qi < C::NQ; ++qi) {
-      // Rows past the end read row 0 (valid memory) and are never written back.
+      // Rows past the end read row 0 (valid memory; its frame's LDS row is
+      // the workgroup's first) and are never written back.
       const int row = rw + 16 * qi + c;
       const bool ok = row < nrows;
       const int rr = ok ? row : 0;
       const int mf = rr / H, h = rr % H;
       lim[qi] = ok ? mf / s : 0;
+      fl[qi] = ok ? mf - f0 : 0;
       const size_t qoff = ((size_t)b * Tn + mf) * H + h;
       const size_t coff = (size_t)b * Tn + mf;
-      float dot = 0.0f;
+      dot[qi] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int k = 32 * ks + 8 * g;
-        bf16x8 d;
-        if (k < C::R) {
+        if (k < C::R)
           load8(q[qi][ks], (const bf16 *)a.qt + qoff * C::R + k);
-          load8(d, (const bf16 *)a.Cp + coff * C::R + k);
-        } else {
+        else
           load8(q[qi][ks], (const bf16 *)a.QR + qoff * C::DR + (k - C::R));
-          load8(d, (const bf16 *)a.KR + coff * C::DR + (k - C::R));
-        }
+        if (!self_lds) {
+          bf16x8 d;
+          if (k < C::R)
+            load8(d, (const bf16 *)a.Cp + coff * C::R + k);
+          else
+            load8(d, (const bf16 *)a.KR + coff * C::DR + (k - C::R));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot += to_f32(q[qi][ks][e]) * to_f32(d[e]);
+          for (int e = 0; e < 8; ++e) dot[qi] += to_f32(q[qi][ks][e]) * to_f32(d[e]);
+        }
+      }
+    }
+    // The value waves' copy of the frames' rows has landed.
+    bar();
+#pragma unroll
+    for (int qi = 0; qi < C::NQ; ++qi) {
+      if (self_lds) {
+        // Row (frame f) at (f - f0) * RB; k-step ks, lane group g: bytes
+        // 64 ks + 16 g, the same offset in C' (k < R) and K^R (k >= R).
+        const char *dr = selfb + fl[qi] * C::RB + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 d = *(const bf16x8 *)(dr + 64 * ks);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dot[qi] += to_f32(q[qi][ks][e]) * to_f32(d[e]);
+        }
       }
       // The row's own state seeds the softmax: weight 1 at reference max m.
-      m[qi] = sum_g(dot) * a.sl2;
+      m[qi] = sum_g(dot[qi]) * a.sl2;
       l[qi] = (g == 0) ? 1.0f : 0.0f;
     }
-    asm volatile("" ::: "memory");
+    // The frame rows are read before stage 0's P overwrites them.
+    wait_lgkm0();
 
     // Keys below wmin are visible to every row of the wave: no mask needed.
     const int wmin = rw < nrows ? ((rw / H) / s) : 0;
@@ -627,6 +658,27 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
       const int r0 = qtile * C::ROWS + u * C::ROWS_W, r1 = min(r0 + C::ROWS_W, nrows) - 1;
       wl[u] = r1 >= r0 ? (r1 / H) / s : 0;
     }
+    if (self_lds) {
+      // Copy the frames' rows into LDS for the score waves' self terms:
+      // 16-byte chunk i of the region is chunk i mod (RB/16) of frame
+      // f0 + i / (RB/16); the last load's lanes past the end repeat the last
+      // frame (inside the region).
+      constexpr int CPR = C::RB / 16, RCH = C::R / 8;
+      const int nld = (nfr * CPR + 63) / 64;
+      for (int i = v; i < nld; i += 4) {
+        const int ch = i * 64 + lane;
+        const int fr = min(ch / CPR, nfr - 1), part = ch - (ch / CPR) * CPR;
+        const size_t f = (size_t)b * Tn + f0 + fr;
+        const bf16 *src = part < RCH ? (const bf16 *)a.Cp + f * C::R + 8 * part
+                                     : (const bf16 *)a.KR + f * C::DR + 8 * (part - RCH);
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(pbase + i * 1024), 16, 0,
+                                         0);
+      }
+      wait_vm<0>();
+    }
+    bar();
+    // Starting O^T: the rows' own states C'_m (read from global memory: an
+    // LDS-sourced copy here raises the loop's register demand past 256).
 #pragma unroll
     for (int rt = 0; rt < C::NRT; ++rt) {
       const int row = qtile * C::ROWS + 16 * rt + c;

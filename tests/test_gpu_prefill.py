@@ -56,7 +56,8 @@ def test_fp32_strides_and_ragged_lengths(s, T):
 
 
 @pytest.mark.parametrize("s,T,H", [(2, 300, 8), (3, 250, 8), (2, 97, 16), (4, 160, 32), (2, 64, 3),
-                                     (1, 130, 8), (2, 1, 8), (80, 64, 4), (2, 520, 2)])
+                                     (1, 130, 8), (2, 1, 8), (80, 64, 4), (2, 520, 2),
+                                     (2, 333, 5), (3, 211, 6)])
 def test_bf16_multi_sequence(s, T, H):
     needs_gpu()
     dims = Dims(d=512, H=H, d_h=64, r=256, d_hR=32, s=s)
