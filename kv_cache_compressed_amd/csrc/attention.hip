@@ -346,16 +346,30 @@ struct WsCfg {
   static constexpr int P_B = NRT * 64 * 16;      // P slot: row tiles x 64 lanes x 16 B
   static constexpr int A_B = 16 * NRT * 4;       // per-row floats [lane row c][row tile]
   static constexpr int F_B = 16;                 // rescale flags of the 4 score waves
-  static constexpr int EXTRA = 2 * P_B + 3 * A_B + 2 * F_B + 1024;
-  static constexpr int MAX_NST = 6;
-  // Before stage 0's P is written, the two P slots hold the rows [C'_f | K^R_f]
-  // of the workgroup's frames (RB bytes each), copied in 1 KB loads: at most
-  // SELF_FR frames (every H >= 5; fewer heads read them per lane instead).
-  static constexpr int SELF_FR = (2 * P_B / 1024) * (1024 / 16) / (RB / 16);
+  // The rows [C'_f | K^R_f] of the workgroup's frames (RB bytes each) stay in
+  // LDS for the whole workgroup when they fit SELF_B: at most SELF_FR frames
+  // (every H >= 5); with fewer heads they are read per lane instead.
+  static constexpr int SELF_B = 24 * 1024;
+  static constexpr int SELF_FR = (SELF_B / 16) / (RB / 16);
+  static constexpr int EXTRA = 2 * P_B + 3 * A_B + 2 * F_B + 1024 + SELF_B;
+  // Ring depth, fixed at compile time so that slot indices need no runtime
+  // division: six 18 KB stages plus the P, rescale and flag buffers fill
+  // 135 KB of the 160 KB LDS.
+  static constexpr int NST = 6;
   static_assert(KS == NSEG, "a K^T fragment row spans one 1 KB block per k-step");
+  static_assert(NST * STAGE_B + EXTRA <= 160 * 1024, "the ring and buffers fit the LDS");
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// acc + sum of the 8 products x[e] y[e], in fp32 (four v_dot2_f32_bf16).
+__device__ __forceinline__ float dot8(const bf16x8 &x, const bf16x8 &y, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2)
+    acc = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){x[e], x[e + 1]}, (bf16x2){y[e], y[e + 1]}, acc,
+                                          false);
+  return acc;
+}
 
 __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
   using C = WsCfg;
@@ -364,7 +378,8 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int H = a.H, Tn = a.T, s = a.s, nst = a.nst;
+  const int H = a.H, Tn = a.T, s = a.s;
+  constexpr int nst = C::NST;
 
   int b, qtile;
   {
@@ -392,11 +407,13 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
   float *lbuf = abase + 2 * (C::A_B / 4);          // row sums
   float *fbase = lbuf + C::A_B / 4;                // rescale flags, two slots
   char *dummy = (char *)(fbase + 2 * (C::F_B / 4));
-  // Frames of the workgroup's rows: the self terms and the value waves'
-  // starting O^T come from their rows, each copied once into LDS when they fit.
+  char *selfb = dummy + 1024;                      // the frames' rows
+  float *sbuf = abase;   // after the loop: each row's self-term factor
+  // Frames of the workgroup's rows: each row's own term (its score seeds the
+  // softmax, its value C'_m joins the output at the end) comes from the
+  // frame's row, copied once into LDS when the frames fit.
   const int f0 = (qtile * C::ROWS) / H, nfr = glast / H - f0 + 1;
   const bool self_lds = nfr <= C::SELF_FR;
-  const char *selfb = pbase;
 
   if (wave < 4) {
     // ---------------- score wave ----------------
@@ -421,8 +438,9 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
     for (int k = 0; k < pro; ++k) issue(k);
 
     bf16x8 q[C::NQ][C::KS];
-    float m[C::NQ], l[C::NQ], dot[C::NQ];
+    float m[C::NQ], l[C::NQ], dot[C::NQ], m0[C::NQ];
     int lim[C::NQ], fl[C::NQ];
+    size_t qoff[C::NQ], coff[C::NQ];
 #pragma unroll
     for (int qi = 0; qi < C::NQ; ++qi) {
       // Rows past the end read row 0 (valid memory; its frame's LDS row is
@@ -433,26 +451,38 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
       const int mf = rr / H, h = rr % H;
       lim[qi] = ok ? mf / s : 0;
       fl[qi] = ok ? mf - f0 : 0;
-      const size_t qoff = ((size_t)b * Tn + mf) * H + h;
-      const size_t coff = (size_t)b * Tn + mf;
+      qoff[qi] = ((size_t)b * Tn + mf) * H + h;
+      coff[qi] = (size_t)b * Tn + mf;
       dot[qi] = 0.0f;
+    }
+    // Queries (lane group g: values 32 ks + 8 g .. + 7 of k-step ks); with
+    // few heads, the rows' own states too, read per lane.
+    auto load_q = [&](int qi, int ks) {
+      const int k = 32 * ks + 8 * g;
+      if (k < C::R)
+        load8(q[qi][ks], (const bf16 *)a.qt + qoff[qi] * C::R + k);
+      else
+        load8(q[qi][ks], (const bf16 *)a.QR + qoff[qi] * C::DR + (k - C::R));
+    };
+    if (self_lds) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int k = 32 * ks + 8 * g;
-        if (k < C::R)
-          load8(q[qi][ks], (const bf16 *)a.qt + qoff * C::R + k);
-        else
-          load8(q[qi][ks], (const bf16 *)a.QR + qoff * C::DR + (k - C::R));
-        if (!self_lds) {
+      for (int qi = 0; qi < C::NQ; ++qi)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) load_q(qi, ks);
+    } else {
+#pragma unroll
+      for (int qi = 0; qi < C::NQ; ++qi)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          load_q(qi, ks);
+          const int k = 32 * ks + 8 * g;
           bf16x8 d;
           if (k < C::R)
-            load8(d, (const bf16 *)a.Cp + coff * C::R + k);
+            load8(d, (const bf16 *)a.Cp + coff[qi] * C::R + k);
           else
-            load8(d, (const bf16 *)a.KR + coff * C::DR + (k - C::R));
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dot[qi] += to_f32(q[qi][ks][e]) * to_f32(d[e]);
+            load8(d, (const bf16 *)a.KR + coff[qi] * C::DR + (k - C::R));
+          dot[qi] = dot8(q[qi][ks], d, dot[qi]);
         }
-      }
     }
     // The value waves' copy of the frames' rows has landed.
     bar();
@@ -463,18 +493,16 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
         // 64 ks + 16 g, the same offset in C' (k < R) and K^R (k >= R).
         const char *dr = selfb + fl[qi] * C::RB + 16 * g;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 d = *(const bf16x8 *)(dr + 64 * ks);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) dot[qi] += to_f32(q[qi][ks][e]) * to_f32(d[e]);
-        }
+        for (int ks = 0; ks < C::KS; ++ks)
+          dot[qi] = dot8(q[qi][ks], *(const bf16x8 *)(dr + 64 * ks), dot[qi]);
       }
-      // The row's own state seeds the softmax: weight 1 at reference max m.
+      // The row's own state seeds the softmax: weight 1 at reference max m0.
+      // The value waves start from O^T = 0 and add C'_m with the factor
+      // 2^(m0 - m) that the later moves of m leave on that weight.
       m[qi] = sum_g(dot[qi]) * a.sl2;
+      m0[qi] = m[qi];
       l[qi] = (g == 0) ? 1.0f : 0.0f;
     }
-    // The frame rows are read before stage 0's P overwrites them.
-    wait_lgkm0();
 
     // Keys below wmin are visible to every row of the wave: no mask needed.
     const int wmin = rw < nrows ? ((rw / H) / s) : 0;
@@ -640,10 +668,14 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
 #pragma unroll
     for (int qi = 0; qi < C::NQ; ++qi) {
       const float lt = sum_g(l[qi]);
-      if (g == 0) lbuf[c * C::NRT + C::NQ * w + qi] = lt;
+      if (g == 0) {
+        lbuf[c * C::NRT + C::NQ * w + qi] = lt;
+        sbuf[c * C::NRT + C::NQ * w + qi] = __builtin_amdgcn_exp2f(m0[qi] - m[qi]);
+      }
     }
     wait_lgkm0();
     bar();
+    bar();   // the value waves' staged output is complete (they store it)
   } else {
     // ---------------- value wave ----------------
     // Value wave v holds O^T for all NRT row tiles of the workgroup and the
@@ -658,11 +690,14 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
       const int r0 = qtile * C::ROWS + u * C::ROWS_W, r1 = min(r0 + C::ROWS_W, nrows) - 1;
       wl[u] = r1 >= r0 ? (r1 / H) / s : 0;
     }
+#pragma unroll
+    for (int rt = 0; rt < C::NRT; ++rt)
+#pragma unroll
+      for (int mb = 0; mb < C::NB; ++mb) o[rt][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (self_lds) {
-      // Copy the frames' rows into LDS for the score waves' self terms:
-      // 16-byte chunk i of the region is chunk i mod (RB/16) of frame
-      // f0 + i / (RB/16); the last load's lanes past the end repeat the last
-      // frame (inside the region).
+      // Copy the frames' rows into LDS: 16-byte chunk i of the region is
+      // chunk i mod (RB/16) of frame f0 + i / (RB/16); the last load's lanes
+      // past the end repeat the last frame (inside the region).
       constexpr int CPR = C::RB / 16, RCH = C::R / 8;
       const int nld = (nfr * CPR + 63) / 64;
       for (int i = v; i < nld; i += 4) {
@@ -671,23 +706,12 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
         const size_t f = (size_t)b * Tn + f0 + fr;
         const bf16 *src = part < RCH ? (const bf16 *)a.Cp + f * C::R + 8 * part
                                      : (const bf16 *)a.KR + f * C::DR + 8 * (part - RCH);
-        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(pbase + i * 1024), 16, 0,
+        __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(selfb + i * 1024), 16, 0,
                                          0);
       }
       wait_vm<0>();
     }
     bar();
-    // Starting O^T: the rows' own states C'_m (read from global memory: an
-    // LDS-sourced copy here raises the loop's register demand past 256).
-#pragma unroll
-    for (int rt = 0; rt < C::NRT; ++rt) {
-      const int row = qtile * C::ROWS + 16 * rt + c;
-      const int rr = row < nrows ? row : 0;
-      const size_t coff = (size_t)b * Tn + rr / H;
-#pragma unroll
-      for (int mb = 0; mb < C::NB; ++mb)
-        o[rt][mb] = load4f((const bf16 *)a.Cp + coff * C::R + 64 * v + 16 * mb + 4 * g);
-    }
     // O^T += C^T P^T for row tiles [r0, r1) of stage kk.
     auto pv = [&](int kk, const bf16x8 (&vf)[C::NB], auto r0c, auto r1c) {
       constexpr int r0 = decltype(r0c)::value, r1 = decltype(r1c)::value;
@@ -748,16 +772,68 @@ __global__ __launch_bounds__(512) void prefill_ws_kernel(PrefillArgs a) {
       if (act) pv(kk, vf, Half(), Full());
     }
     bar();
-    const float *lb = lbuf + c * C::NRT;
+    // Output: normalised O rows staged through the (now idle) key ring in
+    // row-major order, OST bytes apart, then stored whole: each 16-byte lane
+    // store then covers an eighth of a 128-byte line, instead of the
+    // accumulator layout's 32 bytes of each of 16 rows.
+    constexpr int OST = C::R * 2 + 16;
+    static_assert(C::ROWS * OST <= C::NST * C::STAGE_B, "the output fits the ring");
+    const float *lb = lbuf + c * C::NRT, *sf = sbuf + c * C::NRT;
+    // Each row's own value C'_m (from the LDS copy, else from global memory:
+    // two separate loops, so that each read's address space is known).
+    auto stage_out = [&](auto cmrow) {
+      // Frame of row 16 rt + c, relative to f0: q0 + floor((r0 + 16 rt + 1/2) / H)
+      // with (q0, r0) = divmod(first row of the lane, H).  The numerator stays
+      // below 240, so the fp32 reciprocal cannot move it across an integer.
+      const int rl = qtile * C::ROWS + c, q0 = rl / H - f0, r0 = rl - (rl / H) * H;
+      const float invH = 1.0f / (float)H;
+      // Row tile rt+1's operands are read before row tile rt's results are
+      // written: the compiler cannot tell that the LDS copy and the staging
+      // area do not overlap, and would otherwise wait out each read behind
+      // the previous write.
+      bf16x4 cvn[C::NB];
+      float ln, sn;
+      auto fetch = [&](int rt) {
+        const int row = qtile * C::ROWS + 16 * rt + c;
+        const int fq = q0 + (int)(((float)(r0 + 16 * rt) + 0.5f) * invH);
+        const bf16 *cm = cmrow(row < nrows ? fq : 0) + 64 * v + 4 * g;   // rows past the end are not stored
 #pragma unroll
-    for (int rt = 0; rt < C::NRT; ++rt) {
-      const int row = qtile * C::ROWS + 16 * rt + c;
-      if (row < nrows) {
-        const float inv = 1.0f / lb[rt];
-        bf16 *dst = (bf16 *)a.O + ((size_t)b * nrows + row) * C::R + 64 * v + 4 * g;
+        for (int mb = 0; mb < C::NB; ++mb) cvn[mb] = *(const bf16x4 *)(cm + 16 * mb);
+        ln = lb[rt];
+        sn = sf[rt];
+      };
+      fetch(0);
 #pragma unroll
-        for (int mb = 0; mb < C::NB; ++mb) store4f(dst + 16 * mb, o[rt][mb] * inv);
+      for (int rt = 0; rt < C::NRT; ++rt) {
+        bf16x4 cv[C::NB];
+#pragma unroll
+        for (int mb = 0; mb < C::NB; ++mb) cv[mb] = cvn[mb];
+        const float inv = __builtin_amdgcn_rcpf(ln), fs = sn * inv;
+        if (rt + 1 < C::NRT) fetch(rt + 1);
+        char *srow = smem + (16 * rt + c) * OST + 2 * (64 * v + 4 * g);
+#pragma unroll
+        for (int mb = 0; mb < C::NB; ++mb) {
+          const f32x4 x = o[rt][mb] * inv + fs * (f32x4){to_f32(cv[mb][0]), to_f32(cv[mb][1]),
+                                                         to_f32(cv[mb][2]), to_f32(cv[mb][3])};
+          *(bf16x4 *)(srow + 32 * mb) = (bf16x4){(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        }
       }
+    };
+    if (self_lds)
+      stage_out([&](int frl) { return (const bf16 *)(selfb + frl * C::RB); });
+    else
+      stage_out([&](int frl) { return (const bf16 *)a.Cp + ((size_t)b * Tn + f0 + frl) * C::R; });
+    wait_lgkm0();
+    bar();
+    // Value wave v stores rows [48 v, 48 v + 48): two 512-byte rows per
+    // instruction, lane i covering bytes 16 (i mod 32) of row 2 j + i / 32.
+    const int row0 = qtile * C::ROWS;
+#pragma unroll 4
+    for (int j = 0; j < C::ROWS / 8; ++j) {
+      const int r = (C::ROWS / 4) * v + 2 * j + (lane >> 5);
+      const u32x4 x = *(const u32x4 *)(smem + r * OST + 16 * (lane & 31));
+      if (row0 + r < nrows)
+        *(u32x4 *)((char *)a.O + ((size_t)b * nrows + row0 + r) * (C::R * 2) + 16 * (lane & 31)) = x;
     }
   }
 }
@@ -767,8 +843,7 @@ hipError_t prefill_ws(int B, int T_len, int H, int s, float sl2, const void *qt,
                       hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   using C = WsCfg;
   const int tiles = (T_len * H + C::ROWS - 1) / C::ROWS;
-  int nst = (int)((159 * 1024 - C::EXTRA) / C::STAGE_B);
-  if (nst > C::MAX_NST) nst = C::MAX_NST;
+  const int nst = C::NST;
   const size_t lds = (size_t)nst * C::STAGE_B + C::EXTRA;
   allow_lds<prefill_ws_kernel>();
   // Masked scores are -inf before the fused scale-and-subtract, which needs
