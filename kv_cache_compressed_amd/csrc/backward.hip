@@ -647,46 +647,57 @@ __global__ __launch_bounds__(256) void sum_b_kernel(const float *part, int B, in
   out[i] = acc;
 }
 
-// out[ch] += column sums of x [M, N] (fp32), each workgroup a block of rows
-// (eight independent partial sums per thread keep eight loads in flight).
-// out[ch] = sum over the M rows of x[., ch]: workgroup (column block, row
-// chunk) sums its chunk, stores the partial (XCD-coherent), and the last
-// chunk of a column block to finish adds the chunks' partials in chunk
-// order (deterministic).  part: [chunks, N]; ctr: one int per column block,
-// zero on entry and again on exit.
+// out[N] = column sums of x [M, N] (fp32), in a fixed order.  Workgroup =
+// 64 columns x 4 row lanes, one chunk of rows (blockIdx.y): row lane q adds
+// rows q, q + 4, ... of the chunk into eight interleaved sums, and the four
+// lanes' totals meet in LDS, so each chunk's partial does not depend on
+// timing.  The last chunk of a column block to finish adds the partials in
+// chunk order, again spread over the four row lanes (lane q: chunks q,
+// q + 4, ...) and combined the same way.
 __global__ __launch_bounds__(256) void colsum_kernel(const float *x, int M, int N, int rows,
                                                      float *part, int *ctr, float *out) {
-  const int ch = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int ch = blockIdx.x * 64 + lane;
   const int chunks = gridDim.y;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)chunks * N * 4));
+  __shared__ float red[4][64];
+  __shared__ int last;
+  auto combine = [&](float v) {   // ((q0 + q1) + (q2 + q3)), in thread q == 0
+    red[q][lane] = v;
+    __syncthreads();
+    return (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  };
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (ch < N) {
     const int r0 = blockIdx.y * rows, r1 = min(M, r0 + rows);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int r = r0;
-    for (; r + 8 <= r1; r += 8)
+    int r = r0 + q;
+    for (; r + 28 < r1; r += 32)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[(size_t)(r + e) * N + ch];
-    for (; r < r1; ++r) acc[0] += x[(size_t)r * N + ch];
-    st_coh1(rp, (uint32_t)(((size_t)blockIdx.y * N + ch) * 4),
-            ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])));
+      for (int e = 0; e < 8; ++e) acc[e] += x[(size_t)(r + 4 * e) * N + ch];
+    for (int e = 0; r < r1; r += 4, ++e) acc[e & 7] += x[(size_t)r * N + ch];
   }
-  __shared__ int last;
+  const float mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  const float tot = combine(mine);
+  if (q == 0 && ch < N) st_coh1(rp, (uint32_t)(((size_t)blockIdx.y * N + ch) * 4), tot);
   __syncthreads();   // this workgroup's partial stores have completed
   if (threadIdx.x == 0) last = ctr_add(&ctr[blockIdx.x], 1) == chunks - 1;
   __syncthreads();
   if (!last) return;
+  float v = 0.0f;
   if (ch < N) {
-    float v = 0.0f;
-    for (int c0 = 0; c0 < chunks; c0 += 8) {
-      float pv[8];
+    for (int c0 = q; c0 < chunks; c0 += 4 * 16) {
+      float pv[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = ld_coh1(rp, (uint32_t)(((size_t)min(c0 + u, chunks - 1) * N + ch) * 4));
+      for (int u = 0; u < 16; ++u)
+        pv[u] = ld_coh1(rp, (uint32_t)(((size_t)min(c0 + 4 * u, chunks - 1) * N + ch) * 4));
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < chunks) v += pv[u];
+      for (int u = 0; u < 16; ++u)
+        if (c0 + 4 * u < chunks) v += pv[u];
     }
-    out[ch] = v;
   }
+  __syncthreads();   // every lane has read red[] above before it is reused
+  const float res = combine(v);
+  if (q == 0 && ch < N) out[ch] = res;
   if (threadIdx.x == 0) __hip_atomic_store(&ctr[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -722,117 +733,115 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *in, int R, i
 }
 
 // out[N1, N2] = A[M, N1]^T B[M, N2] (fp32).  M may be split over
-// workgroups (blockIdx.z): the splits' partial tiles then meet in the last
-// split of each tile to finish, which adds them in split order and stores
-// the result (part: tn_gemm_part_bytes; ctr: one int per tile, zero on
-// entry and again on exit).  Workgroup tile 64 x 64, each
-// wave 32 x 32 (2 x 2 MFMA tiles); per step 32 rows of A and B are staged in
-// LDS as two 16-row tiles each, and both operands come from transposing
-// reads (lane (g, c): column c of rows 4g..4g+3 of each tile -- the same
-// row order for A and B, so the products pair the right rows).
+// workgroups (blockIdx.z): each split then stores its partial tile, in row
+// order, into its own slab of `part` (split z at z * N1 * N2 floats), and
+// tn_sum_kernel adds the slabs in split order.  Workgroup tile 128 x 128,
+// each wave 64 x 64 (4 x 4 MFMA tiles); per step 32 rows of A and B are
+// staged in LDS as two 16-row tiles each (rows of 256 bytes), and both
+// operands come from transposing reads (lane (g, c): column c of rows
+// 4g..4g+3 of each tile -- the same row order for A and B, so the products
+// pair the right rows).
+constexpr int TN_T = 128;
 __global__ __launch_bounds__(256) void tn_gemm_kernel(const bf16 *A, int lda, const bf16 *Bm,
                                                       int ldb, int M, int N1, int N2, int mchunk,
-                                                      float *out, int ldo, float *part, int *ctr) {
-  __shared__ __attribute__((aligned(1024))) char lds[2][2 * 2048];   // [A|B][2 tiles x 2 blocks]
+                                                      float *out, int ldo, float *part) {
+  constexpr int RT = 16 * TN_T * 2;   // one 16-row tile: 16 rows x 256 bytes
+  __shared__ __attribute__((aligned(1024))) char lds[2][2 * RT];   // [A|B][2 row tiles]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n2_0 = blockIdx.x * 64, n1_0 = blockIdx.y * 64;
+  const int n2_0 = blockIdx.x * TN_T, n1_0 = blockIdx.y * TN_T;
   const int m_lo = blockIdx.z * mchunk, m_hi = min(M, m_lo + mchunk);
   const int wy = wave >> 1, wx = wave & 1;
-  f32x4 acc[2][2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // Staging: thread t moves 16 bytes of A and of B: row t/8 of the step,
-  // 8-column chunk t%8.
-  const int sr = tid >> 3, sc8 = (tid & 7) * 8;
-  auto fetch = [&](const bf16 *X, int ld, int n0, int N, int m0) {
-    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    const int m = m0 + sr, n = n0 + sc8;
-    if (m < m_hi && n < N) {
-      if (n + 8 <= N && ((((size_t)m * ld + n) & 7) == 0)) {
-        v = ldg16(X + (size_t)m * ld + n);
-      } else {
-        bf16x8 t8;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t8[e] = n + e < N ? X[(size_t)m * ld + n + e] : (bf16)0.0f;
-        v = __builtin_bit_cast(u32x4, t8);
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // Staging: thread t moves 32 bytes of A and of B: row t/8 of the step,
+  // 16-column chunk t%8 (two 8-column halves).  Rows past the split and
+  // columns past N are zero.
+  const int sr = tid >> 3, sc16 = (tid & 7) * 16;
+  auto fetch = [&](const bf16 *X, int ld, int n0, int N, int m0, u32x4 (&v)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v[h] = (u32x4){0u, 0u, 0u, 0u};
+      const int m = m0 + sr, n = n0 + sc16 + 8 * h;
+      if (m < m_hi && n < N) {
+        if (n + 8 <= N && ((((size_t)m * ld + n) & 7) == 0)) {
+          v[h] = ldg16(X + (size_t)m * ld + n);
+        } else {
+          bf16x8 t8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) t8[e] = n + e < N ? X[(size_t)m * ld + n + e] : (bf16)0.0f;
+          v[h] = __builtin_bit_cast(u32x4, t8);
+        }
       }
     }
-    return v;
   };
-  u32x4 va = fetch(A, lda, n1_0, N1, m_lo), vb = fetch(Bm, ldb, n2_0, N2, m_lo);
+  u32x4 va[2], vb[2];
+  fetch(A, lda, n1_0, N1, m_lo, va);
+  fetch(Bm, ldb, n2_0, N2, m_lo, vb);
   for (int m0 = m_lo; m0 < m_hi; m0 += 32) {
     __syncthreads();
-    const int to = (sr >> 4) * 2048 + tile_off(sr & 15, sc8 * 2);
-    *(u32x4 *)(lds[0] + to) = va;
-    *(u32x4 *)(lds[1] + to) = vb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int to = (sr >> 4) * RT + tile_off(sr & 15, (sc16 + 8 * h) * 2);
+      *(u32x4 *)(lds[0] + to) = va[h];
+      *(u32x4 *)(lds[1] + to) = vb[h];
+    }
     __syncthreads();
     if (m0 + 32 < m_hi) {
-      va = fetch(A, lda, n1_0, N1, m0 + 32);
-      vb = fetch(Bm, ldb, n2_0, N2, m0 + 32);
+      fetch(A, lda, n1_0, N1, m0 + 32, va);
+      fetch(Bm, ldb, n2_0, N2, m0 + 32, vb);
     }
-    bf16x8 fa[2], fb[2];
+    bf16x8 fa[4], fb[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const char *pa = lds[0] + tile_off(4 * g + (c >> 2), (32 * wy + 16 * i + 4 * (c & 3)) * 2);
+    for (int i = 0; i < 4; ++i) {
+      const char *pa = lds[0] + tile_off(4 * g + (c >> 2), (64 * wy + 16 * i + 4 * (c & 3)) * 2);
       fa[i] = join(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)pa),
-                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)(pa + 2048)));
-      const char *pb = lds[1] + tile_off(4 * g + (c >> 2), (32 * wx + 16 * i + 4 * (c & 3)) * 2);
+                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)(pa + RT)));
+      const char *pb = lds[1] + tile_off(4 * g + (c >> 2), (64 * wx + 16 * i + 4 * (c & 3)) * 2);
       fb[i] = join(__builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)pb),
-                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)(pb + 2048)));
+                   __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4 *)(pb + RT)));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma_k32(fa[i], fb[jj], acc[i][jj]);
+      for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mma_k32(fa[i], fb[jj], acc[i][jj]);
   }
   // acc[i][jj]: lane (g, c) holds column n2 = .. + c, rows n1 = .. + 4g + e.
-  auto store = [&](int i, int jj, f32x4 v) {
-    const int n2 = n2_0 + 32 * wx + 16 * jj + c;
+  float *dst = gridDim.z == 1 ? out : part + (size_t)blockIdx.z * N1 * N2;
+  const int ld = gridDim.z == 1 ? ldo : N2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int n1 = n1_0 + 32 * wy + 16 * i + 4 * g + e;
-      if (n1 < N1 && n2 < N2) out[(size_t)n1 * ldo + n2] = v[e];
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n2 = n2_0 + 64 * wx + 16 * jj + c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n1 = n1_0 + 64 * wy + 16 * i + 4 * g + e;
+        if (n1 < N1 && n2 < N2) dst[(size_t)n1 * ld + n2] = acc[i][jj][e];
+      }
     }
-  };
-  const int splits = gridDim.z;
-  if (splits == 1) {
+}
+
+// out[n1, n2] = sum over the splits, in split order, of the slabs of
+// tn_gemm_kernel (one thread per output element).
+__global__ __launch_bounds__(256) void tn_sum_kernel(const float *part, int splits, int N1, int N2,
+                                                     float *out, int ldo) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x, n = (size_t)N1 * N2;
+  if (i >= n) return;
+  float v = 0.0f;
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float pv[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < 8; ++u) pv[u] = part[(size_t)(s + u) * n + i];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) store(i, jj, acc[i][jj]);
-    return;
+    for (int u = 0; u < 8; ++u) v += pv[u];
   }
-  // Split over M: fp32 partial tiles in fragment order (XCD-coherent
-  // stores); the last split of the tile to finish adds them in split order.
-  const int tiles = gridDim.x * gridDim.y, tile = blockIdx.y * gridDim.x + blockIdx.x;
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((size_t)splits * tiles * 16384));
-  auto poff = [&](int sp, int f) {
-    return (uint32_t)(((((size_t)sp * tiles + tile) * 4 + wave) * 4 + f) * 64 + lane) * 16;
-  };
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) st_coh4(rp, poff(blockIdx.z, 2 * i + jj), acc[i][jj]);
-  __shared__ int last;
-  __syncthreads();   // this workgroup's partial stores have completed
-  if (tid == 0) last = ctr_add(&ctr[tile], 1) == splits - 1;
-  __syncthreads();
-  if (!last) return;
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-      f32x4 pv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = ld_coh4(rp, poff(min(s0 + u, splits - 1), f));
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < splits) v += pv[u];
-    }
-    store(f >> 1, f & 1, v);
-  }
-  if (tid == 0) __hip_atomic_store(&ctr[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (; s < splits; ++s) v += part[(size_t)s * n + i];
+  out[(i / N2) * ldo + i % N2] = v;
 }
 
 }  // namespace
@@ -908,16 +917,16 @@ hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b
 }
 
 namespace {
-int colsum_chunks(int M) { return M < 64 ? (M > 0 ? M : 1) : 64; }
+int colsum_chunks(int M) { return M < 256 ? (M > 0 ? M : 1) : 256; }
 }  // namespace
 
 size_t colsum_part_bytes(int M, int N) { return (size_t)colsum_chunks(M) * N * 4; }
-int colsum_counters(int N) { return (N + 255) / 256; }
+int colsum_counters(int N) { return (N + 63) / 64; }
 
 hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, float *out,
                          hipStream_t stream) {
   const int chunks = colsum_chunks(M), rows = (M + chunks - 1) / chunks;
-  dim3 grid((N + 255) / 256, (M + rows - 1) / rows);
+  dim3 grid((N + 63) / 64, (M + rows - 1) / rows);
   hipLaunchKernelGGL(colsum_kernel, grid, dim3(256), 0, stream, x, M, N, rows, part, ctr, out);
   return hipGetLastError();
 }
@@ -953,11 +962,11 @@ struct TnPlan {
 };
 TnPlan tn_plan(int M, int N1, int N2) {
   TnPlan p;
-  p.tiles = ((N1 + 63) / 64) * ((N2 + 63) / 64);
-  int splits = (1024 + p.tiles - 1) / p.tiles;   // about 1024 workgroups
-  const int maxs = (M + 255) / 256;              // at least 8 steps each
+  p.tiles = ((N1 + TN_T - 1) / TN_T) * ((N2 + TN_T - 1) / TN_T);
+  int splits = (768 + p.tiles - 1) / p.tiles;   // about three workgroups per CU
+  const int maxs = (M + 255) / 256;             // at least 8 steps each
   if (splits > maxs) splits = maxs;
-  if (splits > 32) splits = 32;                  // a short in-order sum of the partials
+  if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
   p.mchunk = ((M + splits - 1) / splits + 31) / 32 * 32;
   p.splits = (M + p.mchunk - 1) / p.mchunk;
@@ -967,16 +976,19 @@ TnPlan tn_plan(int M, int N1, int N2) {
 
 size_t tn_gemm_part_bytes(int M, int N1, int N2) {
   const TnPlan p = tn_plan(M, N1, N2);
-  return p.splits > 1 ? (size_t)p.splits * p.tiles * 16384 : 0;
+  return p.splits > 1 ? (size_t)p.splits * N1 * N2 * 4 : 0;
 }
-int tn_gemm_counters(int N1, int N2) { return ((N1 + 63) / 64) * ((N2 + 63) / 64); }
-
 hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
-                          float *out, int ldo, float *part, int *ctr, hipStream_t stream) {
+                          float *out, int ldo, float *part, hipStream_t stream) {
   const TnPlan p = tn_plan(M, N1, N2);
-  dim3 grid((N2 + 63) / 64, (N1 + 63) / 64, p.splits);
+  dim3 grid((N2 + TN_T - 1) / TN_T, (N1 + TN_T - 1) / TN_T, p.splits);
   hipLaunchKernelGGL(tn_gemm_kernel, grid, dim3(256), 0, stream, (const bf16 *)A, lda,
-                     (const bf16 *)Bm, ldb, M, N1, N2, p.mchunk, out, ldo, part, ctr);
+                     (const bf16 *)Bm, ldb, M, N1, N2, p.mchunk, out, ldo, part);
+  if (p.splits > 1) {
+    const size_t n = (size_t)N1 * N2;
+    hipLaunchKernelGGL(tn_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)part, p.splits, N1, N2, out, ldo);
+  }
   return hipGetLastError();
 }
 

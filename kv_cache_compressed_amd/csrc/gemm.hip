@@ -398,7 +398,8 @@ hipError_t run_gemm(const T *A, int lda, const BSeg &bs, int M, int N, int K, Ep
   if (M <= 0 || N <= 0) return hipSuccess;
   // Stored outputs of large bf16 products take the 256 x 256 tile; fp32
   // read-modify-write epilogues stay here (they outweigh its gain).
-  if constexpr (sizeof(T) == 2 && (std::is_same_v<Epi, EpiStore<bf16>> || std::is_same_v<Epi, EpiProj<bf16>>))
+  if constexpr (sizeof(T) == 2 && (std::is_same_v<Epi, EpiStore<bf16>> || std::is_same_v<Epi, EpiProj<bf16>> ||
+                                   std::is_same_v<Epi, EpiAccF32>))
     if (gemm_big_supported(M, N, K) && epi.four_aligned())
       return launch_gemm_big(A, lda, bs, M, N, K, epi, stream);
   if (M <= 128 || sizeof(T) == 4) {

@@ -201,5 +201,7 @@ template hipError_t launch_gemm_big<EpiStore<bf16>>(const bf16 *, int, const BSe
                                                     EpiStore<bf16>, hipStream_t);
 template hipError_t launch_gemm_big<EpiProj<bf16>>(const bf16 *, int, const BSeg &, int, int, int,
                                                    EpiProj<bf16>, hipStream_t);
+template hipError_t launch_gemm_big<EpiAccF32>(const bf16 *, int, const BSeg &, int, int, int,
+                                               EpiAccF32, hipStream_t);
 
 }  // namespace mtla

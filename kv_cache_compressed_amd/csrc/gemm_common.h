@@ -37,6 +37,14 @@ struct EpiAccF32 {
     float *p = out + (size_t)m * ldc + n;
     *p = add ? *p + v : v;
   }
+  // Columns n .. n+3 of row m (n + 3 < N, n a multiple of 4).
+  __device__ void four(int m, int n, f32x4 v) const {
+    f32x4 *p = (f32x4 *)(out + (size_t)m * ldc + n);
+    *p = add ? *p + v : v;
+  }
+  // The 256 x 256 tile takes stored outputs only: its epilogue, one
+  // workgroup per CU, would wait out every read of an accumulation in turn.
+  bool four_aligned() const { return !add && ldc % 4 == 0 && ((uintptr_t)out & 15) == 0; }
 };
 
 struct EpiBiasF32 {

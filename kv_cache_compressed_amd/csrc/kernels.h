@@ -184,7 +184,7 @@ hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b
                                 void *dab, float *dc32, void *cb, float *dPpart, int rows,
                                 float *dPtab, hipStream_t stream);
 // out[N] = column sums of x [M, N] (fp32), partial sums over row chunks
-// added in chunk order: part holds colsum_part_bytes, ctr colsum_counters
+// added in a fixed order: part holds colsum_part_bytes, ctr colsum_counters
 // ints (zero on entry, zero again on exit).
 hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, float *out,
                          hipStream_t stream);
@@ -197,11 +197,10 @@ hipError_t launch_zero_i32(int *p, size_t n, hipStream_t stream);
 hipError_t launch_transpose(const void *in, int R, int C, int ldi, void *out, int ldo,
                             hipStream_t stream);
 // out[N1, N2] (fp32, row stride ldo) = A[M, N1]^T B[M, N2] (bf16), split
-// over M; the splits' partials are added in split order.
+// over M; the splits' partials (in part) are added in split order.
 hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
-                          float *out, int ldo, float *part, int *ctr, hipStream_t stream);
-// Partials (bytes) and counters launch_tn_gemm needs for this shape.
+                          float *out, int ldo, float *part, hipStream_t stream);
+// Partials (bytes) launch_tn_gemm needs for this shape.
 size_t tn_gemm_part_bytes(int M, int N1, int N2);
-int tn_gemm_counters(int N1, int N2);
 
 }  // namespace mtla

@@ -176,7 +176,7 @@ struct BwdWs {
   HeadsWs f;
   size_t O_, lse, WOt, WKVt, Whct, Wdkvt, WQt, dO, D, dKVc, dKRc, dKV, dKRh, dQ, dCp, da32, dab,
       dc32, cb, dcb, dX32, dPpart, red_part, red_ctr, total;
-  int nctr;   // ints at red_ctr: counters of the ordered reductions (zero between uses)
+  int nctr;   // ints at red_ctr: counters of the bias column sums (zero between uses)
 };
 
 BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
@@ -214,18 +214,12 @@ BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
   const size_t tp[6] = {mtla::tn_gemm_part_bytes(Mi, di, HDi), mtla::tn_gemm_part_bytes(Mi, HDi, di),
                         mtla::tn_gemm_part_bytes(Mi, HDi, ri), mtla::tn_gemm_part_bytes(Mi, HDi, ri),
                         mtla::tn_gemm_part_bytes(Mi, ri, ri), mtla::tn_gemm_part_bytes(Mi, ri, di)};
-  const int tc[6] = {mtla::tn_gemm_counters(di, HDi), mtla::tn_gemm_counters(HDi, di),
-                     mtla::tn_gemm_counters(HDi, ri), mtla::tn_gemm_counters(HDi, ri),
-                     mtla::tn_gemm_counters(ri, ri), mtla::tn_gemm_counters(ri, di)};
   size_t pmax = mtla::colsum_part_bytes(Mi, ri);
-  int cmax = mtla::colsum_counters(ri);
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < 6; ++i)
     if (tp[i] > pmax) pmax = tp[i];
-    if (tc[i] > cmax) cmax = tc[i];
-  }
   w.red_part = take(pmax);
-  w.nctr = cmax;
-  w.red_ctr = take((size_t)cmax * 4);
+  w.nctr = mtla::colsum_counters(ri);
+  w.red_ctr = take((size_t)w.nctr * 4);
   w.total = off;
   return w;
 }
@@ -707,22 +701,24 @@ mtla_status prefill_unabsorbed_backward_impl(
          "dc");
   LAUNCH(mtla::launch_f32_to_bf16(F(ws.dc32), (size_t)M * r, P(ws.dcb), s), "dc to bf16");
   // inputs
-  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), d, false, s),
-         "dX from the latent map");
-  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, true, s),
+  // The query map's product (K = H d_h) stores and the latent map's (K = r)
+  // adds: the longer product then qualifies for the large-tile kernel.
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, false, s),
          "dX from the query map");
+  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), d, true, s),
+         "dX from the latent map");
   LAUNCH(mtla::launch_f32_to_bf16(F(ws.dX32), (size_t)M * d, dX, s), "dX to bf16");
   // weight gradients (each product's partials added in split order)
-  LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, rpart, rctr, s), "dW_O");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, rpart, rctr, s), "dW_Q");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, rpart, rctr, s),
+  LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, rpart, s), "dW_O");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, rpart, s), "dW_Q");
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, rpart, s),
          "dW_K");
   LAUNCH(mtla::launch_tn_gemm((char *)P(ws.dKV) + (size_t)HD * 2, 2 * HD, Cp, r, M, HD, r, gr->dW_V,
-                              r, rpart, rctr, s),
+                              r, rpart, s),
          "dW_V");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, rpart, rctr, s),
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, rpart, s),
          "dW_hc");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, rpart, rctr, s),
+  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, rpart, s),
          "dW_dkv");
   return ok();
 }
