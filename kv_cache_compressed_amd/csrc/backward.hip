@@ -701,16 +701,6 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float *x, int M, int 
   if (threadIdx.x == 0) __hip_atomic_store(&ctr[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *x, size_t n, bf16 *y) {
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= n) return;
-  if (i + 4 <= n) {
-    store4f(y + i, *(const f32x4 *)(x + i));
-  } else {
-    for (size_t k = i; k < n; ++k) y[k] = (bf16)x[k];
-  }
-}
-
 __global__ __launch_bounds__(256) void zero_f32_kernel(float *p, size_t n) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -928,12 +918,6 @@ hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, fl
   const int chunks = colsum_chunks(M), rows = (M + chunks - 1) / chunks;
   dim3 grid((N + 63) / 64, (M + rows - 1) / rows);
   hipLaunchKernelGGL(colsum_kernel, grid, dim3(256), 0, stream, x, M, N, rows, part, ctr, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_f32_to_bf16(const float *x, size_t n, void *y, hipStream_t stream) {
-  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream,
-                     x, n, (bf16 *)y);
   return hipGetLastError();
 }
 

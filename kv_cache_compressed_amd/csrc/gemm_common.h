@@ -47,6 +47,18 @@ struct EpiAccF32 {
   bool four_aligned() const { return !add && ldc % 4 == 0 && ((uintptr_t)out & 15) == 0; }
 };
 
+// bf16 output = an fp32 term already computed + the product (the last of a
+// sum of products, rounded once).
+struct EpiAddBf16 {
+  const float *acc;
+  bf16 *out;
+  int ldc;
+  __device__ void operator()(int m, int n, float v) const {
+    const size_t i = (size_t)m * ldc + n;
+    out[i] = (bf16)(acc[i] + v);
+  }
+};
+
 struct EpiBiasF32 {
   float *out;
   const void *bias;

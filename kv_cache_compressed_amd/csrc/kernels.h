@@ -26,6 +26,11 @@ hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1,
 hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, int ldb, int M, int N,
                            int K, float *out, int ldc, bool add, hipStream_t stream);
 
+// out[M, N] (bf16, row stride ldc) = acc[M, N] (fp32, same stride) + A[M, K] B[N, K]^T
+// (bf16 operands).
+hipError_t launch_gemm_add_bf16(const void *A, int lda, const void *Bm, int ldb, int M, int N, int K,
+                                const float *acc, void *out, int ldc, hipStream_t stream);
+
 // out[M, N] (fp32) = A[M, K] [B1; B2]^T (columns < N1 from B1's rows).
 hipError_t launch_gemm_f32_2(int dtype, const void *A, int lda, const void *B1, const void *B2,
                              int N1, int ldb, int M, int N, int K, float *out, int ldc,
@@ -190,7 +195,6 @@ hipError_t launch_colsum(const float *x, int M, int N, float *part, int *ctr, fl
                          hipStream_t stream);
 size_t colsum_part_bytes(int M, int N);
 int colsum_counters(int N);
-hipError_t launch_f32_to_bf16(const float *x, size_t n, void *y, hipStream_t stream);
 hipError_t launch_zero_f32(float *p, size_t n, hipStream_t stream);
 hipError_t launch_zero_i32(int *p, size_t n, hipStream_t stream);
 // out[C, R] (row stride ldo) = in[R, C]^T (bf16, row stride ldi).

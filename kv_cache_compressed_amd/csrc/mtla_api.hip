@@ -697,17 +697,17 @@ mtla_status prefill_unabsorbed_backward_impl(
                                     w->gate_pos_rows, gr->dgate_pos, s),
          "group scan and gate backward");
   LAUNCH(mtla::launch_colsum(F(ws.da32), M, r, rpart, rctr, gr->db_hc, s), "db");
-  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), r, true, s),
+  LAUNCH(mtla::launch_gemm_add_bf16(P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), P(ws.dcb), r,
+                                    s),
          "dc");
-  LAUNCH(mtla::launch_f32_to_bf16(F(ws.dc32), (size_t)M * r, P(ws.dcb), s), "dc to bf16");
   // inputs
-  // The query map's product (K = H d_h) stores and the latent map's (K = r)
-  // adds: the longer product then qualifies for the large-tile kernel.
+  // The query map's product (K = H d_h) is stored in fp32 and the latent
+  // map's (K = r) added to it, the sum rounded once to bf16: the longer
+  // product then qualifies for the large-tile kernel.
   LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, false, s),
          "dX from the query map");
-  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), d, true, s),
+  LAUNCH(mtla::launch_gemm_add_bf16(P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), dX, d, s),
          "dX from the latent map");
-  LAUNCH(mtla::launch_f32_to_bf16(F(ws.dX32), (size_t)M * d, dX, s), "dX to bf16");
   // weight gradients (each product's partials added in split order)
   LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, rpart, s), "dW_O");
   LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, rpart, s), "dW_Q");
