@@ -183,8 +183,12 @@ bool gemm_big_supported(int M, int N, int K) {
   // projection of the parallel form (65,536 rows, 2,560 columns) takes
   // 13-30 us less than in gemm_nt_kernel; at K = 2048 the output projection
   // 172 against 206 us.
+  // The column tiles must also be at least three quarters used: the
+  // rotary inputs' product (N = 288) took 82 us on two 256-wide tiles against
+  // 43 us in gemm_nt_kernel.
+  const int ntiles = (N + 255) / 256;
   return M >= 2048 && N >= 256 && K >= MTLA_GEMM_BIG_MIN_K && K % 64 == 0 &&
-         (size_t)((M + 255) / 256) * ((N + 255) / 256) >= 256;
+         4 * N >= 3 * 256 * ntiles && (size_t)((M + 255) / 256) * ntiles >= 256;
 }
 
 template <class Epi>
