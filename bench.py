@@ -552,6 +552,19 @@ def roofline(rec: dict, workload: str) -> dict:
             "avg_kernel_us": round(rec["attn_ms"] * 1e3, 3)}
 
 
+def mfma_roofline(rec: dict, kernel: str, traffic_workload=None) -> dict:
+    """Roofline block of a bf16 attention kernel (bound by the matrix cores):
+    algorithmic flops on visible pairs per launch over the kernel's HIP-event
+    time, against the dense bf16 peak; traffic from the kernel's counter
+    summary when one is valid for its sources."""
+    tr = measured_traffic(traffic_workload, kernel) if traffic_workload else None
+    traffic = round(tr["fetch_bytes_per_launch"] + tr["write_bytes_per_launch"]) if tr else None
+    return {"bound": "mfma", "kernel": kernel, "achieved": round(rec["attn_tflops"], 1),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(rec["attn_tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "flops_per_launch": rec["attn_flops"], "avg_kernel_us": round(rec["attn_ms"] * 1e3, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -591,11 +604,11 @@ def main():
     if args.only == "prefill_b16_t4096_backward":
         print(json.dumps(run_backward(args.steps, args.warmup)), flush=True)
         return
-    if args.only == "prefill_b16_t4096_per_head":
-        print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup)), flush=True)
-        return
-    if args.only == "prefill_b8_t4096_dh128_per_head":
-        print(json.dumps(run_prefill_unabsorbed(args.steps, args.warmup, wide=True)), flush=True)
+    if args.only in ("prefill_b16_t4096_per_head", "prefill_b8_t4096_dh128_per_head"):
+        rec = run_prefill_unabsorbed(args.steps, args.warmup,
+                                     wide=args.only == "prefill_b8_t4096_dh128_per_head")
+        rec["roofline"] = mfma_roofline(rec, "heads_attn_kernel")
+        print(json.dumps(rec), flush=True)
         return
     if args.only == "prefill_b8_t4096_dh128_backward":
         print(json.dumps(run_backward(args.steps, args.warmup, wide=True)), flush=True)
@@ -608,8 +621,8 @@ def main():
                "llm_decode_b128_ctx32768": 5, "prefill_b16_t4096": 4}[args.only]
         rec = run_prefill(args.steps, args.warmup) if cfg == 4 else \
             run_decode(cfg, args.steps, args.warmup)
-        if cfg != 4:
-            rec["roofline"] = roofline(rec, args.only)
+        rec["roofline"] = roofline(rec, args.only) if cfg != 4 else \
+            mfma_roofline(rec, "prefill_ws_kernel", "prefill_b16_t4096")
         print(json.dumps(rec), flush=True)
         return
     log("llm_decode_b128_ctx32768 ...")
@@ -629,27 +642,24 @@ def main():
     torch.cuda.empty_cache()
     log("prefill_b16_t4096 ...")
     p = extra["prefill_b16_t4096"] = run_prefill()
-    p["attn_mfma_frac"] = p["attn_tflops"] / BF16_PEAK_TFLOPS
-    ptr = measured_traffic("prefill_b16_t4096", "prefill_ws_kernel")
-    if ptr:
-        p["attn_hbm_traffic_bytes"] = round(ptr["fetch_bytes_per_launch"] + ptr["write_bytes_per_launch"])
+    p["roofline"] = mfma_roofline(p, "prefill_ws_kernel", "prefill_b16_t4096")
     log(f"  prefill: attention {p['attn_ms']:.3f} ms {p['attn_tflops']:.0f} TFLOP/s "
-        f"({p['attn_mfma_frac']:.1%}), forward {p['forward_ms']:.3f} ms")
+        f"({p['roofline']['frac']:.1%}), forward {p['forward_ms']:.3f} ms")
     log("prefill_b16_t4096_per_head ...")
     u = extra["prefill_b16_t4096_per_head"] = run_prefill_unabsorbed()
-    u["attn_mfma_frac"] = u["attn_tflops"] / BF16_PEAK_TFLOPS
+    u["roofline"] = mfma_roofline(u, "heads_attn_kernel")
     log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
-        f"({u['attn_mfma_frac']:.1%}), forward {u['forward_ms']:.3f} ms")
+        f"({u['roofline']['frac']:.1%}), forward {u['forward_ms']:.3f} ms")
     log("prefill_b16_t4096_backward ...")
     bw = extra["prefill_b16_t4096_backward"] = run_backward()
     log(f"  backward (per-head form, forward recomputed): {bw['step_ms']:.3f} ms")
     torch.cuda.empty_cache()
     log("prefill_b8_t4096_dh128 (per-head form and backward at d_h = 128) ...")
     uw = extra["prefill_b8_t4096_dh128_per_head"] = run_prefill_unabsorbed(wide=True)
-    uw["attn_mfma_frac"] = uw["attn_tflops"] / BF16_PEAK_TFLOPS
+    uw["roofline"] = mfma_roofline(uw, "heads_attn_kernel")
     bww = extra["prefill_b8_t4096_dh128_backward"] = run_backward(wide=True)
     log(f"  d_h=128 per-head: attention {uw['attn_ms']:.3f} ms {uw['attn_tflops']:.0f} TFLOP/s "
-        f"({uw['attn_mfma_frac']:.1%}), forward {uw['forward_ms']:.3f} ms; backward {bww['step_ms']:.3f} ms")
+        f"({uw['roofline']['frac']:.1%}), forward {uw['forward_ms']:.3f} ms; backward {bww['step_ms']:.3f} ms")
     log("decode_b32_ctx2048_s1 (the MLA reduction, one slot per frame) ...")
     m1 = extra["decode_b32_ctx2048_s1"] = run_decode(2, 50, 10, stride=1)
     m1["cache_bytes_vs_s2"] = m1["cache_bytes"] / c2["cache_bytes"]
