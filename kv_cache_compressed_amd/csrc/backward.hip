@@ -956,18 +956,46 @@ TnPlan tn_plan(int M, int N1, int N2) {
   p.splits = (M + p.mchunk - 1) / p.mchunk;
   return p;
 }
+// The 256 x 256 tile: about one workgroup per CU, at least 64 frames each.
+TnPlan tn_big_plan(int M, int N1, int N2) {
+  TnPlan p;
+  p.tiles = ((N1 + 255) / 256) * ((N2 + 255) / 256);
+  int splits = (256 + p.tiles - 1) / p.tiles;
+  const int maxs = (M + 63) / 64;
+  if (splits > maxs) splits = maxs;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  p.mchunk = ((M + splits - 1) / splits + 63) / 64 * 64;
+  p.splits = (M + p.mchunk - 1) / p.mchunk;
+  return p;
+}
 }  // namespace
 
 size_t tn_gemm_part_bytes(int M, int N1, int N2) {
   const TnPlan p = tn_plan(M, N1, N2);
-  return p.splits > 1 ? (size_t)p.splits * N1 * N2 * 4 : 0;
+  size_t b = p.splits > 1 ? (size_t)p.splits * N1 * N2 * 4 : 0;
+  if (tn_big_supported(N1, N2)) {
+    const TnPlan q = tn_big_plan(M, N1, N2);
+    if (q.splits > 1 && (size_t)q.splits * N1 * N2 * 4 > b) b = (size_t)q.splits * N1 * N2 * 4;
+  }
+  return b;
 }
 hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
                           float *out, int ldo, float *part, hipStream_t stream) {
-  const TnPlan p = tn_plan(M, N1, N2);
-  dim3 grid((N2 + TN_T - 1) / TN_T, (N1 + TN_T - 1) / TN_T, p.splits);
-  hipLaunchKernelGGL(tn_gemm_kernel, grid, dim3(256), 0, stream, (const bf16 *)A, lda,
-                     (const bf16 *)Bm, ldb, M, N1, N2, p.mchunk, out, ldo, part);
+  // The large tile reads 16-byte row pieces with direct loads: it needs
+  // 16-byte aligned rows.
+  const bool big = tn_big_supported(N1, N2) && lda % 8 == 0 && ldb % 8 == 0 &&
+                   ((uintptr_t)A & 15) == 0 && ((uintptr_t)Bm & 15) == 0;
+  const TnPlan p = big ? tn_big_plan(M, N1, N2) : tn_plan(M, N1, N2);
+  if (big) {
+    const hipError_t e =
+        launch_tn_big(A, lda, Bm, ldb, M, N1, N2, p.mchunk, p.splits, out, ldo, part, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    dim3 grid((N2 + TN_T - 1) / TN_T, (N1 + TN_T - 1) / TN_T, p.splits);
+    hipLaunchKernelGGL(tn_gemm_kernel, grid, dim3(256), 0, stream, (const bf16 *)A, lda,
+                       (const bf16 *)Bm, ldb, M, N1, N2, p.mchunk, out, ldo, part);
+  }
   if (p.splits > 1) {
     const size_t n = (size_t)N1 * N2;
     hipLaunchKernelGGL(tn_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,

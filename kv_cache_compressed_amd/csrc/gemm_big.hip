@@ -35,6 +35,7 @@ constexpr int GB_LPW = 2 * GB_ROWT / 4;          // loads per wave per stage
 constexpr int GB_LDS = GB_NST * GB_STAGE;
 
 typedef bf16x8 GbFrag[8];
+typedef __attribute__((address_space(3))) bf16x4 gb_lds_b4;
 
 template <class Epi>
 __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict__ A, int lda,
@@ -174,7 +175,180 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
   }
 }
 
+// out[N1, N2] (fp32) = A[M, N1]^T B[M, N2] (bf16, rows of both operands
+// indexed by the frame m, the contraction index), for the weight gradients of
+// the backward.  The same tile as gemm_big_kernel -- 256 x 256 per
+// workgroup, 128 x 128 per wave in AGPRs, a ring of 4 LDS stages of 32
+// frames filled by direct loads, stage kt+1's fragments read while stage kt's
+// products run -- except that both operands are column slices of row-major
+// [M, N] arrays, so each fragment is two transposing reads (lane (g, c):
+// column c of rows 4g..4g+3 of each 16-row tile; the same row order for A and
+// B, so the products pair the right frames).  Frames are split over
+// blockIdx.z (mchunk each); split z stores its partial product, in row order,
+// into slab z of `part` (N1 x N2 floats), or into `out` when there is one
+// split.  Needs N1, N2 multiples of 32 and 16-byte aligned rows.
+constexpr int TB_TILE = 16 * 512;       // 16 frames x 256 columns of bf16
+constexpr int TB_OP = 2 * TB_TILE;      // 32 frames of one operand
+constexpr int TB_STAGE = 2 * TB_OP;     // A then B: 32 KB
+constexpr int TB_NST = 4;
+constexpr int TB_LPW = 2 * 2 * 8 / 4;   // 1 KB blocks per wave per stage
+constexpr int TB_LDS = TB_NST * TB_STAGE;
+
+__global__ __launch_bounds__(256, 1) void tn_big_kernel(const bf16 *__restrict__ A, int lda,
+                                                        const bf16 *__restrict__ Bm, int ldb, int M,
+                                                        int N1, int N2, int mchunk, float *out,
+                                                        int ldo, float *part) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int wy = wave >> 1, wx = wave & 1;
+  const int n1_0 = blockIdx.y * 256, n2_0 = blockIdx.x * 256;
+  const int m_lo = blockIdx.z * mchunk, m_hi = min(M, m_lo + mchunk);
+  // Steps of 32 frames, rounded up to even so that the two fragment sets
+  // alternate in a fixed pattern; a step past the split is all masked.
+  const int KT = ((m_hi - m_lo + 63) / 64) * 2;
+
+  // This wave's 1 KB blocks of a stage: i < 4 are A's, i >= 4 B's, block
+  // blk = wave + 4 (i mod 4) in [0, 16) of its operand being 16-frame tile
+  // blk / 8 and 64-byte column segment blk mod 8.  Lane l copies frame l / 4
+  // of the tile.  Frames past the split read its last frame and segments past
+  // N the last whole one (valid memory; their products are masked or never
+  // stored).
+  const char *cp[TB_LPW];
+  int q[TB_LPW], rt[TB_LPW], ld[TB_LPW], doff[TB_LPW];
+#pragma unroll
+  for (int i = 0; i < TB_LPW; ++i) {
+    const int blk = wave + 4 * (i & 3);
+    const bool isb = i >= 4;
+    const int N = isb ? N2 : N1, n0 = isb ? n2_0 : n1_0;
+    rt[i] = blk >> 3;
+    q[i] = min(blk & 7, (N - n0) / 32 - 1);   // source segment (clamped)
+    ld[i] = isb ? ldb : lda;
+    cp[i] = (const char *)((isb ? Bm : A) + n0);
+    doff[i] = (isb ? TB_OP : 0) + rt[i] * TB_TILE + (blk & 7) * 1024;   // the block's own slot
+  }
+  auto issue = [&](int kt) {
+    char *sb = smem + (kt % TB_NST) * TB_STAGE;
+#pragma unroll
+    for (int i = 0; i < TB_LPW; ++i) {
+      const int m = min(m_lo + 32 * kt + 16 * rt[i] + (lane >> 2), m_hi - 1);
+      dma_block(cp[i] + (size_t)m * ld[i] * 2, q[i], sb + doff[i]);
+    }
+  };
+  // Fragments of stage kt: A columns 128 wy + 16 i, B columns 128 wx + 16 j;
+  // in the last step, frames past the split are zeroed in both.
+  auto frags = [&](int kt, GbFrag &fa, GbFrag &fb) {
+    const char *sb = smem + (kt % TB_NST) * TB_STAGE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const char *pa = sb + tile_off(4 * g + (c >> 2), (128 * wy + 16 * i + 4 * (c & 3)) * 2);
+      const char *pb = sb + TB_OP + tile_off(4 * g + (c >> 2), (128 * wx + 16 * i + 4 * (c & 3)) * 2);
+      const bf16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((gb_lds_b4 *)pa);
+      const bf16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((gb_lds_b4 *)(pa + TB_TILE));
+      const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((gb_lds_b4 *)pb);
+      const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((gb_lds_b4 *)(pb + TB_TILE));
+      fa[i] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      fb[i] = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const int valid = m_hi - (m_lo + 32 * kt);
+    if (valid < 32) {
+      // Element e of a fragment is frame (e < 4 ? 0 : 16) + 4 g + (e mod 4):
+      // clear the 16-bit halves of the frames past the split.
+      u32x4 mk;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int f0 = (w < 2 ? 0 : 16) + 4 * g + 2 * (w & 1);
+        mk[w] = (f0 < valid ? 0xffffu : 0u) | (f0 + 1 < valid ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        fa[i] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, fa[i]) & mk);
+        fb[i] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, fb[i]) & mk);
+      }
+    }
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int pro = min(TB_NST, KT);
+  for (int kt = 0; kt < pro; ++kt) issue(kt);
+  int last = pro - 1;
+  wait_stages<TB_LPW>(last - min(1, KT - 1));
+  bar();
+  GbFrag fa0, fb0, fa1, fb1;
+  frags(0, fa0, fb0);
+  wait_lgkm0();
+
+  // Iteration kt: stage kt+1's fragments into the other set, refill stage
+  // kt's slot with stage kt + NST (its fragments were read in iteration
+  // kt-1, before the last barrier), the 64 products of stage kt, stage kt+2
+  // resident, then the barrier.
+  auto iter = [&](int kt, GbFrag &fa, GbFrag &fb, GbFrag &na, GbFrag &nb) {
+    const bool refill = kt + TB_NST < KT;
+    if (refill) last = kt + TB_NST;
+    if (kt + 1 < KT) frags(kt + 1, na, nb);
+    char *rs = smem + (kt % TB_NST) * TB_STAGE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (refill) {
+        const int m = min(m_lo + 32 * (kt + TB_NST) + 16 * rt[i] + (lane >> 2), m_hi - 1);
+        dma_block(cp[i] + (size_t)m * ld[i] * 2, q[i], rs + doff[i]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mma_k32(fb[j], fa[i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kt + 2 < KT) wait_stages<TB_LPW>(last - (kt + 2));
+    wait_lgkm0();
+    bar();
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    iter(kt, fa0, fb0, fa1, fb1);
+    iter(kt + 1, fa1, fb1, fa0, fb0);
+  }
+
+  // acc[i][j]: lane (g, c) holds n1 = 128 wy + 16 i + c and the four
+  // consecutive n2 = 128 wx + 16 j + 4 g .. + 3.  Rows pass through the wave's
+  // own LDS block (the ring is idle after the last barrier), 16 at a time,
+  // and are stored as whole row runs.
+  float *dst = gridDim.z == 1 ? out : part + (size_t)blockIdx.z * N1 * N2;
+  const int ldd = gridDim.z == 1 ? ldo : N2;
+  constexpr int SROW = 528;
+  char *stg = smem + wave * 16 * SROW;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *(f32x4 *)(stg + c * SROW + (16 * j + 4 * g) * 4) = acc[i][j];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 2 * k + (lane >> 5), cc = 4 * (lane & 31);
+      const f32x4 v = *(const f32x4 *)(stg + rr * SROW + cc * 4);
+      const int n1 = n1_0 + 128 * wy + 16 * i + rr, n2 = n2_0 + 128 * wx + cc;
+      if (n1 < N1 && n2 < N2) *(f32x4 *)(dst + (size_t)n1 * ldd + n2) = v;
+    }
+  }
+}
+
 }  // namespace
+
+bool tn_big_supported(int N1, int N2) {
+  return N1 % 32 == 0 && N2 % 32 == 0 && ((N1 + 255) / 256) * ((N2 + 255) / 256) >= 4;
+}
+
+hipError_t launch_tn_big(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
+                         int mchunk, int splits, float *out, int ldo, float *part,
+                         hipStream_t stream) {
+  allow_lds<tn_big_kernel>();
+  dim3 grid((N2 + 255) / 256, (N1 + 255) / 256, splits);
+  hipLaunchKernelGGL(tn_big_kernel, grid, dim3(256), TB_LDS, stream, (const bf16 *)A, lda,
+                     (const bf16 *)Bm, ldb, M, N1, N2, mchunk, out, ldo, part);
+  return hipGetLastError();
+}
 
 bool gemm_big_supported(int M, int N, int K) {
   // Enough 256 x 256 tiles to fill the compute units, and K long enough

@@ -206,5 +206,12 @@ hipError_t launch_tn_gemm(const void *A, int lda, const void *Bm, int ldb, int M
                           float *out, int ldo, float *part, hipStream_t stream);
 // Partials (bytes) launch_tn_gemm needs for this shape.
 size_t tn_gemm_part_bytes(int M, int N1, int N2);
+// The 256 x 256 tile of A^T B (csrc/gemm_big.hip): shapes it takes, and the
+// launch of its product over `splits` frame chunks of mchunk (slab z of part
+// at z * N1 * N2 floats, or out when splits == 1).
+bool tn_big_supported(int N1, int N2);
+hipError_t launch_tn_big(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
+                         int mchunk, int splits, float *out, int ldo, float *part,
+                         hipStream_t stream);
 
 }  // namespace mtla
