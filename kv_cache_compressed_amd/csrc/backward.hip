@@ -130,10 +130,11 @@ struct AttnBwdArgs {
   float *dKRc;       // [B*nS, H, DR]:   key-role dK^R per head
   bf16 *dKV;         // [B*T, 2*H*DH]: total dK | dV of every frame
   float *dKRh;       // [B*T, H, DR]:   total dK^R per head of every frame
-  bf16 *dQ;          // [B*T, H*DH]
+  bf16 *dQ;          // [B*T, H*DH] at row stride ldq
   bf16 *dQR;         // [B*T, H, DR]
   int B, T, H, s, nS, nK, tiles;
   float sl2, scale;
+  int ldq;
 };
 
 // ---------------------------------------------------------------------------
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(256, C::OCC) void attn_bwd_dq_kernel(AttnBwdArgs a)
     const int fr = rw + 16 * qi + c;
     if (fr < Tn) {
       const size_t row = (size_t)b * Tn + fr;
-      bf16 *dst = a.dQ + row * H * DH + h * DH + 4 * g;
+      bf16 *dst = a.dQ + row * a.ldq + h * DH + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) store4f(dst + 16 * mb, dq[qi][mb]);
       bf16 *dr = a.dQR + (row * H + h) * DR + 4 * g;
@@ -845,13 +846,13 @@ template <class C>
 hipError_t attn_bwd_t(int B, int T, int H, int s, float scale, const void *q, const void *QR,
                       const void *KV, const void *KR, const void *dO, const float *lse,
                       const float *D, float *dKVc, float *dKRc, void *dKV, float *dKRh, void *dQ,
-                      void *dQR, hipStream_t stream) {
+                      void *dQR, int ldq, hipStream_t stream) {
   const int nS = (T + s - 1) / s, nK = (T - 1) / s;
   float sl2 = scale * kLog2e;
   if (!(sl2 >= FLT_MIN)) sl2 = FLT_MIN;
   AttnBwdArgs a{(const bf16 *)q, (const bf16 *)QR, (const bf16 *)KV, (const bf16 *)KR,
                 (const bf16 *)dO, lse, D, dKVc, dKRc, (bf16 *)dKV, dKRh, (bf16 *)dQ,
-                (bf16 *)dQR, B, T, H, s, nS, nK, (T + C::GROWS - 1) / C::GROWS, sl2, scale};
+                (bf16 *)dQR, B, T, H, s, nS, nK, (T + C::GROWS - 1) / C::GROWS, sl2, scale, ldq};
   const size_t lds = (size_t)C::NST * C::STAGE_B + 1024;
   allow_lds<attn_bwd_dkdv_kernel<C>>();
   allow_lds<attn_bwd_dq_kernel<C>>();
@@ -869,12 +870,12 @@ hipError_t attn_bwd_t(int B, int T, int H, int s, float scale, const void *q, co
 hipError_t launch_attn_bwd(int B, int T, int H, int d_h, int s, float scale, const void *q,
                            const void *QR, const void *KV, const void *KR, const void *dO,
                            const float *lse, const float *D, float *dKVc, float *dKRc, void *dKV,
-                           float *dKRh, void *dQ, void *dQR, hipStream_t stream) {
+                           float *dKRh, void *dQ, void *dQR, int ldq, hipStream_t stream) {
   if (d_h == 128)
     return attn_bwd_t<Bw128>(B, T, H, s, scale, q, QR, KV, KR, dO, lse, D, dKVc, dKRc, dKV, dKRh,
-                             dQ, dQR, stream);
+                             dQ, dQR, ldq, stream);
   return attn_bwd_t<Bw64>(B, T, H, s, scale, q, QR, KV, KR, dO, lse, D, dKVc, dKRc, dKV, dKRh, dQ,
-                          dQR, stream);
+                          dQR, ldq, stream);
 }
 
 hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *D,

@@ -596,10 +596,11 @@ hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, in
 }
 
 hipError_t launch_gemm_add_bf16(const void *A, int lda, const void *Bm, int ldb, int M, int N, int K,
-                                const float *acc, void *out, int ldc, hipStream_t stream) {
+                                const float *acc, int ldacc, void *out, int ldc,
+                                hipStream_t stream) {
   BSeg bs{Bm, Bm, Bm, N, N, ldb};
-  return run_gemm<bf16>((const bf16 *)A, lda, bs, M, N, K, EpiAddBf16{acc, (bf16 *)out, ldc},
-                        stream);
+  return run_gemm<bf16>((const bf16 *)A, lda, bs, M, N, K,
+                        EpiAddBf16{acc, ldacc, (bf16 *)out, ldc}, stream);
 }
 
 hipError_t launch_gemm_f32_2(int dtype, const void *A, int lda, const void *B1, const void *B2,

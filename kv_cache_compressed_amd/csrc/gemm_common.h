@@ -51,11 +51,11 @@ struct EpiAccF32 {
 // sum of products, rounded once).
 struct EpiAddBf16 {
   const float *acc;
+  int lda;
   bf16 *out;
   int ldc;
   __device__ void operator()(int m, int n, float v) const {
-    const size_t i = (size_t)m * ldc + n;
-    out[i] = (bf16)(acc[i] + v);
+    out[(size_t)m * ldc + n] = (bf16)(acc[(size_t)m * lda + n] + v);
   }
 };
 

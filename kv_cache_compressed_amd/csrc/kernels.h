@@ -26,10 +26,11 @@ hipError_t launch_gemm_store2(int dtype, const void *A, int lda, const void *B1,
 hipError_t launch_gemm_f32(int dtype, const void *A, int lda, const void *Bm, int ldb, int M, int N,
                            int K, float *out, int ldc, bool add, hipStream_t stream);
 
-// out[M, N] (bf16, row stride ldc) = acc[M, N] (fp32, same stride) + A[M, K] B[N, K]^T
+// out[M, N] (bf16, row stride ldc) = acc[M, N] (fp32, row stride ldacc) + A[M, K] B[N, K]^T
 // (bf16 operands).
 hipError_t launch_gemm_add_bf16(const void *A, int lda, const void *Bm, int ldb, int M, int N, int K,
-                                const float *acc, void *out, int ldc, hipStream_t stream);
+                                const float *acc, int ldacc, void *out, int ldc,
+                                hipStream_t stream);
 
 // out[M, N] (fp32) = A[M, K] [B1; B2]^T (columns < N1 from B1's rows).
 hipError_t launch_gemm_f32_2(int dtype, const void *A, int lda, const void *B1, const void *B2,
@@ -169,11 +170,11 @@ bool attn_bwd_supported(int dtype, int H, int d_h, int dR);
 // D = rowsum(dO * O): key-role gradients of the compact keys into dKVc
 // [B*nS, 2*H*d_h] and dKRc [B*nS, H, dR] (fp32 scratch), then every frame's
 // total dK | dV into dKV [B*T, 2*H*d_h] (bf16) and per-head dK^R into dKRh
-// [B*T, H, dR] (fp32), and dQ [B*T, H*d_h], dQR [B*T, H, dR] (bf16).
+// [B*T, H, dR] (fp32), and dQ [B*T, H*d_h] (row stride ldq), dQR [B*T, H, dR] (bf16).
 hipError_t launch_attn_bwd(int B, int T, int H, int d_h, int s, float scale, const void *q,
                            const void *QR, const void *KV, const void *KR, const void *dO,
                            const float *lse, const float *D, float *dKVc, float *dKRc, void *dKV,
-                           float *dKRh, void *dQ, void *dQR, hipStream_t stream);
+                           float *dKRh, void *dQ, void *dQR, int ldq, hipStream_t stream);
 // D[i] = sum over d_h channels of dO[i, :] * O[i, :], i < MH (rows of d_h).
 hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *D,
                          hipStream_t stream);

@@ -174,8 +174,10 @@ HeadsWs heads_ws(const mtla_dims *d, int B, int T) {
 // transposed weights, and the backward's intermediate gradients.
 struct BwdWs {
   HeadsWs f;
-  size_t O_, lse, WOt, WKVt, Whct, Wdkvt, WQt, dO, D, dKVc, dKRc, dKV, dKRh, dQ, dCp, da32, dab,
-      dc32, cb, dcb, dX32, dPpart, red_part, red_ctr, total;
+  // Wc = [W_Q^T | W_dkv^T] and dQc = [dQ | dc] side by side (row stride
+  // H d_h + r), so that dX = dQ W_Q + dc W_dkv is one product.
+  size_t O_, lse, WOt, WKVt, Whct, Wc, dO, D, dKVc, dKRc, dKV, dKRh, dQc, dCp, da32, dab, dc32, cb,
+      dPpart, red_part, red_ctr, total;
   int nctr;   // ints at red_ctr: counters of the bias column sums (zero between uses)
 };
 
@@ -191,22 +193,19 @@ BwdWs bwd_ws(const mtla_dims *d, int B, int T) {
   w.WOt = take(HD * dd * e);
   w.WKVt = take(r * 2 * HD * e);
   w.Whct = take(r * r * e);
-  w.Wdkvt = take(dd * r * e);
-  w.WQt = take(dd * HD * e);
+  w.Wc = take(dd * (HD + r) * e);
   w.dO = take(M * HD * e);
   w.D = take(M * H * 4);
   w.dKVc = take((size_t)B * nS * 2 * HD * 4);
   w.dKRc = take((size_t)B * nS * H * dR * 4);
   w.dKV = take(M * 2 * HD * e);
   w.dKRh = take(M * H * dR * 4);
-  w.dQ = take(M * HD * e);
+  w.dQc = take(M * (HD + r) * e);
   w.dCp = take(M * r * 4);
   w.da32 = take(M * r * 4);
   w.dab = take(M * r * e);
   w.dc32 = take(M * r * 4);
   w.cb = take(M * r * e);
-  w.dcb = take(M * r * e);
-  w.dX32 = take(M * dd * 4);
   w.dPpart = take((size_t)B * nS * r * 4);
   // Partials of the ordered reductions (weight-gradient products and the
   // bias column sums run one after another and share one buffer).
@@ -674,14 +673,19 @@ mtla_status prefill_unabsorbed_backward_impl(
   LAUNCH(mtla::launch_transpose(w->W_V, HD, r, r, (char *)P(ws.WKVt) + (size_t)HD * 2, 2 * HD, s),
          "transpose W_V");
   LAUNCH(mtla::launch_transpose(W_hc, r, r, r, P(ws.Whct), r, s), "transpose W_hc");
-  LAUNCH(mtla::launch_transpose(w->W_dkv, r, d, d, P(ws.Wdkvt), r, s), "transpose W_dkv");
-  LAUNCH(mtla::launch_transpose(w->W_Q, HD, d, d, P(ws.WQt), HD, s), "transpose W_Q");
+  // [dQ | dc] and [W_Q^T | W_dkv^T]: row stride HD + r, dc and W_dkv^T at column HD.
+  const int ldc2 = HD + r;
+  void *dQ = P(ws.dQc), *dcb = (char *)P(ws.dQc) + (size_t)HD * esize(dims);
+  LAUNCH(mtla::launch_transpose(w->W_Q, HD, d, d, P(ws.Wc), ldc2, s), "transpose W_Q");
+  LAUNCH(mtla::launch_transpose(w->W_dkv, r, d, d, (char *)P(ws.Wc) + (size_t)HD * esize(dims), ldc2,
+                                s),
+         "transpose W_dkv");
   // output map
   LAUNCH(mtla::launch_gemm_store(dt, dY, d, P(ws.WOt), d, M, HD, d, P(ws.dO), HD, s), "dO");
   LAUNCH(mtla::launch_rowdot(P(ws.dO), O, M * H, dims->d_h, F(ws.D), s), "rowsum dO * O");
   // attention
   LAUNCH(mtla::launch_attn_bwd(B, T, H, dims->d_h, dims->s, scale, q, QR, KV, KR, P(ws.dO), lse, F(ws.D),
-                               F(ws.dKVc), F(ws.dKRc), P(ws.dKV), F(ws.dKRh), P(ws.dQ), dQR, s),
+                               F(ws.dKVc), F(ws.dKRc), P(ws.dKV), F(ws.dKRh), dQ, dQR, ldc2, s),
          "attention backward");
   LAUNCH(mtla::launch_head_sum(F(ws.dKRh), M, H, dims->d_hR, dKR, s), "dK^R over heads");
   // key and value maps
@@ -697,20 +701,16 @@ mtla_status prefill_unabsorbed_backward_impl(
                                     w->gate_pos_rows, gr->dgate_pos, s),
          "group scan and gate backward");
   LAUNCH(mtla::launch_colsum(F(ws.da32), M, r, rpart, rctr, gr->db_hc, s), "db");
-  LAUNCH(mtla::launch_gemm_add_bf16(P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), P(ws.dcb), r,
+  LAUNCH(mtla::launch_gemm_add_bf16(P(ws.dab), r, P(ws.Whct), r, M, r, r, F(ws.dc32), r, dcb, ldc2,
                                     s),
          "dc");
   // inputs
-  // The query map's product (K = H d_h) is stored in fp32 and the latent
-  // map's (K = r) added to it, the sum rounded once to bf16: the longer
-  // product then qualifies for the large-tile kernel.
-  LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dQ), HD, P(ws.WQt), HD, M, d, HD, F(ws.dX32), d, false, s),
-         "dX from the query map");
-  LAUNCH(mtla::launch_gemm_add_bf16(P(ws.dcb), r, P(ws.Wdkvt), r, M, d, r, F(ws.dX32), dX, d, s),
-         "dX from the latent map");
+  // dX = [dQ | dc] [W_Q^T | W_dkv^T]^T: one product over K = HD + r.
+  LAUNCH(mtla::launch_gemm_store(dt, dQ, ldc2, P(ws.Wc), ldc2, M, d, ldc2, dX, d, s),
+         "dX from the query and latent maps");
   // weight gradients (each product's partials added in split order)
   LAUNCH(mtla::launch_tn_gemm(dY, d, O, HD, M, d, HD, gr->dW_O, HD, rpart, s), "dW_O");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dQ), HD, X, d, M, HD, d, gr->dW_Q, d, rpart, s), "dW_Q");
+  LAUNCH(mtla::launch_tn_gemm(dQ, ldc2, X, d, M, HD, d, gr->dW_Q, d, rpart, s), "dW_Q");
   LAUNCH(mtla::launch_tn_gemm(P(ws.dKV), 2 * HD, Cp, r, M, HD, r, gr->dW_K, r, rpart, s),
          "dW_K");
   LAUNCH(mtla::launch_tn_gemm((char *)P(ws.dKV) + (size_t)HD * 2, 2 * HD, Cp, r, M, HD, r, gr->dW_V,
@@ -718,7 +718,7 @@ mtla_status prefill_unabsorbed_backward_impl(
          "dW_V");
   LAUNCH(mtla::launch_tn_gemm(P(ws.dab), r, P(ws.cb), r, M, r, r, gr->dW_hc, r, rpart, s),
          "dW_hc");
-  LAUNCH(mtla::launch_tn_gemm(P(ws.dcb), r, X, d, M, r, d, gr->dW_dkv, d, rpart, s),
+  LAUNCH(mtla::launch_tn_gemm(dcb, ldc2, X, d, M, r, d, gr->dW_dkv, d, rpart, s),
          "dW_dkv");
   return ok();
 }
