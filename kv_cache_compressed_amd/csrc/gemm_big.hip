@@ -111,6 +111,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(const bf16 *__restrict
   // the entry made it wait for every LDS read, including the next stage's,
   // before the products of each even stage.
   wait_lgkm0();
+  // Every wave has read stage 0 before iteration 0 refills its slot.
+  bar();
 
   // Iteration kt: refill the slot of stage kt (its fragments were read in
   // iteration kt-1, before the last barrier) with stage kt + NST; read stage
@@ -283,6 +285,7 @@ __global__ __launch_bounds__(256, 1) void tn_big_kernel(const bf16 *__restrict__
   GbFrag fa0, fb0, fa1, fb1;
   frags(0, fa0, fb0);
   wait_lgkm0();
+  bar();   // every wave has read stage 0 before iteration 0 refills its slot
 
   // Iteration kt: stage kt+1's fragments into the other set, refill stage
   // kt's slot with stage kt + NST (its fragments were read in iteration
