@@ -24,9 +24,11 @@
 // the forward -- one stationary in the queries (dQ, dQ^R, and every frame's
 // own column), one stationary in the compact keys (dK, dV, dK^R of the
 // group-final frames) -- the reverse group scan with the gate backward, a
-// split-M product A^T B for the weight gradients, and small helpers.  Every
-// reduction across workgroups adds its partials in a fixed order (the last
-// workgroup to finish sums them), so the gradients repeat bit for bit.
+// split-M product A^T B for the weight gradients (the 256 x 256 form is in
+// gemm_big.hip), and small helpers.  Every reduction across workgroups adds
+// its partials in a fixed order (a separate pass over the weight-gradient
+// slabs; the last workgroup to finish for the bias column sums), so the
+// gradients repeat bit for bit.
 
 #include <float.h>
 #include <math.h>
