@@ -60,6 +60,7 @@ CSRC = os.path.join(ROOT, "kv_cache_compressed_amd", "csrc")
 KERNEL_SOURCES = {
     "decode_ws_kernel": ("decode.hip", "common.h"),
     "prefill_ws_kernel": ("attention.hip", "common.h"),
+    "heads_attn_kernel": ("heads.hip", "common.h"),
 }
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "decode tokens/s + achieved HBM GB/s (compressed cache); prefill TFLOP/s, 1 GPU"
@@ -607,7 +608,7 @@ def main():
     if args.only in ("prefill_b16_t4096_per_head", "prefill_b8_t4096_dh128_per_head"):
         rec = run_prefill_unabsorbed(args.steps, args.warmup,
                                      wide=args.only == "prefill_b8_t4096_dh128_per_head")
-        rec["roofline"] = mfma_roofline(rec, "heads_attn_kernel")
+        rec["roofline"] = mfma_roofline(rec, "heads_attn_kernel", args.only)
         print(json.dumps(rec), flush=True)
         return
     if args.only == "prefill_b8_t4096_dh128_backward":
@@ -647,7 +648,7 @@ def main():
         f"({p['roofline']['frac']:.1%}), forward {p['forward_ms']:.3f} ms")
     log("prefill_b16_t4096_per_head ...")
     u = extra["prefill_b16_t4096_per_head"] = run_prefill_unabsorbed()
-    u["roofline"] = mfma_roofline(u, "heads_attn_kernel")
+    u["roofline"] = mfma_roofline(u, "heads_attn_kernel", "prefill_b16_t4096_per_head")
     log(f"  per-head prefill: attention {u['attn_ms']:.3f} ms {u['attn_tflops']:.0f} TFLOP/s "
         f"({u['roofline']['frac']:.1%}), forward {u['forward_ms']:.3f} ms")
     log("prefill_b16_t4096_backward ...")
@@ -656,7 +657,7 @@ def main():
     torch.cuda.empty_cache()
     log("prefill_b8_t4096_dh128 (per-head form and backward at d_h = 128) ...")
     uw = extra["prefill_b8_t4096_dh128_per_head"] = run_prefill_unabsorbed(wide=True)
-    uw["roofline"] = mfma_roofline(uw, "heads_attn_kernel")
+    uw["roofline"] = mfma_roofline(uw, "heads_attn_kernel", "prefill_b8_t4096_dh128_per_head")
     bww = extra["prefill_b8_t4096_dh128_backward"] = run_backward(wide=True)
     log(f"  d_h=128 per-head: attention {uw['attn_ms']:.3f} ms {uw['attn_tflops']:.0f} TFLOP/s "
         f"({uw['roofline']['frac']:.1%}), forward {uw['forward_ms']:.3f} ms; backward {bww['step_ms']:.3f} ms")
