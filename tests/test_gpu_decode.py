@@ -199,7 +199,7 @@ def test_decode_is_deterministic():
 def test_llm_scale_decode_sampled():
     """Full-size LLM-scale step (B=128, H=32, r=512, 16384 slots, the
     benchmark's launch configuration); the cache is seeded random bf16 made
-    on the GPU; the oracle checks sampled sequences."""
+    on the GPU; the oracle checks seven sampled sequences."""
     needs_gpu()
     name, dims, ex = synth.config(5)
     B, ctx = ex["B"], ex["ctx"]
@@ -213,7 +213,9 @@ def test_llm_scale_decode_sampled():
     cache[..., :dims.r].normal_(0.0, 0.7, generator=gen)
     cache[..., dims.r:].normal_(0.0, 1.0, generator=gen)
     cache[:, ctx // dims.s:] = float("nan")
-    sample = [0, 77, 127]
+    # Both ends of the batch and of each half (the work list gives every
+    # sequence two splits of 8192 slots here), plus an interior sequence.
+    sample = [0, 1, 63, 64, 77, 126, 127]
     before = {b: host(cache[b]) for b in sample}
     step = synth.make_step(dims, w, pos, seed=synth.seed_for(5) + 2)
     say("decode", name, "running")
