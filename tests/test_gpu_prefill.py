@@ -74,9 +74,9 @@ def test_bf16_wide_latent():
 
 def test_full_size_prefill_sampled():
     """The benchmark's prefill launch (B=16, T=4096, s=2): intermediate states
-    and cache in full on three sequences, outputs on their sampled rows
-    computed one by one from the oracle's visible sets, and every output row
-    of one sequence against the oracle's dense masked form."""
+    and cache of all sixteen sequences in full, outputs of three sequences on
+    sampled rows computed one by one from the oracle's visible sets, and every
+    output row of one sequence against the oracle's dense masked form."""
     needs_gpu()
     name, dims, ex = synth.config(4)
     B, T = ex["B"], ex["T"]
@@ -91,16 +91,19 @@ def test_full_size_prefill_sampled():
                   cache=cache, Cprime=Cp)
     torch.cuda.synchronize()
     rng = np.random.default_rng(4)
+    Cprs = {}
+    for b in range(B):
+        # Intermediate states and cache of every sequence, in full.
+        _, U = om.gated_latents(seq["X"][b], W, dims.s)
+        Cpr = Cprs[b] = om.intermediate_states(U, dims.s)
+        lat, rk, _ = om.compressed_cache(Cpr, seq["KR"][b], dims.s)
+        assert relerr(host(Cp[b]), Cpr) < TOL["bf16"], b
+        cg = host(cache[b])
+        assert relerr(cg[:, :dims.r], lat) < TOL["bf16"], b
+        assert np.array_equal(cg[:, dims.r:], rk), b
     for b in (0, 9, 15):
         X, QR, KR = seq["X"][b], seq["QR"][b], seq["KR"][b]
-        _, U = om.gated_latents(X, W, dims.s)
-        Cpr = om.intermediate_states(U, dims.s)
-        lat, rk, _ = om.compressed_cache(Cpr, KR, dims.s)
-        Cpg = host(Cp[b])
-        assert relerr(Cpg, Cpr) < TOL["bf16"]
-        cg = host(cache[b])
-        assert relerr(cg[:, :dims.r], lat) < TOL["bf16"]
-        assert np.array_equal(cg[:, dims.r:], rk)
+        Cpr = Cprs[b]
         rows = sorted(set([0, 1, 2, 3, T - 2, T - 1] + list(rng.integers(0, T, size=40))))
         Yg = host(Y[b, rows])
         Yr = []
