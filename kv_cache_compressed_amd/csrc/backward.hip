@@ -40,8 +40,6 @@ namespace mtla {
 
 namespace {
 
-constexpr float kNegInfB = -INFINITY;
-
 // Head widths and tiling of the attention backward: (DH, DR) = (64, 32) with
 // two 16-row tiles (32 keys, or 32 query frames) per wave, or (128, 64) with
 // one (the accumulators of twice the width then fit the 256 registers of two
