@@ -88,10 +88,10 @@ def _replay_check(fn, outs, tol=None, n=3, reset=None):
         del junk
 
 
-def test_graph_replay_per_head_prefill_and_backward():
-    """The per-head forward (bit-exact) and its backward (inputs' gradients
-    bit-exact; weight gradients, summed with atomic adds in any order, within
-    1e-5) from captured graphs."""
+def test_graph_replay_prefill_and_backward():
+    """The absorbed and per-head forwards and the per-head backward from
+    captured graphs, bit for bit (the backward adds its partial sums in a
+    fixed order)."""
     needs_gpu()
     from synth import Dims
     import oracle.mtla as om
@@ -107,6 +107,9 @@ def test_graph_replay_per_head_prefill_and_backward():
     cache = L.new_cache(B, ms)
     say("graph: per-head forward")
     _replay_check(lambda: L.prefill_unabsorbed(X, QR, KR, Y, cache=cache), [Y, cache])
+    say("graph: absorbed forward")
+    Cp = torch.empty(B, T, dims.r, dtype=torch.bfloat16, device="cuda")
+    _replay_check(lambda: L.prefill(X, QR, KR, Y, cache=cache, Cprime=Cp), [Y, cache, Cp])
     dY = dev(np.random.default_rng(9902).normal(size=(B, T, dims.d)), "bf16")
     outs = {}
 
@@ -123,8 +126,7 @@ def test_graph_replay_per_head_prefill_and_backward():
         L.dims, L.wu, L.t["W_hc"], X, QR, KR, dY, {k: fixed[k] for k in GRAD_NAMES},
         fixed["dX"], fixed["dQR"], fixed["dKR"], ws)
     say("graph: backward")
-    _replay_check(fn, [fixed["dX"], fixed["dQR"], fixed["dKR"]])
-    _replay_check(fn, [fixed[k] for k in GRAD_NAMES], tol=1e-5)
+    _replay_check(fn, [fixed["dX"], fixed["dQR"], fixed["dKR"]] + [fixed[k] for k in GRAD_NAMES])
 
 
 def test_graph_replay_chunk_append_and_rope():
