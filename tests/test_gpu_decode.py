@@ -196,6 +196,19 @@ def test_decode_is_deterministic():
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
 
 
+def test_llm_dims_ragged_decode():
+    """The LLM-scale model dims (d = 4096, H = 32, d_h = 128, r = 512,
+    bf16) with ragged positions: the first frame, open and live partial
+    newest slots, and sequences of up to 8192 slots spread over several
+    stages and splits of the balanced work list; every sequence against the
+    oracle."""
+    needs_gpu()
+    dims = Dims(d=4096, H=32, d_h=128, r=512, d_hR=64, s=2)
+    pos = [0, 1, 2, 63, 64, 1023, 2048, 4095, 7777, 12000, 16382, 16383]
+    say("decode LLM dims, ragged", pos)
+    _decode_case(dims, pos, "bf16", 7700)
+
+
 def test_llm_scale_decode_sampled():
     """Full-size LLM-scale step (B=128, H=32, r=512, 16384 slots, the
     benchmark's launch configuration); the cache is seeded random bf16 made
