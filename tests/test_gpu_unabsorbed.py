@@ -69,16 +69,10 @@ def test_unabsorbed_llm_head_width(s, T, H, B):
     _case(dims, B, T, 9400 + 13 * s + T + H)
 
 
-def test_unabsorbed_full_size_sampled():
-    """The benchmark's per-head launch (B=16, T=4096, s=2), checked on
-    sampled rows of two sequences against the oracle's per-head attention of
-    each sampled row."""
-    needs_gpu()
-    name, dims, ex = synth.config(4)
-    B, T = ex["B"], ex["T"]
+def _full_size_sampled(dims, B, T, seed):
     ms = om.n_slots(T, dims.s)
-    w, W, L = _layer(dims, synth.seed_for(4), ms)
-    seq = synth.make_sequence(dims, w, B, T, synth.seed_for(4) + 1, "bf16")
+    w, W, L = _layer(dims, seed, ms)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, "bf16")
     Cp = torch.empty(B, T, dims.r, dtype=L.dtype, device="cuda")
     Y = L.prefill_unabsorbed(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"),
                              dev(seq["KR"], "bf16"), Cprime=Cp)
@@ -107,6 +101,26 @@ def test_unabsorbed_full_size_sampled():
         e = relerr(Yg, np.stack(Yr))
         say(f"  b={b} sampled-row relerr {e:.3g}")
         assert e < TOL["bf16"]
+
+
+def test_unabsorbed_full_size_sampled():
+    """The benchmark's per-head launch (B=16, T=4096, s=2), checked on
+    sampled rows of two sequences against the oracle's per-head attention of
+    each sampled row."""
+    needs_gpu()
+    name, dims, ex = synth.config(4)
+    say("prefill per-head full size", name)
+    _full_size_sampled(dims, ex["B"], ex["T"], synth.seed_for(4))
+
+
+def test_unabsorbed_llm_head_width_full_size_sampled():
+    """The benchmark's per-head launch at the LLM-scale head widths (8
+    sequences of 4096 frames, d = 1024, H = 8, d_h = 128, d_hR = 64,
+    r = 512), checked the same way."""
+    needs_gpu()
+    dims = Dims(d=1024, H=8, d_h=128, r=512, d_hR=64, s=2)
+    say("prefill per-head full size, d_h = 128")
+    _full_size_sampled(dims, 8, 4096, 9450)
 
 
 def test_unabsorbed_equals_absorbed_form():
