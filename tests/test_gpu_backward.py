@@ -101,6 +101,17 @@ def test_backward_full_size_prefix():
     _check(dims, ex["B"], ex["T"], 9600, T0=320, rows=[0, ex["B"] - 1])
 
 
+def test_backward_llm_head_width_full_size_prefix():
+    """The benchmark's backward launch at the LLM-scale head widths (8
+    sequences of 4096 frames, d = 1024, H = 8, d_h = 128, r = 512) with the
+    loss on the first 256 frames of two sequences: those gradients against
+    the oracle, everything else exactly zero."""
+    needs_gpu()
+    dims = Dims(d=1024, H=8, d_h=128, r=512, d_hR=64, s=2)
+    say("backward full size, d_h = 128")
+    _check(dims, 8, 4096, 9650, T0=256, rows=[0, 7])
+
+
 @pytest.mark.parametrize("d_h,r,dR", [(64, 256, 32), (128, 512, 64)])
 def test_backward_is_deterministic(d_h, r, dR):
     """Two calls on the same inputs give the same bits in every output:
