@@ -259,8 +259,10 @@ typedef struct {
  * the column block of head h of W_O, the absorbed maps A[h] = Wk_h^T Wq_h
  * and Bvo[:, h, :] = Wo_h Wv_h make this exactly mtla_prefill_strided; the
  * per-head form spends 2 (d_h + d_hR) + 2 d_h flops per visible pair and head
- * on attention instead of 2 (r + d_hR) + 2 r.  Supported: bf16 storage with
- * (d_h, d_hR) = (64, 32) or (128, 64) (else MTLA_ERR_UNSUPPORTED).  Workspace:
+ * on attention instead of 2 (r + d_hR) + 2 r.  Supported: (d_h, d_hR) =
+ * (64, 32) or (128, 64) (else MTLA_ERR_UNSUPPORTED), with bf16 storage (MFMA
+ * attention) or fp32 storage (a correctness-oriented fp32 attention kernel;
+ * the backward below stays bf16 only).  Workspace:
  * mtla_workspace_bytes(op=4, B, T). */
 mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
                                     const void *X, const void *QR, const void *KR, int32_t B,

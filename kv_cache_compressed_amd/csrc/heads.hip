@@ -365,7 +365,8 @@ __global__ __launch_bounds__(64 * C::NW, C::OCC) void heads_attn_kernel(HeadsArg
 }  // namespace
 
 bool heads_attention_supported(int dtype, int H, int d_h, int dR) {
-  return dtype == 1 && ((d_h == 64 && dR == 32) || (d_h == 128 && dR == 64)) && H >= 1 && H <= 64;
+  return (dtype == 0 || dtype == 1) && ((d_h == 64 && dR == 32) || (d_h == 128 && dR == 64)) &&
+         H >= 1 && H <= 64;
 }
 
 namespace {

@@ -161,6 +161,12 @@ hipError_t launch_heads_attention(int B, int T, int H, int d_h, int s, float sca
                                   const void *QR, const void *KV, const void *KR, void *O,
                                   float *lse, hipStream_t stream, hipEvent_t ev0 = nullptr,
                                   hipEvent_t ev1 = nullptr);
+// The same attention with fp32 storage (heads_f32.hip): a correctness-
+// oriented kernel with the same operand layouts (no log-sum-exp output).
+hipError_t launch_heads_attention_f32(int B, int T, int H, int d_h, int s, float scale,
+                                      const void *q, const void *QR, const void *KV,
+                                      const void *KR, void *O, hipStream_t stream,
+                                      hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 bool heads_attention_supported(int dtype, int H, int d_h, int dR);
 
 // ---- backward of the per-head parallel form (bf16, (d_h, dR) = (64, 32) or (128, 64)) ----

@@ -567,7 +567,7 @@ mtla_status prefill_unabsorbed_impl(const mtla_dims *dims, const mtla_unabsorbed
   if ((int64_t)B * T * dims->H * dims->d_h > 0x7fffffffLL / 4)
     return fail(MTLA_ERR_UNSUPPORTED, "B*T*H*d_h too large");
   if (!mtla::heads_attention_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR))
-    return fail(MTLA_ERR_UNSUPPORTED, "per-head form needs bf16 storage and (d_h, d_hR) = (64, 32) or (128, 64)");
+    return fail(MTLA_ERR_UNSUPPORTED, "per-head form needs (d_h, d_hR) = (64, 32) or (128, 64)");
   const int nS = (T + dims->s - 1) / dims->s;
   if ((T - 1) / dims->s >= w->gate_pos_rows)
     return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
@@ -595,9 +595,14 @@ mtla_status prefill_unabsorbed_impl(const mtla_dims *dims, const mtla_unabsorbed
   LAUNCH(mtla::launch_gemm_store2(dims->dtype, Cp, dims->r, w->W_K, w->W_V, HD, dims->r, M, 2 * HD,
                                   dims->r, KV, 2 * HD, s),
          "per-head key and value projection");
-  LAUNCH(mtla::launch_heads_attention(B, T, dims->H, dims->d_h, dims->s, eff_scale(dims), q, QR, KV, KR, O,
-                                      nullptr, s, ev0(events), ev1(events)),
-         "per-head strided attention");
+  if (dims->dtype == MTLA_BF16)
+    LAUNCH(mtla::launch_heads_attention(B, T, dims->H, dims->d_h, dims->s, eff_scale(dims), q, QR,
+                                        KV, KR, O, nullptr, s, ev0(events), ev1(events)),
+           "per-head strided attention");
+  else
+    LAUNCH(mtla::launch_heads_attention_f32(B, T, dims->H, dims->d_h, dims->s, eff_scale(dims), q,
+                                            QR, KV, KR, O, s, ev0(events), ev1(events)),
+           "per-head strided attention (fp32)");
   LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HD, w->W_O, dims->d, Y, nullptr, nullptr, s),
          "output projection");
   return ok();

@@ -13,22 +13,23 @@ from gpu_util import TOL, dev, host, needs_gpu, relerr, say
 pytestmark = pytest.mark.gpu
 
 
-def _layer(dims, seed, pe_rows):
-    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
-    w = synth.make_weights(dims, seed, "bf16", pe_rows=pe_rows)
+def _layer(dims, seed, pe_rows, storage="bf16"):
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16, MTLA_F32
+    w = synth.make_weights(dims, seed, storage, pe_rows=pe_rows)
     W = om.with_position_table(w, pe_rows)
-    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)},
+                              MTLA_BF16 if storage == "bf16" else MTLA_F32)
     return w, W, L
 
 
-def _case(dims, B, T, seed):
+def _case(dims, B, T, seed, storage="bf16"):
     ms = om.n_slots(T, dims.s) + 2
-    w, W, L = _layer(dims, seed, ms)
-    seq = synth.make_sequence(dims, w, B, T, seed + 1, "bf16")
+    w, W, L = _layer(dims, seed, ms, storage)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, storage)
     cache = L.new_cache(B, ms, fill=float("nan"))
     Cp = torch.empty(B, T, dims.r, dtype=L.dtype, device="cuda")
-    Y = L.prefill_unabsorbed(dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"),
-                             dev(seq["KR"], "bf16"), cache=cache, Cprime=Cp)
+    Y = L.prefill_unabsorbed(dev(seq["X"], storage), dev(seq["QR"], storage),
+                             dev(seq["KR"], storage), cache=cache, Cprime=Cp)
     torch.cuda.synchronize()
     Yg, Cpg, cg = host(Y), host(Cp), host(cache)
     n = om.n_slots(T, dims.s)
@@ -39,9 +40,9 @@ def _case(dims, B, T, seed):
                                  dims.s, dims.scale)
         ey, ec = relerr(Yg[b], yref), relerr(Cpg[b], ref["Cp"])
         say(f"  b={b} Y relerr {ey:.3g}  C' relerr {ec:.3g}")
-        assert ey < TOL["bf16"], (b, ey)
-        assert ec < TOL["bf16"], (b, ec)
-        assert relerr(cg[b, :n, :dims.r], ref["cache_lat"]) < TOL["bf16"]
+        assert ey < TOL[storage], (b, ey)
+        assert ec < TOL[storage], (b, ec)
+        assert relerr(cg[b, :n, :dims.r], ref["cache_lat"]) < TOL[storage]
         assert np.array_equal(cg[b, :n, dims.r:], ref["cache_rope"])
         assert np.all(np.isnan(cg[b, n:]))
 
@@ -101,6 +102,17 @@ def _full_size_sampled(dims, B, T, seed):
         e = relerr(Yg, np.stack(Yr))
         say(f"  b={b} sampled-row relerr {e:.3g}")
         assert e < TOL["bf16"]
+
+
+@pytest.mark.parametrize("d_h,r,dR", [(64, 256, 32), (128, 512, 64)])
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 4, 1), (2, 300, 4, 2), (3, 257, 2, 1), (1, 64, 2, 2),
+                                       (80, 100, 2, 1), (5, 200, 3, 1)])
+def test_unabsorbed_fp32(s, T, H, B, d_h, r, dR):
+    """The per-head form with fp32 storage at both head widths (1e-4)."""
+    needs_gpu()
+    dims = Dims(d=256, H=H, d_h=d_h, r=r, d_hR=dR, s=s)
+    say("prefill per-head fp32", d_h, s, T, H, B)
+    _case(dims, B, T, 9800 + 13 * s + T + H + d_h, "f32")
 
 
 def test_unabsorbed_full_size_sampled():
