@@ -261,8 +261,8 @@ typedef struct {
  * per-head form spends 2 (d_h + d_hR) + 2 d_h flops per visible pair and head
  * on attention instead of 2 (r + d_hR) + 2 r.  Supported: (d_h, d_hR) =
  * (64, 32) or (128, 64) (else MTLA_ERR_UNSUPPORTED), with bf16 storage (MFMA
- * attention) or fp32 storage (a correctness-oriented fp32 attention kernel;
- * the backward below stays bf16 only).  Workspace:
+ * attention) or fp32 storage (a correctness-oriented fp32 attention
+ * kernel).  Workspace:
  * mtla_workspace_bytes(op=4, B, T). */
 mtla_status mtla_prefill_unabsorbed(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
                                     const void *X, const void *QR, const void *KR, int32_t B,
@@ -294,8 +294,9 @@ typedef struct {
  * content branch is differentiated in the pages' form, Linear(c) = W_hc c +
  * b_hc, so W_hc [r, r] (storage dtype) is passed besides the folded W_gate
  * the forward uses; the position branch is differentiated as its table.
- * The forward is recomputed inside.  Supported: bf16 storage with
- * (d_h, d_hR) = (64, 32) or (128, 64).  Workspace:
+ * The forward is recomputed inside.  Supported: (d_h, d_hR) = (64, 32) or
+ * (128, 64) (else MTLA_ERR_UNSUPPORTED), with bf16 storage (MFMA kernels)
+ * or fp32 storage (correctness-oriented fp32 kernels).  Workspace:
  * mtla_workspace_bytes(op=5, B, T).
  * Reproducibility: every output repeats bit for bit from call to call --
  * the sums over frames and sequences behind the weight gradients, db_hc and

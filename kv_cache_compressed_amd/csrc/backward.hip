@@ -592,22 +592,25 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const bf16 *dO, const bf16 
 }
 
 // dKR[row, ch] = sum_h dKRh[row, h, ch] (the RoPE key is shared by the heads).
+template <class OutT>
 __global__ __launch_bounds__(256) void head_sum_kernel(const float *dKRh, int M, int H, int DR,
-                                                       bf16 *dKR) {
+                                                       OutT *dKR) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= M * DR) return;
   const int row = i / DR, ch = i % DR;
   float acc = 0.0f;
   for (int hh = 0; hh < H; ++hh) acc += dKRh[((size_t)row * H + hh) * DR + ch];
-  dKR[i] = (bf16)acc;
+  dKR[i] = (OutT)acc;
 }
 
 // Reverse group scan and gate backward, one thread per (sequence b, slot j,
 // latent channel).  dU runs over the frames of the group from the last one
 // down: dU_i = dC'_i + dU_{i+1}.  Writes da (fp32 and bf16), dc's direct term
-// dU w (fp32), c (bf16, for dW_hc), and adds dP_j.
+// dU w (fp32), c (bf16, for dW_hc), and adds dP_j.  BiasT: the storage type
+// of b_hc.
+template <class BiasT>
 __global__ __launch_bounds__(256) void scan_gate_bwd_kernel(const float *dCp, const float *cg,
-                                                            const bf16 *b_hc, const float *table,
+                                                            const BiasT *b_hc, const float *table,
                                                             int T, int R, int s, int nS,
                                                             float *da32, bf16 *dab, float *dc32,
                                                             bf16 *cb, float *dPpart) {
@@ -886,20 +889,32 @@ hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *
   return hipGetLastError();
 }
 
-hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, hipStream_t stream) {
-  hipLaunchKernelGGL(head_sum_kernel, dim3((M * dR + 255) / 256), dim3(256), 0, stream, dKRh, M, H,
-                     dR, (bf16 *)dKR);
+hipError_t launch_head_sum(int dtype, const float *dKRh, int M, int H, int dR, void *dKR,
+                           hipStream_t stream) {
+  const dim3 grid((M * dR + 255) / 256);
+  if (dtype == 0)
+    hipLaunchKernelGGL(head_sum_kernel<float>, grid, dim3(256), 0, stream, dKRh, M, H, dR,
+                       (float *)dKR);
+  else
+    hipLaunchKernelGGL(head_sum_kernel<bf16>, grid, dim3(256), 0, stream, dKRh, M, H, dR,
+                       (bf16 *)dKR);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b_hc,
+hipError_t launch_scan_gate_bwd(int dtype, const float *dCp, const float *cg, const void *b_hc,
                                 const float *table, int B, int T, int R, int s, float *da32,
                                 void *dab, float *dc32, void *cb, float *dPpart, int rows,
                                 float *dPtab, hipStream_t stream) {
   const int nS = (T + s - 1) / s;
   dim3 grid((unsigned)(((int64_t)nS * R + 255) / 256), B);
-  hipLaunchKernelGGL(scan_gate_bwd_kernel, grid, dim3(256), 0, stream, dCp, cg, (const bf16 *)b_hc,
-                     table, T, R, s, nS, da32, (bf16 *)dab, dc32, (bf16 *)cb, dPpart);
+  if (dtype == 0)
+    hipLaunchKernelGGL(scan_gate_bwd_kernel<float>, grid, dim3(256), 0, stream, dCp, cg,
+                       (const float *)b_hc, table, T, R, s, nS, da32, (bf16 *)dab, dc32,
+                       (bf16 *)cb, dPpart);
+  else
+    hipLaunchKernelGGL(scan_gate_bwd_kernel<bf16>, grid, dim3(256), 0, stream, dCp, cg,
+                       (const bf16 *)b_hc, table, T, R, s, nS, da32, (bf16 *)dab, dc32,
+                       (bf16 *)cb, dPpart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sum_b_kernel, dim3((unsigned)(((size_t)rows * R + 255) / 256)), dim3(256), 0,

@@ -22,6 +22,8 @@
 // exchange, and both lanes run the same online softmax in log2 units (the
 // running maximum moved whenever a score exceeds it) and update their half
 // of the output.  Each frame's own column seeds the softmax with weight 1.
+// For the backward the kernel can also write each row's log2-sum-exp of the
+// scores in log2 units, lse [B*T, H].
 
 #include <math.h>
 
@@ -45,7 +47,8 @@ __global__ __launch_bounds__(128) void heads_attn_f32_kernel(const float *__rest
                                                              const float *__restrict__ QR,
                                                              const float *__restrict__ KV,
                                                              const float *__restrict__ KR,
-                                                             float *__restrict__ O, int T, int H,
+                                                             float *__restrict__ O,
+                                                             float *__restrict__ lse, int T, int H,
                                                              int s, float sl2) {
   using C = F32Heads<DH, DR>;
   __shared__ float kt[C::KEYS * C::RW];
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(128) void heads_attn_f32_kernel(const float *__rest
     }
   }
   if (!ok) return;
+  if (lse && half == 0) lse[row * H + h] = mx + log2f(l);   // log2 units
   const float inv = 1.0f / l;
   float *op = O + row * HD + (size_t)h * DH + half * C::HQ;
 #pragma unroll
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(128) void heads_attn_f32_kernel(const float *__rest
 
 template <int DH, int DR>
 hipError_t heads_f32_t(int B, int T, int H, int s, float sl2, const void *q, const void *QR,
-                       const void *KV, const void *KR, void *O, hipStream_t stream,
+                       const void *KV, const void *KR, void *O, float *lse, hipStream_t stream,
                        hipEvent_t ev0, hipEvent_t ev1) {
   using C = F32Heads<DH, DR>;
   const dim3 grid((T + C::ROWS - 1) / C::ROWS, H, B);
@@ -141,7 +145,7 @@ hipError_t heads_f32_t(int B, int T, int H, int s, float sl2, const void *q, con
               *krf = (const float *)KR;
   float *of = (float *)O;
   void *args[] = {(void *)&qf, (void *)&qrf, (void *)&kvf, (void *)&krf, (void *)&of,
-                  (void *)&T,  (void *)&H,   (void *)&s,   (void *)&sl2};
+                  (void *)&lse, (void *)&T,  (void *)&H,   (void *)&s,   (void *)&sl2};
   if (ev0) (void)hipEventRecord(ev0, stream);
   const hipError_t e =
       hipLaunchKernel((const void *)kern, grid, dim3(C::THREADS), args, 0, stream);
@@ -153,12 +157,12 @@ hipError_t heads_f32_t(int B, int T, int H, int s, float sl2, const void *q, con
 
 hipError_t launch_heads_attention_f32(int B, int T, int H, int d_h, int s, float scale,
                                       const void *q, const void *QR, const void *KV,
-                                      const void *KR, void *O, hipStream_t stream, hipEvent_t ev0,
-                                      hipEvent_t ev1) {
+                                      const void *KR, void *O, float *lse, hipStream_t stream,
+                                      hipEvent_t ev0, hipEvent_t ev1) {
   const float sl2 = scale * kLog2e;
   if (d_h == 128)
-    return heads_f32_t<128, 64>(B, T, H, s, sl2, q, QR, KV, KR, O, stream, ev0, ev1);
-  return heads_f32_t<64, 32>(B, T, H, s, sl2, q, QR, KV, KR, O, stream, ev0, ev1);
+    return heads_f32_t<128, 64>(B, T, H, s, sl2, q, QR, KV, KR, O, lse, stream, ev0, ev1);
+  return heads_f32_t<64, 32>(B, T, H, s, sl2, q, QR, KV, KR, O, lse, stream, ev0, ev1);
 }
 
 }  // namespace mtla

@@ -162,14 +162,15 @@ hipError_t launch_heads_attention(int B, int T, int H, int d_h, int s, float sca
                                   float *lse, hipStream_t stream, hipEvent_t ev0 = nullptr,
                                   hipEvent_t ev1 = nullptr);
 // The same attention with fp32 storage (heads_f32.hip): a correctness-
-// oriented kernel with the same operand layouts (no log-sum-exp output).
+// oriented kernel with the same operand layouts; lse (optional, [B*T, H])
+// receives each row's log2-sum-exp of the scores in log2 units.
 hipError_t launch_heads_attention_f32(int B, int T, int H, int d_h, int s, float scale,
                                       const void *q, const void *QR, const void *KV,
-                                      const void *KR, void *O, hipStream_t stream,
+                                      const void *KR, void *O, float *lse, hipStream_t stream,
                                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 bool heads_attention_supported(int dtype, int H, int d_h, int dR);
 
-// ---- backward of the per-head parallel form (bf16, (d_h, dR) = (64, 32) or (128, 64)) ----
+// ---- backward of the per-head parallel form (bf16 MFMA kernels, (d_h, dR) = (64, 32) or (128, 64)) ----
 
 bool attn_bwd_supported(int dtype, int H, int d_h, int dR);
 // Attention backward over the forward's q, QR, KV, KR, its lse and
@@ -184,14 +185,15 @@ hipError_t launch_attn_bwd(int B, int T, int H, int d_h, int s, float scale, con
 // D[i] = sum over d_h channels of dO[i, :] * O[i, :], i < MH (rows of d_h).
 hipError_t launch_rowdot(const void *dO, const void *O, int MH, int d_h, float *D,
                          hipStream_t stream);
-// dKR [M, dR] (bf16) = sum over heads of dKRh [M, H, dR].
-hipError_t launch_head_sum(const float *dKRh, int M, int H, int dR, void *dKR, hipStream_t stream);
+// dKR [M, dR] (storage dtype) = sum over heads of dKRh [M, H, dR].
+hipError_t launch_head_sum(int dtype, const float *dKRh, int M, int H, int dR, void *dKR,
+                           hipStream_t stream);
 // Reverse group scan and gate backward from dC' [B*T, R] (fp32) and the
 // forward's cg: da (fp32 and bf16), dc's direct term (fp32), c (bf16).
 // dPpart [B, ceil(T/s), R] receives each sequence's position-branch
 // gradient, and dPtab [rows, R] = their sum over the sequences in order
 // (rows past ceil(T/s) are zero).
-hipError_t launch_scan_gate_bwd(const float *dCp, const float *cg, const void *b_hc,
+hipError_t launch_scan_gate_bwd(int dtype, const float *dCp, const float *cg, const void *b_hc,
                                 const float *table, int B, int T, int R, int s, float *da32,
                                 void *dab, float *dc32, void *cb, float *dPpart, int rows,
                                 float *dPtab, hipStream_t stream);
@@ -220,5 +222,24 @@ bool tn_big_supported(int N1, int N2);
 hipError_t launch_tn_big(const void *A, int lda, const void *Bm, int ldb, int M, int N1, int N2,
                          int mchunk, int splits, float *out, int ldo, float *part,
                          hipStream_t stream);
+
+// ---- backward of the per-head parallel form with fp32 storage (backward_f32.hip) ----
+
+// Attention backward from the fp32 forward's q, QR, KV, KR, lse (log2
+// units) and D = rowsum(dO * O): every frame's dK | dV into dKV [B*T,
+// 2*H*d_h], per-head dK^R into dKRh [B*T, H, dR], dQ [B*T, H*d_h] (row
+// stride ldq) and dQR [B*T, H, dR], all fp32.  d_h = 64 (dR = 32) or 128 (64).
+hipError_t launch_attn_bwd_f32(int B, int T, int H, int d_h, int s, float scale, const float *q,
+                               const float *QR, const float *KV, const float *KR, const float *dO,
+                               const float *lse, const float *D, float *dKV, float *dKRh,
+                               float *dQ, int ldq, float *dQR, hipStream_t stream);
+// D[i] = sum over d_h channels of dO[i, :] * O[i, :] (fp32), i < MH.
+hipError_t launch_rowdot_f32(const float *dO, const float *O, int MH, int d_h, float *D,
+                             hipStream_t stream);
+// C[m, n] (row stride ldc) = C0[m, n] (row stride ldc0; C0 may be C, or
+// null for zero) + sum over k < K in order of A[m sam + k sak] B[k sbk + n sbn], fp32.
+hipError_t launch_gemm_f32s(const float *A, size_t sam, size_t sak, const float *Bm, size_t sbk,
+                            size_t sbn, int M, int N, int K, const float *C0, size_t ldc0,
+                            float *C, size_t ldc, hipStream_t stream);
 
 }  // namespace mtla

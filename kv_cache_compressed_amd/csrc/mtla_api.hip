@@ -601,10 +601,73 @@ mtla_status prefill_unabsorbed_impl(const mtla_dims *dims, const mtla_unabsorbed
            "per-head strided attention");
   else
     LAUNCH(mtla::launch_heads_attention_f32(B, T, dims->H, dims->d_h, dims->s, eff_scale(dims), q,
-                                            QR, KV, KR, O, s, ev0(events), ev1(events)),
+                                            QR, KV, KR, O, nullptr, s, ev0(events), ev1(events)),
            "per-head strided attention (fp32)");
   LAUNCH(mtla::launch_out_proj(dims->dtype, O, M, HD, w->W_O, dims->d, Y, nullptr, nullptr, s),
          "output projection");
+  return ok();
+}
+
+// The fp32 backward after the shared forward projections and group scan
+// (csrc/backward_f32.hip): the forward attention with its log2-sum-exp,
+// then the chain rule of the bf16 path with strided fp32 products in place
+// of the transposes and split products.
+mtla_status backward_f32_rest(const mtla_dims *dims, const mtla_unabsorbed_weights *w,
+                              const void *W_hc, const void *X, const void *QR, const void *KR,
+                              int B, int T, const void *dY, void *dX, void *dQR, void *dKR,
+                              const mtla_unabsorbed_grads *gr, const BwdWs &ws, char *base,
+                              hipStream_t s) {
+  auto F = [&](size_t off) { return (float *)(base + off); };
+  const int M = B * T, H = dims->H, dh = dims->d_h, HD = H * dh, r = dims->r, d = dims->d;
+  const float scale = eff_scale(dims);
+  const float *Xf = (const float *)X, *dYf = (const float *)dY;
+  const float *WQ = (const float *)w->W_Q, *WK = (const float *)w->W_K, *WV = (const float *)w->W_V;
+  const float *WO = (const float *)w->W_O, *Wdkv = (const float *)w->W_dkv;
+  const float *Whc = (const float *)W_hc;
+  float *q = F(ws.f.q), *KV = F(ws.f.KV), *O = F(ws.f.O), *Cp = F(ws.f.Cp), *cg = F(ws.f.cg);
+  float *lse = F(ws.lse), *dO = F(ws.dO), *D = F(ws.D), *dKV = F(ws.dKV), *dKRh = F(ws.dKRh);
+  float *dCp = F(ws.dCp), *da = F(ws.da32), *dc32 = F(ws.dc32);
+  // [dQ | dc] side by side at row stride HD + r, as in the bf16 path.
+  const int ldc2 = HD + r;
+  float *dQ = F(ws.dQc), *dc = dQ + HD;
+  float *dXf = (float *)dX;
+  LAUNCH(mtla::launch_heads_attention_f32(B, T, H, dh, dims->s, scale, q, QR, KV, KR, O, lse, s),
+         "forward attention (fp32)");
+  // output map: dO = dY W_O (W_O [d, HD])
+  LAUNCH(mtla::launch_gemm_f32s(dYf, d, 1, WO, HD, 1, M, HD, d, nullptr, 0, dO, HD, s), "dO");
+  LAUNCH(mtla::launch_rowdot_f32(dO, O, M * H, dh, D, s), "rowsum dO * O");
+  LAUNCH(mtla::launch_attn_bwd_f32(B, T, H, dh, dims->s, scale, q, (const float *)QR, KV,
+                                   (const float *)KR, dO, lse, D, dKV, dKRh, dQ, ldc2,
+                                   (float *)dQR, s),
+         "attention backward (fp32)");
+  LAUNCH(mtla::launch_head_sum(dims->dtype, dKRh, M, H, dims->d_hR, dKR, s), "dK^R over heads");
+  // key and value maps: dC' = dK W_K + dV W_V (W_K, W_V [HD, r])
+  LAUNCH(mtla::launch_gemm_f32s(dKV, 2 * HD, 1, WK, r, 1, M, r, HD, nullptr, 0, dCp, r, s), "dC' (K)");
+  LAUNCH(mtla::launch_gemm_f32s(dKV + HD, 2 * HD, 1, WV, r, 1, M, r, HD, dCp, r, dCp, r, s),
+         "dC' (V)");
+  // group sums and gate
+  int *rctr = (int *)(base + ws.red_ctr);
+  LAUNCH(mtla::launch_zero_i32(rctr, ws.nctr, s), "clear the reduction counters");
+  LAUNCH(mtla::launch_scan_gate_bwd(dims->dtype, dCp, cg, w->b_hc, w->gate_pos, B, T, r, dims->s,
+                                    da, base + ws.dab, dc32, base + ws.cb, F(ws.dPpart),
+                                    w->gate_pos_rows, gr->dgate_pos, s),
+         "group scan and gate backward");
+  LAUNCH(mtla::launch_colsum(da, M, r, F(ws.red_part), rctr, gr->db_hc, s), "db");
+  // dc = dU w + W_hc^T da (W_hc [r, r])
+  LAUNCH(mtla::launch_gemm_f32s(da, r, 1, Whc, r, 1, M, r, r, dc32, r, dc, ldc2, s), "dc");
+  // inputs: dX = dQ W_Q + dc W_dkv (W_Q [HD, d], W_dkv [r, d])
+  LAUNCH(mtla::launch_gemm_f32s(dQ, ldc2, 1, WQ, d, 1, M, d, HD, nullptr, 0, dXf, d, s), "dX (Q)");
+  LAUNCH(mtla::launch_gemm_f32s(dc, ldc2, 1, Wdkv, d, 1, M, d, r, dXf, d, dXf, d, s), "dX (latent)");
+  // weight gradients: A^T B over the frames (A read along its rows)
+  LAUNCH(mtla::launch_gemm_f32s(dYf, 1, d, O, HD, 1, d, HD, M, nullptr, 0, gr->dW_O, HD, s), "dW_O");
+  LAUNCH(mtla::launch_gemm_f32s(dQ, 1, ldc2, Xf, d, 1, HD, d, M, nullptr, 0, gr->dW_Q, d, s), "dW_Q");
+  LAUNCH(mtla::launch_gemm_f32s(dKV, 1, 2 * HD, Cp, r, 1, HD, r, M, nullptr, 0, gr->dW_K, r, s),
+         "dW_K");
+  LAUNCH(mtla::launch_gemm_f32s(dKV + HD, 1, 2 * HD, Cp, r, 1, HD, r, M, nullptr, 0, gr->dW_V, r, s),
+         "dW_V");
+  LAUNCH(mtla::launch_gemm_f32s(da, 1, r, cg, 2 * r, 1, r, r, M, nullptr, 0, gr->dW_hc, r, s), "dW_hc");
+  LAUNCH(mtla::launch_gemm_f32s(dc, 1, ldc2, Xf, d, 1, r, d, M, nullptr, 0, gr->dW_dkv, d, s),
+         "dW_dkv");
   return ok();
 }
 
@@ -647,8 +710,10 @@ mtla_status prefill_unabsorbed_backward_impl(
   if ((int64_t)B * T * dims->H * dims->d_h > 0x7fffffffLL / 4 ||
       (int64_t)B * T * dims->d > 0x7fffffffLL / 4)
     return fail(MTLA_ERR_UNSUPPORTED, "B*T too large");
-  if (!mtla::attn_bwd_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR))
-    return fail(MTLA_ERR_UNSUPPORTED, "backward needs bf16 storage and (d_h, d_hR) = (64, 32) or (128, 64)");
+  const bool f32 = dims->dtype == MTLA_F32;
+  if (!(f32 ? mtla::heads_attention_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR)
+            : mtla::attn_bwd_supported(dims->dtype, dims->H, dims->d_h, dims->d_hR)))
+    return fail(MTLA_ERR_UNSUPPORTED, "backward needs (d_h, d_hR) = (64, 32) or (128, 64)");
   if ((T - 1) / dims->s >= w->gate_pos_rows)
     return fail(MTLA_ERR_CAPACITY, "slot %d >= gate_pos_rows %d", (T - 1) / dims->s, w->gate_pos_rows);
   const BwdWs ws = bwd_ws(dims, B, T);
@@ -670,6 +735,8 @@ mtla_status prefill_unabsorbed_backward_impl(
          "forward group scan");
   LAUNCH(mtla::launch_gemm_store2(dt, Cp, r, w->W_K, w->W_V, HD, r, M, 2 * HD, r, KV, 2 * HD, s),
          "forward key and value projection");
+  if (f32)
+    return backward_f32_rest(dims, w, W_hc, X, QR, KR, B, T, dY, dX, dQR, dKR, gr, ws, base, s);
   LAUNCH(mtla::launch_heads_attention(B, T, H, dims->d_h, dims->s, scale, q, QR, KV, KR, O, lse, s),
          "forward attention");
   // transposed weights for the products against them
@@ -692,7 +759,7 @@ mtla_status prefill_unabsorbed_backward_impl(
   LAUNCH(mtla::launch_attn_bwd(B, T, H, dims->d_h, dims->s, scale, q, QR, KV, KR, P(ws.dO), lse, F(ws.D),
                                F(ws.dKVc), F(ws.dKRc), P(ws.dKV), F(ws.dKRh), dQ, dQR, ldc2, s),
          "attention backward");
-  LAUNCH(mtla::launch_head_sum(F(ws.dKRh), M, H, dims->d_hR, dKR, s), "dK^R over heads");
+  LAUNCH(mtla::launch_head_sum(dt, F(ws.dKRh), M, H, dims->d_hR, dKR, s), "dK^R over heads");
   // key and value maps
   LAUNCH(mtla::launch_gemm_f32(dt, P(ws.dKV), 2 * HD, P(ws.WKVt), 2 * HD, M, r, 2 * HD, F(ws.dCp), r,
                                false, s),
@@ -701,7 +768,7 @@ mtla_status prefill_unabsorbed_backward_impl(
   int *rctr = (int *)P(ws.red_ctr);
   float *rpart = F(ws.red_part);
   LAUNCH(mtla::launch_zero_i32(rctr, ws.nctr, s), "clear the reduction counters");
-  LAUNCH(mtla::launch_scan_gate_bwd(F(ws.dCp), cg, w->b_hc, w->gate_pos, B, T, r, dims->s,
+  LAUNCH(mtla::launch_scan_gate_bwd(dt, F(ws.dCp), cg, w->b_hc, w->gate_pos, B, T, r, dims->s,
                                     F(ws.da32), P(ws.dab), F(ws.dc32), P(ws.cb), F(ws.dPpart),
                                     w->gate_pos_rows, gr->dgate_pos, s),
          "group scan and gate backward");

@@ -12,11 +12,12 @@ from gpu_util import TOL, dev, host, needs_gpu, relerr, say
 pytestmark = pytest.mark.gpu
 
 
-def _layer(dims, seed, pe_rows):
-    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16
-    w = synth.make_weights(dims, seed, "bf16", pe_rows=pe_rows)
+def _layer(dims, seed, pe_rows, storage="bf16"):
+    from kv_cache_compressed_amd import MTLALayer, MTLA_BF16, MTLA_F32
+    w = synth.make_weights(dims, seed, storage, pe_rows=pe_rows)
     W = om.with_position_table(w, pe_rows)
-    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)}, MTLA_BF16)
+    L = MTLALayer.from_arrays(dims, {**w, **synth.head_maps(w)},
+                              MTLA_F32 if storage == "f32" else MTLA_BF16)
     return w, W, L
 
 
@@ -30,21 +31,21 @@ def _oracle_abi(gr, dims):
                 dW_O=np.transpose(gr["dW_O"], (2, 0, 1)).reshape(d, H * dh))
 
 
-def _check(dims, B, T, seed, T0=None, rows=None):
+def _check(dims, B, T, seed, T0=None, rows=None, storage="bf16"):
     """Backward at [B, T]; dY is nonzero only on sequences `rows` and frames
     < T0 (defaults: all), so the oracle runs on those prefixes only (frames
     before T0 do not depend on later ones) and the rest must be exact zeros."""
     T0 = T if T0 is None else T0
     rows = list(range(B)) if rows is None else rows
     ms = om.n_slots(T, dims.s) + 1
-    w, W, L = _layer(dims, seed, ms)
-    seq = synth.make_sequence(dims, w, B, T, seed + 1, "bf16")
+    w, W, L = _layer(dims, seed, ms, storage)
+    seq = synth.make_sequence(dims, w, B, T, seed + 1, storage)
     rng = np.random.default_rng(seed + 2)
     dY = np.zeros((B, T, dims.d))
     for b in rows:
-        dY[b, :T0] = synth.round_to(rng.normal(size=(T0, dims.d)), "bf16")
-    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
-    dX, dQR, dKR, grads = L.backward_unabsorbed(X, QR, KR, dev(dY, "bf16"))
+        dY[b, :T0] = synth.round_to(rng.normal(size=(T0, dims.d)), storage)
+    X, QR, KR = dev(seq["X"], storage), dev(seq["QR"], storage), dev(seq["KR"], storage)
+    dX, dQR, dKR, grads = L.backward_unabsorbed(X, QR, KR, dev(dY, storage))
     torch.cuda.synchronize()
     gX, gQR, gKR = host(dX), host(dQR), host(dKR)
     ref_w = None
@@ -55,7 +56,7 @@ def _check(dims, B, T, seed, T0=None, rows=None):
         for name, got in (("dX", gX[b, :T0]), ("dQR", gQR[b, :T0]), ("dKR", gKR[b, :T0])):
             e = relerr(got, gr[name])
             worst = max(worst, e)
-            assert e < TOL["bf16"], (b, name, e)
+            assert e < TOL[storage], (b, name, e)
         ab = _oracle_abi(gr, dims)
         ref_w = ab if ref_w is None else {k: ref_w[k] + ab[k] for k in ref_w}
     # frames and sequences without a loss gradient get exactly zero
@@ -65,7 +66,7 @@ def _check(dims, B, T, seed, T0=None, rows=None):
     for k, ref in ref_w.items():
         e = relerr(host(grads[k]), ref)
         worst = max(worst, e)
-        assert e < TOL["bf16"], (k, e)
+        assert e < TOL[storage], (k, e)
     say(f"  worst relerr {worst:.3g}")
 
 
@@ -91,6 +92,18 @@ def test_backward_llm_head_width(s, T, H, B):
     _check(dims, B, T, 9600 + 7 * s + T + H)
 
 
+@pytest.mark.parametrize("d_h,r,dR", [(64, 256, 32), (128, 512, 64)])
+@pytest.mark.parametrize("s,T,H,B", [(2, 1, 4, 1), (2, 130, 4, 2), (3, 257, 2, 1), (1, 64, 2, 2),
+                                       (80, 100, 2, 1), (5, 96, 3, 2)])
+def test_backward_fp32(s, T, H, B, d_h, r, dR):
+    """The backward with fp32 storage at both head widths, every input and
+    weight gradient against the oracle at 1e-4."""
+    needs_gpu()
+    dims = Dims(d=256, H=H, d_h=d_h, r=r, d_hR=dR, s=s)
+    say("backward per-head fp32", d_h, s, T, H, B)
+    _check(dims, B, T, 9900 + 7 * s + T + H + d_h, storage="f32")
+
+
 def test_backward_full_size_prefix():
     """The benchmark's backward launch (B=16, T=4096, s=2) with the loss on
     the first 320 frames of two sequences: those gradients against the
@@ -112,8 +125,9 @@ def test_backward_llm_head_width_full_size_prefix():
     _check(dims, 8, 4096, 9650, T0=256, rows=[0, 7])
 
 
+@pytest.mark.parametrize("storage", ["bf16", "f32"])
 @pytest.mark.parametrize("d_h,r,dR", [(64, 256, 32), (128, 512, 64)])
-def test_backward_is_deterministic(d_h, r, dR):
+def test_backward_is_deterministic(d_h, r, dR, storage):
     """Two calls on the same inputs give the same bits in every output:
     the input gradients and every reduction across workgroups (weight
     gradients, bias and position-table gradients) add their partials in a
@@ -122,17 +136,17 @@ def test_backward_is_deterministic(d_h, r, dR):
     dims = Dims(d=512, H=4, d_h=d_h, r=r, d_hR=dR, s=3)
     B, T = 2, 700
     ms = om.n_slots(T, dims.s) + 1
-    w, W, L = _layer(dims, 9700 + d_h, ms)
-    seq = synth.make_sequence(dims, w, B, T, 9701, "bf16")
+    w, W, L = _layer(dims, 9700 + d_h, ms, storage)
+    seq = synth.make_sequence(dims, w, B, T, 9701, storage)
     rng = np.random.default_rng(9702)
-    dY = dev(synth.round_to(rng.normal(size=(B, T, dims.d)), "bf16"), "bf16")
-    X, QR, KR = dev(seq["X"], "bf16"), dev(seq["QR"], "bf16"), dev(seq["KR"], "bf16")
+    dY = dev(synth.round_to(rng.normal(size=(B, T, dims.d)), storage), storage)
+    X, QR, KR = dev(seq["X"], storage), dev(seq["QR"], storage), dev(seq["KR"], storage)
     outs = []
     for _ in range(2):
         dX, dQR, dKR, grads = L.backward_unabsorbed(X, QR, KR, dY)
         outs.append([dX.clone(), dQR.clone(), dKR.clone()] + [grads[k].clone() for k in sorted(grads)])
     torch.cuda.synchronize()
-    say("backward determinism", d_h)
+    say("backward determinism", d_h, storage)
     names = ["dX", "dQR", "dKR"] + sorted(grads)
     for n, a, b in zip(names, outs[0], outs[1]):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
