@@ -227,3 +227,69 @@ def test_rope_inputs_reject_before_launch():
     assert lib.mtla_rope_inputs(*args(10000.0, M=0)) == L.MTLA_ERR_ARG
     assert lib.mtla_rope_inputs(*args(10000.0, ws_bytes=16)) == L.MTLA_ERR_ARG
     assert K.mtla_workspace_bytes(d, L.OP_ROPE, 4, 1) >= 4 * 9 * 32 * 4
+
+
+def _uw(rows=1024, W_Q=FAKE):
+    return L.UnabsorbedWeights(FAKE, FAKE, FAKE, FAKE, rows, W_Q, FAKE, FAKE, FAKE)
+
+
+def _unabsorbed(dims, w, B=2, T=64, ws_bytes=1 << 30, X=FAKE):
+    return K.load_library().mtla_prefill_unabsorbed(
+        ctypes.byref(dims), ctypes.byref(w), X, FAKE, FAKE, B, T, FAKE, None, None, FAKE, ws_bytes,
+        None)
+
+
+def _unabsorbed_bwd(dims, w, B=2, T=64, ws_bytes=1 << 30, X=FAKE, W_hc=FAKE, grads=True):
+    g = L.UnabsorbedGrads(*([FAKE] * 8))
+    return K.load_library().mtla_prefill_unabsorbed_backward(
+        ctypes.byref(dims), ctypes.byref(w), W_hc, X, FAKE, FAKE, B, T, FAKE, FAKE, FAKE, FAKE,
+        ctypes.byref(g) if grads else None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("dtype", [L.MTLA_F32, L.MTLA_BF16])
+@pytest.mark.parametrize("call", ["forward", "backward"])
+@pytest.mark.parametrize("case,expect", [
+    ("head_width_32", L.MTLA_ERR_UNSUPPORTED),
+    ("wide_head_narrow_rope", L.MTLA_ERR_UNSUPPORTED),
+    ("bad_dtype", L.MTLA_ERR_ARG),
+    ("null_W_Q", L.MTLA_ERR_ARG),
+    ("misaligned_X", L.MTLA_ERR_ARG),
+    ("zero_frames", L.MTLA_ERR_ARG),
+    ("capacity_gate_table", L.MTLA_ERR_CAPACITY),
+    ("small_workspace", L.MTLA_ERR_ARG),
+])
+def test_per_head_form_rejects(case, expect, call, dtype):
+    """The per-head forward and its backward take both storage types at
+    (d_h, d_hR) = (64, 32) and (128, 64); every bad argument fails validation
+    (the last case, a one-byte workspace, is the final check before any
+    launch: reaching it shows the shape and dtype were accepted)."""
+    kw, dkw, w = {}, dict(dtype=dtype), _uw()
+    if case == "head_width_32":
+        dkw.update(d_h=32)
+    elif case == "wide_head_narrow_rope":
+        dkw.update(d_h=128)
+    elif case == "bad_dtype":
+        dkw.update(dtype=7)
+    elif case == "null_W_Q":
+        w = _uw(W_Q=None)
+    elif case == "misaligned_X":
+        kw["X"] = FAKE + 2
+    elif case == "zero_frames":
+        kw["T"] = 0
+    elif case == "capacity_gate_table":
+        w = _uw(rows=8)   # T = 64 frames at s = 2 need slot 31
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 1
+    dims = _dims(**dkw)
+    st = (_unabsorbed if call == "forward" else _unabsorbed_bwd)(dims, w, **kw)
+    detail = K.load_library().mtla_last_error_detail().decode()
+    assert st == expect, (case, st, detail)
+    if case == "small_workspace":
+        assert "workspace" in detail, detail
+
+
+@pytest.mark.parametrize("case", ["null_grads", "null_W_hc"])
+def test_per_head_backward_rejects_missing_buffers(case):
+    dims = _dims(dtype=L.MTLA_F32)
+    kw = {"grads": False} if case == "null_grads" else {"W_hc": None}
+    assert _unabsorbed_bwd(dims, _uw(), **kw) == L.MTLA_ERR_ARG
